@@ -1,0 +1,388 @@
+"""Pins for the fp64 CPU oracle (CPU only, no GPU).
+
+Every check here compares the oracle with something other than itself:
+literal complex arithmetic in the un-rotated frame, special cases that reduce
+to textbook recurrences, a hand-set parity sequence, closed forms, the
+convergence order of the discretisation, linearity in the MIMO ranks and the
+quadratic "1-semiseparable x 2-band" matrix form.  The checks are chosen so
+that a plausible mistake in the oracle (a dropped factor, a wrong sign, an
+off-by-one angle, a transposed operand) fails at least one of them; the
+``test_mutants_are_caught`` test plants such mistakes in the oracle (compiled
+variants, CPU only) and shows that each one is caught.
+
+Sources (by page and section):
+  linkstar.cloud/article/869 -- "第一刀：指数梯形离散化" (alpha, beta, gamma,
+  second-order accuracy, the 1-semiseparable x 2-band form), "第二刀：复值状态
+  空间" (complex state, rotation R(theta), the RoPE form, parity task),
+  "第三刀：多输入多输出" (rank-R products).
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from state_space_sequence_03_amd.inputs import numpy_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# independent references (numpy, written from the pages' statements)
+# --------------------------------------------------------------------------
+
+def complex_literal(inp):
+    """Un-rotated complex recurrence, complex128.
+
+    The continuous system h' = (A + i theta) h + B x, discretised with the
+    exponential-trapezoidal rule (linkstar §第一刀 applied to the complex
+    system of §第二刀): the left endpoint term carries the full complex
+    transition exp(dt (A + i theta)).  Pair (2k, 2k+1) of B is b_k = Re + i Im;
+    C enters as c_k = C[2k] - i C[2k+1] and y = Re(sum_k c_k z_k) (the minus
+    sign on C that makes the real and complex systems agree, §第二刀)."""
+    x, Bm, Cm = inp["x"].astype(np.float64), inp["B"].astype(np.float64), inp["C"].astype(np.float64)
+    dt, A, lam, th = (inp[k].astype(np.float64) for k in ("dt", "A", "lam", "theta"))
+    b, L, H, R, P = x.shape
+    N = Bm.shape[-1]
+    K = N // 2
+    bc = Bm[..., 0::2] + 1j * Bm[..., 1::2]          # (b,L,H,R,K)
+    cc = Cm[..., 0::2] - 1j * Cm[..., 1::2]
+    z = np.zeros((b, H, K, P), np.complex128)
+    if inp.get("h0") is not None:
+        h0 = inp["h0"].astype(np.float64)
+        z = h0[:, :, 0::2, :] + 1j * h0[:, :, 1::2, :]
+    bprev = np.zeros((b, H, R, K), np.complex128)
+    xprev = np.zeros((b, H, R, P))
+    if inp.get("prev_B") is not None:
+        pb = inp["prev_B"].astype(np.float64)
+        bprev = pb[..., 0::2] + 1j * pb[..., 1::2]
+        xprev = inp["prev_x"].astype(np.float64)
+    y = np.zeros((b, L, H, R, P))
+    for t in range(L):
+        a = np.exp(dt[:, t, :, None] * (A[:, t, :, None] + 1j * th[:, t]))      # (b,H,K)
+        u_prev = np.einsum("bhrk,bhrp->bhkp", bprev, xprev)
+        u_cur = np.einsum("bhrk,bhrp->bhkp", bc[:, t], x[:, t])
+        e = ((1 - lam[:, t]) * dt[:, t])[:, :, None, None]
+        g = (lam[:, t] * dt[:, t])[:, :, None, None]
+        z = a[..., None] * z + e * a[..., None] * u_prev + g * u_cur
+        y[:, t] = np.real(np.einsum("bhrk,bhkp->bhrp", cc[:, t], z))
+        bprev, xprev = bc[:, t], x[:, t]
+    hf = np.zeros((b, H, N, P))
+    hf[:, :, 0::2] = z.real
+    hf[:, :, 1::2] = z.imag
+    return y, hf
+
+
+def rotate_by(v, ang):
+    """Multiply pair (2k, 2k+1) of the last axis, read as a complex number, by exp(i*ang[k])."""
+    c = (v[..., 0::2] + 1j * v[..., 1::2]) * np.exp(1j * ang)
+    out = np.empty_like(v, dtype=np.float64)
+    out[..., 0::2] = c.real
+    out[..., 1::2] = c.imag
+    return out
+
+
+def quadratic_form(inp):
+    """The parallel form: L = (1-semiseparable matrix) x (2-band matrix) (linkstar §第一刀).
+
+    Index 0 stands for the token before the sequence (prev_B, prev_x) and for
+    the initial state; indices 1..L are the tokens.  SS[t,u] = prod_{u<v<=t}
+    alpha_v; Band[u,u] = gamma_u, Band[u,u-1] = beta_u (Band[0,0] = 0 because
+    the token before the start is already inside h0).  With the RoPE form
+    (§第二刀) B~_s = R(-phi_s) B_s, C~_t = R(-phi_t) C_t, phi_0 = 0:
+        h~_t = SS[t,0] h0 + sum_s (SS Band)[t,s] B~_s x_s^T,  y_t = C~_t^T h~_t.
+    """
+    x, Bm, Cm = inp["x"].astype(np.float64), inp["B"].astype(np.float64), inp["C"].astype(np.float64)
+    dt, A, lam, th = (inp[k].astype(np.float64) for k in ("dt", "A", "lam", "theta"))
+    b, L, H, R, P = x.shape
+    N = Bm.shape[-1]
+    y = np.zeros((b, L, H, R, P))
+    hf = np.zeros((b, H, N, P))
+    for bi in range(b):
+        for hi in range(H):
+            d, a_, l_ = dt[bi, :, hi], A[bi, :, hi], lam[bi, :, hi]
+            alpha = np.concatenate([[1.0], np.exp(d * a_)])            # alpha_0 unused
+            beta = np.concatenate([[0.0], (1 - l_) * d * np.exp(d * a_)])
+            gamma = np.concatenate([[0.0], l_ * d])
+            n = L + 1
+            SS = np.zeros((n, n))
+            for t in range(n):
+                for u in range(t + 1):
+                    SS[t, u] = np.prod(alpha[u + 1:t + 1])
+            Band = np.diag(gamma)
+            for u in range(1, n):
+                Band[u, u - 1] = beta[u]
+            Lmat = SS @ Band
+            phi = np.concatenate([np.zeros((1, N // 2)), np.cumsum(d[:, None] * th[bi, :, hi], axis=0)])
+            Bt = np.zeros((n, R, N))
+            Ct = np.zeros((n, R, N))
+            X = np.zeros((n, R, P))
+            if inp.get("prev_B") is not None:
+                Bt[0] = inp["prev_B"][bi, hi]
+                X[0] = inp["prev_x"][bi, hi]
+            Bt[1:] = rotate_by(Bm[bi, :, hi], -phi[1:, None, :])
+            Ct[1:] = rotate_by(Cm[bi, :, hi], -phi[1:, None, :])
+            X[1:] = x[bi, :, hi]
+            h0 = inp["h0"][bi, hi].astype(np.float64) if inp.get("h0") is not None else np.zeros((N, P))
+            # scores over virtual rows (token, rank): G[(t,r),(s,r')] = C~_t[r] . B~_s[r']
+            G = np.einsum("trn,sqn->trsq", Ct, Bt)
+            Y = np.einsum("ts,trsq,sqp->trp", Lmat, G, X) + SS[:, 0, None, None] * np.einsum("trn,np->trp", Ct, h0)
+            y[bi, :, hi] = Y[1:]
+            hL = SS[L, 0] * h0 + np.einsum("s,sqn,sqp->np", Lmat[L], Bt, X)
+            hf[bi, hi] = rotate_by(hL.T, phi[L]).T
+    return y, hf
+
+
+def real_recurrence(inp, euler=False):
+    """Real-valued recurrence with no rotation: the theta = 0 case of §第二刀.
+    With euler=True: Mamba-2's exponential-Euler update h = e^{dt A} h + dt B x^T
+    (linkstar, section "先搞清楚Mamba到底是什么")."""
+    x, Bm, Cm = inp["x"].astype(np.float64), inp["B"].astype(np.float64), inp["C"].astype(np.float64)
+    dt, A, lam = (inp[k].astype(np.float64) for k in ("dt", "A", "lam"))
+    b, L, H, R, P = x.shape
+    N = Bm.shape[-1]
+    h = np.zeros((b, H, N, P)) if inp.get("h0") is None else inp["h0"].astype(np.float64).copy()
+    up = np.zeros((b, H, N, P))
+    if inp.get("prev_B") is not None:
+        up = np.einsum("bhrn,bhrp->bhnp", inp["prev_B"].astype(np.float64), inp["prev_x"].astype(np.float64))
+    y = np.zeros_like(x, dtype=np.float64)
+    for t in range(L):
+        al = np.exp(dt[:, t] * A[:, t])[:, :, None, None]
+        uc = np.einsum("bhrn,bhrp->bhnp", Bm[:, t], x[:, t])
+        if euler:
+            h = al * h + dt[:, t][:, :, None, None] * uc
+        else:
+            be = ((1 - lam[:, t]) * dt[:, t])[:, :, None, None] * al
+            ga = (lam[:, t] * dt[:, t])[:, :, None, None]
+            h = al * h + be * up + ga * uc
+        up = uc
+        y[:, t] = np.einsum("bhrn,bhnp->bhrp", Cm[:, t], h)
+    return y, h
+
+
+def rel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def small(seed, b=2, L=23, H=2, P=3, N=6, R=2, h0=True, prev=True, **kw):
+    return numpy_inputs(b, L, H, P, N, R, seed=seed, with_h0=h0, with_prev=prev, **kw)
+
+
+def run(inp, mutant=0):
+    return oracle.forward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["lam"], inp["theta"],
+                          h0=inp.get("h0"), prev_B=inp.get("prev_B"), prev_x=inp.get("prev_x"),
+                          mutant=mutant)
+
+
+# --------------------------------------------------------------------------
+# the pins
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,R,N,h0,prev", [(1, 1, 2, False, False), (2, 2, 6, True, True),
+                                                (3, 4, 8, True, False), (4, 3, 4, False, True)])
+def test_matches_literal_complex(seed, R, N, h0, prev):
+    inp = small(seed, R=R, N=N, h0=h0, prev=prev)
+    y, hf = run(inp)
+    yc, hc = complex_literal(inp)
+    assert rel(y, yc) < 1e-12
+    assert rel(hf, hc) < 1e-12
+
+
+@pytest.mark.parametrize("seed,R", [(5, 1), (6, 3)])
+def test_matches_quadratic_semiseparable_form(seed, R):
+    inp = small(seed, L=17, R=R, N=4)
+    y, hf = run(inp)
+    yq, hq = quadratic_form(inp)
+    assert rel(y, yq) < 1e-12
+    assert rel(hf, hq) < 1e-12
+
+
+def test_lambda_one_is_exponential_euler():
+    """lam = 1 gives beta = 0, gamma = dt: Mamba-2's exponential-Euler update."""
+    inp = small(7, R=2, N=4)
+    inp["lam"][:] = 1.0
+    inp["theta"][:] = 0.0
+    y, hf = run(inp)
+    ye, he = real_recurrence(inp, euler=True)
+    assert rel(y, ye) < 1e-13 and rel(hf, he) < 1e-13
+    # with rotations on, lam = 1 still matches the quadratic form with a diagonal band
+    inp2 = small(8, R=2, N=4)
+    inp2["lam"][:] = 1.0
+    y2, h2 = run(inp2)
+    yq, hq = quadratic_form(inp2)
+    assert rel(y2, yq) < 1e-12 and rel(h2, hq) < 1e-12
+
+
+def test_theta_zero_is_real_case():
+    inp = small(9, R=3, N=6)
+    inp["theta"][:] = 0.0
+    y, hf = run(inp)
+    yr, hr = real_recurrence(inp)
+    assert rel(y, yr) < 1e-13 and rel(hf, hr) < 1e-13
+
+
+def load_parity():
+    with open(os.path.join(GOLDEN, "parity_bits.txt")) as f:
+        lines = [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+    bits = [int(c) for c in lines[0]]
+    expect = [float(v) for v in lines[1].split()]
+    return bits, expect
+
+
+def parity_inputs(bits):
+    L = len(bits)
+    z = lambda *s: np.zeros(s, np.float32)
+    inp = dict(x=z(1, L, 1, 1, 1), B=z(1, L, 1, 1, 2), C=z(1, L, 1, 1, 2),
+               dt=np.ones((1, L, 1), np.float32), A=z(1, L, 1), lam=np.full((1, L, 1), 0.5, np.float32),
+               theta=(np.pi * np.asarray(bits, np.float64)).reshape(1, L, 1, 1),
+               h0=np.array([1.0, 0.0]).reshape(1, 1, 2, 1))
+    inp["C"][..., 0] = 1.0
+    return inp
+
+
+def test_parity_golden():
+    bits, expect = load_parity()
+    # the fixture is self-consistent with its definition
+    assert expect == [(-1.0) ** (sum(bits[:t + 1]) % 2) for t in range(len(bits))]
+    y, hf = run(parity_inputs(bits))
+    assert np.max(np.abs(y[0, :, 0, 0, 0] - np.asarray(expect))) < 1e-12
+    # the final state points back along +-(1, 0)
+    assert abs(abs(hf[0, 0, 0, 0]) - 1.0) < 1e-12 and abs(hf[0, 0, 1, 0]) < 1e-12
+
+
+def test_scalar_closed_form():
+    """One active pair, theta = 0, P = R = 1, x = B = C = 1 on component 0, constant
+    dt, A, lam: h_1 = gamma, h_t = alpha h_{t-1} + beta + gamma, hence
+    h_t = (beta + gamma)(1 - alpha^{t-1})/(1 - alpha) + alpha^{t-1} gamma."""
+    L, d, a, l = 40, 0.3, -0.7, 0.35
+    z = lambda *s: np.zeros(s, np.float64)
+    inp = dict(x=np.ones((1, L, 1, 1, 1)), B=z(1, L, 1, 1, 2), C=z(1, L, 1, 1, 2),
+               dt=np.full((1, L, 1), d), A=np.full((1, L, 1), a), lam=np.full((1, L, 1), l),
+               theta=z(1, L, 1, 1))
+    inp["B"][..., 0] = 1.0
+    inp["C"][..., 0] = 1.0
+    y, hf = run(inp)
+    al = math.exp(d * a)
+    be, ga = (1 - l) * d * al, l * d
+    t = np.arange(1, L + 1)
+    expect = (be + ga) * (1 - al ** (t - 1)) / (1 - al) + al ** (t - 1) * ga
+    assert np.max(np.abs(y[0, :, 0, 0, 0] - expect)) < 1e-14
+    assert abs(hf[0, 0, 0, 0] - expect[-1]) < 1e-14
+
+
+def _ode_error(lam, n_steps, T=2.0, a=-0.8, w=3.0, h0=0.5):
+    """Global error at time T of the oracle on h' = a h + cos(w s), h(0) = h0."""
+    D = T / n_steps
+    s = D * np.arange(1, n_steps + 1)
+    z = lambda *sh: np.zeros(sh, np.float64)
+    inp = dict(x=np.cos(w * s).reshape(1, n_steps, 1, 1, 1), B=z(1, n_steps, 1, 1, 2),
+               C=z(1, n_steps, 1, 1, 2), dt=np.full((1, n_steps, 1), D), A=np.full((1, n_steps, 1), a),
+               lam=np.full((1, n_steps, 1), lam), theta=z(1, n_steps, 1, 1),
+               h0=np.array([h0, 0.0]).reshape(1, 1, 2, 1),
+               prev_B=np.array([1.0, 0.0]).reshape(1, 1, 1, 2), prev_x=np.ones((1, 1, 1, 1)))
+    inp["B"][..., 0] = 1.0
+    inp["C"][..., 0] = 1.0
+    y, _ = run(inp)
+    # exact solution: h(T) = e^{aT} h0 + int_0^T e^{a(T-u)} cos(w u) du
+    ex = math.exp(a * T) * h0 + (w * math.sin(w * T) - a * math.cos(w * T) + a * math.exp(a * T)) / (a * a + w * w)
+    return abs(y[0, -1, 0, 0, 0] - ex)
+
+
+def test_convergence_order():
+    """Second order at lam = 1/2, first order at lam = 1 (linkstar §第一刀)."""
+    r_half = [_ode_error(0.5, n) / _ode_error(0.5, 2 * n) for n in (64, 128, 256)]
+    r_one = [_ode_error(1.0, n) / _ode_error(1.0, 2 * n) for n in (64, 128, 256)]
+    assert all(3.8 < r < 4.2 for r in r_half), r_half
+    assert all(1.8 < r < 2.2 for r in r_one), r_one
+
+
+def test_mimo_superposition():
+    """The state is linear in the rank-R input: a rank-R run equals the sum of R
+    rank-1 runs that share the scalars (§第三刀)."""
+    inp = small(11, R=3, N=4, h0=False, prev=True)
+    y, hf = run(inp)
+    R = inp["x"].shape[3]
+    y_sum = np.zeros_like(y)
+    h_sum = np.zeros_like(hf)
+    for q in range(R):
+        for r in range(R):
+            one = dict(inp)
+            one["x"] = inp["x"][:, :, :, q:q + 1]
+            one["B"] = inp["B"][:, :, :, q:q + 1]
+            one["C"] = inp["C"][:, :, :, r:r + 1]
+            one["prev_x"] = inp["prev_x"][:, :, q:q + 1]
+            one["prev_B"] = inp["prev_B"][:, :, q:q + 1]
+            yo, ho = run(one)
+            y_sum[:, :, :, r] += yo[:, :, :, 0]
+            if r == 0:
+                h_sum += ho
+    assert rel(y, y_sum) < 1e-12 and rel(hf, h_sum) < 1e-12
+
+
+def test_rope_bc_matches_complex_phase():
+    inp = small(12, L=19, R=2, N=8)
+    rng = np.random.default_rng(3)
+    ang0 = rng.uniform(-3, 3, (2, 2, 4))
+    Br, Cr, af = oracle.rope_bc(inp["B"], inp["C"], inp["dt"], inp["theta"], ang0)
+    phi = ang0[:, None] + np.cumsum(inp["dt"][..., None].astype(np.float64) * inp["theta"], axis=1)
+    assert rel(Br, rotate_by(inp["B"].astype(np.float64), -phi[:, :, :, None, :])) < 1e-13
+    assert rel(Cr, rotate_by(inp["C"].astype(np.float64), -phi[:, :, :, None, :])) < 1e-13
+    assert rel(af, phi[:, -1]) < 1e-13
+
+
+def test_continuation_decode_after_forward():
+    """A forward over L tokens followed by k one-token calls (passing the last
+    token's raw B and x as the previous token) equals one forward over L + k."""
+    inp = small(13, L=20, R=2, N=6, prev=True)
+    y_all, h_all = run(inp)
+    L0 = 14
+    head = {k: (v[:, :L0] if k in ("x", "B", "C", "dt", "A", "lam", "theta") else v) for k, v in inp.items()}
+    y0, h = run(head)
+    assert rel(y0, y_all[:, :L0]) < 1e-13
+    pb, px = inp["B"][:, L0 - 1], inp["x"][:, L0 - 1]
+    for t in range(L0, 20):
+        h, yt = oracle.decode_step(h, inp["x"][:, t], inp["B"][:, t], inp["C"][:, t], inp["dt"][:, t],
+                                   inp["A"][:, t], inp["lam"][:, t], inp["theta"][:, t], pb, px)
+        assert rel(yt, y_all[:, t]) < 1e-12
+        pb, px = inp["B"][:, t], inp["x"][:, t]
+    assert rel(h, h_all) < 1e-12
+
+
+def test_empty_sequence_returns_h0():
+    inp = small(14, L=0, R=1, N=4, prev=False)
+    y, hf = run(inp)
+    assert y.shape[1] == 0 and np.array_equal(hf, inp["h0"].astype(np.float64))
+
+
+# --------------------------------------------------------------------------
+# planted mistakes (compiled oracle variants, CPU only)
+# --------------------------------------------------------------------------
+
+def pin_failures(mutant):
+    failed = []
+    checks = {
+        "complex": lambda: (lambda i: (lambda o, c: rel(o[0], c[0]) < 1e-10 and rel(o[1], c[1]) < 1e-10)(
+            run(i, mutant), complex_literal(i)))(small(21, R=2, N=6)),
+        "parity": lambda: (lambda bits_exp: float(np.max(np.abs(
+            run(parity_inputs(bits_exp[0]), mutant)[0][0, :, 0, 0, 0] - np.asarray(bits_exp[1])))) < 1e-10)(
+            load_parity()),
+    }
+    for name, fn in checks.items():
+        if not fn():
+            failed.append(name)
+    return failed
+
+
+@pytest.mark.parametrize("mutant", list(range(1, 10)))
+def test_mutants_are_caught(mutant):
+    assert pin_failures(mutant), f"planted mistake {mutant} was not caught"
+    # and the quadratic form, independent of the complex view, catches them too
+    inp = small(22, L=12, R=2, N=4)
+    y, hf = run(inp, mutant)
+    yq, hq = quadratic_form(inp)
+    assert rel(y, yq) > 1e-8 or rel(hf, hq) > 1e-8
+
+
+def test_unmutated_oracle_passes_the_mutant_screen():
+    assert pin_failures(0) == []
