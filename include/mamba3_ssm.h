@@ -1,0 +1,153 @@
+/*
+ * mamba3_ssm.h -- C ABI of the MI355X (gfx950) Mamba-3 SSM layer core.
+ *
+ * Three operations, all asynchronous on a caller-given HIP stream:
+ *
+ *   mamba3_ssm_chunked_fwd   whole-sequence forward (prefill / training
+ *                            forward) by the chunked parallel form;
+ *   mamba3_ssm_decode_step   one-token state update (generation);
+ *   mamba3_rope_bc           the cumulative-angle rotation of B and C.
+ *
+ * What they compute (pages cited by title and section):
+ *
+ *  - linkstar.cloud/article/869, "第一刀：指数梯形离散化": with
+ *    alpha_t = exp(dt_t A_t), beta_t = (1 - lam_t) dt_t alpha_t and
+ *    gamma_t = lam_t dt_t,
+ *        h_t = alpha_t h_{t-1} + beta_t B_{t-1} x_{t-1}^T + gamma_t B_t x_t^T;
+ *    the same section gives the parallel form (a 1-semiseparable decay matrix
+ *    times a 2-band matrix) that the chunked forward evaluates per chunk.
+ *  - same page, "第二刀：复值状态空间": the complex state is a real state whose
+ *    transition holds 2x2 rotations R(w) = [[cos w, -sin w], [sin w, cos w]]
+ *    with w = dt_t theta_t[k] on pair (2k, 2k+1); equivalently the rotations
+ *    move onto B and C as cumulative angles phi_t = sum_{s<=t} dt_s theta_s
+ *    (B~ = R(-phi) B, C~ = R(-phi) C: a data-dependent RoPE).
+ *  - same page, "第三刀：多输入多输出": B_t is N x R, x_t is P x R, the input
+ *    term is the rank-R product B_t x_t^T, and y_t = C_t^T h_t is R x P.
+ *  - yetianai.com/news/16273, "榨干硬件算力": chunks are computed in parallel
+ *    internally and pass the state from chunk to chunk in order.
+ *
+ * Notation per (batch b, head h): L tokens, P head dim, N state size (even,
+ * N/2 rotation pairs), R MIMO rank, Q chunk length in tokens.
+ *
+ * Layouts: row-major, contiguous, no strides.
+ *   x, y            (B, L, H, R, P)   io dtype
+ *   B, C            (B, L, H, R, N)   io dtype
+ *   dt, A, lam      (B, L, H)         fp32 (dt > 0, already post-softplus)
+ *   theta           (B, L, H, N/2)    fp32, one angle rate per pair
+ *   h0, h_final     (B, H, N, P)      fp32, un-rotated ("true") frame
+ *   prev_B          (B, H, R, N)      io dtype: raw B of the token before x[:,0]
+ *   prev_x          (B, H, R, P)      io dtype: x of that token
+ *   angle0/final    (B, H, N/2)       fp32
+ *   decode: x, y (B, H, R, P); B, C, prev_B (B, H, R, N); prev_x (B, H, R, P);
+ *           dt, A, lam (B, H); theta (B, H, N/2); state (B, H, N, P) fp32.
+ * Pair (2k, 2k+1) of B, C and of the state rows is (real, imaginary) of
+ * complex component k.
+ *
+ * Ownership: the caller owns every buffer (device memory unless stated).  The
+ * library allocates nothing and keeps no mutable global state, so calls are
+ * reentrant and may run on concurrent streams when their buffers are
+ * disjoint.  Alignment: x, B, C, y and the workspace of chunked_fwd, B, C,
+ * B_rot and C_rot of rope_bc, and the state of decode_step must be 16-byte
+ * aligned; every other pointer must be aligned to its element size.
+ *
+ * Errors: every entry point validates its arguments on the host and returns a
+ * status before any HIP call; nothing is launched on error.  M3_ERR_HIP
+ * reports a failed launch.  Device-side faults surface, as usual in HIP, at
+ * the caller's next synchronisation.
+ *
+ * Supported sizes: N in {16,32,64,128}; P in {16,32,64,128}; R in {1,2,4};
+ * Q in {16,32,64}; io dtype fp32 or bf16.  The chunked forward also needs
+ * Q*R <= 256 and its per-chunk tiles to fit in the 160 KiB of LDS of one
+ * compute unit (this excludes bf16 with N = P = 128 and Q*R = 256, and fp32
+ * io with Q*R = 256 unless N and P are small); M3_ERR_UNSUPPORTED otherwise.  batch, seqlen and nheads may be 0 (empty
+ * input: nothing is read; h_final receives h0, or zeros).
+ */
+#ifndef MAMBA3_SSM_H
+#define MAMBA3_SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA3_ABI_VERSION 1
+
+typedef enum {
+  M3_OK = 0,
+  M3_ERR_NULL = 1,        /* a required pointer is NULL, or only one of prev_B/prev_x is given */
+  M3_ERR_SHAPE = 2,       /* a negative size, or an odd dstate */
+  M3_ERR_UNSUPPORTED = 3, /* size outside the supported set listed above */
+  M3_ERR_ALIGN = 4,       /* a pointer breaks the alignment rule above */
+  M3_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than the queried size */
+  M3_ERR_HIP = 6          /* a kernel launch failed */
+} m3_status;
+
+typedef enum { M3_F32 = 0, M3_BF16 = 1 } m3_dtype;
+
+typedef struct {
+  int64_t batch;    /* B */
+  int64_t seqlen;   /* L (ignored by decode_step) */
+  int64_t nheads;   /* H */
+  int64_t headdim;  /* P */
+  int64_t dstate;   /* N, even */
+  int64_t rank;     /* R */
+  int64_t chunk;    /* Q tokens per chunk (chunked_fwd only) */
+  int32_t io_dtype; /* m3_dtype of x, B, C, y, prev_B, prev_x, B_rot, C_rot */
+  int32_t flags;    /* chunked_fwd: bits 0..15 = number of sequence segments
+                       walked in parallel per (b,h) (0 = chosen by the
+                       library); other bits must be 0.  Others: must be 0. */
+} m3_dims;
+
+/* Whole-sequence forward.
+ *   y_t = C_t^T h_t for every token, and h_final = h_L.
+ * h0: nullable, the state before x[:,0] (true frame); NULL means zero.
+ * prev_B, prev_x: nullable pair, the raw B and x of the token before x[:,0]
+ *   (its trapezoid term enters the first update); NULL means none.
+ * y: written (must not alias an input).  h_final: nullable; may alias h0.
+ * workspace: device scratch of at least
+ *   mamba3_ssm_chunked_fwd_workspace_size(d) bytes (may be NULL when that is 0);
+ *   its contents on entry do not matter.
+ * To continue a sequence, pass h_final as h0 and the last token's raw B and x
+ * as prev_B / prev_x. */
+m3_status mamba3_ssm_chunked_fwd(const m3_dims* d,
+                                 const void* x, const void* B, const void* C,
+                                 const float* dt, const float* A, const float* lam, const float* theta,
+                                 const float* h0, const void* prev_B, const void* prev_x,
+                                 void* y, float* h_final,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d);
+
+/* One-token update, in place on the fp32 true-frame state:
+ *   h <- alpha R(dt theta) [h + eps prev_B^T prev_x] + gamma B^T x,
+ *   y  = C^T h (new state),  eps = (1 - lam) dt.
+ * prev_B, prev_x: nullable pair (NULL: no previous token, e.g. the very first
+ * token of a sequence).  seqlen and chunk of d are ignored.  y must not alias
+ * any input. */
+m3_status mamba3_ssm_decode_step(const m3_dims* d, float* state,
+                                 const void* x, const void* B, const void* C,
+                                 const float* dt, const float* A, const float* lam, const float* theta,
+                                 const void* prev_B, const void* prev_x,
+                                 void* y, void* stream);
+
+/* Cumulative-angle rotation:
+ *   phi_t = angle0 + sum_{s<=t} dt_s theta_s (per pair), B_rot = R(-phi_t) B_t,
+ *   C_rot = R(-phi_t) C_t, angle_final = phi_L.
+ * angle0, angle_final: nullable.  B_rot / C_rot must not alias B / C.
+ * workspace: at least mamba3_rope_bc_workspace_size(d) bytes.  chunk of d is
+ * ignored. */
+m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C,
+                         const float* dt, const float* theta, const float* angle0,
+                         void* B_rot, void* C_rot, float* angle_final,
+                         void* workspace, size_t workspace_bytes, void* stream);
+size_t mamba3_rope_bc_workspace_size(const m3_dims* d);
+
+const char* mamba3_status_string(m3_status s);
+int mamba3_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA3_SSM_H */

@@ -6,14 +6,12 @@ package directory).  ``state_space_sequence_03_amd.ops`` is a thin ctypes
 binding with the same entry-point names; it marshals torch tensors (device
 memory and streams only) and raises if the library is missing.
 """
+import importlib
+
 __all__ = ["ops", "inputs"]
 
 
 def __getattr__(name):
-    if name == "ops":
-        from . import ops
-        return ops
-    if name == "inputs":
-        from . import inputs
-        return inputs
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

@@ -1,0 +1,180 @@
+// C ABI of the Mamba-3 SSM layer core: argument validation on the host (no
+// HIP call happens before every check has passed), workspace sizing and
+// dispatch to the gfx950 kernels.  The operations themselves are specified in
+// include/mamba3_ssm.h.
+#include "../../include/mamba3_ssm.h"
+
+#include <hip/hip_runtime.h>
+
+#include "m3_launch.hpp"
+
+namespace {
+
+bool in_set(int64_t v, std::initializer_list<int64_t> s) {
+  for (int64_t e : s)
+    if (v == e) return true;
+  return false;
+}
+
+bool aligned(const void* p, uintptr_t a = 16) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Pointers read or written with 16-byte vector accesses must be 16-byte
+// aligned; the others only need their element alignment.
+bool all_aligned(std::initializer_list<const void*> vec16, std::initializer_list<const void*> elem, uintptr_t esz) {
+  for (const void* p : vec16)
+    if (p && !aligned(p, 16)) return false;
+  for (const void* p : elem)
+    if (p && !aligned(p, esz)) return false;
+  return true;
+}
+
+// Common size checks.  need_chunk: chunked_fwd; need_p: P matters.
+m3_status check_dims(const m3_dims* d, bool need_chunk, bool need_p) {
+  if (!d) return M3_ERR_NULL;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads < 0) return M3_ERR_SHAPE;
+  if (d->dstate <= 0 || d->rank <= 0 || (need_p && d->headdim <= 0)) return M3_ERR_SHAPE;
+  if (need_chunk && d->chunk <= 0) return M3_ERR_SHAPE;
+  if (d->dstate % 2 != 0) return M3_ERR_SHAPE;
+  if (d->io_dtype != M3_F32 && d->io_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
+  if (!in_set(d->dstate, {16, 32, 64, 128})) return M3_ERR_UNSUPPORTED;
+  if (need_p && !in_set(d->headdim, {16, 32, 64, 128})) return M3_ERR_UNSUPPORTED;
+  if (!in_set(d->rank, {1, 2, 4})) return M3_ERR_UNSUPPORTED;
+  if (need_chunk) {
+    if (!in_set(d->chunk, {16, 32, 64})) return M3_ERR_UNSUPPORTED;
+    if (d->chunk * d->rank > 256) return M3_ERR_UNSUPPORTED;
+  }
+  // grid limits: (b, h) pairs index 32-bit block ids
+  if (d->batch > 65535 || d->nheads > 65535) return M3_ERR_UNSUPPORTED;
+  if (d->seqlen > (int64_t(1) << 31) / 64) return M3_ERR_UNSUPPORTED;
+  return M3_OK;
+}
+
+int io_bf16(const m3_dims* d) { return d->io_dtype == M3_BF16 ? 1 : 0; }
+
+int64_t segments_of(const m3_dims* d) {
+  const int64_t req = d->flags & 0xffff;
+  if (req > 0) return req;
+  return 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mamba3_abi_version(void) { return MAMBA3_ABI_VERSION; }
+
+const char* mamba3_status_string(m3_status s) {
+  switch (s) {
+    case M3_OK: return "ok";
+    case M3_ERR_NULL: return "a required pointer is NULL (or only one of prev_B/prev_x was given)";
+    case M3_ERR_SHAPE: return "invalid shape (negative size, zero head/state/rank/chunk, or odd dstate)";
+    case M3_ERR_UNSUPPORTED: return "size outside the supported set";
+    case M3_ERR_ALIGN: return "a pointer is misaligned (16 bytes for vector-accessed buffers, element size otherwise)";
+    case M3_ERR_WORKSPACE: return "workspace missing or smaller than the queried size";
+    case M3_ERR_HIP: return "a HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d) {
+  if (check_dims(d, true, true) != M3_OK) return 0;
+  const int64_t S = segments_of(d);
+  if (S <= 1 || d->seqlen == 0) return 0;
+  const int64_t BH = d->batch * d->nheads, K = d->dstate / 2, NP = d->dstate * d->headdim;
+  const int64_t nchunks = (d->seqlen + d->chunk - 1) / d->chunk;
+  const size_t f = sizeof(float);
+  // segment end states + incoming states, segment totals, per-chunk offsets
+  return f * (size_t)(2 * BH * S * NP + BH * S * (1 + K) + BH * nchunks * (1 + K)) + 256;
+}
+
+m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B, const void* C,
+                                 const float* dt, const float* A, const float* lam, const float* theta,
+                                 const float* h0, const void* prev_B, const void* prev_x, void* y,
+                                 float* h_final, void* workspace, size_t workspace_bytes, void* stream) {
+  m3_status st = check_dims(d, true, true);
+  if (st != M3_OK) return st;
+  if ((d->flags & ~0xffff) != 0) return M3_ERR_UNSUPPORTED;
+  if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0)
+    return M3_ERR_UNSUPPORTED;
+  const int64_t S = segments_of(d);
+  if (S != 1) return M3_ERR_UNSUPPORTED;  // segmented walk: not available in this build
+  const bool empty = d->batch == 0 || d->nheads == 0;
+  const bool has_tokens = !empty && d->seqlen > 0;
+  if ((prev_B == nullptr) != (prev_x == nullptr)) return M3_ERR_NULL;
+  if (has_tokens && (!x || !B || !C || !dt || !A || !lam || !theta || !y)) return M3_ERR_NULL;
+  const uintptr_t esz = d->io_dtype == M3_BF16 ? 2 : 4;
+  if (!all_aligned({x, B, C, y, workspace}, {prev_B, prev_x}, esz) ||
+      !all_aligned({}, {dt, A, lam, theta, h0, h_final}, 4))
+    return M3_ERR_ALIGN;
+  const size_t need = mamba3_ssm_chunked_fwd_workspace_size(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return M3_ERR_WORKSPACE;
+  if (empty) return M3_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t BH = d->batch * d->nheads;
+  if (d->seqlen == 0) {
+    // no token: the final state is h0 (the token before, if any, has no successor)
+    if (h_final && h_final != h0)
+      return m3::launch_copy_f32(h_final, h0, BH * d->dstate * d->headdim, s) == hipSuccess ? M3_OK : M3_ERR_HIP;
+    return M3_OK;
+  }
+  m3::WalkArgs a{};
+  a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.lam = lam; a.theta = theta;
+  a.h0 = h0; a.prev_B = prev_B; a.prev_x = prev_x; a.y = y; a.h_final = h_final;
+  a.batch = d->batch; a.L = d->seqlen; a.H = d->nheads;
+  a.R = (int)d->rank; a.Q = (int)d->chunk; a.S = (int)S;
+  a.seg_len = ((d->seqlen + d->chunk - 1) / d->chunk) * d->chunk;
+  hipError_t e = m3::launch_walk(io_bf16(d), (int)d->dstate, (int)d->headdim, a, s);
+  return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+m3_status mamba3_ssm_decode_step(const m3_dims* d, float* state, const void* x, const void* B,
+                                 const void* C, const float* dt, const float* A, const float* lam,
+                                 const float* theta, const void* prev_B, const void* prev_x, void* y,
+                                 void* stream) {
+  m3_status st = check_dims(d, false, true);
+  if (st != M3_OK) return st;
+  if (d->flags != 0) return M3_ERR_UNSUPPORTED;
+  const bool empty = d->batch == 0 || d->nheads == 0;
+  if ((prev_B == nullptr) != (prev_x == nullptr)) return M3_ERR_NULL;
+  if (!empty && (!state || !x || !B || !C || !dt || !A || !lam || !theta || !y)) return M3_ERR_NULL;
+  const uintptr_t esz = d->io_dtype == M3_BF16 ? 2 : 4;
+  if (!all_aligned({state}, {x, B, C, prev_B, prev_x, y}, esz) || !all_aligned({}, {dt, A, lam, theta}, 4))
+    return M3_ERR_ALIGN;
+  if (empty) return M3_OK;
+  m3::DecodeArgs a{};
+  a.state = state; a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.lam = lam; a.theta = theta;
+  a.prev_B = prev_B; a.prev_x = prev_x; a.y = y;
+  a.BH = d->batch * d->nheads;
+  a.R = (int)d->rank;
+  hipError_t e = m3::launch_decode(io_bf16(d), (int)d->dstate, (int)d->headdim, a, (hipStream_t)stream);
+  return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+size_t mamba3_rope_bc_workspace_size(const m3_dims* d) {
+  if (check_dims(d, false, false) != M3_OK) return 0;
+  const int64_t nchunks = (d->seqlen + m3::ROPE_CHUNK - 1) / m3::ROPE_CHUNK;
+  return sizeof(float) * (size_t)(d->batch * d->nheads * nchunks * (d->dstate / 2));
+}
+
+m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C, const float* dt,
+                         const float* theta, const float* angle0, void* B_rot, void* C_rot,
+                         float* angle_final, void* workspace, size_t workspace_bytes, void* stream) {
+  m3_status st = check_dims(d, false, false);
+  if (st != M3_OK) return st;
+  if (d->flags != 0) return M3_ERR_UNSUPPORTED;
+  const bool empty = d->batch == 0 || d->nheads == 0;
+  const bool has_tokens = !empty && d->seqlen > 0;
+  if (has_tokens && (!B || !C || !dt || !theta || !B_rot || !C_rot)) return M3_ERR_NULL;
+  if (!all_aligned({B, C, B_rot, C_rot}, {dt, theta, angle0, angle_final, workspace}, 4)) return M3_ERR_ALIGN;
+  const size_t need = mamba3_rope_bc_workspace_size(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return M3_ERR_WORKSPACE;
+  if (empty) return M3_OK;
+  m3::RopeArgs a{};
+  a.B = B; a.C = C; a.dt = dt; a.theta = theta; a.angle0 = angle0;
+  a.B_rot = B_rot; a.C_rot = C_rot; a.angle_final = angle_final; a.totals = (float*)workspace;
+  a.batch = d->batch; a.L = d->seqlen; a.H = d->nheads; a.R = (int)d->rank;
+  hipError_t e = m3::launch_rope(io_bf16(d), (int)d->dstate, a, (hipStream_t)stream);
+  return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
+}  // extern "C"

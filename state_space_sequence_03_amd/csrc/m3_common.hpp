@@ -1,0 +1,112 @@
+// Shared device helpers for the gfx950 kernels: io-dtype traits, bf16
+// rounding, vector loads/stores and the MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m3 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16;
+
+struct bf16_t {  // storage tag for bf16 io
+  u16 bits;
+};
+
+// fp32 -> bf16, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ u16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (u16)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(u16 b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// io traits: elements per 16-byte vector and conversions to/from fp32.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct io;
+
+template <>
+struct io<float> {
+  static constexpr int VEC = 4;       // elements per 16 B
+  static constexpr int BYTES = 4;
+  typedef float4 vec;
+  __device__ static void unpack(const vec& v, float* f) { f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w; }
+  __device__ static vec pack(const float* f) { return make_float4(f[0], f[1], f[2], f[3]); }
+  __device__ static float load1(const void* p, int64_t i) { return ((const float*)p)[i]; }
+  __device__ static void store1(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+};
+
+template <>
+struct io<bf16_t> {
+  static constexpr int VEC = 8;
+  static constexpr int BYTES = 2;
+  typedef uint4 vec;
+  __device__ static void unpack(const vec& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static vec pack(const float* f) {
+    vec v;
+    v.x = pack_bf2(f[0], f[1]);
+    v.y = pack_bf2(f[2], f[3]);
+    v.z = pack_bf2(f[4], f[5]);
+    v.w = pack_bf2(f[6], f[7]);
+    return v;
+  }
+  __device__ static float load1(const void* p, int64_t i) { return bf2f(((const u16*)p)[i]); }
+  __device__ static void store1(void* p, int64_t i, float v) { ((u16*)p)[i] = f2bf(v); }
+};
+
+// 16-byte global load / store of an io vector.
+template <typename T>
+__device__ __forceinline__ typename io<T>::vec ldg16(const void* base, int64_t elem) {
+  return *(const typename io<T>::vec*)((const char*)base + elem * io<T>::BYTES);
+}
+template <typename T>
+__device__ __forceinline__ void stg16(void* base, int64_t elem, const typename io<T>::vec& v) {
+  *(typename io<T>::vec*)((char*)base + elem * io<T>::BYTES) = v;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers.  Lane l of a wave: m = l % 16, g = l / 16.
+//  16x16x32 bf16: A lane holds A[m][8g+j], B lane holds B[8g+j][m] (j < 8);
+//  16x16x4 f32:   A lane holds A[m][g],    B lane holds B[g][m];
+//  both:          D lane holds D[4g+i][m] (i < 4).
+// A contraction only needs A's element j and B's element j of lanes with the
+// same g to refer to the same k, so callers may permute k freely as long as
+// both operands use the same permutation.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ float wave_incl_scan(float v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    float u = __shfl_up(v, o, 64);
+    if (l >= o) v += u;
+  }
+  return v;
+}
+
+}  // namespace m3

@@ -1,0 +1,57 @@
+// Launch entry points of the kernels (host side).  Arguments are already
+// validated by the C ABI layer; these functions only pick a template
+// instance, size the grid and launch on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace m3 {
+
+struct DecodeArgs {
+  float* state;
+  const void *x, *B, *C;
+  const float *dt, *A, *lam, *theta;
+  const void *prev_B, *prev_x;
+  void* y;
+  int64_t BH;
+  int R;
+};
+hipError_t launch_decode(int io_bf16, int N, int P, const DecodeArgs& a, hipStream_t s);
+
+struct RopeArgs {
+  const void *B, *C;
+  const float *dt, *theta, *angle0;
+  void *B_rot, *C_rot;
+  float* angle_final;
+  float* totals;  // workspace: (B*H, nchunks, N/2) fp32
+  int64_t batch, L, H;
+  int R;
+};
+constexpr int ROPE_CHUNK = 64;
+hipError_t launch_rope(int io_bf16, int N, const RopeArgs& a, hipStream_t s);
+
+struct WalkArgs {
+  const void *x, *B, *C;
+  const float *dt, *A, *lam, *theta;
+  const float* h0;
+  const void *prev_B, *prev_x;
+  void* y;
+  float* h_final;     // S == 1: final state (nullable)
+  float* seg_end;     // S > 1: (B*H*S, N, P) end state of each segment walked from a zero state
+  float* seg_tot;     // S > 1: (B*H*S, 1 + N/2) segment log-decay and angle totals
+  float* chunk_meta;  // S > 1: (B*H, nchunks, 1 + N/2) segment-relative log-decay and angle at chunk start
+  float* seg_in;      // S > 1: (B*H*S, N, P) true state entering each segment (from the segment scan)
+  int64_t batch, L, H;
+  int R, Q, S;
+  int64_t seg_len;    // tokens per segment, a multiple of Q
+};
+// LDS bytes the walker needs for these sizes (0 if they are not supported).
+size_t walk_lds_bytes(int io_bf16, int N, int P, int Q, int R);
+hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
+
+// Fill n floats of dst with src (or zeros when src is NULL).
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
+
+}  // namespace m3

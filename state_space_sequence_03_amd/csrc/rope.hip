@@ -1,0 +1,166 @@
+// Cumulative-angle rotation of B and C (the data-dependent RoPE form of the
+// complex state, linkstar.cloud/article/869, "第二刀：复值状态空间"):
+//     phi_t = angle0 + sum_{s<=t} dt_s theta_s[k],
+//     B_rot_t = R(-phi_t) B_t,  C_rot_t = R(-phi_t) C_t,  angle_final = phi_L.
+//
+// The scan runs along L, which is long (up to 64K tokens) while B*H*N/2 may be
+// small, so it is split in three launches over 64-token chunks:
+//   1. chunk totals of dt*theta per (b,h,chunk,pair)          -> workspace
+//   2. exclusive scan of the totals over chunks (+ angle0)    -> workspace
+//   3. per chunk: wave-level inclusive scan in LDS + offset, sincos once per
+//      (token, pair), then rotate every rank of B and C with 16-byte accesses.
+// Launch 3 moves almost all the bytes (B, C in and out); 1 and 2 read only
+// dt and theta once more.
+#include "m3_common.hpp"
+#include "m3_launch.hpp"
+
+namespace m3 {
+
+template <int N>
+__global__ __launch_bounds__(256) void rope_totals_kernel(RopeArgs a, int64_t nchunks) {
+  constexpr int K = N / 2;
+  constexpr int TG = 256 / K;
+  const int64_t c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int k = threadIdx.x % K, tg = threadIdx.x / K;
+  float s = 0.0f;
+  for (int t = tg; t < ROPE_CHUNK; t += TG) {
+    const int64_t tok = c * ROPE_CHUNK + t;
+    if (tok < a.L) {
+      const int64_t idx = (b * a.L + tok) * a.H + h;
+      s += a.dt[idx] * a.theta[idx * K + k];
+    }
+  }
+  __shared__ float red[256];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (tg == 0) {
+    for (int q = 1; q < TG; ++q) s += red[q * K + k];
+    a.totals[((b * a.H + h) * nchunks + c) * K + k] = s;
+  }
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void rope_scan_kernel(RopeArgs a, int64_t nchunks) {
+  constexpr int K = N / 2;
+  constexpr int SEG = 256 / K;
+  const int64_t bh = (int64_t)blockIdx.y * a.H + blockIdx.x;
+  const int k = threadIdx.x % K, sg = threadIdx.x / K;
+  const int64_t per = (nchunks + SEG - 1) / SEG;
+  const int64_t c_begin = sg * per;
+  const int64_t c_end = c_begin + per < nchunks ? c_begin + per : nchunks;
+  float* tot = a.totals + bh * nchunks * K;
+  float s = 0.0f;
+  for (int64_t c = c_begin; c < c_end; ++c) s += tot[c * K + k];
+  __shared__ float sums[SEG][K];
+  sums[sg][k] = s;
+  __syncthreads();
+  float run = a.angle0 ? a.angle0[bh * K + k] : 0.0f;
+  for (int q = 0; q < sg; ++q) run += sums[q][k];
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    const float v = tot[c * K + k];
+    tot[c * K + k] = run;
+    run += v;
+  }
+  if (sg == SEG - 1 && a.angle_final) a.angle_final[bh * K + k] = run;
+}
+
+template <typename T, int N>
+__global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nchunks) {
+  constexpr int K = N / 2;
+  constexpr int VEC = io<T>::VEC;
+  const int64_t c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = c * ROPE_CHUNK;
+  const int nvalid = (int)((a.L - c0) < ROPE_CHUNK ? (a.L - c0) : ROPE_CHUNK);
+  __shared__ float om[ROPE_CHUNK][K + 1];
+  __shared__ float2 cs[ROPE_CHUNK][K];
+
+  for (int i = tid; i < ROPE_CHUNK * K; i += 256) {
+    const int t = i / K, k = i % K;
+    float v = 0.0f;
+    if (t < nvalid) {
+      const int64_t idx = (b * a.L + c0 + t) * a.H + h;
+      v = a.dt[idx] * a.theta[idx * K + k];
+    }
+    om[t][k] = v;
+  }
+  __syncthreads();
+  const float* off = a.totals + ((b * a.H + h) * nchunks + c) * K;
+  for (int k = wave; k < K; k += 4) {
+    const float v = wave_incl_scan(om[lane][k]) + off[k];
+    float s, co;
+    sincosf(v, &s, &co);
+    cs[lane][k] = make_float2(co, s);
+  }
+  __syncthreads();
+
+  const int R = a.R;
+  constexpr int VPR = N / VEC;  // vectors per row
+  const int items = nvalid * R * VPR;
+  for (int i = tid; i < items; i += 256) {
+    const int row = i / VPR, n0 = (i % VPR) * VEC;
+    const int t = row / R;
+    const int64_t e = ((b * a.L + c0) * a.H + h) * (int64_t)R * N;  // token c0, rank 0
+    const int64_t off_e = e + ((int64_t)t * a.H * R + (row % R)) * N + n0;
+    float fb[VEC], fc[VEC];
+    io<T>::unpack(ldg16<T>(a.B, off_e), fb);
+    io<T>::unpack(ldg16<T>(a.C, off_e), fc);
+#pragma unroll
+    for (int q = 0; q < VEC / 2; ++q) {
+      const float2 r2 = cs[t][n0 / 2 + q];
+      const float b0 = fb[2 * q], b1 = fb[2 * q + 1];
+      const float c0v = fc[2 * q], c1v = fc[2 * q + 1];
+      // R(-phi) (u, v) = (cos u + sin v, -sin u + cos v)
+      fb[2 * q] = r2.x * b0 + r2.y * b1;
+      fb[2 * q + 1] = r2.x * b1 - r2.y * b0;
+      fc[2 * q] = r2.x * c0v + r2.y * c1v;
+      fc[2 * q + 1] = r2.x * c1v - r2.y * c0v;
+    }
+    stg16<T>(a.B_rot, off_e, io<T>::pack(fb));
+    stg16<T>(a.C_rot, off_e, io<T>::pack(fc));
+  }
+}
+
+template <typename T, int N>
+static hipError_t rope_run(const RopeArgs& a, hipStream_t s) {
+  const int64_t nchunks = (a.L + ROPE_CHUNK - 1) / ROPE_CHUNK;
+  const dim3 g3((unsigned)nchunks, (unsigned)a.H, (unsigned)a.batch);
+  hipLaunchKernelGGL((rope_totals_kernel<N>), g3, dim3(256), 0, s, a, nchunks);
+  hipLaunchKernelGGL((rope_scan_kernel<N>), dim3((unsigned)a.H, (unsigned)a.batch), dim3(256), 0, s, a, nchunks);
+  hipLaunchKernelGGL((rope_apply_kernel<T, N>), g3, dim3(256), 0, s, a, nchunks);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t rope_dispatch(int N, const RopeArgs& a, hipStream_t s) {
+  switch (N) {
+    case 16: return rope_run<T, 16>(a, s);
+    case 32: return rope_run<T, 32>(a, s);
+    case 64: return rope_run<T, 64>(a, s);
+    case 128: return rope_run<T, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_rope(int io_bf16, int N, const RopeArgs& a, hipStream_t s) {
+  if (a.batch == 0 || a.H == 0) return hipSuccess;
+  if (a.L == 0) {
+    if (a.angle_final) return launch_copy_f32(a.angle_final, a.angle0, a.batch * a.H * (N / 2), s);
+    return hipSuccess;
+  }
+  return io_bf16 ? rope_dispatch<bf16_t>(N, a, s) : rope_dispatch<float>(N, a, s);
+}
+
+__global__ void copy_f32_kernel(float* dst, const float* src, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src ? src[i] : 0.0f;
+}
+
+hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst, src, n);
+  return hipGetLastError();
+}
+
+}  // namespace m3

@@ -1,0 +1,185 @@
+"""ctypes binding of the C ABI in ``include/mamba3_ssm.h``.
+
+Argument marshalling only: every step of the computation runs in the gfx950
+kernels of ``libmamba3_ssm.so``.  PyTorch supplies device memory (tensors are
+passed by ``data_ptr()``) and the stream (``torch.cuda.current_stream()``).
+If the library is missing this module raises; there is no fallback.
+
+Entry points keep the ABI's names:
+  mamba3_ssm_chunked_fwd, mamba3_ssm_decode_step, mamba3_rope_bc
+(and the friendlier aliases chunked_fwd, decode_step, rope_bc).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmamba3_ssm.so")
+
+M3_OK, M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_UNSUPPORTED, M3_ERR_ALIGN, M3_ERR_WORKSPACE, M3_ERR_HIP = range(7)
+M3_F32, M3_BF16 = 0, 1
+ABI_SYMBOLS = ("mamba3_ssm_chunked_fwd", "mamba3_ssm_chunked_fwd_workspace_size", "mamba3_ssm_decode_step",
+               "mamba3_rope_bc", "mamba3_rope_bc_workspace_size", "mamba3_status_string", "mamba3_abi_version")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("nheads", ctypes.c_int64),
+                ("headdim", ctypes.c_int64), ("dstate", ctypes.c_int64), ("rank", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class Mamba3Error(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmamba3_ssm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with state_space_sequence_03_amd/build.py "
+                               "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, f = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+        dp = ctypes.POINTER(Dims)
+        L.mamba3_ssm_chunked_fwd.argtypes = [dp] + [vp] * 12 + [vp, sz, vp]
+        L.mamba3_ssm_chunked_fwd.restype = ctypes.c_int
+        L.mamba3_ssm_chunked_fwd_workspace_size.argtypes = [dp]
+        L.mamba3_ssm_chunked_fwd_workspace_size.restype = sz
+        L.mamba3_ssm_decode_step.argtypes = [dp] + [vp] * 11 + [vp]
+        L.mamba3_ssm_decode_step.restype = ctypes.c_int
+        L.mamba3_rope_bc.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
+        L.mamba3_rope_bc.restype = ctypes.c_int
+        L.mamba3_rope_bc_workspace_size.argtypes = [dp]
+        L.mamba3_rope_bc_workspace_size.restype = sz
+        L.mamba3_status_string.argtypes = [ctypes.c_int]
+        L.mamba3_status_string.restype = ctypes.c_char_p
+        L.mamba3_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return lib().mamba3_status_string(int(status)).decode()
+    except Exception:  # library missing: still describe the code
+        return "unknown"
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _io_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return M3_BF16
+    if t.dtype == torch.float32:
+        return M3_F32
+    raise TypeError(f"io dtype must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != M3_OK:
+        raise Mamba3Error(status, what)
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, rank, chunk, io_dtype, flags=0) -> Dims:
+    return Dims(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate), int(rank), int(chunk),
+                int(io_dtype), int(flags))
+
+
+def chunked_fwd_workspace_size(dims: Dims) -> int:
+    return int(lib().mamba3_ssm_chunked_fwd_workspace_size(ctypes.byref(dims)))
+
+
+def rope_bc_workspace_size(dims: Dims) -> int:
+    return int(lib().mamba3_rope_bc_workspace_size(ctypes.byref(dims)))
+
+
+def mamba3_ssm_chunked_fwd(x, B, C, dt, A, lam, theta, h0=None, prev_B=None, prev_x=None, *, chunk=64,
+                           segments=0, y=None, h_final=None, want_final=True, workspace=None, stream=None):
+    """Whole-sequence forward.  Returns (y, h_final) (h_final None if not wanted)."""
+    torch = _torch()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x), flags=segments)
+    if y is None:
+        y = torch.empty_like(x)
+    if h_final is None and want_final:
+        h_final = torch.empty((b, H, N, P), device=x.device, dtype=torch.float32)
+    ws_bytes = chunked_fwd_workspace_size(dims)
+    if ws_bytes > 0 and workspace is None:
+        workspace = torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
+    st = lib().mamba3_ssm_chunked_fwd(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
+                                      _ptr(lam), _ptr(theta), _ptr(h0), _ptr(prev_B), _ptr(prev_x), _ptr(y),
+                                      _ptr(h_final), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+                                      _stream(stream))
+    _check(st, "mamba3_ssm_chunked_fwd")
+    return y, h_final
+
+
+def mamba3_ssm_decode_step(state, x, B, C, dt, A, lam, theta, prev_B=None, prev_x=None, *, y=None, stream=None):
+    """One token, state updated in place.  Shapes: state (b,H,N,P) fp32, x (b,H,R,P),
+    B/C (b,H,R,N), dt/A/lam (b,H), theta (b,H,N/2).  Returns y (b,H,R,P)."""
+    torch = _torch()
+    b, H, R, P = x.shape
+    N = B.shape[-1]
+    dims = make_dims(b, 1, H, P, N, R, 16, _io_code(x))
+    if y is None:
+        y = torch.empty_like(x)
+    st = lib().mamba3_ssm_decode_step(ctypes.byref(dims), _ptr(state), _ptr(x), _ptr(B), _ptr(C), _ptr(dt),
+                                      _ptr(A), _ptr(lam), _ptr(theta), _ptr(prev_B), _ptr(prev_x), _ptr(y),
+                                      _stream(stream))
+    _check(st, "mamba3_ssm_decode_step")
+    return y
+
+
+def mamba3_rope_bc(B, C, dt, theta, angle0=None, *, B_rot=None, C_rot=None, angle_final=None,
+                   want_final=True, workspace=None, stream=None):
+    """Cumulative-angle rotation.  Returns (B_rot, C_rot, angle_final)."""
+    torch = _torch()
+    b, L, H, R, N = B.shape
+    dims = make_dims(b, L, H, 16, N, R, 16, _io_code(B))
+    if B_rot is None:
+        B_rot = torch.empty_like(B)
+    if C_rot is None:
+        C_rot = torch.empty_like(C)
+    if angle_final is None and want_final:
+        angle_final = torch.empty((b, H, N // 2), device=B.device, dtype=torch.float32)
+    ws_bytes = rope_bc_workspace_size(dims)
+    if ws_bytes > 0 and workspace is None:
+        workspace = torch.empty(ws_bytes, device=B.device, dtype=torch.uint8)
+    st = lib().mamba3_rope_bc(ctypes.byref(dims), _ptr(B), _ptr(C), _ptr(dt), _ptr(theta), _ptr(angle0),
+                              _ptr(B_rot), _ptr(C_rot), _ptr(angle_final), _ptr(workspace),
+                              ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+                              _stream(stream))
+    _check(st, "mamba3_rope_bc")
+    return B_rot, C_rot, angle_final
+
+
+chunked_fwd = mamba3_ssm_chunked_fwd
+decode_step = mamba3_ssm_decode_step
+rope_bc = mamba3_rope_bc

@@ -1,0 +1,131 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function that include/mamba3_ssm.h
+declares, and reject bad arguments with the documented status codes before
+making any HIP call.  Only error paths are exercised, so the fake device
+addresses used here are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba3_ssm.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from state_space_sequence_03_amd import ops
+    if not os.path.exists(ops.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return ops
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba3_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = declared_functions()
+    assert set(names) == set(L.ABI_SYMBOLS)
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.mamba3_abi_version() == 1
+
+
+def test_status_strings(L):
+    for s in range(7):
+        assert len(L.status_string(s)) >= 2 and L.status_string(s) != "unknown status"
+    assert L.status_string(0) == "ok"
+
+
+FAKE = 0x7F0000000000  # 16-byte aligned fake device address (never touched)
+
+
+def call_fwd(L, dims, **over):
+    p = {k: ctypes.c_void_p(FAKE) for k in ("x", "B", "C", "dt", "A", "lam", "theta", "y")}
+    p.update(h0=None, prev_B=None, prev_x=None, h_final=None, ws=None)
+    p.update(over)
+    return L.lib().mamba3_ssm_chunked_fwd(ctypes.byref(dims), p["x"], p["B"], p["C"], p["dt"], p["A"], p["lam"],
+                                          p["theta"], p["h0"], p["prev_B"], p["prev_x"], p["y"], p["h_final"],
+                                          p["ws"], ctypes.c_size_t(over.get("ws_bytes", 0)), None)
+
+
+def dims(L, **kw):
+    base = dict(batch=2, seqlen=100, nheads=3, headdim=64, dstate=64, rank=4, chunk=64, io_dtype=L.M3_BF16, flags=0)
+    base.update(kw)
+    return L.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dstate=63), "M3_ERR_SHAPE"), (dict(batch=-1), "M3_ERR_SHAPE"), (dict(seqlen=-5), "M3_ERR_SHAPE"),
+    (dict(headdim=0), "M3_ERR_SHAPE"), (dict(rank=0), "M3_ERR_SHAPE"), (dict(chunk=0), "M3_ERR_SHAPE"),
+    (dict(dstate=48), "M3_ERR_UNSUPPORTED"), (dict(headdim=96), "M3_ERR_UNSUPPORTED"),
+    (dict(rank=3), "M3_ERR_UNSUPPORTED"), (dict(chunk=128), "M3_ERR_UNSUPPORTED"),
+    (dict(io_dtype=7), "M3_ERR_UNSUPPORTED"), (dict(flags=1 << 20), "M3_ERR_UNSUPPORTED"),
+    (dict(dstate=128, headdim=128, rank=4, chunk=64), "M3_ERR_UNSUPPORTED"),     # tiles exceed LDS
+    (dict(io_dtype=0, rank=4, chunk=64), "M3_ERR_UNSUPPORTED"),                # fp32 tiles exceed LDS
+])
+def test_chunked_fwd_rejects_bad_sizes(L, kw, expect):
+    assert call_fwd(L, dims(L, **kw)) == getattr(L, expect)
+
+
+def test_chunked_fwd_null_and_alignment(L):
+    assert L.lib().mamba3_ssm_chunked_fwd(None, *([None] * 12), None, ctypes.c_size_t(0), None) == L.M3_ERR_NULL
+    assert call_fwd(L, dims(L), x=None) == L.M3_ERR_NULL
+    assert call_fwd(L, dims(L), theta=None) == L.M3_ERR_NULL
+    assert call_fwd(L, dims(L), prev_B=ctypes.c_void_p(FAKE)) == L.M3_ERR_NULL       # prev_x missing
+    assert call_fwd(L, dims(L), y=ctypes.c_void_p(FAKE + 8)) == L.M3_ERR_ALIGN
+    assert call_fwd(L, dims(L), h0=ctypes.c_void_p(FAKE + 2)) == L.M3_ERR_ALIGN
+    assert call_fwd(L, dims(L), dt=ctypes.c_void_p(FAKE + 1)) == L.M3_ERR_ALIGN
+
+
+def test_empty_batch_is_a_noop(L):
+    # nothing is read or launched for an empty batch, even with null pointers
+    d = dims(L, batch=0)
+    assert L.lib().mamba3_ssm_chunked_fwd(ctypes.byref(d), *([None] * 12), None, ctypes.c_size_t(0), None) == L.M3_OK
+
+
+def test_workspace_sizes(L):
+    assert L.chunked_fwd_workspace_size(dims(L)) == 0
+    d = dims(L, seqlen=4096)
+    assert L.rope_bc_workspace_size(d) == 4 * 2 * 3 * 64 * 32
+    assert L.rope_bc_workspace_size(dims(L, dstate=7)) == 0
+
+
+def call_decode(L, d, **over):
+    p = {k: ctypes.c_void_p(FAKE) for k in ("state", "x", "B", "C", "dt", "A", "lam", "theta", "y")}
+    p.update(prev_B=None, prev_x=None)
+    p.update(over)
+    return L.lib().mamba3_ssm_decode_step(ctypes.byref(d), p["state"], p["x"], p["B"], p["C"], p["dt"], p["A"],
+                                          p["lam"], p["theta"], p["prev_B"], p["prev_x"], p["y"], None)
+
+
+def test_decode_validation(L):
+    assert call_decode(L, dims(L, dstate=15)) == L.M3_ERR_SHAPE
+    assert call_decode(L, dims(L, headdim=100)) == L.M3_ERR_UNSUPPORTED
+    assert call_decode(L, dims(L, flags=1)) == L.M3_ERR_UNSUPPORTED
+    assert call_decode(L, dims(L), state=None) == L.M3_ERR_NULL
+    assert call_decode(L, dims(L), prev_x=ctypes.c_void_p(FAKE)) == L.M3_ERR_NULL
+    assert call_decode(L, dims(L), B=ctypes.c_void_p(FAKE + 1)) == L.M3_ERR_ALIGN
+    assert call_decode(L, dims(L), state=ctypes.c_void_p(FAKE + 8)) == L.M3_ERR_ALIGN
+
+
+def test_rope_validation(L):
+    lib = L.lib()
+    d = dims(L, seqlen=70)
+    f = ctypes.c_void_p(FAKE)
+    args = lambda **o: [o.get(k, f) for k in ("B", "C", "dt", "theta")] + [None] + [o.get(k, f) for k in ("Br", "Cr")] + [None]
+    assert lib.mamba3_rope_bc(ctypes.byref(d), *args(), None, ctypes.c_size_t(0), None) == L.M3_ERR_WORKSPACE
+    ws = L.rope_bc_workspace_size(d)
+    assert lib.mamba3_rope_bc(ctypes.byref(d), *args(), f, ctypes.c_size_t(ws - 4), None) == L.M3_ERR_WORKSPACE
+    assert lib.mamba3_rope_bc(ctypes.byref(d), *args(Br=None), f, ctypes.c_size_t(ws), None) == L.M3_ERR_NULL
+    assert lib.mamba3_rope_bc(ctypes.byref(d), *args(dt=ctypes.c_void_p(FAKE + 1)), f, ctypes.c_size_t(ws),
+                              None) == L.M3_ERR_ALIGN
+    assert lib.mamba3_rope_bc(ctypes.byref(dims(L, rank=8)), *args(), f, ctypes.c_size_t(ws), None) == L.M3_ERR_UNSUPPORTED
