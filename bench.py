@@ -1,0 +1,235 @@
+"""Benchmark of the Mamba-3 SSM layer core on one MI355X.
+
+One step = one mamba3_ssm_chunked_fwd (scans, RoPE, intra-chunk MFMA work,
+chunk states and the inter-chunk pass: the whole prefill path) over the
+1.5B-scale MIMO workload: batch 8, L=4096, H=64, P=64, N=64, R=4, chunk 64,
+bf16 io, fp32 state, synthetic inputs drawn on the device.  Inputs are resident
+in HBM before the timed region starts.
+
+Printed: one JSON line with the prefill throughput (tokens/s), the roofline of
+the walker kernel (HIP events on its stream), the decode workload (batch 256,
+1024 consecutive one-token steps, fp32 state in HBM) with its achieved
+bandwidth, the rope rotation, and the fp64 CPU oracle timed on a bounded
+sample of the same prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only prefill|decode|rope]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
+BF16_DENSE_TFLOPS = 2516.6       # MI355X dense bf16 MFMA
+
+
+def prefill_bytes_per_token_head(w, s_io=2):
+    """Algorithmic bytes: x, B, C read once, y written once, dt/A/lam fp32, theta fp32 (N/2 per token)."""
+    return s_io * w.rank * (2 * w.headdim + 2 * w.dstate) + 12 + 2 * w.dstate
+
+
+def prefill_flops_per_token_head(w, causal):
+    Q, R, N, P = w.chunk, w.rank, w.dstate, w.headdim
+    if causal:
+        return R * R * (N + P) * (Q + 1) + 4 * R * N * P
+    return 2 * Q * R * R * (N + P) + 4 * R * N * P
+
+
+def decode_bytes_per_step(w, s_io=2):
+    BH, N, P, R = w.batch * w.nheads, w.dstate, w.headdim, w.rank
+    state = 2 * BH * N * P * 4
+    inputs = BH * (R * P + 2 * R * N) * s_io + BH * (R * N + R * P) * s_io  # x, B, C + prev_B, prev_x
+    scal = BH * (3 * 4 + (N // 2) * 4)
+    y = BH * R * P * s_io
+    return state + inputs + scal + y
+
+
+def rope_bytes_per_token_head(w, s_io=2):
+    return 4 * w.rank * w.dstate * s_io + 4 + 2 * w.dstate
+
+
+def timed(fn, steps, warmup, torch):
+    """Run fn warmup+steps times; returns (wall ms/step, event ms/step on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, e0.elapsed_time(e1) / steps
+
+
+def bench_prefill(ops, inputs, w, steps, warmup, torch):
+    d = inputs.torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
+                            seed=inputs.seed_of(w.name))
+    y = torch.empty_like(d["x"])
+    hf = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), device="cuda", dtype=torch.float32)
+    fn = lambda: ops.chunked_fwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], chunk=w.chunk,
+                                 y=y, h_final=hf)
+    wall, ev = timed(fn, steps, warmup, torch)
+    th = w.batch * w.seqlen * w.nheads
+    bytes_ = th * prefill_bytes_per_token_head(w)
+    dense = th * prefill_flops_per_token_head(w, False)
+    causal = th * prefill_flops_per_token_head(w, True)
+    del d, y, hf
+    torch.cuda.empty_cache()
+    return dict(ms=ev, wall_ms=wall, tokens_per_s=w.tokens / (ev * 1e-3), bytes=bytes_,
+                gbps=bytes_ / (ev * 1e-3) / 1e9, tflops_dense=dense / (ev * 1e-3) / 1e12,
+                tflops_causal=causal / (ev * 1e-3) / 1e12)
+
+
+def bench_decode(ops, inputs, w, torch, reps=1):
+    steps = w.decode_steps
+    d = inputs.torch_inputs(w.batch, steps, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
+                            seed=inputs.seed_of(w.name), with_h0=True)
+    sm = {k: d[k].transpose(0, 1).contiguous() for k in ("x", "B", "C", "dt", "A", "lam", "theta")}
+    state = d["h0"]
+    del d
+    torch.cuda.empty_cache()
+    y = torch.empty(sm["x"].shape[1:], dtype=sm["x"].dtype, device="cuda")
+
+    def run_all():
+        for t in range(steps):
+            pb = sm["B"][t - 1] if t > 0 else None
+            px = sm["x"][t - 1] if t > 0 else None
+            ops.decode_step(state, sm["x"][t], sm["B"][t], sm["C"][t], sm["dt"][t], sm["A"][t], sm["lam"][t],
+                            sm["theta"][t], pb, px, y=y)
+
+    wall, ev = timed(run_all, reps, 1, torch)
+    per_step = ev / steps
+    b = decode_bytes_per_step(w)
+    del sm, state, y
+    torch.cuda.empty_cache()
+    return dict(steps=steps, ms_per_step=per_step, steps_per_s=1e3 / per_step, bytes_per_step=b,
+                gbps=b / (per_step * 1e-3) / 1e9)
+
+
+def bench_rope(ops, inputs, w, steps, warmup, torch):
+    d = inputs.torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
+                            seed=inputs.seed_of(w.name))
+    Br, Cr = torch.empty_like(d["B"]), torch.empty_like(d["C"])
+    fn = lambda: ops.rope_bc(d["B"], d["C"], d["dt"], d["theta"], B_rot=Br, C_rot=Cr)
+    wall, ev = timed(fn, steps, warmup, torch)
+    th = w.batch * w.seqlen * w.nheads
+    b = th * rope_bytes_per_token_head(w)
+    del d, Br, Cr
+    torch.cuda.empty_cache()
+    return dict(ms=ev, gbps=b / (ev * 1e-3) / 1e9, bytes=b)
+
+
+def cpu_baseline(inputs, w, budget_s=12.0):
+    """The fp64 oracle on (b,h) slices of the same workload (full L), one thread per slice."""
+    import oracle
+    cores = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
+    # the same distributions as the device draw, drawn on the host, one head per slice
+    def draw(n, seed):
+        t = inputs.torch_inputs(n, w.seqlen, 1, w.headdim, w.dstate, w.rank, io=w.io, seed=seed, device="cpu")
+        return {k: v.float().numpy() for k, v in t.items()}
+
+    one = draw(1, 5)
+    t0 = time.perf_counter()
+    oracle.forward(one["x"], one["B"], one["C"], one["dt"], one["A"], one["lam"], one["theta"], nthreads=1)
+    t_one = time.perf_counter() - t0
+    # whole multiples of the core count, for about budget_s of wall time
+    nsl = cores * max(1, min(16, int(round(budget_s / max(t_one, 1e-3)))))
+    batch = draw(nsl, 6)
+    t0 = time.perf_counter()
+    oracle.forward(batch["x"], batch["B"], batch["C"], batch["dt"], batch["A"], batch["lam"], batch["theta"],
+                   nthreads=min(cores, nsl))
+    dt = time.perf_counter() - t0
+    token_heads_per_s = nsl * w.seqlen / dt
+    return dict(value=token_heads_per_s / w.nheads, unit="tokens/s", cores=min(cores, nsl), kind="oracle",
+                sample=f"{nsl} (b,h) slices x L={w.seqlen} of the {w.name} workload "
+                       f"({nsl * w.seqlen} token-heads in {dt:.1f} s); tokens/s = token-heads/s / H={w.nheads}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode", "rope", "all"], default="all")
+    ap.add_argument("--workload", default="mimo_bf16", choices=["mimo_bf16", "siso_bf16", "long_mimo_bf16"],
+                    help="prefill workload timed by --only prefill (profiling); the headline line uses mimo_bf16")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the (b,h) slices of this "
+              "workload shard with no communication, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from state_space_sequence_03_amd import ops, inputs
+    ops.lib()
+    W = inputs.WORKLOADS
+    w = W["mimo_bf16"] if args.only != "prefill" else W[args.workload]
+    out = {}
+    if args.only in ("prefill", "all"):
+        print(f"[bench] prefill {w.name}: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr, flush=True)
+        pf = bench_prefill(ops, inputs, w, args.steps, args.warmup, torch)
+        out["prefill"] = pf
+    if args.only in ("decode", "all"):
+        wd = W["decode_mimo_bf16"]
+        print(f"[bench] decode {wd.name}: {wd.decode_steps} steps", file=sys.stderr, flush=True)
+        out["decode"] = bench_decode(ops, inputs, wd, torch)
+    if args.only in ("rope", "all"):
+        print(f"[bench] rope_bc on {w.name} shapes", file=sys.stderr, flush=True)
+        out["rope"] = bench_rope(ops, inputs, w, max(3, args.steps // 4), 2, torch)
+    if args.only == "all":
+        for name in ("siso_bf16", "long_mimo_bf16"):
+            print(f"[bench] prefill {name} (context)", file=sys.stderr, flush=True)
+            out[name] = bench_prefill(ops, inputs, W[name], 3, 1, torch)
+
+    line = {"metric": "SSM prefill tokens/s + %MFMA peak (R=4); decode steps/s + HBM GB/s",
+            "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "mimo_bf16 prefill: batch 8, L=4096, H=64, P=64, N=64, R=4, chunk 64, "
+                                   "bf16 io, fp32 state", "global_batch": w.batch, "seq_len": w.seqlen,
+                       "parallelism": "single GPU"}}
+    if "prefill" in out:
+        pf = out["prefill"]
+        line["value"] = round(pf["tokens_per_s"], 1)
+        line["ms_per_step"] = round(pf["ms"], 4)
+        line["roofline"] = {"bound": "hbm", "achieved": round(pf["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(pf["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "kernel": "chunk_walk_kernel<bf16,64,64,8>",
+                            "bytes_per_launch": pf["bytes"]}
+        line["mfma"] = {"tflops_dense": round(pf["tflops_dense"], 1), "tflops_causal": round(pf["tflops_causal"], 1),
+                        "frac_dense": round(pf["tflops_dense"] / BF16_DENSE_TFLOPS, 4),
+                        "frac_causal": round(pf["tflops_causal"] / BF16_DENSE_TFLOPS, 4), "peak_tflops": BF16_DENSE_TFLOPS}
+    if "decode" in out:
+        dc = out["decode"]
+        line["decode"] = {"workload": "decode_mimo_bf16: batch 256, H=64, P=64, N=64, R=4, fp32 state, 1024 steps",
+                          "steps_per_s": round(dc["steps_per_s"], 1), "ms_per_step": round(dc["ms_per_step"], 5),
+                          "achieved_GBps": round(dc["gbps"], 1), "peak_GBps": HBM_PEAK_GBPS,
+                          "frac": round(dc["gbps"] / HBM_PEAK_GBPS, 4), "bytes_per_step": dc["bytes_per_step"]}
+    if "rope" in out:
+        line["rope_bc"] = {"ms": round(out["rope"]["ms"], 4), "achieved_GBps": round(out["rope"]["gbps"], 1),
+                           "frac": round(out["rope"]["gbps"] / HBM_PEAK_GBPS, 4)}
+    for name in ("siso_bf16", "long_mimo_bf16"):
+        if name in out:
+            o = out[name]
+            line[name] = {"tokens_per_s": round(o["tokens_per_s"], 1), "ms": round(o["ms"], 4),
+                          "achieved_GBps": round(o["gbps"], 1), "frac_hbm": round(o["gbps"] / HBM_PEAK_GBPS, 4)}
+    if not args.no_cpu and "prefill" in out:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cb = cpu_baseline(inputs, w)
+        cb["value"] = round(cb["value"], 2)
+        line["cpu_baseline"] = cb
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
