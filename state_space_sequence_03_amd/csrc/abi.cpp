@@ -94,7 +94,8 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
   m3_status st = check_dims(d, true, true);
   if (st != M3_OK) return st;
   if ((d->flags & ~0xffff) != 0) return M3_ERR_UNSUPPORTED;
-  if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0)
+  if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0 &&
+      !m3::walk_fast_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank))
     return M3_ERR_UNSUPPORTED;
   const int64_t S = segments_of(d);
   if (S != 1) return M3_ERR_UNSUPPORTED;  // segmented walk: not available in this build

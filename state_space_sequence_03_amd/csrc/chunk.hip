@@ -35,6 +35,8 @@
 // io-dtype copy H'^T sits in LDS for the next chunk's inter-chunk term.
 // Raw x, B, C, dt, A, lam, theta of the next chunk are loaded into registers
 // while the current chunk computes.
+#include <type_traits>
+
 #include "m3_common.hpp"
 #include "m3_launch.hpp"
 
@@ -85,6 +87,11 @@ struct lds_t { typedef float type; };
 template <>
 struct lds_t<bf16_t> { typedef u16 type; };
 
+// B~ is kept in LDS as fp32 (rotated once at staging) whenever the tiles fit,
+// i.e. for fp32 io and for bf16 io with N, P <= 64; otherwise the raw bf16 B
+// is kept and rotated where it is read.
+__host__ __device__ constexpr bool b_fp32(int esz, int N, int P) { return esz == 4 || (N <= 64 && P <= 64); }
+
 // LDS layout, shared by host (sizing) and device.  Row pads of 16 bytes.
 struct Layout {
   int VP, BLD, XLD, HLD;  // padded virtual rows; leading dims (elements)
@@ -96,13 +103,14 @@ __host__ __device__ inline Layout make_layout(int esz, int N, int P, int Q, int 
   Layout L;
   const int slab = esz == 2 ? 32 : 16;
   const int V = Q * R;
+  const int bsz = b_fp32(esz, N, P) ? 4 : esz;
   L.VP = ((V + slab - 1) / slab) * slab;
   const int pad = 16 / esz;
-  L.BLD = N + pad;
+  L.BLD = N + 16 / bsz;
   L.XLD = L.VP + pad;
   L.HLD = N + pad;
   int o = 0;
-  L.off_B = o; o += L.VP * L.BLD * esz;
+  L.off_B = o; o += L.VP * L.BLD * bsz;
   L.off_X = o; o += P * L.XLD * esz;
   L.off_H = o; o += P * L.HLD * esz;
   o = (o + 15) & ~15;
@@ -123,12 +131,14 @@ size_t walk_lds_bytes(int io_bf16, int N, int P, int Q, int R) {
 
 template <typename T, int N, int P, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
-  typedef typename lds_t<T>::type E;    // LDS element (u16 bits for bf16, float)
+  typedef typename lds_t<T>::type E;    // LDS element of X^T, H'^T (u16 bits for bf16, float)
   typedef mm<T> M;
   typedef typename M::frag frag;
   constexpr int K = N / 2;
   constexpr int NT = NW * 64;
   constexpr int ESZ = sizeof(E);
+  constexpr bool B32 = b_fp32(ESZ, N, P);         // B~ stored rotated in fp32
+  typedef typename std::conditional<B32, float, E>::type EB;
   constexpr int VEC = io<T>::VEC;
   constexpr int SLAB = M::SLAB;
   constexpr int NKS = (N + SLAB - 1) / SLAB;      // slabs over n
@@ -147,7 +157,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
   const int R = a.R, Q = a.Q, V = Q * R;
   const int lgR = R == 4 ? 2 : (R == 2 ? 1 : 0);
   const Layout LY = make_layout(ESZ, N, P, Q, R);
-  E* sB = (E*)(smem + LY.off_B);       // raw B rows (token, rank) x n, exact io values
+  EB* sB = (EB*)(smem + LY.off_B);     // B~ (fp32) or raw B (io) rows (token, rank) x n
   E* sX = (E*)(smem + LY.off_X);       // X^T: p x (token, rank)
   E* sH = (E*)(smem + LY.off_H);       // H'^T: p x n, io precision
   float2* sCS = (float2*)(smem + LY.off_cs);  // (cos, sin) of the chunk-local angle per (token, pair)
@@ -165,6 +175,8 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
   auto tokBC = [&](int64_t tok) { return ((b * L + tok) * H + h) * rowsN; };
   auto tokX = [&](int64_t tok) { return ((b * L + tok) * H + h) * rowsP; };
   auto tokS = [&](int64_t tok) { return (b * L + tok) * H + h; };
+  // in-chunk offsets stay below 2^32 (64 tokens x H x R x max(N, P))
+  const uint32_t strBC = (uint32_t)(H * rowsN), strX = (uint32_t)(H * rowsP);
 
   // column tiles of Y owned by this wave (balanced pairing when NCT == 2 NW)
   const int NCT = V / 16;
@@ -195,12 +207,14 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
 
   auto load_raw = [&](int64_t c0) {
     const int nvalid = (int)((t1 - c0) < Q ? (t1 - c0) : Q);
+    const void* gB = (const char*)a.B + tokBC(c0) * io<T>::BYTES;
+    const void* gX = (const char*)a.x + tokX(c0) * io<T>::BYTES;
 #pragma unroll
     for (int j = 0; j < BIT; ++j) {
       const int i = tid + NT * j;
       const int v = i / (N / VEC), n0 = (i % (N / VEC)) * VEC;
       if (v < V && (v >> lgR) < nvalid)
-        rB[j] = ldg16<T>(a.B, tokBC(c0 + (v >> lgR)) + (v & (R - 1)) * N + n0);
+        rB[j] = ldg16<T>(gB, (uint32_t)(v >> lgR) * strBC + (uint32_t)((v & (R - 1)) * N + n0));
       else
         rB[j] = typename io<T>::vec{};
     }
@@ -209,7 +223,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
       const int i = tid + NT * j;
       const int v = i / (P / VEC), p0 = (i % (P / VEC)) * VEC;
       if (v < V && (v >> lgR) < nvalid)
-        rX[j] = ldg16<T>(a.x, tokX(c0 + (v >> lgR)) + (v & (R - 1)) * P + p0);
+        rX[j] = ldg16<T>(gX, (uint32_t)(v >> lgR) * strX + (uint32_t)((v & (R - 1)) * P + p0));
       else
         rX[j] = typename io<T>::vec{};
     }
@@ -232,32 +246,43 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
 
   auto load_raw_C = [&](int64_t c0) {
     const int nvalid = (int)((t1 - c0) < Q ? (t1 - c0) : Q);
+    const char* gC = (const char*)a.C + tokBC(c0) * io<T>::BYTES;
 #pragma unroll
     for (int ci = 0; ci < 2; ++ci) {
       const int v = (ci < nct ? ctl[ci] : 0) * 16 + m16;
       const bool ok = ci < nct && (v >> lgR) < nvalid;
-      const int64_t base = ok ? tokBC(c0 + (v >> lgR)) + (v & (R - 1)) * N : 0;
+      const uint32_t base = ok ? (uint32_t)(v >> lgR) * strBC + (uint32_t)((v & (R - 1)) * N) : 0;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         if (!ok) { rC[ci][ks] = M::zero(); continue; }
         if constexpr (ESZ == 2) {
-          const u16* row = (const u16*)a.C + base + ks * 32;
+          const u16* row = (const u16*)gC + base + ks * 32;
           const uint2 lo = *(const uint2*)(row + 4 * g);
           uint2 hi = make_uint2(0, 0);
           if (ks * 32 + 16 < N) hi = *(const uint2*)(row + 16 + 4 * g);
           rC[ci][ks] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         } else {
-          rC[ci][ks] = *(const float4*)((const float*)a.C + base + ks * 16 + 4 * g);
+          rC[ci][ks] = *(const float4*)((const float*)gC + base + ks * 16 + 4 * g);
         }
       }
     }
   };
 
-  // Rotated slab of a raw B row: B~ = R(-phi_t) B on the slab positions this
-  // lane feeds to the MFMA (see mm<>), converted to the MFMA operand type.
+  // Slab of a B~ row in the MFMA operand layout (see mm<>): from the fp32 B~
+  // when B32, else rotated here from the raw bf16 B.
   auto bt_frag = [&](int row, int ks) -> frag {
-    const int t = row >> lgR;
-    if constexpr (ESZ == 2) {
+    if constexpr (B32) {
+      const float* rp = (const float*)sB + row * LY.BLD;
+      if constexpr (ESZ == 2) {
+        const bool two = ks * 32 + 16 < N;
+        const float4 lo = *(const float4*)(rp + ks * 32 + 4 * g);
+        const float4 hi = two ? *(const float4*)(rp + ks * 32 + 16 + 4 * g) : make_float4(0, 0, 0, 0);
+        return make_uint4(pack_bf2(lo.x, lo.y), pack_bf2(lo.z, lo.w), pack_bf2(hi.x, hi.y), pack_bf2(hi.z, hi.w));
+      } else {
+        return *(const float4*)(rp + ks * 16 + 4 * g);
+      }
+    } else {
+      const int t = row >> lgR;
       const u16* rp = (const u16*)sB + row * LY.BLD + ks * 32;
       const bool two = ks * 32 + 16 < N;
       const uint2 lo = *(const uint2*)(rp + 4 * g);
@@ -269,16 +294,26 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
       uint32_t o4[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float u = __uint_as_float(w4[q] << 16), w = __uint_as_float(w4[q] & 0xffff0000u);
+        const float u = bf_lo(w4[q]), w = bf_hi(w4[q]);
         o4[q] = pack_bf2(c4[q] * u + s4[q] * w, c4[q] * w - s4[q] * u);
       }
       return make_uint4(o4[0], o4[1], o4[2], o4[3]);
-    } else {
-      const float4 v4 = *(const float4*)((const float*)sB + row * LY.BLD + ks * 16 + 4 * g);
-      const float4 cs = *(const float4*)(sCS + t * K + ks * 8 + 2 * g);
-      return make_float4(cs.x * v4.x + cs.y * v4.y, cs.x * v4.y - cs.y * v4.x,
-                         cs.z * v4.z + cs.w * v4.w, cs.z * v4.w - cs.w * v4.z);
     }
+  };
+
+  // (w B~)^T element for state row n and source row k, in fp32
+  auto wbt = [&](int k, int n) -> float {
+    const int t = k >> lgR;
+    float r;
+    if constexpr (B32) {
+      r = ((const float*)sB)[k * LY.BLD + n];
+    } else {
+      const uint32_t wv = *(const uint32_t*)((const u16*)sB + k * LY.BLD + (n & ~1));
+      const float be = bf_lo(wv), bo = bf_hi(wv);
+      const float2 cs = sCS[t * K + (n >> 1)];
+      r = (n & 1) ? (cs.x * bo - cs.y * be) : (cs.x * be + cs.y * bo);
+    }
+    return r * sSC[SC_W + t];
   };
 
   // ---------------- state H' (fp32, registers) ----------------
@@ -347,7 +382,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
 
   for (int64_t c0 = t0; c0 < t1; c0 += Q) {
     const int nvalid = (int)((t1 - c0) < Q ? (t1 - c0) : Q);
-    // ---------- phase A: scalars and chunk-local scans ----------
+    // ---------- phase A: scalars, chunk-local scans, X^T ----------
     // LDS scalars per token t: SC_LAM = Lam_t * log2(e) (chunk-local, inclusive),
     // SC_EL = exp(Lam_t), SC_Q = q_t = gamma_t + eps_{t+1}, SC_GAM = gamma_t,
     // SC_W = exp(Lam_end - Lam_t) q_t; SC_LEND = Lam_end * log2(e).
@@ -397,13 +432,6 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
         }
       }
     }
-    // ---------- phase B: stage raw B and X^T; rotate own C~ ----------
-#pragma unroll
-    for (int j = 0; j < BIT; ++j) {
-      const int i = tid + NT * j;
-      const int v = i / (N / VEC), n0 = (i % (N / VEC)) * VEC;
-      if (v < V) *(typename io<T>::vec*)(sB + v * LY.BLD + n0) = rB[j];
-    }
 #pragma unroll
     for (int j = 0; j < XIT; ++j) {
       const int i = tid + NT * j;
@@ -424,10 +452,38 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
         }
       }
     }
-    __syncthreads();  // angle table, scalars, B, X^T (and H'^T) ready
-    // prefetch the next chunk's B, x and scalars (their registers are free now)
-    if (c0 + Q < t1) load_raw(c0 + Q);
-
+    if constexpr (!B32) {
+#pragma unroll
+      for (int j = 0; j < BIT; ++j) {
+        const int i = tid + NT * j;
+        const int v = i / (N / VEC), n0 = (i % (N / VEC)) * VEC;
+        if (v < V) *(typename io<T>::vec*)((E*)sB + v * LY.BLD + n0) = rB[j];
+      }
+    }
+    __syncthreads();  // angle table, scalars, X^T (raw B) ready
+    // ---------- phase B: rotated B~ (fp32) and own C~ ----------
+    if constexpr (B32) {
+#pragma unroll
+      for (int j = 0; j < BIT; ++j) {
+        const int i = tid + NT * j;
+        const int v = i / (N / VEC), n0 = (i % (N / VEC)) * VEC;
+        if (v < V) {
+          float f[VEC];
+          io<T>::unpack(rB[j], f);
+          const int t = v >> lgR;
+#pragma unroll
+          for (int q = 0; q < VEC / 2; ++q) {
+            const float2 cs = sCS[t * K + n0 / 2 + q];
+            const float u = f[2 * q], w = f[2 * q + 1];
+            f[2 * q] = cs.x * u + cs.y * w;
+            f[2 * q + 1] = cs.x * w - cs.y * u;
+          }
+          float* dst = (float*)sB + v * LY.BLD + n0;
+#pragma unroll
+          for (int q = 0; q < VEC / 4; ++q) *(float4*)(dst + 4 * q) = make_float4(f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]);
+        }
+      }
+    }
     frag (&cf)[2][NKS] = rC;  // C~ = R(-phi) C, rotated in place
 #pragma unroll
     for (int ci = 0; ci < 2; ++ci) {
@@ -442,7 +498,7 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
           for (int q = 0; q < 4; ++q) {
             const int n = ks * 32 + (q < 2 ? 4 * g + 2 * q : 16 + 4 * g + 2 * (q - 2));
             const float2 cs = n < N ? sCS[t * K + n / 2] : make_float2(1.0f, 0.0f);
-            const float u = __uint_as_float(w4[q] << 16), w = __uint_as_float(w4[q] & 0xffff0000u);
+            const float u = bf_lo(w4[q]), w = bf_hi(w4[q]);
             o4[q] = pack_bf2(cs.x * u + cs.y * w, cs.x * w - cs.y * u);
           }
           cf[ci][ks] = make_uint4(o4[0], o4[1], o4[2], o4[3]);
@@ -460,6 +516,9 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
         }
       }
     }
+    if constexpr (B32) __syncthreads();  // B~ ready
+    // prefetch the next chunk's B, x and scalars (their registers are free now)
+    if (c0 + Q < t1) load_raw(c0 + Q);
 
     // ---------- phase C: outputs ----------
 #pragma unroll
@@ -500,17 +559,25 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
           f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
           for (int ks = 0; ks < NKS; ++ks) acc = M::mac(bt_frag(srow0 + m16, ks), cf[ci][ks], acc);
-          // decay x 2-band mask: M[t,s] = exp(Lam_t - Lam_s) q_s (s < t), gamma_t (s == t)
+          // decay x 2-band mask: M[t,s] = exp(Lam_t - Lam_s) q_s (s < t), gamma_t (s == t), 0 (s > t)
+          if (R == 4) {  // the four rows of a lane belong to one token
+            const int srow = srow0 + 4 * g;
+            const int s = srow >> 2;
+            const float ls = sSC[SC_LAM + s], qs = sSC[SC_Q + s];
+            const float e = exp2f(fminf(Lt - ls, 0.0f)) * qs;
+            const float m = srow < V ? (s < tcol ? e : (s == tcol ? gt : 0.0f)) : 0.0f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int srow = srow0 + 4 * g + i;
-            const int s = srow >> lgR;
-            float m = 0.0f;
-            if (srow < V) {
-              if (s < tcol) m = exp2f(Lt - sSC[SC_LAM + s]) * sSC[SC_Q + s];
-              else if (s == tcol) m = gt;
+            for (int i = 0; i < 4; ++i) gm[sub][i] = acc[i] * m;
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int srow = srow0 + 4 * g + i;
+              const int s = srow >> lgR;
+              const float ls = sSC[SC_LAM + s], qs = sSC[SC_Q + s];
+              const float e = exp2f(fminf(Lt - ls, 0.0f)) * qs;
+              const float m = srow < V ? (s < tcol ? e : (s == tcol ? gt : 0.0f)) : 0.0f;
+              gm[sub][i] = acc[i] * m;
             }
-            gm[sub][i] = acc[i] * m;
           }
         }
         if constexpr (ESZ == 2) {
@@ -562,40 +629,22 @@ __global__ __launch_bounds__(NW * 64, 1) void chunk_walk_kernel(WalkArgs a) {
           if (nt != cur_nt) {
             cur_nt = nt;
             const int n = nt * 16 + m16;
-            const int odd = n & 1;
             if constexpr (ESZ == 2) {
               float f[8];
 #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int k = kb * 32 + 8 * g + e;
-                const int t = k >> lgR;
-                const uint32_t wv = *(const uint32_t*)((const u16*)sB + k * LY.BLD + (n & ~1));
-                const float be = __uint_as_float(wv << 16), bo = __uint_as_float(wv & 0xffff0000u);
-                const float2 cs = sCS[t * K + (n >> 1)];
-                const float r = odd ? (cs.x * bo - cs.y * be) : (cs.x * be + cs.y * bo);
-                f[e] = r * sSC[SC_W + t];
-              }
+              for (int e = 0; e < 8; ++e) f[e] = wbt(kb * 32 + 8 * g + e, n);
               uint32_t h4[4], l4[4];
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 const uint32_t hp = pack_bf2(f[2 * q], f[2 * q + 1]);
                 h4[q] = hp;
-                l4[q] = pack_bf2(f[2 * q] - __uint_as_float(hp << 16), f[2 * q + 1] - __uint_as_float(hp & 0xffff0000u));
+                l4[q] = pack_bf2(f[2 * q] - bf_lo(hp), f[2 * q + 1] - bf_hi(hp));
               }
               ahi = make_uint4(h4[0], h4[1], h4[2], h4[3]);
               alo = make_uint4(l4[0], l4[1], l4[2], l4[3]);
             } else {
-              float f[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const int k = kb * 16 + 4 * g + e;
-                const int t = k >> lgR;
-                const float2 pr = *(const float2*)((const float*)sB + k * LY.BLD + (n & ~1));
-                const float2 cs = sCS[t * K + (n >> 1)];
-                const float r = odd ? (cs.x * pr.y - cs.y * pr.x) : (cs.x * pr.x + cs.y * pr.y);
-                f[e] = r * sSC[SC_W + t];
-              }
-              ahi = make_float4(f[0], f[1], f[2], f[3]);
+              ahi = make_float4(wbt(kb * 16 + 4 * g, n), wbt(kb * 16 + 4 * g + 1, n), wbt(kb * 16 + 4 * g + 2, n),
+                                wbt(kb * 16 + 4 * g + 3, n));
             }
           }
           frag bfr;
@@ -658,8 +707,12 @@ template <typename T, int N, int P, int NW>
 static hipError_t walk_run(const WalkArgs& a, hipStream_t s) {
   const Layout LY = make_layout(sizeof(typename lds_t<T>::type), N, P, a.Q, a.R);
   auto kern = chunk_walk_kernel<T, N, P, NW>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LY.bytes);
-  if (e != hipSuccess) return e;
+  static bool attr_set = false;  // per instantiation; the attribute is per function
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   const int64_t blocks = a.batch * a.H * a.S;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NW * 64), LY.bytes, s, a);
   return hipGetLastError();
@@ -696,6 +749,7 @@ static hipError_t walk_n(int N, int P, const WalkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s) {
+  if (walk_fast_supported(io_bf16, N, P, a.Q, a.R)) return launch_walk_fast(N, P, a, s);
   return io_bf16 ? walk_n<bf16_t>(N, P, a, s) : walk_n<float>(N, P, a, s);
 }
 

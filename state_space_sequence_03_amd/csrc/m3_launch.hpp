@@ -47,8 +47,12 @@ struct WalkArgs {
   int R, Q, S;
   int64_t seg_len;    // tokens per segment, a multiple of Q
 };
-// LDS bytes the walker needs for these sizes (0 if they are not supported).
+// LDS bytes the general walker needs for these sizes (0 if they do not fit).
 size_t walk_lds_bytes(int io_bf16, int N, int P, int Q, int R);
+// The fast walker (bf16 io, N and P <= 64) applies to these sizes.
+bool walk_fast_supported(int io_bf16, int N, int P, int Q, int R);
+hipError_t launch_walk_fast(int N, int P, const WalkArgs& a, hipStream_t s);
+// Chunked forward walk: fast walker when it applies, general walker otherwise.
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
 
 // Fill n floats of dst with src (or zeros when src is NULL).
