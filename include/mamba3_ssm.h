@@ -97,7 +97,9 @@ typedef struct {
   int32_t io_dtype; /* m3_dtype of x, B, C, y, prev_B, prev_x, B_rot, C_rot */
   int32_t flags;    /* chunked_fwd: bits 0..15 = number of sequence segments
                        walked in parallel per (b,h) (0 = chosen by the
-                       library); other bits must be 0.  Others: must be 0. */
+                       library: more than one only for bf16 io when B*H <
+                       256); other bits must be 0.  Segments > 1 need bf16
+                       io and B*H <= 65535.  Other entry points: must be 0. */
 } m3_dims;
 
 /* Whole-sequence forward.
@@ -108,7 +110,11 @@ typedef struct {
  * y: written (must not alias an input).  h_final: nullable; may alias h0.
  * workspace: device scratch of at least
  *   mamba3_ssm_chunked_fwd_workspace_size(d) bytes (may be NULL when that is 0);
- *   its contents on entry do not matter.
+ *   its contents on entry do not matter.  It is non-zero only when the
+ *   sequence is walked as several segments (see flags): the segments are
+ *   walked from a zero state in parallel, then a segment scan supplies the
+ *   true incoming states and their contribution is added to y (linearity of
+ *   the recurrence).
  * To continue a sequence, pass h_final as h0 and the last token's raw B and x
  * as prev_B / prev_x. */
 m3_status mamba3_ssm_chunked_fwd(const m3_dims* d,

@@ -51,10 +51,31 @@ m3_status check_dims(const m3_dims* d, bool need_chunk, bool need_p) {
 
 int io_bf16(const m3_dims* d) { return d->io_dtype == M3_BF16 ? 1 : 0; }
 
-int64_t segments_of(const m3_dims* d) {
-  const int64_t req = d->flags & 0xffff;
-  if (req > 0) return req;
-  return 1;
+// Number of sequence segments walked in parallel per (b,h) and their length
+// (whole chunks).  Requested through the low 16 bits of flags, else chosen so
+// that at least ~512 walkers exist when B*H is small (bf16 io only; each
+// segment keeps at least 4 chunks).  Never more segments than chunks.
+struct SegPlan {
+  int64_t S, seg_len, nchunks;
+};
+SegPlan seg_plan(const m3_dims* d) {
+  SegPlan sp{1, 0, 0};
+  sp.nchunks = d->seqlen > 0 ? (d->seqlen + d->chunk - 1) / d->chunk : 0;
+  int64_t S = d->flags & 0xffff;
+  const int64_t BH = d->batch * d->nheads;
+  if (S == 0) {
+    S = 1;
+    if (d->io_dtype == M3_BF16 && BH > 0 && BH < 256) {
+      S = (512 + BH - 1) / BH;
+      if (S > sp.nchunks / 4) S = sp.nchunks / 4;
+      if (S < 1) S = 1;
+    }
+  }
+  if (S > sp.nchunks) S = sp.nchunks > 0 ? sp.nchunks : 1;
+  const int64_t cps = sp.nchunks > 0 ? (sp.nchunks + S - 1) / S : 1;  // chunks per segment
+  sp.seg_len = cps * d->chunk;
+  sp.S = sp.nchunks > 0 ? (sp.nchunks + cps - 1) / cps : 1;
+  return sp;
 }
 
 }  // namespace
@@ -76,15 +97,30 @@ const char* mamba3_status_string(m3_status s) {
   return "unknown status";
 }
 
+// Workspace of a segmented walk (floats): segment end states, incoming
+// states, segment totals, per-chunk offsets, each 256-byte aligned.
+struct SegWs {
+  size_t end, in, tot, meta, bytes;
+};
+SegWs seg_ws(const m3_dims* d, const SegPlan& sp) {
+  const int64_t BH = d->batch * d->nheads, K = d->dstate / 2, NP = d->dstate * d->headdim;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  SegWs w{};
+  size_t o = 0;
+  w.end = o; o = up(o + sizeof(float) * (size_t)(BH * sp.S * NP));
+  w.in = o; o = up(o + sizeof(float) * (size_t)(BH * sp.S * NP));
+  w.tot = o; o = up(o + sizeof(float) * (size_t)(BH * sp.S * (1 + K)));
+  w.meta = o; o = up(o + sizeof(float) * (size_t)(BH * sp.nchunks * (1 + K)));
+  w.bytes = o;
+  return w;
+}
+
 size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d) {
   if (check_dims(d, true, true) != M3_OK) return 0;
-  const int64_t S = segments_of(d);
-  if (S <= 1 || d->seqlen == 0) return 0;
-  const int64_t BH = d->batch * d->nheads, K = d->dstate / 2, NP = d->dstate * d->headdim;
-  const int64_t nchunks = (d->seqlen + d->chunk - 1) / d->chunk;
-  const size_t f = sizeof(float);
-  // segment end states + incoming states, segment totals, per-chunk offsets
-  return f * (size_t)(2 * BH * S * NP + BH * S * (1 + K) + BH * nchunks * (1 + K)) + 256;
+  if (d->batch == 0 || d->nheads == 0 || d->seqlen == 0) return 0;
+  const SegPlan sp = seg_plan(d);
+  if (sp.S <= 1) return 0;
+  return seg_ws(d, sp).bytes;
 }
 
 m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B, const void* C,
@@ -97,8 +133,8 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
   if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0 &&
       !m3::walk_fast_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank))
     return M3_ERR_UNSUPPORTED;
-  const int64_t S = segments_of(d);
-  if (S != 1) return M3_ERR_UNSUPPORTED;  // segmented walk: not available in this build
+  const SegPlan sp = seg_plan(d);
+  if (sp.S > 1 && (d->io_dtype != M3_BF16 || d->batch * d->nheads > 65535)) return M3_ERR_UNSUPPORTED;
   const bool empty = d->batch == 0 || d->nheads == 0;
   const bool has_tokens = !empty && d->seqlen > 0;
   if ((prev_B == nullptr) != (prev_x == nullptr)) return M3_ERR_NULL;
@@ -122,9 +158,18 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
   a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.lam = lam; a.theta = theta;
   a.h0 = h0; a.prev_B = prev_B; a.prev_x = prev_x; a.y = y; a.h_final = h_final;
   a.batch = d->batch; a.L = d->seqlen; a.H = d->nheads;
-  a.R = (int)d->rank; a.Q = (int)d->chunk; a.S = (int)S;
-  a.seg_len = ((d->seqlen + d->chunk - 1) / d->chunk) * d->chunk;
+  a.R = (int)d->rank; a.Q = (int)d->chunk; a.S = (int)sp.S;
+  a.seg_len = sp.S > 1 ? sp.seg_len : sp.nchunks * d->chunk;
+  if (sp.S > 1) {
+    const SegWs w = seg_ws(d, sp);
+    char* base = (char*)workspace;
+    a.seg_end = (float*)(base + w.end);
+    a.seg_in = (float*)(base + w.in);
+    a.seg_tot = (float*)(base + w.tot);
+    a.chunk_meta = (float*)(base + w.meta);
+  }
   hipError_t e = m3::launch_walk(io_bf16(d), (int)d->dstate, (int)d->headdim, a, s);
+  if (e == hipSuccess && sp.S > 1) e = m3::launch_segment_fixups(io_bf16(d), (int)d->dstate, (int)d->headdim, a, s);
   return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 

@@ -55,6 +55,10 @@ hipError_t launch_walk_fast(int N, int P, const WalkArgs& a, hipStream_t s);
 // Chunked forward walk: fast walker when it applies, general walker otherwise.
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
 
+// After a walk with S > 1 segments: segment scan (true incoming states and
+// h_final) and the output fix-up of segments 1..S-1 (bf16 io).
+hipError_t launch_segment_fixups(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
+
 // Fill n floats of dst with src (or zeros when src is NULL).
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);
 

@@ -94,6 +94,11 @@ def test_empty_batch_is_a_noop(L):
 
 def test_workspace_sizes(L):
     assert L.chunked_fwd_workspace_size(dims(L)) == 0
+    # few (b,h) pairs and a long bf16 sequence: walked as segments, workspace needed
+    long = dims(L, batch=1, seqlen=65536, nheads=32, dstate=128)
+    assert L.chunked_fwd_workspace_size(long) > 0
+    assert L.chunked_fwd_workspace_size(dims(L, batch=1, seqlen=65536, nheads=32, dstate=128, flags=1)) == 0
+    assert L.chunked_fwd_workspace_size(dims(L, batch=8, seqlen=4096, nheads=64)) == 0
     d = dims(L, seqlen=4096)
     assert L.rope_bc_workspace_size(d) == 4 * 2 * 3 * 64 * 32
     assert L.rope_bc_workspace_size(dims(L, dstate=7)) == 0

@@ -356,3 +356,37 @@ def test_full_decode_workload_sampled(ops):
         eh = slice_err(host(st[bi:bi + 1, hi:hi + 1]), ho[i:i + 1], (0, 1))
         say(f"   slice {(bi, hi)}: y {ey:.3e} state {eh:.3e}")
         assert ey < TOL["bf16"] and eh < 1e-3
+
+
+# ---------------------------------------------------------------- sequence segments
+@pytest.mark.parametrize("segs,slow,N,P", [(2, False, 64, 64), (3, True, 64, 64), (5, True, 128, 64),
+                                           (16, False, 128, 64), (4, True, 32, 16)])
+def test_segments_match_single_walk_and_oracle(ops, segs, slow, N, P):
+    """Segments walked from zero + segment scan + fix-up == one sequential walk.
+    With slow decay (A near 0) every chunk of every segment needs the fix-up."""
+    say(f"segments S={segs} slow={slow} N{N} P{P}")
+    kw = dict(a_range=(-30.0, math.log(1e-2))) if slow else {}
+    inp = numpy_inputs(1, 1000, 2, P, N, 4, io="bf16", seed=90 + segs, with_h0=True, with_prev=True, **kw)
+    if slow:
+        inp["dt"] *= 0.2
+    d = to_dev(inp, "bf16")
+    y1, h1 = run_fwd(ops, d, 64, segments=1)
+    ys, hs = run_fwd(ops, d, 64, segments=segs)
+    yo, ho = oracle_fwd(inp)
+    e_y = slice_err(host(ys), yo, (0, 2))
+    e_h = slice_err(host(hs), ho, (0, 1))
+    say(f"   vs oracle: y {e_y:.3e} h {e_h:.3e}; vs single walk: y {slice_err(host(ys), host(y1), (0, 2)):.3e}")
+    assert e_y < TOL["bf16"] and e_h < 1e-3
+    assert slice_err(host(hs), host(h1), (0, 1)) < 1e-3
+
+
+def test_segments_workspace_and_fp32_rejected(ops):
+    w = WORKLOADS["long_mimo_bf16"]
+    dims = ops.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk, ops.M3_BF16)
+    assert ops.chunked_fwd_workspace_size(dims) > 0
+    w2 = WORKLOADS["mimo_bf16"]
+    dims2 = ops.make_dims(w2.batch, w2.seqlen, w2.nheads, w2.headdim, w2.dstate, w2.rank, w2.chunk, ops.M3_BF16)
+    assert ops.chunked_fwd_workspace_size(dims2) == 0
+    inp = to_dev(numpy_inputs(1, 200, 2, 16, 16, 1, io="f32", seed=3), "f32")
+    with pytest.raises(ops.Mamba3Error):
+        run_fwd(ops, inp, 32, segments=2)
