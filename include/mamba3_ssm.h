@@ -142,7 +142,7 @@ m3_status mamba3_ssm_decode_step(const m3_dims* d, float* state,
  *   C_rot = R(-phi_t) C_t, angle_final = phi_L.
  * angle0, angle_final: nullable.  B_rot / C_rot must not alias B / C.
  * workspace: at least mamba3_rope_bc_workspace_size(d) bytes.  chunk of d is
- * ignored. */
+ * ignored.  seqlen is limited to 65535 * 64 tokens (M3_ERR_UNSUPPORTED). */
 m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C,
                          const float* dt, const float* theta, const float* angle0,
                          void* B_rot, void* C_rot, float* angle_final,

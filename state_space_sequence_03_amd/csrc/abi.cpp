@@ -208,6 +208,7 @@ m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C, const f
   m3_status st = check_dims(d, false, false);
   if (st != M3_OK) return st;
   if (d->flags != 0) return M3_ERR_UNSUPPORTED;
+  if ((d->seqlen + m3::ROPE_CHUNK - 1) / m3::ROPE_CHUNK > 65535) return M3_ERR_UNSUPPORTED;  // grid limit
   const bool empty = d->batch == 0 || d->nheads == 0;
   const bool has_tokens = !empty && d->seqlen > 0;
   if (has_tokens && (!B || !C || !dt || !theta || !B_rot || !C_rot)) return M3_ERR_NULL;

@@ -11,64 +11,70 @@
 // Mapping: one 256-thread block per (b,h).  A work item is one rotation pair
 // (rows 2k, 2k+1) x 4 consecutive columns; consecutive threads take
 // consecutive column groups, so each row is read as one contiguous run and the
-// rotation never leaves registers.  y = C^T h is reduced through LDS.
+// rotation never leaves registers.  The state loads are issued first, before
+// the small inputs are staged; y = C^T h is reduced with wave shuffles, then
+// across the four waves in LDS.
 #include "m3_common.hpp"
 #include "m3_launch.hpp"
 
 namespace m3 {
 
-template <typename T, int N, int P>
+template <typename T, int N, int P, int R>
 __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   constexpr int K = N / 2;
-  constexpr int CG = P / 4;                 // column groups of 4 (divides 256)
+  constexpr int CG = P / 4;                 // column groups of 4 (divides 64)
   constexpr int ITEMS = K * CG;
   constexpr int PER = (ITEMS + 255) / 256;  // items per thread
-  constexpr int RMAX = 4;
+  constexpr int RMAX = R;
   const int64_t bh = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int R = a.R;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  __shared__ float sB[RMAX][N], sC[RMAX][N], sPB[RMAX][N];
-  __shared__ float2 sCS[K];
-  __shared__ float red[256][RMAX * 4 + 1];
-
-  const float d = a.dt[bh], lam = a.lam[bh];
-  const float alpha = expf(d * a.A[bh]);
-  const float eps = (1.0f - lam) * d, gam = lam * d;
-  for (int k = tid; k < K; k += 256) {
-    float s, c;
-    sincosf(d * a.theta[bh * K + k], &s, &c);
-    sCS[k] = make_float2(c, s);
-  }
-  const bool has_prev = a.prev_B != nullptr;
-  for (int i = tid; i < R * N; i += 256) {
-    const int r = i / N, n = i % N;
-    sB[r][n] = io<T>::load1(a.B, bh * R * N + i);
-    sC[r][n] = io<T>::load1(a.C, bh * R * N + i);
-    sPB[r][n] = has_prev ? io<T>::load1(a.prev_B, bh * R * N + i) : 0.0f;
-  }
-  const int c = tid % CG;
-  float xv[RMAX][4], pxv[RMAX][4];
-#pragma unroll
-  for (int r = 0; r < RMAX; ++r)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xv[r][j] = r < R ? io<T>::load1(a.x, (bh * R + r) * P + 4 * c + j) : 0.0f;
-      pxv[r][j] = (r < R && has_prev) ? io<T>::load1(a.prev_x, (bh * R + r) * P + 4 * c + j) : 0.0f;
-    }
-  __syncthreads();
-
+  // the state is the only large stream: issue its loads before anything else
   float* st = a.state + bh * (int64_t)N * P;
-  float4 h0[PER], h1[PER];
+  const int c = tid % CG;  // items tid + 256 q share the column group (CG divides 256)
+  f32x4 h0[PER], h1[PER];
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int i = tid + 256 * q;
     if (i < ITEMS) {
       const int k = i / CG;
-      h0[q] = *(const float4*)(st + (2 * k) * P + 4 * c);
-      h1[q] = *(const float4*)(st + (2 * k + 1) * P + 4 * c);
+      h0[q] = *(const f32x4*)(st + (2 * k) * P + 4 * c);
+      h1[q] = *(const f32x4*)(st + (2 * k + 1) * P + 4 * c);
     }
   }
+
+  __shared__ float sB[RMAX][N], sC[RMAX][N], sPB[RMAX][N];
+  __shared__ float2 sCS[K];
+  __shared__ float red[4][RMAX * P];
+
+  const float d = a.dt[bh], lam = a.lam[bh];
+  const float alpha = expf(d * a.A[bh]);
+  // without a previous token its term is absent: weight 0, and the current
+  // token's own buffers stand in as (finite) operands so that no load is
+  // conditional
+  const bool has_prev = a.prev_B != nullptr;
+  const float eps = has_prev ? (1.0f - lam) * d : 0.0f, gam = lam * d;
+  const void* pB = has_prev ? a.prev_B : a.B;
+  const void* px = has_prev ? a.prev_x : a.x;
+  for (int k = tid; k < K; k += 256) {
+    float s, co;
+    sincosf(d * a.theta[bh * K + k], &s, &co);
+    sCS[k] = make_float2(co, s);
+  }
+  for (int i = tid; i < R * N; i += 256) {
+    const int r = i / N, n = i % N;
+    sB[r][n] = io<T>::load1(a.B, bh * R * N + i);
+    sC[r][n] = io<T>::load1(a.C, bh * R * N + i);
+    sPB[r][n] = io<T>::load1(pB, bh * R * N + i);
+  }
+  float xv[RMAX][4], pxv[RMAX][4];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    io<T>::load4(a.x, (bh * R + r) * P + 4 * c, xv[r]);
+    io<T>::load4(px, (bh * R + r) * P + 4 * c, pxv[r]);
+  }
+  __syncthreads();
+
   float yp[RMAX][4];
 #pragma unroll
   for (int r = 0; r < RMAX; ++r)
@@ -81,8 +87,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     if (i < ITEMS) {
       const int k = i / CG;
       const float2 cs = sCS[k];
-      float u0[4] = {h0[q].x, h0[q].y, h0[q].z, h0[q].w};
-      float u1[4] = {h1[q].x, h1[q].y, h1[q].z, h1[q].w};
+      const float u0[4] = {h0[q][0], h0[q][1], h0[q][2], h0[q][3]};
+      const float u1[4] = {h1[q][0], h1[q][1], h1[q][2], h1[q][3]};
       float n0[4], n1[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -96,6 +102,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
             cin1 += sB[r][2 * k + 1] * xv[r][j];
           }
         }
+        // h <- alpha R(w) [h + eps prev_B^T prev_x] + gamma B^T x
         const float v0 = u0[j] + eps * pin0, v1 = u1[j] + eps * pin1;
         n0[j] = alpha * (cs.x * v0 - cs.y * v1) + gam * cin0;
         n1[j] = alpha * (cs.y * v0 + cs.x * v1) + gam * cin1;
@@ -103,38 +110,56 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
         for (int r = 0; r < RMAX; ++r)
           if (r < R) yp[r][j] += sC[r][2 * k] * n0[j] + sC[r][2 * k + 1] * n1[j];
       }
-      *(float4*)(st + (2 * k) * P + 4 * c) = make_float4(n0[0], n0[1], n0[2], n0[3]);
-      *(float4*)(st + (2 * k + 1) * P + 4 * c) = make_float4(n1[0], n1[1], n1[2], n1[3]);
+      *(f32x4*)(st + (2 * k) * P + 4 * c) = f32x4{n0[0], n0[1], n0[2], n0[3]};
+      *(f32x4*)(st + (2 * k + 1) * P + 4 * c) = f32x4{n1[0], n1[1], n1[2], n1[3]};
     }
   }
+  // y[r][p] = sum over pairs: lanes of one wave with the same column group
+  // differ in the bits >= log2(CG) of the lane id
 #pragma unroll
   for (int r = 0; r < RMAX; ++r)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) red[tid][r * 4 + j] = yp[r][j];
+    for (int j = 0; j < 4; ++j) {
+      float v = yp[r][j];
+#pragma unroll
+      for (int o = CG; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+      yp[r][j] = v;
+    }
+  if (lane < CG) {
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r)
+      if (r < R)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) red[wave][r * P + 4 * c + j] = yp[r][j];
+  }
   __syncthreads();
-  // y[r][p]: sum the partials of the threads that own column group p/4
-  constexpr int GROUPS = 256 / CG;
   for (int o = tid; o < R * P; o += 256) {
-    const int r = o / P, p = o % P;
-    const int cg = p / 4, j = p % 4;
-    float s = 0.0f;
-#pragma unroll 4
-    for (int gi = 0; gi < GROUPS; ++gi) s += red[cg + CG * gi][r * 4 + j];
+    const float s = red[0][o] + red[1][o] + red[2][o] + red[3][o];
     io<T>::store1(a.y, bh * R * P + o, s);
   }
 }
 
-template <typename T, int N>
-static hipError_t decode_dispatch_p(int P, const DecodeArgs& a, hipStream_t s) {
+template <typename T, int N, int P>
+static hipError_t decode_dispatch_r(const DecodeArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.BH), block(256);
-  switch (P) {
-    case 16: hipLaunchKernelGGL((decode_step_kernel<T, N, 16>), grid, block, 0, s, a); break;
-    case 32: hipLaunchKernelGGL((decode_step_kernel<T, N, 32>), grid, block, 0, s, a); break;
-    case 64: hipLaunchKernelGGL((decode_step_kernel<T, N, 64>), grid, block, 0, s, a); break;
-    case 128: hipLaunchKernelGGL((decode_step_kernel<T, N, 128>), grid, block, 0, s, a); break;
+  switch (a.R) {
+    case 1: hipLaunchKernelGGL((decode_step_kernel<T, N, P, 1>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_step_kernel<T, N, P, 2>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_step_kernel<T, N, P, 4>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <typename T, int N>
+static hipError_t decode_dispatch_p(int P, const DecodeArgs& a, hipStream_t s) {
+  switch (P) {
+    case 16: return decode_dispatch_r<T, N, 16>(a, s);
+    case 32: return decode_dispatch_r<T, N, 32>(a, s);
+    case 64: return decode_dispatch_r<T, N, 64>(a, s);
+    case 128: return decode_dispatch_r<T, N, 128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <typename T>

@@ -44,6 +44,11 @@ struct io<float> {
   __device__ static vec pack(const float* f) { return make_float4(f[0], f[1], f[2], f[3]); }
   __device__ static float load1(const void* p, int64_t i) { return ((const float*)p)[i]; }
   __device__ static void store1(void* p, int64_t i, float v) { ((float*)p)[i] = v; }
+  // four consecutive elements (one vector access)
+  __device__ static void load4(const void* p, int64_t i, float* f) {
+    const float4 v = *(const float4*)((const float*)p + i);
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  }
 };
 
 template <>
@@ -69,6 +74,12 @@ struct io<bf16_t> {
   }
   __device__ static float load1(const void* p, int64_t i) { return bf2f(((const u16*)p)[i]); }
   __device__ static void store1(void* p, int64_t i, float v) { ((u16*)p)[i] = f2bf(v); }
+  // four consecutive elements (one 8-byte access; AMDGPU global loads accept
+  // 2-byte-aligned addresses)
+  __device__ static void load4(const void* p, int64_t i, float* f) {
+    const uint2 v = *(const uint2*)((const u16*)p + i);
+    f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  }
 };
 
 // 16-byte global load / store of an io vector.
@@ -96,6 +107,10 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+
+// 16-byte fp32 loads / stores with a non-temporal hint (streamed data).
+__device__ __forceinline__ f32x4 ld_nt(const float* p) { return __builtin_nontemporal_load((const f32x4*)p); }
+__device__ __forceinline__ void st_nt(float* p, const f32x4& v) { __builtin_nontemporal_store(v, (f32x4*)p); }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
 

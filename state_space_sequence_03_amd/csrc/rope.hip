@@ -20,7 +20,7 @@ template <int N>
 __global__ __launch_bounds__(256) void rope_totals_kernel(RopeArgs a, int64_t nchunks) {
   constexpr int K = N / 2;
   constexpr int TG = 256 / K;
-  const int64_t c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;  // head fastest
   const int k = threadIdx.x % K, tg = threadIdx.x / K;
   float s = 0.0f;
   for (int t = tg; t < ROPE_CHUNK; t += TG) {
@@ -68,13 +68,34 @@ template <typename T, int N>
 __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nchunks) {
   constexpr int K = N / 2;
   constexpr int VEC = io<T>::VEC;
-  const int64_t c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  constexpr int VPR = N / VEC;                          // vectors per (token, rank) row
+  constexpr int MAXIT = (ROPE_CHUNK * 4 * VPR + 255) / 256;
+  constexpr int BATCH = MAXIT < 8 ? MAXIT : 8;          // vectors per tensor kept in flight
+  // grid: x = head (fastest: concurrent blocks touch adjacent memory), y = chunk, z = batch
+  const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c0 = c * ROPE_CHUNK;
   const int nvalid = (int)((a.L - c0) < ROPE_CHUNK ? (a.L - c0) : ROPE_CHUNK);
+  const int R = a.R;
+  const int items = nvalid * R * VPR;
+  const int64_t e0 = ((b * a.L + c0) * a.H + h) * (int64_t)R * N;  // token c0, rank 0
+  auto off = [&](int i) {
+    const int row = i / VPR, n0 = (i % VPR) * VEC;
+    return e0 + ((int64_t)(row / R) * a.H * R + (row % R)) * N + n0;
+  };
   __shared__ float om[ROPE_CHUNK][K + 1];
   __shared__ float2 cs[ROPE_CHUNK][K];
 
+  // first batch of B and C vectors: in flight while the angles are scanned
+  typename io<T>::vec vb[BATCH], vc[BATCH];
+#pragma unroll
+  for (int j = 0; j < BATCH; ++j) {
+    const int i = tid + 256 * j;
+    if (i < items) {
+      vb[j] = ldg16<T>(a.B, off(i));
+      vc[j] = ldg16<T>(a.C, off(i));
+    }
+  }
   for (int i = tid; i < ROPE_CHUNK * K; i += 256) {
     const int t = i / K, k = i % K;
     float v = 0.0f;
@@ -85,26 +106,21 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
     om[t][k] = v;
   }
   __syncthreads();
-  const float* off = a.totals + ((b * a.H + h) * nchunks + c) * K;
+  const float* offs = a.totals + ((b * a.H + h) * nchunks + c) * K;
   for (int k = wave; k < K; k += 4) {
-    const float v = wave_incl_scan(om[lane][k]) + off[k];
+    const float v = wave_incl_scan(om[lane][k]) + offs[k];
     float s, co;
     sincosf(v, &s, &co);
     cs[lane][k] = make_float2(co, s);
   }
   __syncthreads();
 
-  const int R = a.R;
-  constexpr int VPR = N / VEC;  // vectors per row
-  const int items = nvalid * R * VPR;
-  for (int i = tid; i < items; i += 256) {
+  auto rotate_store = [&](int i, const typename io<T>::vec& bv, const typename io<T>::vec& cv) {
     const int row = i / VPR, n0 = (i % VPR) * VEC;
     const int t = row / R;
-    const int64_t e = ((b * a.L + c0) * a.H + h) * (int64_t)R * N;  // token c0, rank 0
-    const int64_t off_e = e + ((int64_t)t * a.H * R + (row % R)) * N + n0;
     float fb[VEC], fc[VEC];
-    io<T>::unpack(ldg16<T>(a.B, off_e), fb);
-    io<T>::unpack(ldg16<T>(a.C, off_e), fc);
+    io<T>::unpack(bv, fb);
+    io<T>::unpack(cv, fc);
 #pragma unroll
     for (int q = 0; q < VEC / 2; ++q) {
       const float2 r2 = cs[t][n0 / 2 + q];
@@ -116,18 +132,24 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
       fc[2 * q] = r2.x * c0v + r2.y * c1v;
       fc[2 * q + 1] = r2.x * c1v - r2.y * c0v;
     }
-    stg16<T>(a.B_rot, off_e, io<T>::pack(fb));
-    stg16<T>(a.C_rot, off_e, io<T>::pack(fc));
+    stg16<T>(a.B_rot, off(i), io<T>::pack(fb));
+    stg16<T>(a.C_rot, off(i), io<T>::pack(fc));
+  };
+#pragma unroll
+  for (int j = 0; j < BATCH; ++j) {
+    const int i = tid + 256 * j;
+    if (i < items) rotate_store(i, vb[j], vc[j]);
   }
+  for (int i = tid + 256 * BATCH; i < items; i += 256) rotate_store(i, ldg16<T>(a.B, off(i)), ldg16<T>(a.C, off(i)));
 }
 
 template <typename T, int N>
 static hipError_t rope_run(const RopeArgs& a, hipStream_t s) {
   const int64_t nchunks = (a.L + ROPE_CHUNK - 1) / ROPE_CHUNK;
-  const dim3 g3((unsigned)nchunks, (unsigned)a.H, (unsigned)a.batch);
-  hipLaunchKernelGGL((rope_totals_kernel<N>), g3, dim3(256), 0, s, a, nchunks);
+  const dim3 g3h((unsigned)a.H, (unsigned)nchunks, (unsigned)a.batch);
+  hipLaunchKernelGGL((rope_totals_kernel<N>), g3h, dim3(256), 0, s, a, nchunks);
   hipLaunchKernelGGL((rope_scan_kernel<N>), dim3((unsigned)a.H, (unsigned)a.batch), dim3(256), 0, s, a, nchunks);
-  hipLaunchKernelGGL((rope_apply_kernel<T, N>), g3, dim3(256), 0, s, a, nchunks);
+  hipLaunchKernelGGL((rope_apply_kernel<T, N>), g3h, dim3(256), 0, s, a, nchunks);
   return hipGetLastError();
 }
 

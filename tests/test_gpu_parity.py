@@ -390,3 +390,39 @@ def test_segments_workspace_and_fp32_rejected(ops):
     inp = to_dev(numpy_inputs(1, 200, 2, 16, 16, 1, io="f32", seed=3), "f32")
     with pytest.raises(ops.Mamba3Error):
         run_fwd(ops, inp, 32, segments=2)
+
+
+def test_decode_graph_replays_match_eager(ops):
+    """Decode steps captured in a HIP graph: every replay (with eager work and
+    synchronisation between replays) equals the eager result bit for bit."""
+    b, H, P, N, R, steps = 4, 3, 64, 64, 4, 8
+    inp = numpy_inputs(b, steps, H, P, N, R, io="bf16", seed=55, with_h0=True, with_prev=True)
+    d = to_dev(inp, "bf16")
+    sm = {k: d[k].transpose(0, 1).contiguous() for k in ("x", "B", "C", "dt", "A", "lam", "theta")}
+    st = torch.empty_like(d["h0"])
+    y = torch.empty(sm["x"].shape[1:], dtype=torch.bfloat16, device="cuda")
+
+    def run_all():
+        for t in range(steps):
+            pb = sm["B"][t - 1] if t > 0 else d["prev_B"]
+            px = sm["x"][t - 1] if t > 0 else d["prev_x"]
+            ops.decode_step(st, sm["x"][t], sm["B"][t], sm["C"][t], sm["dt"][t], sm["A"][t], sm["lam"][t],
+                            sm["theta"][t], pb, px, y=y)
+
+    say("decode graph: eager")
+    st.copy_(d["h0"])
+    run_all()
+    torch.cuda.synchronize()
+    ref_state, ref_y = st.clone(), y.clone()
+    g = torch.cuda.CUDAGraph()
+    st.copy_(d["h0"])
+    with torch.cuda.graph(g):
+        run_all()
+    for rep in range(3):
+        say(f"decode graph: replay {rep}")
+        st.copy_(d["h0"])
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(st, ref_state) and torch.equal(y, ref_y)
+        _ = (st * 2).sum().item()  # eager work between replays
