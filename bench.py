@@ -34,8 +34,28 @@ def prefill_bytes_per_token_head(w, s_io=2):
     return s_io * w.rank * (2 * w.headdim + 2 * w.dstate) + 12 + 2 * w.dstate
 
 
+def walked_chunk(w):
+    """Chunk length the library walks with: the 32-token walker takes requested
+    chunks of 32 or 64 for bf16 io with N = P = 64 (mirrors the dispatch in
+    csrc/chunk_walk32.hip)."""
+    if w.io == "bf16" and w.dstate == 64 and w.headdim == 64 and w.chunk in (32, 64):
+        return 32
+    return w.chunk
+
+
+def walker_kernel(w):
+    if walked_chunk(w) == 32 and w.chunk in (32, 64) and w.dstate == 64 and w.headdim == 64:
+        return f"walk32_kernel<{w.rank}>"
+    if w.io == "bf16" and w.dstate <= 64 and w.headdim <= 64:
+        return f"chunk_walk_fast_kernel<{w.dstate},{w.headdim},{w.rank}>"
+    return f"chunk_walk_kernel<{w.io},{w.dstate},{w.headdim},8>"
+
+
 def prefill_flops_per_token_head(w, causal):
-    Q, R, N, P = w.chunk, w.rank, w.dstate, w.headdim
+    """MFMA work of the chunked algorithm at the walked chunk length Q: scores
+    and masked scores x X within the chunk (Q R x Q R, causal or dense), the
+    inter-chunk output C H' and the chunk state (w B)^T X."""
+    Q, R, N, P = walked_chunk(w), w.rank, w.dstate, w.headdim
     if causal:
         return R * R * (N + P) * (Q + 1) + 4 * R * N * P
     return 2 * Q * R * R * (N + P) + 4 * R * N * P
@@ -214,8 +234,9 @@ def main():
             "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": "mimo_bf16 prefill: batch 8, L=4096, H=64, P=64, N=64, R=4, chunk 64, "
-                                   "bf16 io, fp32 state", "global_batch": w.batch, "seq_len": w.seqlen,
+            "config": {"workload": f"mimo_bf16 prefill: batch 8, L=4096, H=64, P=64, N=64, R=4, chunk 64 "
+                                   f"(walked as {walked_chunk(w)}-token chunks), bf16 io, fp32 state",
+                       "global_batch": w.batch, "seq_len": w.seqlen,
                        "parallelism": "single GPU"}}
     if "prefill" in out:
         pf = out["prefill"]
@@ -223,7 +244,7 @@ def main():
         line["ms_per_step"] = round(pf["ms"], 4)
         line["roofline"] = {"bound": "hbm", "achieved": round(pf["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(pf["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
-                            "kernel": "chunk_walk_kernel<bf16,64,64,8>",
+                            "kernel": walker_kernel(w),
                             "bytes_per_launch": pf["bytes"]}
         line["mfma"] = {"tflops_dense": round(pf["tflops_dense"], 1), "tflops_causal": round(pf["tflops_causal"], 1),
                         "frac_dense": round(pf["tflops_dense"] / BF16_DENSE_TFLOPS, 4),

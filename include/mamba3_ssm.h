@@ -46,9 +46,9 @@
  * Ownership: the caller owns every buffer (device memory unless stated).  The
  * library allocates nothing and keeps no mutable global state, so calls are
  * reentrant and may run on concurrent streams when their buffers are
- * disjoint.  Alignment: x, B, C, y and the workspace of chunked_fwd, B, C,
- * B_rot and C_rot of rope_bc, and the state of decode_step must be 16-byte
- * aligned; every other pointer must be aligned to its element size.
+ * disjoint.  Alignment: x, B, C, theta, y and the workspace of chunked_fwd,
+ * B, C, B_rot and C_rot of rope_bc, and the state of decode_step must be
+ * 16-byte aligned; every other pointer must be aligned to its element size.
  *
  * Errors: every entry point validates its arguments on the host and returns a
  * status before any HIP call; nothing is launched on error.  M3_ERR_HIP
@@ -93,7 +93,10 @@ typedef struct {
   int64_t headdim;  /* P */
   int64_t dstate;   /* N, even */
   int64_t rank;     /* R */
-  int64_t chunk;    /* Q tokens per chunk (chunked_fwd only) */
+  int64_t chunk;    /* Q tokens per chunk (chunked_fwd only).  For bf16 io
+                       with N = P = 64 and Q in {32, 64} the library walks
+                       32-token chunks (the chunked form is exact for any
+                       split); the workspace size follows the walked length. */
   int32_t io_dtype; /* m3_dtype of x, B, C, y, prev_B, prev_x, B_rot, C_rot */
   int32_t flags;    /* chunked_fwd: bits 0..15 = number of sequence segments
                        walked in parallel per (b,h) (0 = chosen by the

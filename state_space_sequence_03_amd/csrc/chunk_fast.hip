@@ -33,30 +33,6 @@ namespace m3 {
 
 namespace {
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// 8 bytes per lane from LDS with the 16-bit transpose: within each group of 16
-// lanes, output lane i, element j = input lane 4j + i/4, element i % 4.
-__device__ __forceinline__ uint2 lds_tr16(const u16* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
-
-// sin and cos of x after a two-constant reduction by 2*pi (Cody-Waite); the
-// reduced argument lies in [-pi, pi] where the hardware sine/cosine are
-// accurate to about 1e-6.
-__device__ __forceinline__ void fast_sincos(float x, float* s, float* c) {
-  const float kInv2Pi = 0.15915494309189535f;
-  const float k2PiHi = 6.28318548202514648f;     // float(2 pi)
-  const float k2PiLo = -1.7484555314695172e-07f;  // 2 pi - float(2 pi)
-  const float n = rintf(x * kInv2Pi);
-  float r = fmaf(-n, k2PiHi, x);
-  r = fmaf(-n, k2PiLo, r);
-  *s = __sinf(r);
-  *c = __cosf(r);
-}
-
 struct FLayout {
   int VP, BS, WS, XS, HS;
   int off_B, off_Wh, off_Wl, off_X, off_H, off_phi, off_th, off_sc;

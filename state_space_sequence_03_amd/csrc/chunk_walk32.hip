@@ -1,0 +1,589 @@
+// Prefill walker for bf16 io with N = P = 64 (the 1.5B-scale head shapes):
+// 32-token sub-chunks, two blocks per compute unit.
+//
+// Computes what the other walkers compute (chunk.hip, chunk_fast.hip): the
+// chunked form of the exponential-trapezoidal recurrence with data-dependent
+// RoPE and rank-R inputs (linkstar.cloud/article/869, "第一刀", "第二刀",
+// "第三刀"; yetianai.com/news/16273, "榨干硬件算力").  A requested chunk of 32
+// or 64 tokens is walked as 32-token sub-chunks: the chunked form holds for
+// any split of the sequence, because the state carried across a boundary is
+// the exact state there.
+//
+// gfx950 data flow:
+//  * 256 threads and under 80 KB of LDS per block, so two blocks (two (b,h)
+//    sequences) share a compute unit and one block's staging and loads overlap
+//    the other block's matrix work.
+//  * Coalesced loads.  Staging thread (t, c) owns token t of the sub-chunk and
+//    the 16-byte column c of each rank row of B and x and of theta's row, so a
+//    wave instruction reads whole 128-byte rows.  Each wave keeps the C rows
+//    of its own output tiles in the MFMA operand layout (16 bytes per lane).
+//  * Cumulative log-decay and angles: wave scans over the 8 tokens a wave
+//    holds, plus an exchange of wave totals through LDS.  The wave scans of
+//    the next sub-chunk run at the end of the current one, so the exchange
+//    shares the sub-chunk's first barrier.
+//  * sin/cos are computed once per (token, pair) by the staging thread, which
+//    rotates all R ranks of B with them and stores them as an fp16 table for
+//    the rotation of C (C~ is rounded to bf16 afterwards, so the table's 2^-11
+//    rounding is far below the operand rounding).
+//  * LDS arrays keep their natural row layout with the 16-byte columns
+//    XOR-swizzled per row, so the 16-byte operand reads and the transpose
+//    reads (ds_read_b64_tr_b16) of 16 lanes fall in distinct banks.
+//  * Two barriers per sub-chunk: after the previous sub-chunk's last LDS read
+//    (and the scan exchange), and after staging.
+//
+// Precision matches the other bf16 walkers: bf16 MFMA operands with fp32
+// accumulation; the chunk state uses w B~ split into bf16 hi + lo parts.
+#include "m3_common.hpp"
+#include "m3_launch.hpp"
+
+namespace m3 {
+
+namespace {
+
+constexpr int W32_QS = 32;  // tokens per sub-chunk
+
+template <int R>
+struct W32 {
+  static constexpr int N = 64, P = 64, K = 32, QS = W32_QS, V = QS * R;
+  static constexpr int WROW = 2 * V;      // bytes per row of (w B~)^T
+  static constexpr int WCPR = WROW / 16;  // 16-byte columns per row of (w B~)^T
+  static constexpr int OFF_B = 0;                       // B~   [V][64] bf16
+  static constexpr int OFF_X = OFF_B + V * 128;         // X    [V][64] bf16
+  static constexpr int OFF_WH = OFF_X + V * 128;        // (w B~)^T hi [64][V] bf16
+  static constexpr int OFF_WL = OFF_WH + N * WROW;      // (w B~)^T lo
+  static constexpr int OFF_H = OFF_WL + N * WROW;       // H'^T [64][64] bf16
+  static constexpr int OFF_CS = OFF_H + P * 128;        // cos/sin [QS][K] fp16 pairs
+  static constexpr int OFF_SC = OFF_CS + QS * 128;      // per-token scalars [4][QS] fp32
+  static constexpr int OFF_TOT = OFF_SC + 4 * QS * 4;   // wave totals [4][36] fp32
+  static constexpr int OFF_TH = OFF_TOT + 4 * 36 * 4;   // chunk-total rotation [K] float2
+  static constexpr int BYTES = OFF_TH + K * 8;
+};
+static_assert(W32<4>::BYTES <= 80 * 1024, "two blocks per compute unit");
+
+// byte offset of 16-byte column `chunk` of row `row` in an array of 128-byte rows
+__device__ __forceinline__ int sw128(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+// the same for the rows of (w B~)^T (WCPR 16-byte columns per row)
+template <int WCPR>
+__device__ __forceinline__ int swW(int n, int chunk) {
+  const int f = WCPR == 4 ? ((n ^ (n >> 2)) & 3) : ((n ^ (n >> 3)) & (WCPR - 1));
+  return n * (WCPR * 16) + ((chunk ^ f) << 4);
+}
+// byte offset of the 8 bytes at (row, p0) of a 128-byte-row bf16 array (p0 % 4 == 0)
+__device__ __forceinline__ int sw128_8(int row, int p0) {
+  return sw128(row, p0 >> 3) + ((p0 & 4) << 1);
+}
+
+typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
+
+// v if keep, else zeros (component-wise selects: a select of the whole vector
+// struct is lowered through private memory)
+__device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
+  return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
+}
+__device__ __forceinline__ float4 keep_or_zero(bool keep, const float4& v) {
+  return make_float4(keep ? v.x : 0.0f, keep ? v.y : 0.0f, keep ? v.z : 0.0f, keep ? v.w : 0.0f);
+}
+
+}  // namespace
+
+bool walk32_supported(int io_bf16, int N, int P, int Q, int R) {
+  return io_bf16 && N == 64 && P == 64 && (Q == 32 || Q == 64) && (R == 1 || R == 2 || R == 4);
+}
+
+int walk_chunk(int io_bf16, int N, int P, int Q, int R) {
+  return walk32_supported(io_bf16, N, P, Q, R) ? W32_QS : Q;
+}
+
+template <int R>
+__global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
+  typedef W32<R> Ly;
+  constexpr int N = 64, P = 64, K = 32, QS = W32_QS, V = Ly::V, NW = 4;
+  constexpr int lgR = R == 4 ? 2 : (R == 2 ? 1 : 0);
+  constexpr int NCT = V / 16;               // column tiles of Y (16 virtual rows each)
+  constexpr int NCW = NCT == 8 ? 2 : 1;     // column tiles per wave
+  constexpr int PTW = NCT >= 4 ? 4 : 2;     // 16-wide p tiles per wave
+  constexpr int NKB = V / 32;               // 32-row slabs of the sub-chunk
+  constexpr float LOG2E = 1.4426950408889634f;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  unsigned char* sB = smem + Ly::OFF_B;
+  unsigned char* sX = smem + Ly::OFF_X;
+  unsigned char* sWh = smem + Ly::OFF_WH;
+  unsigned char* sWl = smem + Ly::OFF_WL;
+  unsigned char* sH = smem + Ly::OFF_H;
+  unsigned char* sCS = smem + Ly::OFF_CS;
+  float* sSC = (float*)(smem + Ly::OFF_SC);    // [0] log2 decay, [1] exp(decay), [2] q, [3] gamma
+  float* sTot = (float*)(smem + Ly::OFF_TOT);  // per wave: 32 angle totals, log-decay total
+  float2* sTh = (float2*)(smem + Ly::OFF_TH);
+
+  const int wave = threadIdx.x >> 6;
+  // lane coordinates; re-derived from an opaque copy of the thread id in every
+  // sub-chunk so that the compiler recomputes the LDS addresses next to their
+  // uses instead of hoisting dozens of them into registers for the whole walk
+  int tid, lane, m16, g, jj, uu, st_t, st_c;
+  auto coords = [&](int id) __attribute__((always_inline)) {
+    tid = id;
+    lane = id & 63;
+    m16 = lane & 15;
+    g = lane >> 4;
+    jj = m16 >> 2;          // transpose-read coordinates
+    uu = lane & 3;
+    st_t = id >> 3;         // staging: token, 16-byte column
+    st_c = id & 7;
+  };
+  coords(threadIdx.x);
+
+  const int64_t S = a.S;
+  const int64_t blk = blockIdx.x;
+  const int64_t seg = blk % S, bh = blk / S;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int64_t L = a.L, H = a.H;
+  const int64_t t0 = seg * a.seg_len;
+  const int64_t t1 = (t0 + a.seg_len < L) ? t0 + a.seg_len : L;
+  auto tokBC = [&](int64_t tok) { return ((b * L + tok) * H + h) * (int64_t)(R * N); };
+  auto tokX = [&](int64_t tok) { return ((b * L + tok) * H + h) * (int64_t)(R * P); };
+  auto tokS = [&](int64_t tok) { return (b * L + tok) * H + h; };
+  const int64_t nchunks_total = (L + QS - 1) / QS;
+
+  // output tiles of this wave: the causal work of tiles (w, NCT-1-w) is equal
+  int ctl[NCW];
+  if constexpr (NCW == 2) {
+    ctl[0] = NCT - 1 - wave;  // larger causal range first
+    ctl[1] = wave;
+  } else if constexpr (NCT == 4) {
+    ctl[0] = wave;
+  } else {
+    ctl[0] = wave & 1;
+  }
+  const int pt0 = PTW == 4 ? 0 : 2 * (wave >> 1);
+
+  // ---------------- prefetch registers (next sub-chunk) ----------------
+  uint4 rB[R], rX[R];
+  float4 rTh;
+  float rdt, rA, rlam, rdt1, rlam1;
+  uint4 rC[NCW][2];
+
+  auto load_BX = [&](int64_t c0) __attribute__((always_inline)) {
+    const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
+    const bool tv = st_t < nvalid;
+    const int64_t tok = c0 + (tv ? st_t : 0);
+    const u16* gB = (const u16*)a.B + tokBC(tok) + 8 * st_c;
+    const u16* gX = (const u16*)a.x + tokX(tok) + 8 * st_c;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      rB[r] = keep_or_zero(tv, *(const uint4*)(gB + r * N));
+      rX[r] = keep_or_zero(tv, *(const uint4*)(gX + r * P));
+    }
+  };
+  auto load_scal = [&](int64_t c0) __attribute__((always_inline)) {
+    const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
+    const bool tv = st_t < nvalid;
+    const int64_t tok = c0 + (tv ? st_t : 0);
+    const int64_t ts = tokS(tok);
+    rTh = keep_or_zero(tv, *(const float4*)(a.theta + ts * K + 4 * st_c));
+    const float d = a.dt[ts], av = a.A[ts], l = a.lam[ts];
+    rdt = tv ? d : 0.0f;
+    rA = tv ? av : 0.0f;
+    rlam = tv ? l : 0.0f;
+    // the following token (its epsilon weights this token's input in the state)
+    const bool tv1 = c0 + st_t + 1 < t1;
+    const int64_t ts1 = tokS(tv1 ? c0 + st_t + 1 : c0);
+    const float d1 = a.dt[ts1], l1 = a.lam[ts1];
+    rdt1 = tv1 ? d1 : 0.0f;
+    rlam1 = tv1 ? l1 : 0.0f;
+  };
+
+  auto load_C = [&](int64_t c0) __attribute__((always_inline)) {
+    const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
+#pragma unroll
+    for (int ci = 0; ci < NCW; ++ci) {
+      const int v = ctl[ci] * 16 + m16;
+      const bool ok = (v >> lgR) < nvalid;
+      const u16* row = (const u16*)a.C + tokBC(c0 + (ok ? (v >> lgR) : 0)) + (v & (R - 1)) * N + 8 * g;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        rC[ci][ks] = keep_or_zero(ok, *(const uint4*)(row + ks * 32));
+      }
+    }
+  };
+
+  // wave-level inclusive scans over this wave's 8 tokens (lanes 8 apart), for
+  // the sub-chunk held in the prefetch registers; wave totals go to LDS
+  float sc_l, sc_p[4];
+  auto local_scan = [&]() __attribute__((always_inline)) {
+    float v[5] = {rdt * rA, rdt * rTh.x, rdt * rTh.y, rdt * rTh.z, rdt * rTh.w};
+#pragma unroll
+    for (int o = 8; o < 64; o <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const float u = __shfl_up(v[i], o, 64);
+        if (lane >= o) v[i] += u;
+      }
+    }
+    sc_l = v[0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc_p[j] = v[1 + j];
+    if (lane >= 56) {
+      *(float4*)(sTot + wave * 36 + 4 * st_c) = make_float4(v[1], v[2], v[3], v[4]);
+      if (st_c == 0) sTot[wave * 36 + 32] = v[0];
+    }
+  };
+
+  // ---------------- state H' (fp32 registers): n-tile = wave, 4 p-tiles ----------------
+  f32x4 hst[4];
+  {
+    const void* pB = nullptr;
+    const void* px = nullptr;
+    int64_t pBo = 0, pxo = 0;
+    if (seg == 0) {
+      if (a.prev_B) { pB = a.prev_B; px = a.prev_x; pBo = bh * (int64_t)(R * N); pxo = bh * (int64_t)(R * P); }
+    } else {
+      pB = a.B; px = a.x; pBo = tokBC(t0 - 1); pxo = tokX(t0 - 1);
+    }
+    const float eps1 = (t0 < t1) ? (1.0f - a.lam[tokS(t0)]) * a.dt[tokS(t0)] : 0.0f;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const int p = pt * 16 + m16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = wave * 16 + 4 * g + i;
+        float v = 0.0f;
+        if (seg == 0 && a.h0) v = a.h0[bh * (int64_t)(N * P) + n * P + p];
+        if (pB) {
+          float acc = 0.0f;
+          for (int r = 0; r < R; ++r)
+            acc += bf2f(((const u16*)pB)[pBo + r * N + n]) * bf2f(((const u16*)px)[pxo + r * P + p]);
+          v += eps1 * acc;
+        }
+        hst[pt][i] = v;
+      }
+    }
+  }
+
+  float segLam = 0.0f, segPhi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float sub_lend = 0.0f;  // log-decay total of the current sub-chunk
+
+  if (t0 < t1) {
+    load_scal(t0);
+    load_BX(t0);
+    load_C(t0);
+    local_scan();
+  }
+
+  for (int64_t c0 = t0; c0 < t1; c0 += QS) {
+    {
+      int id = tid;
+      asm volatile("" : "+v"(id));
+      coords(id);
+    }
+    const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
+    __syncthreads();  // wave totals are in LDS; the previous sub-chunk's LDS reads are done
+
+    // H'^T (bf16) for the inter-chunk output
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const int p = pt * 16 + m16;
+      *(uint2*)(sH + sw128_8(p, wave * 16 + 4 * g)) =
+          make_uint2(pack_bf2(hst[pt][0], hst[pt][1]), pack_bf2(hst[pt][2], hst[pt][3]));
+    }
+
+    // ---------- staging ----------
+    {
+      float lpre = 0.0f, ltot = 0.0f, ppre[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ptot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const float4 pv = *(const float4*)(sTot + w2 * 36 + 4 * st_c);
+        const float lv = sTot[w2 * 36 + 32];
+        const bool below = w2 < wave;
+        lpre += below ? lv : 0.0f;
+        ppre[0] += below ? pv.x : 0.0f;
+        ppre[1] += below ? pv.y : 0.0f;
+        ppre[2] += below ? pv.z : 0.0f;
+        ppre[3] += below ? pv.w : 0.0f;
+        ltot += lv;
+        ptot[0] += pv.x;
+        ptot[1] += pv.y;
+        ptot[2] += pv.z;
+        ptot[3] += pv.w;
+      }
+      sub_lend = ltot;
+      const float lam_c = sc_l + lpre;  // Lambda_t, inclusive, from the sub-chunk start
+      const float gam = rlam * rdt;
+      const float q = gam + (1.0f - rlam1) * rdt1;  // gamma_t + epsilon_{t+1}
+      const float l2 = lam_c * LOG2E;
+      const float wt = __builtin_amdgcn_exp2f((ltot - lam_c) * LOG2E) * q;
+      if (st_c == 0) {
+        sSC[st_t] = l2;
+        sSC[QS + st_t] = __builtin_amdgcn_exp2f(l2);
+        sSC[2 * QS + st_t] = q;
+        sSC[3 * QS + st_t] = gam;
+      }
+      if (S > 1) {  // segment-relative offsets of this sub-chunk, for the fix-up pass
+        const int64_t mi = (bh * nchunks_total + c0 / QS) * (1 + K);
+        if (seg > 0) {
+          if (tid == 0) a.chunk_meta[mi] = segLam;
+          if (st_t == QS - 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.chunk_meta[mi + 1 + 4 * st_c + j] = segPhi[j];
+          }
+        }
+        segLam += ltot;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) segPhi[j] += ptot[j];
+      }
+      if (st_t == QS - 1) {  // rotation by the sub-chunk's total angle, for the state pass
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float s2, c2;
+          fast_sincos(ptot[j], &s2, &c2);
+          sTh[4 * st_c + j] = make_float2(c2, s2);
+        }
+      }
+      float cs[4], sn[4];
+      uint32_t tab[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        fast_sincos(sc_p[j] + ppre[j], &sn[j], &cs[j]);
+        tab[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cs[j], sn[j]));
+      }
+      *(uint4*)(sCS + sw128(st_t, st_c)) = make_uint4(tab[0], tab[1], tab[2], tab[3]);
+
+      // B~ = R(-phi) B for every rank; w B~ kept in fp32 for the hi/lo split
+      float wb[R][8];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const uint32_t w4[4] = {rB[r].x, rB[r].y, rB[r].z, rB[r].w};
+        float bt[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float u = bf_lo(w4[j]), w = bf_hi(w4[j]);
+          bt[2 * j] = cs[j] * u + sn[j] * w;
+          bt[2 * j + 1] = cs[j] * w - sn[j] * u;
+        }
+        *(uint4*)(sB + sw128(R * st_t + r, st_c)) =
+            make_uint4(pack_bf2(bt[0], bt[1]), pack_bf2(bt[2], bt[3]), pack_bf2(bt[4], bt[5]), pack_bf2(bt[6], bt[7]));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wb[r][e] = wt * bt[e];
+        *(uint4*)(sX + sw128(R * st_t + r, st_c)) = rX[r];
+      }
+      // (w B~)^T: row n, columns (token, rank): the R ranks of token t are adjacent
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int n = 8 * st_c + e;
+        const int byte = 2 * R * st_t;
+        const int off = swW<Ly::WCPR>(n, byte >> 4) + (byte & 15);
+        if constexpr (R == 4) {
+          const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]), h23 = pack_bf2(wb[2][e], wb[3][e]);
+          const uint32_t l01 = pack_bf2(wb[0][e] - bf_lo(h01), wb[1][e] - bf_hi(h01));
+          const uint32_t l23 = pack_bf2(wb[2][e] - bf_lo(h23), wb[3][e] - bf_hi(h23));
+          *(uint2*)(sWh + off) = make_uint2(h01, h23);
+          *(uint2*)(sWl + off) = make_uint2(l01, l23);
+        } else if constexpr (R == 2) {
+          const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]);
+          *(uint32_t*)(sWh + off) = h01;
+          *(uint32_t*)(sWl + off) = pack_bf2(wb[0][e] - bf_lo(h01), wb[1][e] - bf_hi(h01));
+        } else {
+          const uint32_t h0 = pack_bf2(wb[0][e], 0.0f);
+          *(u16*)(sWh + off) = (u16)(h0 & 0xffffu);
+          *(u16*)(sWl + off) = (u16)(pack_bf2(wb[0][e] - bf_lo(h0), 0.0f) & 0xffffu);
+        }
+      }
+    }
+    __syncthreads();  // B~, X, (w B~)^T, H'^T, the cos/sin table and the scalars are in LDS
+    const bool more = c0 + QS < t1;
+    if (more) load_scal(c0 + QS);
+
+    // own C~ fragments (operand layout: row v = tile*16 + m16, n = ks*32 + 8g + j)
+    uint4 rCt[NCW][2];
+#pragma unroll
+    for (int ci = 0; ci < NCW; ++ci) {
+      const int t = (ctl[ci] * 16 + m16) >> lgR;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 tb = *(const uint4*)(sCS + sw128(t, 4 * ks + g));
+        const uint32_t tw[4] = {tb.x, tb.y, tb.z, tb.w};
+        const uint32_t cw[4] = {rC[ci][ks].x, rC[ci][ks].y, rC[ci][ks].z, rC[ci][ks].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const half2_t cs2 = __builtin_bit_cast(half2_t, tw[j]);
+          const float co = (float)cs2[0], si = (float)cs2[1];
+          const float u = bf_lo(cw[j]), w = bf_hi(cw[j]);
+          o[j] = pack_bf2(co * u + si * w, co * w - si * u);
+        }
+        rCt[ci][ks] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+
+    // ---------- outputs: Y^T = exp(Lam_t) H'^T C~^T + X^T (G o M)^T ----------
+    {
+      f32x4 yacc[NCW][PTW];
+      int tcol[NCW];
+      float Lt[NCW], gt[NCW];
+#pragma unroll
+      for (int ci = 0; ci < NCW; ++ci) {
+        tcol[ci] = (ctl[ci] * 16 + m16) >> lgR;
+        Lt[ci] = sSC[tcol[ci]];
+        gt[ci] = sSC[3 * QS + tcol[ci]];
+        const float eLt = sSC[QS + tcol[ci]];
+#pragma unroll
+        for (int pp = 0; pp < PTW; ++pp) {
+          const int p = (pt0 + pp) * 16 + m16;
+          f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const uint4 hf = *(const uint4*)(sH + sw128(p, 4 * ks + g));
+            acc = mfma_bf16(as_bf16x8(hf), as_bf16x8(rCt[ci][ks]), acc);
+          }
+          yacc[ci][pp] = acc * eLt;
+        }
+      }
+      // shared loop over 32-row source slabs; tile 0 has the larger causal range
+      const int nkb0 = ((ctl[0] + 1) * 16 + 31) / 32;
+      const int nkb1 = NCW == 2 ? ((ctl[NCW - 1] + 1) * 16 + 31) / 32 : 0;
+      for (int kb = 0; kb < nkb0; ++kb) {
+        uint4 bfr[2][2];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            bfr[sub][ks] = *(const uint4*)(sB + sw128(kb * 32 + sub * 16 + m16, 4 * ks + g));
+#pragma unroll
+        for (int ci = 0; ci < NCW; ++ci) {
+          if (ci == 1 && kb >= nkb1) continue;
+          float gm[2][4];
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            f32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc = mfma_bf16(as_bf16x8(bfr[sub][ks]), as_bf16x8(rCt[ci][ks]), acc);
+            const int srow0 = kb * 32 + sub * 16 + 4 * g;
+            // s < t: decay * q_s;  s == t: gamma_t;  else 0 (selected arithmetically)
+            if constexpr (R == 4) {
+              const int s = srow0 >> 2;
+              const float e = __builtin_amdgcn_exp2f(fminf(Lt[ci] - sSC[s], 0.0f)) * sSC[2 * QS + s];
+              const float m = ((s < tcol[ci]) ? 1.0f : 0.0f) * e + ((s == tcol[ci]) ? gt[ci] : 0.0f);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) gm[sub][i] = acc[i] * m;
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int s = (srow0 + i) >> lgR;
+                const float e = __builtin_amdgcn_exp2f(fminf(Lt[ci] - sSC[s], 0.0f)) * sSC[2 * QS + s];
+                const float m = ((s < tcol[ci]) ? 1.0f : 0.0f) * e + ((s == tcol[ci]) ? gt[ci] : 0.0f);
+                gm[sub][i] = acc[i] * m;
+              }
+            }
+          }
+          const uint4 gfr = make_uint4(pack_bf2(gm[0][0], gm[0][1]), pack_bf2(gm[0][2], gm[0][3]),
+                                       pack_bf2(gm[1][0], gm[1][1]), pack_bf2(gm[1][2], gm[1][3]));
+          // X^T fragments in the score operand's k order (rows 4g.. and 16 + 4g.. of the slab)
+#pragma unroll
+          for (int pp = 0; pp < PTW; ++pp) {
+            const int p0 = (pt0 + pp) * 16 + 4 * uu;
+            const uint2 f0 = lds_tr16(sX + sw128_8(kb * 32 + 4 * g + jj, p0));
+            const uint2 f1 = lds_tr16(sX + sw128_8(kb * 32 + 16 + 4 * g + jj, p0));
+            yacc[ci][pp] = mfma_bf16(as_bf16x8(make_uint4(f0.x, f0.y, f1.x, f1.y)), as_bf16x8(gfr), yacc[ci][pp]);
+          }
+        }
+      }
+      // store y
+#pragma unroll
+      for (int ci = 0; ci < NCW; ++ci) {
+        if (tcol[ci] >= nvalid) continue;
+        const int vcol = ctl[ci] * 16 + m16;
+        u16* yrow = (u16*)a.y + tokX(c0 + tcol[ci]) + (vcol & (R - 1)) * P;
+#pragma unroll
+        for (int pp = 0; pp < PTW; ++pp)
+          *(uint2*)(yrow + (pt0 + pp) * 16 + 4 * g) = make_uint2(pack_bf2(yacc[ci][pp][0], yacc[ci][pp][1]),
+                                                                 pack_bf2(yacc[ci][pp][2], yacc[ci][pp][3]));
+      }
+    }
+
+    if (more) {
+      load_BX(c0 + QS);
+      load_C(c0 + QS);
+    }
+
+    // ---------- sub-chunk state S = (w B~)^T X (hi + lo) and the state pass ----------
+    {
+      f32x4 sacc[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) sacc[pt] = f32x4{0, 0, 0, 0};
+      const int n = wave * 16 + m16;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const uint4 ah = *(const uint4*)(sWh + swW<Ly::WCPR>(n, kb * 4 + g));
+        const uint4 al = *(const uint4*)(sWl + swW<Ly::WCPR>(n, kb * 4 + g));
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const int p0 = pt * 16 + 4 * uu;
+          const uint2 f0 = lds_tr16(sX + sw128_8(kb * 32 + 8 * g + jj, p0));
+          const uint2 f1 = lds_tr16(sX + sw128_8(kb * 32 + 8 * g + 4 + jj, p0));
+          const uint4 xb = make_uint4(f0.x, f0.y, f1.x, f1.y);
+          sacc[pt] = mfma_bf16(as_bf16x8(ah), as_bf16x8(xb), sacc[pt]);
+          sacc[pt] = mfma_bf16(as_bf16x8(al), as_bf16x8(xb), sacc[pt]);
+        }
+      }
+      const float eLend = __builtin_amdgcn_exp2f(sub_lend * LOG2E);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float2 cs = sTh[wave * 8 + 2 * g + q];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          const float u = eLend * hst[pt][2 * q] + sacc[pt][2 * q];
+          const float w = eLend * hst[pt][2 * q + 1] + sacc[pt][2 * q + 1];
+          hst[pt][2 * q] = cs.x * u - cs.y * w;
+          hst[pt][2 * q + 1] = cs.y * u + cs.x * w;
+        }
+      }
+    }
+    if (more) local_scan();
+  }
+
+  // ---------------- epilogue ----------------
+  float* dst = (S == 1) ? a.h_final : a.seg_end + blk * (int64_t)(N * P);
+  if (dst) {
+    float* base = (S == 1 ? dst + bh * (int64_t)(N * P) : dst);
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base[(wave * 16 + 4 * g + i) * P + pt * 16 + m16] = hst[pt][i];
+  }
+  if (S > 1) {
+    float* tot = a.seg_tot + blk * (1 + K);
+    if (tid == 0) tot[0] = segLam;
+    if (st_t == QS - 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tot[1 + 4 * st_c + j] = segPhi[j];
+    }
+  }
+}
+
+template <int R>
+static hipError_t w32_run(const WalkArgs& a, hipStream_t s) {
+  auto kern = walk32_kernel<R>;
+  static bool attr_set = false;  // per instantiation; the attribute is per function
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, W32<R>::BYTES);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int64_t blocks = a.batch * a.H * a.S;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), W32<R>::BYTES, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_walk32(const WalkArgs& a, hipStream_t s) {
+  if (a.Q != W32_QS) return hipErrorInvalidValue;
+  switch (a.R) {
+    case 1: return w32_run<1>(a, s);
+    case 2: return w32_run<2>(a, s);
+    case 4: return w32_run<4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace m3

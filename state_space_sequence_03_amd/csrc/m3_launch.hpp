@@ -52,6 +52,13 @@ size_t walk_lds_bytes(int io_bf16, int N, int P, int Q, int R);
 // The fast walker (bf16 io, N and P <= 64) applies to these sizes.
 bool walk_fast_supported(int io_bf16, int N, int P, int Q, int R);
 hipError_t launch_walk_fast(int N, int P, const WalkArgs& a, hipStream_t s);
+// The 32-token sub-chunk walker (bf16 io, N = P = 64, requested chunk 32 or 64)
+// applies to these sizes; it walks with chunk length 32.
+bool walk32_supported(int io_bf16, int N, int P, int Q, int R);
+hipError_t launch_walk32(const WalkArgs& a, hipStream_t s);
+// Chunk length the walk actually uses for a requested chunk Q (segment
+// lengths, per-chunk offsets and the fix-up pass follow it).
+int walk_chunk(int io_bf16, int N, int P, int Q, int R);
 // Chunked forward walk: fast walker when it applies, general walker otherwise.
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
 
