@@ -45,46 +45,36 @@ constexpr int W32_QS = 32;  // tokens per sub-chunk
 template <int R>
 struct W32 {
   static constexpr int N = 64, P = 64, K = 32, QS = W32_QS, V = QS * R;
+  static constexpr int XP = 144;          // bytes per X row (128 + 16: transpose reads of 4 rows hit distinct banks)
   static constexpr int WROW = 2 * V;      // bytes per row of (w B~)^T
   static constexpr int WCPR = WROW / 16;  // 16-byte columns per row of (w B~)^T
-  static constexpr int OFF_B = 0;                       // B~   [V][64] bf16
-  static constexpr int OFF_X = OFF_B + V * 128;         // X    [V][64] bf16
-  static constexpr int OFF_WH = OFF_X + V * 128;        // (w B~)^T hi [64][V] bf16
+  static constexpr int OFF_B = 0;                       // B~   [V][64] bf16, swizzled
+  static constexpr int OFF_X = OFF_B + V * 128;         // X    [V][64] bf16, padded rows
+  static constexpr int OFF_WH = OFF_X + V * XP;         // (w B~)^T hi [64][V] bf16, swizzled
   static constexpr int OFF_WL = OFF_WH + N * WROW;      // (w B~)^T lo
-  static constexpr int OFF_H = OFF_WL + N * WROW;       // H'^T [64][64] bf16
-  static constexpr int OFF_CS = OFF_H + P * 128;        // cos/sin [QS][K] fp16 pairs
-  static constexpr int OFF_SC = OFF_CS + QS * 128;      // per-token scalars [4][QS] fp32
-  static constexpr int OFF_TOT = OFF_SC + 4 * QS * 4;   // wave totals [4][36] fp32
+  static constexpr int OFF_H = OFF_WL + N * WROW;       // H'^T [64][64] bf16, swizzled
+  static constexpr int OFF_CS = OFF_H + P * 128;        // cos/sin [QS][K] fp16 pairs, swizzled
+  static constexpr int OFF_SC = OFF_CS + QS * 128;      // per token: log2 decay, q, gamma, exp(decay)
+  static constexpr int OFF_TOT = OFF_SC + QS * 16;      // wave totals [4][36] fp32
   static constexpr int OFF_TH = OFF_TOT + 4 * 36 * 4;   // chunk-total rotation [K] float2
   static constexpr int BYTES = OFF_TH + K * 8;
 };
 static_assert(W32<4>::BYTES <= 80 * 1024, "two blocks per compute unit");
 
-// byte offset of 16-byte column `chunk` of row `row` in an array of 128-byte rows
-__device__ __forceinline__ int sw128(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
-// the same for the rows of (w B~)^T (WCPR 16-byte columns per row)
+// Swizzle of an array of 128-byte rows: 16-byte column c of row r is stored
+// at column c ^ f(r).  f depends only on r mod 16, so the rows of a 16-row
+// tile, at any tile offset, share one pattern, and 16 consecutive rows read
+// at one logical column fall in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int f16rows(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int sw128(int row, int chunk) { return row * 128 + ((chunk ^ f16rows(row)) << 4); }
+// rows of (w B~)^T (WCPR 16-byte columns): 16 consecutive rows, and the 8
+// rows 8 apart that one staging instruction writes, both spread over banks
 template <int WCPR>
-__device__ __forceinline__ int swW(int n, int chunk) {
-  const int f = WCPR == 4 ? ((n ^ (n >> 2)) & 3) : ((n ^ (n >> 3)) & (WCPR - 1));
-  return n * (WCPR * 16) + ((chunk ^ f) << 4);
-}
-// byte offset of the 8 bytes at (row, p0) of a 128-byte-row bf16 array (p0 % 4 == 0)
-__device__ __forceinline__ int sw128_8(int row, int p0) {
-  return sw128(row, p0 >> 3) + ((p0 & 4) << 1);
+__device__ __forceinline__ int fW(int n) {
+  return WCPR == 4 ? ((n ^ (n >> 2)) & 3) : ((n ^ (n >> 3)) & (WCPR - 1));
 }
 
 typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
-
-// v if keep, else zeros (component-wise selects: a select of the whole vector
-// struct is lowered through private memory)
-__device__ __forceinline__ uint4 keep_or_zero(bool keep, const uint4& v) {
-  return make_uint4(keep ? v.x : 0u, keep ? v.y : 0u, keep ? v.z : 0u, keep ? v.w : 0u);
-}
-__device__ __forceinline__ float4 keep_or_zero(bool keep, const float4& v) {
-  return make_float4(keep ? v.x : 0.0f, keep ? v.y : 0.0f, keep ? v.z : 0.0f, keep ? v.w : 0.0f);
-}
 
 }  // namespace
 
@@ -114,7 +104,7 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
   unsigned char* sWl = smem + Ly::OFF_WL;
   unsigned char* sH = smem + Ly::OFF_H;
   unsigned char* sCS = smem + Ly::OFF_CS;
-  float* sSC = (float*)(smem + Ly::OFF_SC);    // [0] log2 decay, [1] exp(decay), [2] q, [3] gamma
+  float4* sSC = (float4*)(smem + Ly::OFF_SC);  // per token: log2 decay, q, gamma, exp(decay)
   float* sTot = (float*)(smem + Ly::OFF_TOT);  // per wave: 32 angle totals, log-decay total
   float2* sTh = (float2*)(smem + Ly::OFF_TH);
 
@@ -165,31 +155,32 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
   float rdt, rA, rlam, rdt1, rlam1;
   uint4 rC[NCW][2];
 
+  // Tokens past the end of the segment read the last valid token instead: only
+  // their dt, lam (hence q = gamma = 0) are zeroed, which removes them exactly
+  // from the scores, the outputs and the state while every operand stays finite.
   auto load_BX = [&](int64_t c0) __attribute__((always_inline)) {
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
-    const bool tv = st_t < nvalid;
-    const int64_t tok = c0 + (tv ? st_t : 0);
-    const u16* gB = (const u16*)a.B + tokBC(tok) + 8 * st_c;
-    const u16* gX = (const u16*)a.x + tokX(tok) + 8 * st_c;
+    const int64_t row = tokS(c0 + (st_t < nvalid ? st_t : nvalid - 1));
+    const u16* gB = (const u16*)a.B + row * (R * N) + 8 * st_c;
+    const u16* gX = (const u16*)a.x + row * (R * P) + 8 * st_c;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      rB[r] = keep_or_zero(tv, *(const uint4*)(gB + r * N));
-      rX[r] = keep_or_zero(tv, *(const uint4*)(gX + r * P));
+      rB[r] = *(const uint4*)(gB + r * N);
+      rX[r] = *(const uint4*)(gX + r * P);
     }
   };
   auto load_scal = [&](int64_t c0) __attribute__((always_inline)) {
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
     const bool tv = st_t < nvalid;
-    const int64_t tok = c0 + (tv ? st_t : 0);
-    const int64_t ts = tokS(tok);
-    rTh = keep_or_zero(tv, *(const float4*)(a.theta + ts * K + 4 * st_c));
+    const int64_t ts = tokS(c0 + (tv ? st_t : nvalid - 1));
+    rTh = *(const float4*)(a.theta + ts * K + 4 * st_c);
     const float d = a.dt[ts], av = a.A[ts], l = a.lam[ts];
     rdt = tv ? d : 0.0f;
     rA = tv ? av : 0.0f;
     rlam = tv ? l : 0.0f;
     // the following token (its epsilon weights this token's input in the state)
     const bool tv1 = c0 + st_t + 1 < t1;
-    const int64_t ts1 = tokS(tv1 ? c0 + st_t + 1 : c0);
+    const int64_t ts1 = tv1 ? ts + H : ts;
     const float d1 = a.dt[ts1], l1 = a.lam[ts1];
     rdt1 = tv1 ? d1 : 0.0f;
     rlam1 = tv1 ? l1 : 0.0f;
@@ -200,12 +191,10 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
 #pragma unroll
     for (int ci = 0; ci < NCW; ++ci) {
       const int v = ctl[ci] * 16 + m16;
-      const bool ok = (v >> lgR) < nvalid;
-      const u16* row = (const u16*)a.C + tokBC(c0 + (ok ? (v >> lgR) : 0)) + (v & (R - 1)) * N + 8 * g;
+      const int t = (v >> lgR) < nvalid ? (v >> lgR) : nvalid - 1;
+      const u16* row = (const u16*)a.C + tokS(c0 + t) * (R * N) + (v & (R - 1)) * N + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        rC[ci][ks] = keep_or_zero(ok, *(const uint4*)(row + ks * 32));
-      }
+      for (int ks = 0; ks < 2; ++ks) rC[ci][ks] = *(const uint4*)(row + ks * 32);
     }
   };
 
@@ -279,63 +268,56 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       coords(id);
     }
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
+    const int fm = f16rows(m16);  // swizzle of the rows m16 (+ multiples of 16) of a tile
     __syncthreads();  // wave totals are in LDS; the previous sub-chunk's LDS reads are done
 
-    // H'^T (bf16) for the inter-chunk output
+    // H'^T (bf16) for the inter-chunk output: row p = 16 pt + m16, columns n = 16 wave + 4g ..
+    {
+      unsigned char* hw = sH + m16 * 128 + (((2 * wave + (g >> 1)) ^ fm) << 4) + 8 * (g & 1);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const int p = pt * 16 + m16;
-      *(uint2*)(sH + sw128_8(p, wave * 16 + 4 * g)) =
-          make_uint2(pack_bf2(hst[pt][0], hst[pt][1]), pack_bf2(hst[pt][2], hst[pt][3]));
+      for (int pt = 0; pt < 4; ++pt)
+        *(uint2*)(hw + pt * 2048) = make_uint2(pack_bf2(hst[pt][0], hst[pt][1]), pack_bf2(hst[pt][2], hst[pt][3]));
     }
 
     // ---------- staging ----------
     {
-      float lpre = 0.0f, ltot = 0.0f, ppre[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ptot[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
+      // prefix over the lower waves (uniform loop) and the sub-chunk's log-decay total
+      float lpre = 0.0f, ppre[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int w2 = 0; w2 < wave; ++w2) {
         const float4 pv = *(const float4*)(sTot + w2 * 36 + 4 * st_c);
-        const float lv = sTot[w2 * 36 + 32];
-        const bool below = w2 < wave;
-        lpre += below ? lv : 0.0f;
-        ppre[0] += below ? pv.x : 0.0f;
-        ppre[1] += below ? pv.y : 0.0f;
-        ppre[2] += below ? pv.z : 0.0f;
-        ppre[3] += below ? pv.w : 0.0f;
-        ltot += lv;
-        ptot[0] += pv.x;
-        ptot[1] += pv.y;
-        ptot[2] += pv.z;
-        ptot[3] += pv.w;
+        lpre += sTot[w2 * 36 + 32];
+        ppre[0] += pv.x;
+        ppre[1] += pv.y;
+        ppre[2] += pv.z;
+        ppre[3] += pv.w;
       }
+      const float ltot = sTot[32] + sTot[36 + 32] + sTot[72 + 32] + sTot[108 + 32];
       sub_lend = ltot;
       const float lam_c = sc_l + lpre;  // Lambda_t, inclusive, from the sub-chunk start
       const float gam = rlam * rdt;
       const float q = gam + (1.0f - rlam1) * rdt1;  // gamma_t + epsilon_{t+1}
       const float l2 = lam_c * LOG2E;
       const float wt = __builtin_amdgcn_exp2f((ltot - lam_c) * LOG2E) * q;
-      if (st_c == 0) {
-        sSC[st_t] = l2;
-        sSC[QS + st_t] = __builtin_amdgcn_exp2f(l2);
-        sSC[2 * QS + st_t] = q;
-        sSC[3 * QS + st_t] = gam;
-      }
+      if (st_c == 0) sSC[st_t] = make_float4(l2, q, gam, __builtin_amdgcn_exp2f(l2));
       if (S > 1) {  // segment-relative offsets of this sub-chunk, for the fix-up pass
-        const int64_t mi = (bh * nchunks_total + c0 / QS) * (1 + K);
-        if (seg > 0) {
-          if (tid == 0) a.chunk_meta[mi] = segLam;
-          if (st_t == QS - 1) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a.chunk_meta[mi + 1 + 4 * st_c + j] = segPhi[j];
-          }
-        }
+        if (seg > 0 && tid == 0) a.chunk_meta[(bh * nchunks_total + c0 / QS) * (1 + K)] = segLam;
         segLam += ltot;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) segPhi[j] += ptot[j];
       }
-      if (st_t == QS - 1) {  // rotation by the sub-chunk's total angle, for the state pass
+      if (st_t == QS - 1) {  // last token: the sub-chunk's total angles
+        float ptot[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j) ptot[j] = sc_p[j] + ppre[j];
+        if (S > 1) {
+          if (seg > 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              a.chunk_meta[(bh * nchunks_total + c0 / QS) * (1 + K) + 1 + 4 * st_c + j] = segPhi[j];
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) segPhi[j] += ptot[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // rotation by the total angle, for the state pass
           float s2, c2;
           fast_sincos(ptot[j], &s2, &c2);
           sTh[4 * st_c + j] = make_float2(c2, s2);
@@ -352,6 +334,7 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
 
       // B~ = R(-phi) B for every rank; w B~ kept in fp32 for the hi/lo split
       float wb[R][8];
+      unsigned char* xw = sX + R * st_t * Ly::XP + 16 * st_c;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const uint32_t w4[4] = {rB[r].x, rB[r].y, rB[r].z, rB[r].w};
@@ -366,34 +349,42 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
             make_uint4(pack_bf2(bt[0], bt[1]), pack_bf2(bt[2], bt[3]), pack_bf2(bt[4], bt[5]), pack_bf2(bt[6], bt[7]));
 #pragma unroll
         for (int e = 0; e < 8; ++e) wb[r][e] = wt * bt[e];
-        *(uint4*)(sX + sw128(R * st_t + r, st_c)) = rX[r];
+        *(uint4*)(xw + r * Ly::XP) = make_uint4(rX[r].x, rX[r].y, rX[r].z, rX[r].w);
       }
-      // (w B~)^T: row n, columns (token, rank): the R ranks of token t are adjacent
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int n = 8 * st_c + e;
+      // (w B~)^T: row n = 8 st_c + e, columns (token, rank): the R ranks of token t are adjacent
+      {
         const int byte = 2 * R * st_t;
-        const int off = swW<Ly::WCPR>(n, byte >> 4) + (byte & 15);
-        if constexpr (R == 4) {
-          const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]), h23 = pack_bf2(wb[2][e], wb[3][e]);
-          const uint32_t l01 = pack_bf2(wb[0][e] - bf_lo(h01), wb[1][e] - bf_hi(h01));
-          const uint32_t l23 = pack_bf2(wb[2][e] - bf_lo(h23), wb[3][e] - bf_hi(h23));
-          *(uint2*)(sWh + off) = make_uint2(h01, h23);
-          *(uint2*)(sWl + off) = make_uint2(l01, l23);
-        } else if constexpr (R == 2) {
-          const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]);
-          *(uint32_t*)(sWh + off) = h01;
-          *(uint32_t*)(sWl + off) = pack_bf2(wb[0][e] - bf_lo(h01), wb[1][e] - bf_hi(h01));
-        } else {
-          const uint32_t h0 = pack_bf2(wb[0][e], 0.0f);
-          *(u16*)(sWh + off) = (u16)(h0 & 0xffffu);
-          *(u16*)(sWl + off) = (u16)(pack_bf2(wb[0][e] - bf_lo(h0), 0.0f) & 0xffffu);
+        const int cb = byte >> 4;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int n = 8 * st_c + e;
+          const int off = n * Ly::WROW + ((cb ^ fW<Ly::WCPR>(n)) << 4) + (byte & 15);
+          if constexpr (R == 4) {
+            const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]), h23 = pack_bf2(wb[2][e], wb[3][e]);
+            const uint32_t l01 = pack_bf2(wb[0][e] - bf_lo(h01), wb[1][e] - bf_hi(h01));
+            const uint32_t l23 = pack_bf2(wb[2][e] - bf_lo(h23), wb[3][e] - bf_hi(h23));
+            *(uint2*)(sWh + off) = make_uint2(h01, h23);
+            *(uint2*)(sWl + off) = make_uint2(l01, l23);
+          } else if constexpr (R == 2) {
+            const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]);
+            *(uint32_t*)(sWh + off) = h01;
+            *(uint32_t*)(sWl + off) = pack_bf2(wb[0][e] - bf_lo(h01), wb[1][e] - bf_hi(h01));
+          } else {
+            const uint32_t h0 = pack_bf2(wb[0][e], 0.0f);
+            *(u16*)(sWh + off) = (u16)(h0 & 0xffffu);
+            *(u16*)(sWl + off) = (u16)(pack_bf2(wb[0][e] - bf_lo(h0), 0.0f) & 0xffffu);
+          }
         }
       }
     }
     __syncthreads();  // B~, X, (w B~)^T, H'^T, the cos/sin table and the scalars are in LDS
+    // next sub-chunk's loads go out as early as their registers are free: they
+    // then have the whole Y and S phases to arrive
     const bool more = c0 + QS < t1;
-    if (more) load_scal(c0 + QS);
+    if (more) {
+      load_scal(c0 + QS);
+      load_BX(c0 + QS);
+    }
 
     // own C~ fragments (operand layout: row v = tile*16 + m16, n = ks*32 + 8g + j)
     uint4 rCt[NCW][2];
@@ -417,27 +408,39 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       }
     }
 
+    if (more) load_C(c0 + QS);
+
     // ---------- outputs: Y^T = exp(Lam_t) H'^T C~^T + X^T (G o M)^T ----------
     {
+      // per-lane bases: the 16-row tiles of B~ and H'^T at n column 8g (ks = 0) and
+      // 32 + 8g (ks = 1); the X^T transpose reads at rows 4g + jj and p = pt0*16 + 4uu
+      const unsigned char* bB[2];
+      const unsigned char* bH[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bB[ks] = sB + m16 * 128 + (((4 * ks + g) ^ fm) << 4);
+        bH[ks] = sH + m16 * 128 + (((4 * ks + g) ^ fm) << 4);
+      }
+      const unsigned char* bXt = sX + (4 * g + jj) * Ly::XP + 2 * (pt0 * 16 + 4 * uu);
+
       f32x4 yacc[NCW][PTW];
       int tcol[NCW];
       float Lt[NCW], gt[NCW];
 #pragma unroll
       for (int ci = 0; ci < NCW; ++ci) {
         tcol[ci] = (ctl[ci] * 16 + m16) >> lgR;
-        Lt[ci] = sSC[tcol[ci]];
-        gt[ci] = sSC[3 * QS + tcol[ci]];
-        const float eLt = sSC[QS + tcol[ci]];
+        const float4 sc = sSC[tcol[ci]];
+        Lt[ci] = sc.x;
+        gt[ci] = sc.z;
 #pragma unroll
         for (int pp = 0; pp < PTW; ++pp) {
-          const int p = (pt0 + pp) * 16 + m16;
           f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) {
-            const uint4 hf = *(const uint4*)(sH + sw128(p, 4 * ks + g));
+            const uint4 hf = *(const uint4*)(bH[ks] + (pt0 + pp) * 2048);
             acc = mfma_bf16(as_bf16x8(hf), as_bf16x8(rCt[ci][ks]), acc);
           }
-          yacc[ci][pp] = acc * eLt;
+          yacc[ci][pp] = acc * sc.w;
         }
       }
       // shared loop over 32-row source slabs; tile 0 has the larger causal range
@@ -449,7 +452,8 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
-            bfr[sub][ks] = *(const uint4*)(sB + sw128(kb * 32 + sub * 16 + m16, 4 * ks + g));
+            bfr[sub][ks] = *(const uint4*)(bB[ks] + (kb * 32 + sub * 16) * 128);
+        const float2* scs = (const float2*)(sSC + kb * 8 + g);  // (log2 decay, q) of the lane's source token
 #pragma unroll
         for (int ci = 0; ci < NCW; ++ci) {
           if (ci == 1 && kb >= nkb1) continue;
@@ -459,19 +463,20 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
             f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) acc = mfma_bf16(as_bf16x8(bfr[sub][ks]), as_bf16x8(rCt[ci][ks]), acc);
-            const int srow0 = kb * 32 + sub * 16 + 4 * g;
             // s < t: decay * q_s;  s == t: gamma_t;  else 0 (selected arithmetically)
             if constexpr (R == 4) {
-              const int s = srow0 >> 2;
-              const float e = __builtin_amdgcn_exp2f(fminf(Lt[ci] - sSC[s], 0.0f)) * sSC[2 * QS + s];
+              const int s = kb * 8 + sub * 4 + g;
+              const float2 lq = scs[sub * 8];
+              const float e = __builtin_amdgcn_exp2f(fminf(Lt[ci] - lq.x, 0.0f)) * lq.y;
               const float m = ((s < tcol[ci]) ? 1.0f : 0.0f) * e + ((s == tcol[ci]) ? gt[ci] : 0.0f);
 #pragma unroll
               for (int i = 0; i < 4; ++i) gm[sub][i] = acc[i] * m;
             } else {
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const int s = (srow0 + i) >> lgR;
-                const float e = __builtin_amdgcn_exp2f(fminf(Lt[ci] - sSC[s], 0.0f)) * sSC[2 * QS + s];
+                const int s = (kb * 32 + sub * 16 + 4 * g + i) >> lgR;
+                const float2 lq = *(const float2*)(sSC + s);
+                const float e = __builtin_amdgcn_exp2f(fminf(Lt[ci] - lq.x, 0.0f)) * lq.y;
                 const float m = ((s < tcol[ci]) ? 1.0f : 0.0f) * e + ((s == tcol[ci]) ? gt[ci] : 0.0f);
                 gm[sub][i] = acc[i] * m;
               }
@@ -480,11 +485,11 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
           const uint4 gfr = make_uint4(pack_bf2(gm[0][0], gm[0][1]), pack_bf2(gm[0][2], gm[0][3]),
                                        pack_bf2(gm[1][0], gm[1][1]), pack_bf2(gm[1][2], gm[1][3]));
           // X^T fragments in the score operand's k order (rows 4g.. and 16 + 4g.. of the slab)
+          const unsigned char* xk = bXt + kb * 32 * Ly::XP;
 #pragma unroll
           for (int pp = 0; pp < PTW; ++pp) {
-            const int p0 = (pt0 + pp) * 16 + 4 * uu;
-            const uint2 f0 = lds_tr16(sX + sw128_8(kb * 32 + 4 * g + jj, p0));
-            const uint2 f1 = lds_tr16(sX + sw128_8(kb * 32 + 16 + 4 * g + jj, p0));
+            const uint2 f0 = lds_tr16(xk + pp * 32);
+            const uint2 f1 = lds_tr16(xk + 16 * Ly::XP + pp * 32);
             yacc[ci][pp] = mfma_bf16(as_bf16x8(make_uint4(f0.x, f0.y, f1.x, f1.y)), as_bf16x8(gfr), yacc[ci][pp]);
           }
         }
@@ -501,27 +506,24 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
                                                                  pack_bf2(yacc[ci][pp][2], yacc[ci][pp][3]));
       }
     }
-
-    if (more) {
-      load_BX(c0 + QS);
-      load_C(c0 + QS);
-    }
-
     // ---------- sub-chunk state S = (w B~)^T X (hi + lo) and the state pass ----------
     {
       f32x4 sacc[4];
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) sacc[pt] = f32x4{0, 0, 0, 0};
       const int n = wave * 16 + m16;
+      const int gf = g ^ fW<Ly::WCPR>(n);
+      const unsigned char* bW = sWh + n * Ly::WROW;
+      const unsigned char* bXs = sX + (8 * g + jj) * Ly::XP + 8 * uu;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const uint4 ah = *(const uint4*)(sWh + swW<Ly::WCPR>(n, kb * 4 + g));
-        const uint4 al = *(const uint4*)(sWl + swW<Ly::WCPR>(n, kb * 4 + g));
+        const int wo = ((4 * kb) ^ gf) << 4;
+        const uint4 ah = *(const uint4*)(bW + wo);
+        const uint4 al = *(const uint4*)(bW + (Ly::OFF_WL - Ly::OFF_WH) + wo);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const int p0 = pt * 16 + 4 * uu;
-          const uint2 f0 = lds_tr16(sX + sw128_8(kb * 32 + 8 * g + jj, p0));
-          const uint2 f1 = lds_tr16(sX + sw128_8(kb * 32 + 8 * g + 4 + jj, p0));
+          const uint2 f0 = lds_tr16(bXs + kb * 32 * Ly::XP + pt * 32);
+          const uint2 f1 = lds_tr16(bXs + (kb * 32 + 4) * Ly::XP + pt * 32);
           const uint4 xb = make_uint4(f0.x, f0.y, f1.x, f1.y);
           sacc[pt] = mfma_bf16(as_bf16x8(ah), as_bf16x8(xb), sacc[pt]);
           sacc[pt] = mfma_bf16(as_bf16x8(al), as_bf16x8(xb), sacc[pt]);

@@ -101,6 +101,13 @@ FWD_CASES = [
     ("bf16", 1, 5, 2, 16, 16, 1, 16, True, True),
     ("bf16", 1, 64, 1, 128, 64, 4, 32, False, False),
     ("bf16", 1, 33, 2, 16, 128, 1, 16, True, True),
+    # the 32-token walker (bf16, N = P = 64, Q 32 or 64): every rank, ragged
+    # tails, a single-token tail, and sequences shorter than one sub-chunk
+    ("bf16", 2, 161, 2, 64, 64, 2, 32, True, False),
+    ("bf16", 1, 97, 3, 64, 64, 4, 32, False, True),
+    ("bf16", 1, 31, 2, 64, 64, 2, 64, True, True),
+    ("bf16", 1, 33, 1, 64, 64, 1, 32, False, False),
+    ("bf16", 3, 64, 2, 64, 64, 4, 64, True, True),
 ]
 
 
