@@ -22,9 +22,11 @@
 //    the next sub-chunk run at the end of the current one, so the exchange
 //    shares the sub-chunk's first barrier.
 //  * sin/cos are computed once per (token, pair) by the staging thread, which
-//    rotates all R ranks of B with them and stores them as an fp16 table for
-//    the rotation of C (C~ is rounded to bf16 afterwards, so the table's 2^-11
-//    rounding is far below the operand rounding).
+//    rotates all R ranks of B with them and stores them as a bf16 table for
+//    the rotation of C: two bf16 dot products per pair (fp32 sums), the result
+//    rounded to bf16 like every MFMA operand.
+//  * y leaves the wave as 32 contiguous bytes per lane after a 4 x 4 transpose
+//    across the wave's 16-lane rows.
 //  * LDS arrays keep their natural row layout with the 16-byte columns
 //    XOR-swizzled per row, so the 16-byte operand reads and the transpose
 //    reads (ds_read_b64_tr_b16) of 16 lanes fall in distinct banks.
@@ -53,7 +55,7 @@ struct W32 {
   static constexpr int OFF_WH = OFF_X + V * XP;         // (w B~)^T hi [64][V] bf16, swizzled
   static constexpr int OFF_WL = OFF_WH + N * WROW;      // (w B~)^T lo
   static constexpr int OFF_H = OFF_WL + N * WROW;       // H'^T [64][64] bf16, swizzled
-  static constexpr int OFF_CS = OFF_H + P * 128;        // cos/sin [QS][K] fp16 pairs, swizzled
+  static constexpr int OFF_CS = OFF_H + P * 128;        // (cos, sin) [QS][K] bf16 pairs, swizzled
   static constexpr int OFF_SC = OFF_CS + QS * 128;      // per token: log2 decay, q, gamma, exp(decay)
   static constexpr int OFF_TOT = OFF_SC + QS * 16;      // wave totals [4][36] fp32
   static constexpr int OFF_TH = OFF_TOT + 4 * 36 * 4;   // chunk-total rotation [K] float2
@@ -74,7 +76,24 @@ __device__ __forceinline__ int fW(int n) {
   return WCPR == 4 ? ((n ^ (n >> 2)) & 3) : ((n ^ (n >> 3)) & (WCPR - 1));
 }
 
-typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
+// d[k] of 16-lane row r becomes d[r] of row k: a 4 x 4 transpose of (row of
+// the wave) x (register) with the gfx950 row swaps (permlane32_swap exchanges
+// rows 2,3 of its first operand with rows 0,1 of its second; permlane16_swap
+// the odd rows of the first with the even rows of the second)
+__device__ __forceinline__ void transpose_rows4(uint32_t* d) {
+  auto s = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  d[0] = s[0];
+  d[2] = s[1];
+  s = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  d[1] = s[0];
+  d[3] = s[1];
+  s = __builtin_amdgcn_permlane16_swap(d[0], d[1], false, false);
+  d[0] = s[0];
+  d[1] = s[1];
+  s = __builtin_amdgcn_permlane16_swap(d[2], d[3], false, false);
+  d[2] = s[0];
+  d[3] = s[1];
+}
 
 }  // namespace
 
@@ -298,6 +317,10 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       const float q = gam + (1.0f - rlam1) * rdt1;  // gamma_t + epsilon_{t+1}
       const float l2 = lam_c * LOG2E;
       const float wt = __builtin_amdgcn_exp2f((ltot - lam_c) * LOG2E) * q;
+      // R >= 2: the next sub-chunk's scalars, B and x are requested as soon as
+      // this staging has read their registers (measured: slower for R = 1)
+      if constexpr (R >= 2)
+        if (c0 + QS < t1) load_scal(c0 + QS);
       if (st_c == 0) sSC[st_t] = make_float4(l2, q, gam, __builtin_amdgcn_exp2f(l2));
       if (S > 1) {  // segment-relative offsets of this sub-chunk, for the fix-up pass
         if (seg > 0 && tid == 0) a.chunk_meta[(bh * nchunks_total + c0 / QS) * (1 + K)] = segLam;
@@ -328,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         fast_sincos(sc_p[j] + ppre[j], &sn[j], &cs[j]);
-        tab[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(cs[j], sn[j]));
+        tab[j] = pack_bf2(cs[j], sn[j]);
       }
       *(uint4*)(sCS + sw128(st_t, st_c)) = make_uint4(tab[0], tab[1], tab[2], tab[3]);
 
@@ -351,6 +374,8 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
         for (int e = 0; e < 8; ++e) wb[r][e] = wt * bt[e];
         *(uint4*)(xw + r * Ly::XP) = make_uint4(rX[r].x, rX[r].y, rX[r].z, rX[r].w);
       }
+      if constexpr (R >= 2)
+        if (c0 + QS < t1) load_BX(c0 + QS);
       // (w B~)^T: row n = 8 st_c + e, columns (token, rank): the R ranks of token t are adjacent
       {
         const int byte = 2 * R * st_t;
@@ -381,9 +406,11 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
     // next sub-chunk's loads go out as early as their registers are free: they
     // then have the whole Y and S phases to arrive
     const bool more = c0 + QS < t1;
-    if (more) {
-      load_scal(c0 + QS);
-      load_BX(c0 + QS);
+    if constexpr (R == 1) {
+      if (more) {
+        load_scal(c0 + QS);
+        load_BX(c0 + QS);
+      }
     }
 
     // own C~ fragments (operand layout: row v = tile*16 + m16, n = ks*32 + 8g + j)
@@ -399,10 +426,13 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const half2_t cs2 = __builtin_bit_cast(half2_t, tw[j]);
-          const float co = (float)cs2[0], si = (float)cs2[1];
-          const float u = bf_lo(cw[j]), w = bf_hi(cw[j]);
-          o[j] = pack_bf2(co * u + si * w, co * w - si * u);
+          // R(-phi)(u, w) = ((u, w).(cos, sin), (u, w).(-sin, cos)), bf16 pairs, fp32 sums
+          const uint32_t ms = __builtin_amdgcn_alignbit(tw[j], tw[j], 16) ^ 0x8000u;  // (-sin, cos)
+          const float o0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cw[j]),
+                                                           __builtin_bit_cast(bf16x2, tw[j]), 0.0f, false);
+          const float o1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cw[j]),
+                                                           __builtin_bit_cast(bf16x2, ms), 0.0f, false);
+          o[j] = pack_bf2(o0, o1);
         }
         rCt[ci][ks] = make_uint4(o[0], o[1], o[2], o[3]);
       }
@@ -497,13 +527,29 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       // store y
 #pragma unroll
       for (int ci = 0; ci < NCW; ++ci) {
-        if (tcol[ci] >= nvalid) continue;
         const int vcol = ctl[ci] * 16 + m16;
-        u16* yrow = (u16*)a.y + tokX(c0 + tcol[ci]) + (vcol & (R - 1)) * P;
+        u16* yrow = (u16*)a.y + tokX(c0 + (tcol[ci] < nvalid ? tcol[ci] : 0)) + (vcol & (R - 1)) * P;
+        if constexpr (PTW == 4) {
+          // transpose (16-lane row g) x (p tile) so that lane g holds p = 16g .. 16g + 15
+          // of its row: 32 contiguous bytes per lane instead of four 8-byte pieces
+          uint32_t d0[4], d1[4];
 #pragma unroll
-        for (int pp = 0; pp < PTW; ++pp)
-          *(uint2*)(yrow + (pt0 + pp) * 16 + 4 * g) = make_uint2(pack_bf2(yacc[ci][pp][0], yacc[ci][pp][1]),
-                                                                 pack_bf2(yacc[ci][pp][2], yacc[ci][pp][3]));
+          for (int pp = 0; pp < 4; ++pp) {
+            d0[pp] = pack_bf2(yacc[ci][pp][0], yacc[ci][pp][1]);
+            d1[pp] = pack_bf2(yacc[ci][pp][2], yacc[ci][pp][3]);
+          }
+          transpose_rows4(d0);
+          transpose_rows4(d1);
+          if (tcol[ci] < nvalid) {
+            *(uint4*)(yrow + 16 * g) = make_uint4(d0[0], d1[0], d0[1], d1[1]);
+            *(uint4*)(yrow + 16 * g + 8) = make_uint4(d0[2], d1[2], d0[3], d1[3]);
+          }
+        } else if (tcol[ci] < nvalid) {
+#pragma unroll
+          for (int pp = 0; pp < PTW; ++pp)
+            *(uint2*)(yrow + (pt0 + pp) * 16 + 4 * g) = make_uint2(pack_bf2(yacc[ci][pp][0], yacc[ci][pp][1]),
+                                                                   pack_bf2(yacc[ci][pp][2], yacc[ci][pp][3]));
+        }
       }
     }
     // ---------- sub-chunk state S = (w B~)^T X (hi + lo) and the state pass ----------
