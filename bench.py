@@ -34,18 +34,26 @@ def prefill_bytes_per_token_head(w, s_io=2):
     return s_io * w.rank * (2 * w.headdim + 2 * w.dstate) + 12 + 2 * w.dstate
 
 
+def subwalk_applies(w):
+    """The sub-chunk walker's sizes (mirrors subwalk_supported in csrc/chunk_subwalk.hip)."""
+    if w.io != "bf16" or w.headdim != 64:
+        return False
+    if w.dstate == 64:
+        return w.chunk in (32, 64) and w.rank in (1, 2, 4)
+    return w.dstate == 128 and w.chunk in (16, 32, 64) and w.rank in (2, 4)
+
+
 def walked_chunk(w):
-    """Chunk length the library walks with: the 32-token walker takes requested
-    chunks of 32 or 64 for bf16 io with N = P = 64 (mirrors the dispatch in
-    csrc/chunk_walk32.hip)."""
-    if w.io == "bf16" and w.dstate == 64 and w.headdim == 64 and w.chunk in (32, 64):
-        return 32
+    """Chunk length the library walks with: the sub-chunk walker walks 32-token
+    (N = 64) or 16-token (N = 128) pieces of the requested chunk."""
+    if subwalk_applies(w):
+        return 32 if w.dstate == 64 else 16
     return w.chunk
 
 
 def walker_kernel(w):
-    if walked_chunk(w) == 32 and w.chunk in (32, 64) and w.dstate == 64 and w.headdim == 64:
-        return f"walk32_kernel<{w.rank}>"
+    if subwalk_applies(w):
+        return f"subchunk_walk_kernel<{w.dstate},{w.rank}>"
     if w.io == "bf16" and w.dstate <= 64 and w.headdim <= 64:
         return f"chunk_walk_fast_kernel<{w.dstate},{w.headdim},{w.rank}>"
     return f"chunk_walk_kernel<{w.io},{w.dstate},{w.headdim},8>"

@@ -94,9 +94,10 @@ typedef struct {
   int64_t dstate;   /* N, even */
   int64_t rank;     /* R */
   int64_t chunk;    /* Q tokens per chunk (chunked_fwd only).  For bf16 io
-                       with N = P = 64 and Q in {32, 64} the library walks
-                       32-token chunks (the chunked form is exact for any
-                       split); the workspace size follows the walked length. */
+                       with P = 64 and N = 64 (Q in {32, 64}) or N = 128
+                       (R in {2, 4}) the library walks each chunk as 32- or
+                       16-token sub-chunks (the chunked form is exact for
+                       any split); segments and workspace follow Q. */
   int32_t io_dtype; /* m3_dtype of x, B, C, y, prev_B, prev_x, B_rot, C_rot */
   int32_t flags;    /* chunked_fwd: bits 0..15 = number of sequence segments
                        walked in parallel per (b,h) (0 = chosen by the

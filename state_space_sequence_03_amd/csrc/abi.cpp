@@ -51,14 +51,6 @@ m3_status check_dims(const m3_dims* d, bool need_chunk, bool need_p) {
 
 int io_bf16(const m3_dims* d) { return d->io_dtype == M3_BF16 ? 1 : 0; }
 
-// The dims with the chunk length the walk actually uses (the 32-token walker
-// walks a requested 64-token chunk as two 32-token chunks).
-m3_dims walk_dims(const m3_dims* d) {
-  m3_dims e = *d;
-  e.chunk = m3::walk_chunk(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank);
-  return e;
-}
-
 // Number of sequence segments walked in parallel per (b,h) and their length
 // (whole chunks).  Requested through the low 16 bits of flags, else chosen so
 // that at least ~512 walkers exist when B*H is small (bf16 io only; each
@@ -126,10 +118,9 @@ SegWs seg_ws(const m3_dims* d, const SegPlan& sp) {
 size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d) {
   if (check_dims(d, true, true) != M3_OK) return 0;
   if (d->batch == 0 || d->nheads == 0 || d->seqlen == 0) return 0;
-  const m3_dims e = walk_dims(d);
-  const SegPlan sp = seg_plan(&e);
+  const SegPlan sp = seg_plan(d);
   if (sp.S <= 1) return 0;
-  return seg_ws(&e, sp).bytes;
+  return seg_ws(d, sp).bytes;
 }
 
 m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B, const void* C,
@@ -141,10 +132,9 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
   if ((d->flags & ~0xffff) != 0) return M3_ERR_UNSUPPORTED;
   if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0 &&
       !m3::walk_fast_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) &&
-      !m3::walk32_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank))
+      !m3::subwalk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank))
     return M3_ERR_UNSUPPORTED;
-  const m3_dims ed = walk_dims(d);
-  const SegPlan sp = seg_plan(&ed);
+  const SegPlan sp = seg_plan(d);
   if (sp.S > 1 && (d->io_dtype != M3_BF16 || d->batch * d->nheads > 65535)) return M3_ERR_UNSUPPORTED;
   const bool empty = d->batch == 0 || d->nheads == 0;
   const bool has_tokens = !empty && d->seqlen > 0;
@@ -169,10 +159,10 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
   a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.lam = lam; a.theta = theta;
   a.h0 = h0; a.prev_B = prev_B; a.prev_x = prev_x; a.y = y; a.h_final = h_final;
   a.batch = d->batch; a.L = d->seqlen; a.H = d->nheads;
-  a.R = (int)d->rank; a.Q = (int)ed.chunk; a.S = (int)sp.S;
-  a.seg_len = sp.S > 1 ? sp.seg_len : sp.nchunks * ed.chunk;
+  a.R = (int)d->rank; a.Q = (int)d->chunk; a.S = (int)sp.S;
+  a.seg_len = sp.S > 1 ? sp.seg_len : sp.nchunks * d->chunk;
   if (sp.S > 1) {
-    const SegWs w = seg_ws(&ed, sp);
+    const SegWs w = seg_ws(d, sp);
     char* base = (char*)workspace;
     a.seg_end = (float*)(base + w.end);
     a.seg_in = (float*)(base + w.in);

@@ -1,26 +1,28 @@
-// Prefill walker for bf16 io with N = P = 64 (the 1.5B-scale head shapes):
-// 32-token sub-chunks, two blocks per compute unit.
+// Prefill walker for bf16 io with P = 64 and N in {64, 128} (the 1.5B-scale
+// and the long-context head shapes): the sequence is walked in sub-chunks of
+// QS tokens (32 for N = 64, 16 for N = 128), two blocks per compute unit.
 //
 // Computes what the other walkers compute (chunk.hip, chunk_fast.hip): the
 // chunked form of the exponential-trapezoidal recurrence with data-dependent
 // RoPE and rank-R inputs (linkstar.cloud/article/869, "第一刀", "第二刀",
-// "第三刀"; yetianai.com/news/16273, "榨干硬件算力").  A requested chunk of 32
-// or 64 tokens is walked as 32-token sub-chunks: the chunked form holds for
-// any split of the sequence, because the state carried across a boundary is
-// the exact state there.
+// "第三刀"; yetianai.com/news/16273, "榨干硬件算力").  A requested chunk (a
+// multiple of QS) is walked as QS-token sub-chunks: the chunked form holds
+// for any split of the sequence, because the state carried across a boundary
+// is the exact state there.  Segment offsets for the fix-up pass are still
+// recorded at the requested chunk boundaries.
 //
 // gfx950 data flow:
 //  * 256 threads and under 80 KB of LDS per block, so two blocks (two (b,h)
-//    sequences) share a compute unit and one block's staging and loads overlap
-//    the other block's matrix work.
+//    sequences or segments) share a compute unit and one block's staging and
+//    loads overlap the other block's matrix work.
 //  * Coalesced loads.  Staging thread (t, c) owns token t of the sub-chunk and
-//    the 16-byte column c of each rank row of B and x and of theta's row, so a
-//    wave instruction reads whole 128-byte rows.  Each wave keeps the C rows
+//    the 16-byte column c of each rank row of B (and of x, and of theta's
+//    row), so a wave instruction reads whole rows.  Each wave keeps the C rows
 //    of its own output tiles in the MFMA operand layout (16 bytes per lane).
-//  * Cumulative log-decay and angles: wave scans over the 8 tokens a wave
-//    holds, plus an exchange of wave totals through LDS.  The wave scans of
-//    the next sub-chunk run at the end of the current one, so the exchange
-//    shares the sub-chunk's first barrier.
+//  * Cumulative log-decay and angles: wave scans over the tokens a wave holds,
+//    plus an exchange of wave totals through LDS.  The wave scans of the next
+//    sub-chunk run at the end of the current one, so the exchange shares the
+//    sub-chunk's first barrier.
 //  * sin/cos are computed once per (token, pair) by the staging thread, which
 //    rotates all R ranks of B with them and stores them as a bf16 table for
 //    the rotation of C: two bf16 dot products per pair (fp32 sums), the result
@@ -28,8 +30,9 @@
 //  * y leaves the wave as 32 contiguous bytes per lane after a 4 x 4 transpose
 //    across the wave's 16-lane rows.
 //  * LDS arrays keep their natural row layout with the 16-byte columns
-//    XOR-swizzled per row, so the 16-byte operand reads and the transpose
-//    reads (ds_read_b64_tr_b16) of 16 lanes fall in distinct banks.
+//    XOR-swizzled per row (x rows padded instead), so the 16-byte operand
+//    reads and the transpose reads (ds_read_b64_tr_b16) of 16 lanes fall in
+//    distinct banks.
 //  * Two barriers per sub-chunk: after the previous sub-chunk's last LDS read
 //    (and the scan exchange), and after staging.
 //
@@ -42,79 +45,62 @@ namespace m3 {
 
 namespace {
 
-constexpr int W32_QS = 32;  // tokens per sub-chunk
-
-template <int R>
-struct W32 {
-  static constexpr int N = 64, P = 64, K = 32, QS = W32_QS, V = QS * R;
-  static constexpr int XP = 144;          // bytes per X row (128 + 16: transpose reads of 4 rows hit distinct banks)
-  static constexpr int WROW = 2 * V;      // bytes per row of (w B~)^T
+// LDS layout of one block
+template <int N, int R>
+struct SW {
+  static constexpr int P = 64, K = N / 2, QS = N == 64 ? 32 : 16, V = QS * R;
+  static constexpr int CH = N / 8;        // 16-byte columns of a B / C rank row = staging threads per token
+  static constexpr int BROW = 2 * N;      // bytes per row of B~ [V][N]
+  static constexpr int XP = 144;          // bytes per row of X [V][64] (128 + 16: transpose reads of 4 rows hit distinct banks)
+  static constexpr int WROW = 2 * V;      // bytes per row of (w B~)^T [N][V]
   static constexpr int WCPR = WROW / 16;  // 16-byte columns per row of (w B~)^T
-  static constexpr int OFF_B = 0;                       // B~   [V][64] bf16, swizzled
-  static constexpr int OFF_X = OFF_B + V * 128;         // X    [V][64] bf16, padded rows
-  static constexpr int OFF_WH = OFF_X + V * XP;         // (w B~)^T hi [64][V] bf16, swizzled
-  static constexpr int OFF_WL = OFF_WH + N * WROW;      // (w B~)^T lo
-  static constexpr int OFF_H = OFF_WL + N * WROW;       // H'^T [64][64] bf16, swizzled
-  static constexpr int OFF_CS = OFF_H + P * 128;        // (cos, sin) [QS][K] bf16 pairs, swizzled
-  static constexpr int OFF_SC = OFF_CS + QS * 128;      // per token: log2 decay, q, gamma, exp(decay)
-  static constexpr int OFF_TOT = OFF_SC + QS * 16;      // wave totals [4][36] fp32
-  static constexpr int OFF_TH = OFF_TOT + 4 * 36 * 4;   // chunk-total rotation [K] float2
+  static constexpr int HROW = 2 * N;      // bytes per row of H'^T [64][N]
+  static constexpr int CSROW = 4 * K;     // bytes per row of the (cos, sin) table [QS][K]
+  static constexpr int TOTW = K + 4;      // floats per wave in the scan exchange
+  static constexpr int OFF_B = 0;
+  static constexpr int OFF_X = OFF_B + V * BROW;
+  static constexpr int OFF_WH = OFF_X + V * XP;
+  static constexpr int OFF_WL = OFF_WH + N * WROW;
+  static constexpr int OFF_H = OFF_WL + N * WROW;
+  static constexpr int OFF_CS = OFF_H + P * HROW;
+  static constexpr int OFF_SC = OFF_CS + QS * CSROW;   // per token: log2 decay, q, gamma, exp(decay)
+  static constexpr int OFF_TOT = OFF_SC + QS * 16;
+  static constexpr int OFF_TH = OFF_TOT + 4 * TOTW * 4;  // sub-chunk total rotation [K] float2
   static constexpr int BYTES = OFF_TH + K * 8;
 };
-static_assert(W32<4>::BYTES <= 80 * 1024, "two blocks per compute unit");
+static_assert(SW<64, 4>::BYTES <= 80 * 1024 && SW<128, 4>::BYTES <= 80 * 1024, "two blocks per compute unit");
 
-// Swizzle of an array of 128-byte rows: 16-byte column c of row r is stored
-// at column c ^ f(r).  f depends only on r mod 16, so the rows of a 16-row
-// tile, at any tile offset, share one pattern, and 16 consecutive rows read
-// at one logical column fall in 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int f16rows(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int sw128(int row, int chunk) { return row * 128 + ((chunk ^ f16rows(row)) << 4); }
-// rows of (w B~)^T (WCPR 16-byte columns): 16 consecutive rows, and the 8
-// rows 8 apart that one staging instruction writes, both spread over banks
+// rows of (w B~)^T: 16 consecutive rows, and the rows 8 apart that one staging
+// instruction writes, spread over the banks
 template <int WCPR>
 __device__ __forceinline__ int fW(int n) {
   return WCPR == 4 ? ((n ^ (n >> 2)) & 3) : ((n ^ (n >> 3)) & (WCPR - 1));
 }
 
-// d[k] of 16-lane row r becomes d[r] of row k: a 4 x 4 transpose of (row of
-// the wave) x (register) with the gfx950 row swaps (permlane32_swap exchanges
-// rows 2,3 of its first operand with rows 0,1 of its second; permlane16_swap
-// the odd rows of the first with the even rows of the second)
-__device__ __forceinline__ void transpose_rows4(uint32_t* d) {
-  auto s = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
-  d[0] = s[0];
-  d[2] = s[1];
-  s = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
-  d[1] = s[0];
-  d[3] = s[1];
-  s = __builtin_amdgcn_permlane16_swap(d[0], d[1], false, false);
-  d[0] = s[0];
-  d[1] = s[1];
-  s = __builtin_amdgcn_permlane16_swap(d[2], d[3], false, false);
-  d[2] = s[0];
-  d[3] = s[1];
-}
-
 }  // namespace
 
-bool walk32_supported(int io_bf16, int N, int P, int Q, int R) {
-  return io_bf16 && N == 64 && P == 64 && (Q == 32 || Q == 64) && (R == 1 || R == 2 || R == 4);
+bool subwalk_supported(int io_bf16, int N, int P, int Q, int R) {
+  if (!io_bf16 || P != 64) return false;
+  if (N == 64) return (Q == 32 || Q == 64) && (R == 1 || R == 2 || R == 4);
+  if (N == 128) return (Q == 16 || Q == 32 || Q == 64) && (R == 2 || R == 4);
+  return false;
 }
 
-int walk_chunk(int io_bf16, int N, int P, int Q, int R) {
-  return walk32_supported(io_bf16, N, P, Q, R) ? W32_QS : Q;
-}
-
-template <int R>
-__global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
-  typedef W32<R> Ly;
-  constexpr int N = 64, P = 64, K = 32, QS = W32_QS, V = Ly::V, NW = 4;
+template <int N, int R>
+__global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
+  typedef SW<N, R> Ly;
+  constexpr int P = 64, K = Ly::K, QS = Ly::QS, V = Ly::V, NW = 4, CH = Ly::CH;
   constexpr int lgR = R == 4 ? 2 : (R == 2 ? 1 : 0);
+  constexpr int NKS = N / 32;               // 32-wide slabs of the state dimension (MFMA k steps)
   constexpr int NCT = V / 16;               // column tiles of Y (16 virtual rows each)
   constexpr int NCW = NCT == 8 ? 2 : 1;     // column tiles per wave
   constexpr int PTW = NCT >= 4 ? 4 : 2;     // 16-wide p tiles per wave
   constexpr int NKB = V / 32;               // 32-row slabs of the sub-chunk
+  constexpr int NTW = N / 64;               // 16-row state tiles per wave
+  constexpr int XIT = R * 8 / CH;           // x row pieces per staging thread
+  constexpr int BCPR = N / 8;               // 16-byte columns per row of B~, H'^T and the table
   constexpr float LOG2E = 1.4426950408889634f;
+  static_assert(XIT >= 1 && NCT >= 2, "shape");
 
   extern __shared__ __align__(16) unsigned char smem[];
   unsigned char* sB = smem + Ly::OFF_B;
@@ -124,7 +110,7 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
   unsigned char* sH = smem + Ly::OFF_H;
   unsigned char* sCS = smem + Ly::OFF_CS;
   float4* sSC = (float4*)(smem + Ly::OFF_SC);  // per token: log2 decay, q, gamma, exp(decay)
-  float* sTot = (float*)(smem + Ly::OFF_TOT);  // per wave: 32 angle totals, log-decay total
+  float* sTot = (float*)(smem + Ly::OFF_TOT);  // per wave: K angle totals, log-decay total
   float2* sTh = (float2*)(smem + Ly::OFF_TH);
 
   const int wave = threadIdx.x >> 6;
@@ -139,8 +125,8 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
     g = lane >> 4;
     jj = m16 >> 2;          // transpose-read coordinates
     uu = lane & 3;
-    st_t = id >> 3;         // staging: token, 16-byte column
-    st_c = id & 7;
+    st_t = id / CH;         // staging: token, 16-byte column
+    st_c = id % CH;
   };
   coords(threadIdx.x);
 
@@ -151,10 +137,9 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
   const int64_t L = a.L, H = a.H;
   const int64_t t0 = seg * a.seg_len;
   const int64_t t1 = (t0 + a.seg_len < L) ? t0 + a.seg_len : L;
-  auto tokBC = [&](int64_t tok) { return ((b * L + tok) * H + h) * (int64_t)(R * N); };
-  auto tokX = [&](int64_t tok) { return ((b * L + tok) * H + h) * (int64_t)(R * P); };
   auto tokS = [&](int64_t tok) { return (b * L + tok) * H + h; };
-  const int64_t nchunks_total = (L + QS - 1) / QS;
+  const int64_t QM = a.Q;                          // chunk of the segment offsets (a multiple of QS)
+  const int64_t nchunks_meta = (L + QM - 1) / QM;
 
   // output tiles of this wave: the causal work of tiles (w, NCT-1-w) is equal
   int ctl[NCW];
@@ -169,10 +154,10 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
   const int pt0 = PTW == 4 ? 0 : 2 * (wave >> 1);
 
   // ---------------- prefetch registers (next sub-chunk) ----------------
-  uint4 rB[R], rX[R];
+  uint4 rB[R], rX[XIT];
   float4 rTh;
   float rdt, rA, rlam, rdt1, rlam1;
-  uint4 rC[NCW][2];
+  uint4 rC[NCW][NKS];
 
   // Tokens past the end of the segment read the last valid token instead: only
   // their dt, lam (hence q = gamma = 0) are zeroed, which removes them exactly
@@ -181,11 +166,13 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
     const int64_t row = tokS(c0 + (st_t < nvalid ? st_t : nvalid - 1));
     const u16* gB = (const u16*)a.B + row * (R * N) + 8 * st_c;
-    const u16* gX = (const u16*)a.x + row * (R * P) + 8 * st_c;
+    const u16* gX = (const u16*)a.x + row * (R * P);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      rB[r] = *(const uint4*)(gB + r * N);
-      rX[r] = *(const uint4*)(gX + r * P);
+    for (int r = 0; r < R; ++r) rB[r] = *(const uint4*)(gB + r * N);
+#pragma unroll
+    for (int k = 0; k < XIT; ++k) {
+      const int i = st_c + CH * k;  // piece i: rank i / 8, 16-byte column i % 8
+      rX[k] = *(const uint4*)(gX + (i >> 3) * P + 8 * (i & 7));
     }
   };
   auto load_scal = [&](int64_t c0) __attribute__((always_inline)) {
@@ -213,17 +200,17 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       const int t = (v >> lgR) < nvalid ? (v >> lgR) : nvalid - 1;
       const u16* row = (const u16*)a.C + tokS(c0 + t) * (R * N) + (v & (R - 1)) * N + 8 * g;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) rC[ci][ks] = *(const uint4*)(row + ks * 32);
+      for (int ks = 0; ks < NKS; ++ks) rC[ci][ks] = *(const uint4*)(row + ks * 32);
     }
   };
 
-  // wave-level inclusive scans over this wave's 8 tokens (lanes 8 apart), for
+  // wave-level inclusive scans over this wave's tokens (lanes CH apart), for
   // the sub-chunk held in the prefetch registers; wave totals go to LDS
   float sc_l, sc_p[4];
   auto local_scan = [&]() __attribute__((always_inline)) {
     float v[5] = {rdt * rA, rdt * rTh.x, rdt * rTh.y, rdt * rTh.z, rdt * rTh.w};
 #pragma unroll
-    for (int o = 8; o < 64; o <<= 1) {
+    for (int o = CH; o < 64; o <<= 1) {
 #pragma unroll
       for (int i = 0; i < 5; ++i) {
         const float u = __shfl_up(v[i], o, 64);
@@ -233,14 +220,14 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
     sc_l = v[0];
 #pragma unroll
     for (int j = 0; j < 4; ++j) sc_p[j] = v[1 + j];
-    if (lane >= 56) {
-      *(float4*)(sTot + wave * 36 + 4 * st_c) = make_float4(v[1], v[2], v[3], v[4]);
-      if (st_c == 0) sTot[wave * 36 + 32] = v[0];
+    if (lane >= 64 - CH) {  // the wave's last token
+      *(float4*)(sTot + wave * Ly::TOTW + 4 * st_c) = make_float4(v[1], v[2], v[3], v[4]);
+      if (st_c == 0) sTot[wave * Ly::TOTW + K] = v[0];
     }
   };
 
-  // ---------------- state H' (fp32 registers): n-tile = wave, 4 p-tiles ----------------
-  f32x4 hst[4];
+  // ---------------- state H' (fp32 registers): n-tiles NTW*wave.., 4 p-tiles ----------------
+  f32x4 hst[NTW][4];
   {
     const void* pB = nullptr;
     const void* px = nullptr;
@@ -248,26 +235,28 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
     if (seg == 0) {
       if (a.prev_B) { pB = a.prev_B; px = a.prev_x; pBo = bh * (int64_t)(R * N); pxo = bh * (int64_t)(R * P); }
     } else {
-      pB = a.B; px = a.x; pBo = tokBC(t0 - 1); pxo = tokX(t0 - 1);
+      pB = a.B; px = a.x; pBo = tokS(t0 - 1) * (R * N); pxo = tokS(t0 - 1) * (R * P);
     }
     const float eps1 = (t0 < t1) ? (1.0f - a.lam[tokS(t0)]) * a.dt[tokS(t0)] : 0.0f;
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      const int p = pt * 16 + m16;
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = wave * 16 + 4 * g + i;
-        float v = 0.0f;
-        if (seg == 0 && a.h0) v = a.h0[bh * (int64_t)(N * P) + n * P + p];
-        if (pB) {
-          float acc = 0.0f;
-          for (int r = 0; r < R; ++r)
-            acc += bf2f(((const u16*)pB)[pBo + r * N + n]) * bf2f(((const u16*)px)[pxo + r * P + p]);
-          v += eps1 * acc;
+      for (int pt = 0; pt < 4; ++pt) {
+        const int p = pt * 16 + m16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = (wave * NTW + j) * 16 + 4 * g + i;
+          float v = 0.0f;
+          if (seg == 0 && a.h0) v = a.h0[bh * (int64_t)(N * P) + n * P + p];
+          if (pB) {
+            float acc = 0.0f;
+            for (int r = 0; r < R; ++r)
+              acc += bf2f(((const u16*)pB)[pBo + r * N + n]) * bf2f(((const u16*)px)[pxo + r * P + p]);
+            v += eps1 * acc;
+          }
+          hst[j][pt][i] = v;
         }
-        hst[pt][i] = v;
       }
-    }
   }
 
   float segLam = 0.0f, segPhi[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -287,15 +276,19 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       coords(id);
     }
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
-    const int fm = f16rows(m16);  // swizzle of the rows m16 (+ multiples of 16) of a tile
+    const int fm = fsw<BCPR>(m16);  // swizzle of the rows m16 (+ multiples of 16) of B~ and H'^T tiles
+    const bool meta = S > 1 && seg > 0 && (c0 % QM) == 0;  // a requested chunk starts here
     __syncthreads();  // wave totals are in LDS; the previous sub-chunk's LDS reads are done
 
-    // H'^T (bf16) for the inter-chunk output: row p = 16 pt + m16, columns n = 16 wave + 4g ..
-    {
-      unsigned char* hw = sH + m16 * 128 + (((2 * wave + (g >> 1)) ^ fm) << 4) + 8 * (g & 1);
+    // H'^T (bf16) for the inter-chunk output: row p = 16 pt + m16, columns n = 16 nt + 4g ..
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int nt = wave * NTW + j;
+      unsigned char* hw = sH + m16 * Ly::HROW + (((2 * nt + (g >> 1)) ^ fm) << 4) + 8 * (g & 1);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
-        *(uint2*)(hw + pt * 2048) = make_uint2(pack_bf2(hst[pt][0], hst[pt][1]), pack_bf2(hst[pt][2], hst[pt][3]));
+        *(uint2*)(hw + pt * 16 * Ly::HROW) =
+            make_uint2(pack_bf2(hst[j][pt][0], hst[j][pt][1]), pack_bf2(hst[j][pt][2], hst[j][pt][3]));
     }
 
     // ---------- staging ----------
@@ -303,14 +296,14 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       // prefix over the lower waves (uniform loop) and the sub-chunk's log-decay total
       float lpre = 0.0f, ppre[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int w2 = 0; w2 < wave; ++w2) {
-        const float4 pv = *(const float4*)(sTot + w2 * 36 + 4 * st_c);
-        lpre += sTot[w2 * 36 + 32];
+        const float4 pv = *(const float4*)(sTot + w2 * Ly::TOTW + 4 * st_c);
+        lpre += sTot[w2 * Ly::TOTW + K];
         ppre[0] += pv.x;
         ppre[1] += pv.y;
         ppre[2] += pv.z;
         ppre[3] += pv.w;
       }
-      const float ltot = sTot[32] + sTot[36 + 32] + sTot[72 + 32] + sTot[108 + 32];
+      const float ltot = sTot[K] + sTot[Ly::TOTW + K] + sTot[2 * Ly::TOTW + K] + sTot[3 * Ly::TOTW + K];
       sub_lend = ltot;
       const float lam_c = sc_l + lpre;  // Lambda_t, inclusive, from the sub-chunk start
       const float gam = rlam * rdt;
@@ -322,8 +315,8 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       if constexpr (R >= 2)
         if (c0 + QS < t1) load_scal(c0 + QS);
       if (st_c == 0) sSC[st_t] = make_float4(l2, q, gam, __builtin_amdgcn_exp2f(l2));
-      if (S > 1) {  // segment-relative offsets of this sub-chunk, for the fix-up pass
-        if (seg > 0 && tid == 0) a.chunk_meta[(bh * nchunks_total + c0 / QS) * (1 + K)] = segLam;
+      if (S > 1) {  // segment-relative offsets at requested chunk starts, for the fix-up pass
+        if (meta && tid == 0) a.chunk_meta[(bh * nchunks_meta + c0 / QM) * (1 + K)] = segLam;
         segLam += ltot;
       }
       if (st_t == QS - 1) {  // last token: the sub-chunk's total angles
@@ -331,10 +324,10 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) ptot[j] = sc_p[j] + ppre[j];
         if (S > 1) {
-          if (seg > 0) {
+          if (meta) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              a.chunk_meta[(bh * nchunks_total + c0 / QS) * (1 + K) + 1 + 4 * st_c + j] = segPhi[j];
+              a.chunk_meta[(bh * nchunks_meta + c0 / QM) * (1 + K) + 1 + 4 * st_c + j] = segPhi[j];
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) segPhi[j] += ptot[j];
@@ -353,11 +346,10 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
         fast_sincos(sc_p[j] + ppre[j], &sn[j], &cs[j]);
         tab[j] = pack_bf2(cs[j], sn[j]);
       }
-      *(uint4*)(sCS + sw128(st_t, st_c)) = make_uint4(tab[0], tab[1], tab[2], tab[3]);
+      *(uint4*)(sCS + swz<BCPR>(st_t, st_c)) = make_uint4(tab[0], tab[1], tab[2], tab[3]);
 
       // B~ = R(-phi) B for every rank; w B~ kept in fp32 for the hi/lo split
       float wb[R][8];
-      unsigned char* xw = sX + R * st_t * Ly::XP + 16 * st_c;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const uint32_t w4[4] = {rB[r].x, rB[r].y, rB[r].z, rB[r].w};
@@ -368,11 +360,15 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
           bt[2 * j] = cs[j] * u + sn[j] * w;
           bt[2 * j + 1] = cs[j] * w - sn[j] * u;
         }
-        *(uint4*)(sB + sw128(R * st_t + r, st_c)) =
+        *(uint4*)(sB + swz<BCPR>(R * st_t + r, st_c)) =
             make_uint4(pack_bf2(bt[0], bt[1]), pack_bf2(bt[2], bt[3]), pack_bf2(bt[4], bt[5]), pack_bf2(bt[6], bt[7]));
 #pragma unroll
         for (int e = 0; e < 8; ++e) wb[r][e] = wt * bt[e];
-        *(uint4*)(xw + r * Ly::XP) = make_uint4(rX[r].x, rX[r].y, rX[r].z, rX[r].w);
+      }
+#pragma unroll
+      for (int k = 0; k < XIT; ++k) {
+        const int i = st_c + CH * k;
+        *(uint4*)(sX + (R * st_t + (i >> 3)) * Ly::XP + 16 * (i & 7)) = make_uint4(rX[k].x, rX[k].y, rX[k].z, rX[k].w);
       }
       if constexpr (R >= 2)
         if (c0 + QS < t1) load_BX(c0 + QS);
@@ -403,8 +399,6 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       }
     }
     __syncthreads();  // B~, X, (w B~)^T, H'^T, the cos/sin table and the scalars are in LDS
-    // next sub-chunk's loads go out as early as their registers are free: they
-    // then have the whole Y and S phases to arrive
     const bool more = c0 + QS < t1;
     if constexpr (R == 1) {
       if (more) {
@@ -414,13 +408,13 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
     }
 
     // own C~ fragments (operand layout: row v = tile*16 + m16, n = ks*32 + 8g + j)
-    uint4 rCt[NCW][2];
+    uint4 rCt[NCW][NKS];
 #pragma unroll
     for (int ci = 0; ci < NCW; ++ci) {
       const int t = (ctl[ci] * 16 + m16) >> lgR;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint4 tb = *(const uint4*)(sCS + sw128(t, 4 * ks + g));
+      for (int ks = 0; ks < NKS; ++ks) {
+        const uint4 tb = *(const uint4*)(sCS + swz<BCPR>(t, 4 * ks + g));
         const uint32_t tw[4] = {tb.x, tb.y, tb.z, tb.w};
         const uint32_t cw[4] = {rC[ci][ks].x, rC[ci][ks].y, rC[ci][ks].z, rC[ci][ks].w};
         uint32_t o[4];
@@ -437,19 +431,18 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
         rCt[ci][ks] = make_uint4(o[0], o[1], o[2], o[3]);
       }
     }
-
     if (more) load_C(c0 + QS);
 
     // ---------- outputs: Y^T = exp(Lam_t) H'^T C~^T + X^T (G o M)^T ----------
     {
-      // per-lane bases: the 16-row tiles of B~ and H'^T at n column 8g (ks = 0) and
-      // 32 + 8g (ks = 1); the X^T transpose reads at rows 4g + jj and p = pt0*16 + 4uu
-      const unsigned char* bB[2];
-      const unsigned char* bH[2];
+      // per-lane bases: the 16-row tiles of B~ and H'^T at n column 32 ks + 8g;
+      // the X^T transpose reads at rows 4g + jj and p = pt0*16 + 4uu
+      const unsigned char* bB[NKS];
+      const unsigned char* bH[NKS];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bB[ks] = sB + m16 * 128 + (((4 * ks + g) ^ fm) << 4);
-        bH[ks] = sH + m16 * 128 + (((4 * ks + g) ^ fm) << 4);
+      for (int ks = 0; ks < NKS; ++ks) {
+        bB[ks] = sB + m16 * Ly::BROW + (((4 * ks + g) ^ fm) << 4);
+        bH[ks] = sH + m16 * Ly::HROW + (((4 * ks + g) ^ fm) << 4);
       }
       const unsigned char* bXt = sX + (4 * g + jj) * Ly::XP + 2 * (pt0 * 16 + 4 * uu);
 
@@ -466,8 +459,8 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
         for (int pp = 0; pp < PTW; ++pp) {
           f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const uint4 hf = *(const uint4*)(bH[ks] + (pt0 + pp) * 2048);
+          for (int ks = 0; ks < NKS; ++ks) {
+            const uint4 hf = *(const uint4*)(bH[ks] + (pt0 + pp) * 16 * Ly::HROW);
             acc = mfma_bf16(as_bf16x8(hf), as_bf16x8(rCt[ci][ks]), acc);
           }
           yacc[ci][pp] = acc * sc.w;
@@ -477,13 +470,13 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
       const int nkb0 = ((ctl[0] + 1) * 16 + 31) / 32;
       const int nkb1 = NCW == 2 ? ((ctl[NCW - 1] + 1) * 16 + 31) / 32 : 0;
       for (int kb = 0; kb < nkb0; ++kb) {
-        uint4 bfr[2][2];
+        uint4 bfr[2][NKS];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            bfr[sub][ks] = *(const uint4*)(bB[ks] + (kb * 32 + sub * 16) * 128);
-        const float2* scs = (const float2*)(sSC + kb * 8 + g);  // (log2 decay, q) of the lane's source token
+          for (int ks = 0; ks < NKS; ++ks)
+            bfr[sub][ks] = *(const uint4*)(bB[ks] + (kb * 32 + sub * 16) * Ly::BROW);
+        const float2* scs = (const float2*)(sSC + kb * 8 + g);  // (log2 decay, q) of the lane's source token (R = 4)
 #pragma unroll
         for (int ci = 0; ci < NCW; ++ci) {
           if (ci == 1 && kb >= nkb1) continue;
@@ -492,7 +485,7 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
           for (int sub = 0; sub < 2; ++sub) {
             f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) acc = mfma_bf16(as_bf16x8(bfr[sub][ks]), as_bf16x8(rCt[ci][ks]), acc);
+            for (int ks = 0; ks < NKS; ++ks) acc = mfma_bf16(as_bf16x8(bfr[sub][ks]), as_bf16x8(rCt[ci][ks]), acc);
             // s < t: decay * q_s;  s == t: gamma_t;  else 0 (selected arithmetically)
             if constexpr (R == 4) {
               const int s = kb * 8 + sub * 4 + g;
@@ -528,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
 #pragma unroll
       for (int ci = 0; ci < NCW; ++ci) {
         const int vcol = ctl[ci] * 16 + m16;
-        u16* yrow = (u16*)a.y + tokX(c0 + (tcol[ci] < nvalid ? tcol[ci] : 0)) + (vcol & (R - 1)) * P;
+        u16* yrow = (u16*)a.y + tokS(c0 + (tcol[ci] < nvalid ? tcol[ci] : 0)) * (R * P) + (vcol & (R - 1)) * P;
         if constexpr (PTW == 4) {
           // transpose (16-lane row g) x (p tile) so that lane g holds p = 16g .. 16g + 15
           // of its row: 32 contiguous bytes per lane instead of four 8-byte pieces
@@ -552,41 +545,52 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
         }
       }
     }
+
     // ---------- sub-chunk state S = (w B~)^T X (hi + lo) and the state pass ----------
     {
-      f32x4 sacc[4];
+      f32x4 sacc[NTW][4];
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) sacc[pt] = f32x4{0, 0, 0, 0};
-      const int n = wave * 16 + m16;
-      const int gf = g ^ fW<Ly::WCPR>(n);
-      const unsigned char* bW = sWh + n * Ly::WROW;
+      for (int j = 0; j < NTW; ++j)
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) sacc[j][pt] = f32x4{0, 0, 0, 0};
       const unsigned char* bXs = sX + (8 * g + jj) * Ly::XP + 8 * uu;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const int wo = ((4 * kb) ^ gf) << 4;
-        const uint4 ah = *(const uint4*)(bW + wo);
-        const uint4 al = *(const uint4*)(bW + (Ly::OFF_WL - Ly::OFF_WH) + wo);
+        uint4 xb[4];
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
           const uint2 f0 = lds_tr16(bXs + kb * 32 * Ly::XP + pt * 32);
           const uint2 f1 = lds_tr16(bXs + (kb * 32 + 4) * Ly::XP + pt * 32);
-          const uint4 xb = make_uint4(f0.x, f0.y, f1.x, f1.y);
-          sacc[pt] = mfma_bf16(as_bf16x8(ah), as_bf16x8(xb), sacc[pt]);
-          sacc[pt] = mfma_bf16(as_bf16x8(al), as_bf16x8(xb), sacc[pt]);
+          xb[pt] = make_uint4(f0.x, f0.y, f1.x, f1.y);
+        }
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+          const int n = (wave * NTW + j) * 16 + m16;
+          const int wo = ((4 * kb) ^ g ^ fW<Ly::WCPR>(n)) << 4;
+          const unsigned char* bW = sWh + n * Ly::WROW + wo;
+          const uint4 ah = *(const uint4*)bW;
+          const uint4 al = *(const uint4*)(bW + (Ly::OFF_WL - Ly::OFF_WH));
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) {
+            sacc[j][pt] = mfma_bf16(as_bf16x8(ah), as_bf16x8(xb[pt]), sacc[j][pt]);
+            sacc[j][pt] = mfma_bf16(as_bf16x8(al), as_bf16x8(xb[pt]), sacc[j][pt]);
+          }
         }
       }
       const float eLend = __builtin_amdgcn_exp2f(sub_lend * LOG2E);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float2 cs = sTh[wave * 8 + 2 * g + q];
+      for (int j = 0; j < NTW; ++j)
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const float u = eLend * hst[pt][2 * q] + sacc[pt][2 * q];
-          const float w = eLend * hst[pt][2 * q + 1] + sacc[pt][2 * q + 1];
-          hst[pt][2 * q] = cs.x * u - cs.y * w;
-          hst[pt][2 * q + 1] = cs.y * u + cs.x * w;
+        for (int q = 0; q < 2; ++q) {
+          const float2 cs = sTh[(wave * NTW + j) * 8 + 2 * g + q];
+#pragma unroll
+          for (int pt = 0; pt < 4; ++pt) {
+            const float u = eLend * hst[j][pt][2 * q] + sacc[j][pt][2 * q];
+            const float w = eLend * hst[j][pt][2 * q + 1] + sacc[j][pt][2 * q + 1];
+            hst[j][pt][2 * q] = cs.x * u - cs.y * w;
+            hst[j][pt][2 * q + 1] = cs.y * u + cs.x * w;
+          }
         }
-      }
     }
     if (more) local_scan();
   }
@@ -596,9 +600,12 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
   if (dst) {
     float* base = (S == 1 ? dst + bh * (int64_t)(N * P) : dst);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
+    for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) base[(wave * 16 + 4 * g + i) * P + pt * 16 + m16] = hst[pt][i];
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          base[((wave * NTW + j) * 16 + 4 * g + i) * P + pt * 16 + m16] = hst[j][pt][i];
   }
   if (S > 1) {
     float* tot = a.seg_tot + blk * (1 + K);
@@ -610,28 +617,40 @@ __global__ __launch_bounds__(256, 2) void walk32_kernel(WalkArgs a) {
   }
 }
 
-template <int R>
-static hipError_t w32_run(const WalkArgs& a, hipStream_t s) {
-  auto kern = walk32_kernel<R>;
+template <int N, int R>
+static hipError_t sw_run(const WalkArgs& a, hipStream_t s) {
+  auto kern = subchunk_walk_kernel<N, R>;
+  constexpr int lds = SW<N, R>::BYTES;
   static bool attr_set = false;  // per instantiation; the attribute is per function
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, W32<R>::BYTES);
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int64_t blocks = a.batch * a.H * a.S;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), W32<R>::BYTES, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_walk32(const WalkArgs& a, hipStream_t s) {
-  if (a.Q != W32_QS) return hipErrorInvalidValue;
-  switch (a.R) {
-    case 1: return w32_run<1>(a, s);
-    case 2: return w32_run<2>(a, s);
-    case 4: return w32_run<4>(a, s);
-    default: return hipErrorInvalidValue;
+hipError_t launch_subwalk(int N, const WalkArgs& a, hipStream_t s) {
+  if (N == 64) {
+    if (a.Q % SW<64, 1>::QS != 0) return hipErrorInvalidValue;
+    switch (a.R) {
+      case 1: return sw_run<64, 1>(a, s);
+      case 2: return sw_run<64, 2>(a, s);
+      case 4: return sw_run<64, 4>(a, s);
+      default: return hipErrorInvalidValue;
+    }
   }
+  if (N == 128) {
+    if (a.Q % SW<128, 2>::QS != 0) return hipErrorInvalidValue;
+    switch (a.R) {
+      case 2: return sw_run<128, 2>(a, s);
+      case 4: return sw_run<128, 4>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace m3

@@ -151,4 +151,36 @@ __device__ __forceinline__ void fast_sincos(float x, float* s, float* c) {
   *c = __cosf(r);
 }
 
+// Swizzle of arrays of rows of CPR 16-byte columns: column c of row r is
+// stored at column c ^ f(r), with f depending on r mod 16 only (the pattern
+// repeats for every 16-row tile).  With 64 four-byte banks (16 groups of 16
+// bytes), 16 consecutive rows read at one logical column fall in 16 distinct
+// bank groups: rows of 128 bytes use two rows per bank period, rows of 256
+// bytes one.
+template <int CPR>
+__device__ __forceinline__ int fsw(int row) {
+  if constexpr (CPR == 16) return row & 15;
+  else return (row & 7) ^ ((row >> 3) & 1);
+}
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int chunk) { return row * (CPR * 16) + ((chunk ^ fsw<CPR>(row)) << 4); }
+// d[k] of 16-lane row r becomes d[r] of row k: a 4 x 4 transpose of (row of
+// the wave) x (register) with the gfx950 row swaps (permlane32_swap exchanges
+// rows 2,3 of its first operand with rows 0,1 of its second; permlane16_swap
+// the odd rows of the first with the even rows of the second)
+__device__ __forceinline__ void transpose_rows4(uint32_t* d) {
+  auto s = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+  d[0] = s[0];
+  d[2] = s[1];
+  s = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+  d[1] = s[0];
+  d[3] = s[1];
+  s = __builtin_amdgcn_permlane16_swap(d[0], d[1], false, false);
+  d[0] = s[0];
+  d[1] = s[1];
+  s = __builtin_amdgcn_permlane16_swap(d[2], d[3], false, false);
+  d[2] = s[0];
+  d[3] = s[1];
+}
+
 }  // namespace m3

@@ -52,14 +52,13 @@ size_t walk_lds_bytes(int io_bf16, int N, int P, int Q, int R);
 // The fast walker (bf16 io, N and P <= 64) applies to these sizes.
 bool walk_fast_supported(int io_bf16, int N, int P, int Q, int R);
 hipError_t launch_walk_fast(int N, int P, const WalkArgs& a, hipStream_t s);
-// The 32-token sub-chunk walker (bf16 io, N = P = 64, requested chunk 32 or 64)
-// applies to these sizes; it walks with chunk length 32.
-bool walk32_supported(int io_bf16, int N, int P, int Q, int R);
-hipError_t launch_walk32(const WalkArgs& a, hipStream_t s);
-// Chunk length the walk actually uses for a requested chunk Q (segment
-// lengths, per-chunk offsets and the fix-up pass follow it).
-int walk_chunk(int io_bf16, int N, int P, int Q, int R);
-// Chunked forward walk: fast walker when it applies, general walker otherwise.
+// The sub-chunk walker (bf16 io, P = 64, N = 64 with Q in {32, 64}, or
+// N = 128 with R in {2, 4}) applies to these sizes; it walks 32-token (N = 64)
+// or 16-token (N = 128) sub-chunks and records segment offsets every Q tokens.
+bool subwalk_supported(int io_bf16, int N, int P, int Q, int R);
+hipError_t launch_subwalk(int N, const WalkArgs& a, hipStream_t s);
+// Chunked forward walk: the sub-chunk walker or the fast walker when one
+// applies, the general walker otherwise.
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
 
 // After a walk with S > 1 segments: segment scan (true incoming states and

@@ -100,11 +100,11 @@ def test_workspace_sizes(L):
     assert L.chunked_fwd_workspace_size(long) > 0
     assert L.chunked_fwd_workspace_size(dims(L, batch=1, seqlen=65536, nheads=32, dstate=128, flags=1)) == 0
     assert L.chunked_fwd_workspace_size(dims(L, batch=8, seqlen=4096, nheads=64)) == 0
-    # segments walked by the 32-token walker: per-chunk offsets for 32-token chunks,
-    # so requested chunks of 32 and 64 need the same workspace
+    # segment offsets are kept per requested chunk (the sub-chunk walkers walk
+    # shorter pieces): a smaller chunk needs more of them
     few = dict(batch=1, seqlen=8192, nheads=4, dstate=64, headdim=64, rank=4)
     w32, w64 = (L.chunked_fwd_workspace_size(dims(L, chunk=q, **few)) for q in (32, 64))
-    assert w32 > 0 and w32 == w64
+    assert w32 > w64 > 0
     d = dims(L, seqlen=4096)
     assert L.rope_bc_workspace_size(d) == 4 * 2 * 3 * 64 * 32
     assert L.rope_bc_workspace_size(dims(L, dstate=7)) == 0

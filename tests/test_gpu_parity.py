@@ -108,6 +108,10 @@ FWD_CASES = [
     ("bf16", 1, 31, 2, 64, 64, 2, 64, True, True),
     ("bf16", 1, 33, 1, 64, 64, 1, 32, False, False),
     ("bf16", 3, 64, 2, 64, 64, 4, 64, True, True),
+    # the sub-chunk walker at N = 128 (16-token sub-chunks)
+    ("bf16", 2, 75, 2, 64, 128, 2, 16, True, True),
+    ("bf16", 1, 40, 3, 64, 128, 4, 32, False, True),
+    ("bf16", 1, 15, 1, 64, 128, 4, 64, True, False),
 ]
 
 
