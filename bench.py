@@ -17,8 +17,10 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only pr
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -98,6 +100,20 @@ def timed(fn, steps, warmup, torch):
     return wall, e0.elapsed_time(e1) / steps
 
 
+def step_percentiles(fn, steps, torch):
+    """p10 / p50 / p90 of single-step times (HIP events around each step)."""
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in ev:
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    pick = lambda f: t[min(len(t) - 1, int(round(f * (len(t) - 1))))]
+    return pick(0.1), pick(0.5), pick(0.9)
+
+
 def bench_prefill(ops, inputs, w, steps, warmup, torch):
     d = inputs.torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
                             seed=inputs.seed_of(w.name))
@@ -106,6 +122,7 @@ def bench_prefill(ops, inputs, w, steps, warmup, torch):
     fn = lambda: ops.chunked_fwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], chunk=w.chunk,
                                  y=y, h_final=hf)
     wall, ev = timed(fn, steps, warmup, torch)
+    pct = step_percentiles(fn, steps, torch)
     th = w.batch * w.seqlen * w.nheads
     bytes_ = th * prefill_bytes_per_token_head(w)
     dense = th * prefill_flops_per_token_head(w, False)
@@ -114,7 +131,7 @@ def bench_prefill(ops, inputs, w, steps, warmup, torch):
     torch.cuda.empty_cache()
     return dict(ms=ev, wall_ms=wall, tokens_per_s=w.tokens / (ev * 1e-3), bytes=bytes_,
                 gbps=bytes_ / (ev * 1e-3) / 1e9, tflops_dense=dense / (ev * 1e-3) / 1e12,
-                tflops_causal=causal / (ev * 1e-3) / 1e12)
+                tflops_causal=causal / (ev * 1e-3) / 1e12, p10_p50_p90=pct)
 
 
 def bench_decode(ops, inputs, w, torch, reps=3):
@@ -201,13 +218,60 @@ def cpu_baseline(inputs, w, budget_s=12.0):
                        f"({nsl * w.seqlen} token-heads in {dt:.1f} s); tokens/s = token-heads/s / H={w.nheads}")
 
 
+def bench_copy(torch, nbytes=1 << 30, reps=3):
+    """A plain device copy of known size: the reference for scaling the FETCH_SIZE
+    and WRITE_SIZE counters to bytes (run under rocprofv3 --pmc)."""
+    src = torch.randn(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return dict(bytes_read=nbytes, bytes_written=nbytes, ms=ms, gbps=2 * nbytes / (ms * 1e-3) / 1e9)
+
+
+WALKER_SOURCES = ("state_space_sequence_03_amd/csrc/chunk_subwalk.hip", "state_space_sequence_03_amd/csrc/m3_common.hpp")
+TRAFFIC_SUMMARY = "profiles/subchunk_walk_kernel_64_4__mimo_bf16__hbm_traffic.md"
+
+
+def walker_source_sha256():
+    h = hashlib.sha256()
+    for f in WALKER_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the prefill walker from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same
+    counter reads for a plain copy of known size), or None when the summary is
+    missing or was taken on other walker sources."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    vals = dict(re.findall(r"^- (\w+): ([0-9a-fA-F.e+-]+)\s*$", text, re.M))
+    try:
+        if vals["walker_source_sha256"] != walker_source_sha256():
+            return None
+        return (float(vals["fetch_kib_per_dispatch"]) * float(vals["fetch_scale"])
+                + float(vals["write_kib_per_dispatch"]) * float(vals["write_scale"])) * 1024.0
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "rope", "all"], default="all")
+    ap.add_argument("--only", choices=["prefill", "decode", "rope", "copy", "all"], default="all")
     ap.add_argument("--workload", default="mimo_bf16", choices=["mimo_bf16", "siso_bf16", "long_mimo_bf16"],
                     help="prefill workload timed by --only prefill (profiling); the headline line uses mimo_bf16")
     args = ap.parse_args()
@@ -217,6 +281,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.only == "copy":
+        print(json.dumps({"copy": bench_copy(torch)}), flush=True)
+        return
     from state_space_sequence_03_amd import ops, inputs
     ops.lib()
     W = inputs.WORKLOADS
@@ -250,10 +317,13 @@ def main():
         pf = out["prefill"]
         line["value"] = round(pf["tokens_per_s"], 1)
         line["ms_per_step"] = round(pf["ms"], 4)
+        traffic = measured_traffic() if w.name == "mimo_bf16" else None
         line["roofline"] = {"bound": "hbm", "achieved": round(pf["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": round(pf["gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "frac": round(pf["gbps"] / HBM_PEAK_GBPS, 4),
+                            "traffic": None if traffic is None else round(traffic),
                             "kernel": walker_kernel(w),
                             "bytes_per_launch": pf["bytes"]}
+        line["ms_p10_p50_p90"] = [round(v, 4) for v in pf["p10_p50_p90"]]
         line["mfma"] = {"tflops_dense": round(pf["tflops_dense"], 1), "tflops_causal": round(pf["tflops_causal"], 1),
                         "frac_dense": round(pf["tflops_dense"] / BF16_DENSE_TFLOPS, 4),
                         "frac_causal": round(pf["tflops_causal"] / BF16_DENSE_TFLOPS, 4), "peak_tflops": BF16_DENSE_TFLOPS}
