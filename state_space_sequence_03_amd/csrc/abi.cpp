@@ -132,7 +132,7 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
   if ((d->flags & ~0xffff) != 0) return M3_ERR_UNSUPPORTED;
   if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0 &&
       !m3::walk_fast_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) &&
-      !m3::subwalk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank))
+      !m3::subwalk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank, d->nheads))
     return M3_ERR_UNSUPPORTED;
   const SegPlan sp = seg_plan(d);
   if (sp.S > 1 && (d->io_dtype != M3_BF16 || d->batch * d->nheads > 65535)) return M3_ERR_UNSUPPORTED;

@@ -749,7 +749,7 @@ static hipError_t walk_n(int N, int P, const WalkArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s) {
-  if (subwalk_supported(io_bf16, N, P, a.Q, a.R)) return launch_subwalk(N, a, s);
+  if (subwalk_supported(io_bf16, N, P, a.Q, a.R, a.H)) return launch_subwalk(N, a, s);
   if (walk_fast_supported(io_bf16, N, P, a.Q, a.R)) return launch_walk_fast(N, P, a, s);
   return io_bf16 ? walk_n<bf16_t>(N, P, a, s) : walk_n<float>(N, P, a, s);
 }

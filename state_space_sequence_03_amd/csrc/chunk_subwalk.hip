@@ -73,14 +73,27 @@ static_assert(SW<64, 4>::BYTES <= 80 * 1024 && SW<128, 4>::BYTES <= 80 * 1024, "
 // rows of (w B~)^T: 16 consecutive rows, and the rows 8 apart that one staging
 // instruction writes, spread over the banks
 template <int WCPR>
-__device__ __forceinline__ int fW(int n) {
+__host__ __device__ constexpr int fW(int n) {
   return WCPR == 4 ? ((n ^ (n >> 2)) & 3) : ((n ^ (n >> 3)) & (WCPR - 1));
 }
+// The staging thread of column c writes rows n = 8c + e (e < 8); their
+// swizzles differ from those of rows 8c and 8c + 4 by e & 3 only, so one
+// xor-add per row forms the address.
+template <int WCPR>
+constexpr bool fW_rows_of_column_ok() {
+  for (int c = 0; c < 64; ++c)
+    for (int e = 0; e < 8; ++e)
+      if (fW<WCPR>(8 * c + e) != (fW<WCPR>(8 * c + 4 * (e >> 2)) ^ (e & 3))) return false;
+  return true;
+}
+static_assert(fW_rows_of_column_ok<4>() && fW_rows_of_column_ok<8>() && fW_rows_of_column_ok<16>(), "row swizzle");
 
 }  // namespace
 
-bool subwalk_supported(int io_bf16, int N, int P, int Q, int R) {
+bool subwalk_supported(int io_bf16, int N, int P, int Q, int R, int64_t H) {
   if (!io_bf16 || P != 64) return false;
+  // per-thread offsets within a sub-chunk are 32-bit: 32 tokens of (H, R, N or P) bf16
+  if (H <= 0 || H * R * (N > P ? N : P) > (int64_t(1) << 24)) return false;
   if (N == 64) return (Q == 32 || Q == 64) && (R == 1 || R == 2 || R == 4);
   if (N == 128) return (Q == 16 || Q == 32 || Q == 64) && (R == 2 || R == 4);
   return false;
@@ -102,7 +115,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   constexpr float LOG2E = 1.4426950408889634f;
   static_assert(XIT >= 1 && NCT >= 2, "shape");
 
-  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ __align__(16) unsigned char smem[Ly::BYTES];
   unsigned char* sB = smem + Ly::OFF_B;
   unsigned char* sX = smem + Ly::OFF_X;
   unsigned char* sWh = smem + Ly::OFF_WH;
@@ -138,8 +151,18 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   const int64_t t0 = seg * a.seg_len;
   const int64_t t1 = (t0 + a.seg_len < L) ? t0 + a.seg_len : L;
   auto tokS = [&](int64_t tok) { return (b * L + tok) * H + h; };
+  // Global addresses: a block-uniform base at the sub-chunk's first token plus
+  // a 32-bit per-thread offset (tokens t < QS of the sub-chunk are t * H rows
+  // further; the launch checks that these offsets fit in 32 bits).
+  const uint32_t Hu = (uint32_t)H;
+  auto rowp = [&](const void* base, int64_t c0, int rowbytes) __attribute__((always_inline)) {
+    return (const unsigned char*)base + tokS(c0) * rowbytes;
+  };
   const int64_t QM = a.Q;                          // chunk of the segment offsets (a multiple of QS)
   const int64_t nchunks_meta = (L + QM - 1) / QM;
+  const int spc = a.Q / QS;                        // sub-chunks per requested chunk: 1, 2 or 4
+  int kin = 0;                                     // sub-chunk index within the requested chunk
+  int64_t meta_at = (bh * nchunks_meta + t0 / QM) * (1 + K);  // offsets of the current requested chunk
 
   // output tiles of this wave: the causal work of tiles (w, NCT-1-w) is equal
   int ctl[NCW];
@@ -164,43 +187,48 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   // from the scores, the outputs and the state while every operand stays finite.
   auto load_BX = [&](int64_t c0) __attribute__((always_inline)) {
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
-    const int64_t row = tokS(c0 + (st_t < nvalid ? st_t : nvalid - 1));
-    const u16* gB = (const u16*)a.B + row * (R * N) + 8 * st_c;
-    const u16* gX = (const u16*)a.x + row * (R * P);
+    const uint32_t tr = (uint32_t)(st_t < nvalid ? st_t : nvalid - 1) * Hu;  // token row offset
+    const unsigned char* gB = rowp(a.B, c0, R * N * 2);
+    const unsigned char* gX = rowp(a.x, c0, R * P * 2);
+    const uint32_t ob = tr * (R * N * 2) + 16 * st_c, ox = tr * (R * P * 2);
 #pragma unroll
-    for (int r = 0; r < R; ++r) rB[r] = *(const uint4*)(gB + r * N);
+    for (int r = 0; r < R; ++r) rB[r] = *(const uint4*)(gB + (ob + r * N * 2));
 #pragma unroll
     for (int k = 0; k < XIT; ++k) {
       const int i = st_c + CH * k;  // piece i: rank i / 8, 16-byte column i % 8
-      rX[k] = *(const uint4*)(gX + (i >> 3) * P + 8 * (i & 7));
+      rX[k] = *(const uint4*)(gX + (ox + (i >> 3) * P * 2 + 16 * (i & 7)));
     }
   };
   auto load_scal = [&](int64_t c0) __attribute__((always_inline)) {
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
     const bool tv = st_t < nvalid;
-    const int64_t ts = tokS(c0 + (tv ? st_t : nvalid - 1));
-    rTh = *(const float4*)(a.theta + ts * K + 4 * st_c);
-    const float d = a.dt[ts], av = a.A[ts], l = a.lam[ts];
+    const uint32_t tr = (uint32_t)(tv ? st_t : nvalid - 1) * Hu;
+    rTh = *(const float4*)(rowp(a.theta, c0, K * 4) + (tr * (K * 4) + 16 * st_c));
+    const float d = *(const float*)(rowp(a.dt, c0, 4) + tr * 4);
+    const float av = *(const float*)(rowp(a.A, c0, 4) + tr * 4);
+    const float l = *(const float*)(rowp(a.lam, c0, 4) + tr * 4);
     rdt = tv ? d : 0.0f;
     rA = tv ? av : 0.0f;
     rlam = tv ? l : 0.0f;
     // the following token (its epsilon weights this token's input in the state)
     const bool tv1 = c0 + st_t + 1 < t1;
-    const int64_t ts1 = tv1 ? ts + H : ts;
-    const float d1 = a.dt[ts1], l1 = a.lam[ts1];
+    const uint32_t tr1 = tv1 ? tr + Hu : tr;
+    const float d1 = *(const float*)(rowp(a.dt, c0, 4) + tr1 * 4);
+    const float l1 = *(const float*)(rowp(a.lam, c0, 4) + tr1 * 4);
     rdt1 = tv1 ? d1 : 0.0f;
     rlam1 = tv1 ? l1 : 0.0f;
   };
 
   auto load_C = [&](int64_t c0) __attribute__((always_inline)) {
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
+    const unsigned char* gC = rowp(a.C, c0, R * N * 2);
 #pragma unroll
     for (int ci = 0; ci < NCW; ++ci) {
       const int v = ctl[ci] * 16 + m16;
       const int t = (v >> lgR) < nvalid ? (v >> lgR) : nvalid - 1;
-      const u16* row = (const u16*)a.C + tokS(c0 + t) * (R * N) + (v & (R - 1)) * N + 8 * g;
+      const uint32_t oc = (uint32_t)t * Hu * (R * N * 2) + (v & (R - 1)) * N * 2 + 16 * g;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) rC[ci][ks] = *(const uint4*)(row + ks * 32);
+      for (int ks = 0; ks < NKS; ++ks) rC[ci][ks] = *(const uint4*)(gC + (oc + ks * 64));
     }
   };
 
@@ -277,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
     }
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
     const int fm = fsw<BCPR>(m16);  // swizzle of the rows m16 (+ multiples of 16) of B~ and H'^T tiles
-    const bool meta = S > 1 && seg > 0 && (c0 % QM) == 0;  // a requested chunk starts here
+    const bool meta = S > 1 && seg > 0 && kin == 0;  // a requested chunk starts here (segments start at one)
     __syncthreads();  // wave totals are in LDS; the previous sub-chunk's LDS reads are done
 
     // H'^T (bf16) for the inter-chunk output: row p = 16 pt + m16, columns n = 16 nt + 4g ..
@@ -316,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
         if (c0 + QS < t1) load_scal(c0 + QS);
       if (st_c == 0) sSC[st_t] = make_float4(l2, q, gam, __builtin_amdgcn_exp2f(l2));
       if (S > 1) {  // segment-relative offsets at requested chunk starts, for the fix-up pass
-        if (meta && tid == 0) a.chunk_meta[(bh * nchunks_meta + c0 / QM) * (1 + K)] = segLam;
+        if (meta && tid == 0) a.chunk_meta[meta_at] = segLam;
         segLam += ltot;
       }
       if (st_t == QS - 1) {  // last token: the sub-chunk's total angles
@@ -327,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
           if (meta) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-              a.chunk_meta[(bh * nchunks_meta + c0 / QM) * (1 + K) + 1 + 4 * st_c + j] = segPhi[j];
+              a.chunk_meta[meta_at + 1 + 4 * st_c + j] = segPhi[j];
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) segPhi[j] += ptot[j];
@@ -335,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {  // rotation by the total angle, for the state pass
           float s2, c2;
-          fast_sincos(ptot[j], &s2, &c2);
+          sincos_rev(ptot[j], &s2, &c2);
           sTh[4 * st_c + j] = make_float2(c2, s2);
         }
       }
@@ -343,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
       uint32_t tab[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        fast_sincos(sc_p[j] + ppre[j], &sn[j], &cs[j]);
+        sincos_rev(sc_p[j] + ppre[j], &sn[j], &cs[j]);
         tab[j] = pack_bf2(cs[j], sn[j]);
       }
       *(uint4*)(sCS + swz<BCPR>(st_t, st_c)) = make_uint4(tab[0], tab[1], tab[2], tab[3]);
@@ -372,28 +400,40 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
       }
       if constexpr (R >= 2)
         if (c0 + QS < t1) load_BX(c0 + QS);
-      // (w B~)^T: row n = 8 st_c + e, columns (token, rank): the R ranks of token t are adjacent
+      // (w B~)^T: row n = 8 st_c + e, columns (token, rank): the R ranks of token t are adjacent.
+      // lo = w B~ - hi comes from one dot product per element: hi . (-1, 0) + w B~.
       {
         const int byte = 2 * R * st_t;
         const int cb = byte >> 4;
+        int z0 = (cb ^ fW<Ly::WCPR>(8 * st_c)) << 4, z1 = (cb ^ fW<Ly::WCPR>(8 * st_c + 4)) << 4;
+        asm volatile("" : "+v"(z0), "+v"(z1));  // keeps (z ^ 16k) + base as one xor-add per row
+        const int base = 8 * st_c * Ly::WROW + (byte & 15);
+        // (-1, 0) and (0, -1) as bf16 pairs, held in scalar registers: as an inline
+        // constant the compiler would encode (-1, 0) as -1.0, which this operand
+        // reads as the fp32 bit pattern, i.e. (0, -1) (measured)
+        uint32_t nlo_b = 0x0000bf80u, nhi_b = 0xbf800000u;
+        asm volatile("" : "+s"(nlo_b), "+s"(nhi_b));
+        const bf16x2 nlo = __builtin_bit_cast(bf16x2, nlo_b), nhi = __builtin_bit_cast(bf16x2, nhi_b);
+        auto lo2 = [&](uint32_t hw, float w0, float w1) __attribute__((always_inline)) {
+          const bf16x2 hv = __builtin_bit_cast(bf16x2, hw);
+          return pack_bf2(__builtin_amdgcn_fdot2_f32_bf16(hv, nlo, w0, false),
+                          __builtin_amdgcn_fdot2_f32_bf16(hv, nhi, w1, false));
+        };
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int n = 8 * st_c + e;
-          const int off = n * Ly::WROW + ((cb ^ fW<Ly::WCPR>(n)) << 4) + (byte & 15);
+          const int off = (((e < 4 ? z0 : z1) ^ (16 * (e & 3))) + base) + e * Ly::WROW;
           if constexpr (R == 4) {
             const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]), h23 = pack_bf2(wb[2][e], wb[3][e]);
-            const uint32_t l01 = pack_bf2(wb[0][e] - bf_lo(h01), wb[1][e] - bf_hi(h01));
-            const uint32_t l23 = pack_bf2(wb[2][e] - bf_lo(h23), wb[3][e] - bf_hi(h23));
             *(uint2*)(sWh + off) = make_uint2(h01, h23);
-            *(uint2*)(sWl + off) = make_uint2(l01, l23);
+            *(uint2*)(sWl + off) = make_uint2(lo2(h01, wb[0][e], wb[1][e]), lo2(h23, wb[2][e], wb[3][e]));
           } else if constexpr (R == 2) {
             const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]);
             *(uint32_t*)(sWh + off) = h01;
-            *(uint32_t*)(sWl + off) = pack_bf2(wb[0][e] - bf_lo(h01), wb[1][e] - bf_hi(h01));
+            *(uint32_t*)(sWl + off) = lo2(h01, wb[0][e], wb[1][e]);
           } else {
             const uint32_t h0 = pack_bf2(wb[0][e], 0.0f);
             *(u16*)(sWh + off) = (u16)(h0 & 0xffffu);
-            *(u16*)(sWl + off) = (u16)(pack_bf2(wb[0][e] - bf_lo(h0), 0.0f) & 0xffffu);
+            *(u16*)(sWl + off) = (u16)(lo2(h0, wb[0][e], 0.0f) & 0xffffu);
           }
         }
       }
@@ -420,13 +460,10 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
         uint32_t o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          // R(-phi)(u, w) = ((u, w).(cos, sin), (u, w).(-sin, cos)), bf16 pairs, fp32 sums
-          const uint32_t ms = __builtin_amdgcn_alignbit(tw[j], tw[j], 16) ^ 0x8000u;  // (-sin, cos)
+          // R(-phi)(u, w) = ((u, w).(cos, sin), (w, u).(cos, -sin)), bf16 pairs, fp32 sums
           const float o0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cw[j]),
                                                            __builtin_bit_cast(bf16x2, tw[j]), 0.0f, false);
-          const float o1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, cw[j]),
-                                                           __builtin_bit_cast(bf16x2, ms), 0.0f, false);
-          o[j] = pack_bf2(o0, o1);
+          o[j] = pack_bf2(o0, dot2_bf16_neghi(__builtin_amdgcn_alignbit(cw[j], cw[j], 16), tw[j]));
         }
         rCt[ci][ks] = make_uint4(o[0], o[1], o[2], o[3]);
       }
@@ -521,7 +558,8 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
 #pragma unroll
       for (int ci = 0; ci < NCW; ++ci) {
         const int vcol = ctl[ci] * 16 + m16;
-        u16* yrow = (u16*)a.y + tokS(c0 + (tcol[ci] < nvalid ? tcol[ci] : 0)) * (R * P) + (vcol & (R - 1)) * P;
+        u16* yrow = (u16*)(rowp(a.y, c0, R * P * 2) + ((uint32_t)(tcol[ci] < nvalid ? tcol[ci] : 0) * Hu * (R * P * 2) +
+                                                          (vcol & (R - 1)) * P * 2));
         if constexpr (PTW == 4) {
           // transpose (16-lane row g) x (p tile) so that lane g holds p = 16g .. 16g + 15
           // of its row: 32 contiguous bytes per lane instead of four 8-byte pieces
@@ -593,6 +631,10 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
         }
     }
     if (more) local_scan();
+    if (++kin == spc) {
+      kin = 0;
+      meta_at += 1 + K;
+    }
   }
 
   // ---------------- epilogue ----------------
@@ -619,16 +661,9 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
 
 template <int N, int R>
 static hipError_t sw_run(const WalkArgs& a, hipStream_t s) {
-  auto kern = subchunk_walk_kernel<N, R>;
-  constexpr int lds = SW<N, R>::BYTES;
-  static bool attr_set = false;  // per instantiation; the attribute is per function
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  auto kern = subchunk_walk_kernel<N, R>;  // LDS is static (SW<N, R>::BYTES)
   const int64_t blocks = a.batch * a.H * a.S;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), lds, s, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

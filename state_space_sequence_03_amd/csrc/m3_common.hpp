@@ -151,6 +151,25 @@ __device__ __forceinline__ void fast_sincos(float x, float* s, float* c) {
   *c = __cosf(r);
 }
 
+// sin and cos of x (radians) with the hardware sine/cosine, which take their
+// argument in revolutions: x / (2 pi) reduced to [-1/2, 1/2] by subtracting
+// the nearest integer (exact), so the only added error is the rounding of the
+// product, |x| / (2 pi) * 2^-24 revolutions.
+__device__ __forceinline__ void sincos_rev(float x, float* s, float* c) {
+  const float y = x * 0.15915494309189535f;
+  const float r = y - rintf(y);
+  *s = __builtin_amdgcn_sinf(r);
+  *c = __builtin_amdgcn_cosf(r);
+}
+
+// a.lo * b.lo - a.hi * b.hi over bf16 pairs with an fp32 sum: the dot product
+// instruction with the high half of b negated by its operand modifier.
+__device__ __forceinline__ float dot2_bf16_neghi(uint32_t a, uint32_t b) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
 // Swizzle of arrays of rows of CPR 16-byte columns: column c of row r is
 // stored at column c ^ f(r), with f depending on r mod 16 only (the pattern
 // repeats for every 16-row tile).  With 64 four-byte banks (16 groups of 16

@@ -55,7 +55,7 @@ hipError_t launch_walk_fast(int N, int P, const WalkArgs& a, hipStream_t s);
 // The sub-chunk walker (bf16 io, P = 64, N = 64 with Q in {32, 64}, or
 // N = 128 with R in {2, 4}) applies to these sizes; it walks 32-token (N = 64)
 // or 16-token (N = 128) sub-chunks and records segment offsets every Q tokens.
-bool subwalk_supported(int io_bf16, int N, int P, int Q, int R);
+bool subwalk_supported(int io_bf16, int N, int P, int Q, int R, int64_t H);
 hipError_t launch_subwalk(int N, const WalkArgs& a, hipStream_t s);
 // Chunked forward walk: the sub-chunk walker or the fast walker when one
 // applies, the general walker otherwise.
