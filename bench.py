@@ -179,6 +179,40 @@ def bench_decode(ops, inputs, w, torch, reps=3):
                 gbps=b / (per_step * 1e-3) / 1e9)
 
 
+def verify_bytes_per_call(w, k, s_io=2):
+    """k tokens on a decode state: the state read and written once, the
+    previous token's B and x once, and per token x, B, C, dt, A, lam, theta, y."""
+    BH, N, P, R = w.batch * w.nheads, w.dstate, w.headdim, w.rank
+    state = 2 * BH * N * P * 4
+    prev = BH * (R * N + R * P) * s_io
+    per_token = BH * ((R * P + 2 * R * N) * s_io + 3 * 4 + (N // 2) * 4 + R * P * s_io)
+    return state + prev + k * per_token
+
+
+def bench_verify(ops, inputs, w, k, steps, warmup, torch):
+    """k tokens per call on the decode state (chunked_fwd with h0 = h_final =
+    the state, prev given): the short-sequence path, and the chunk walk forced
+    for comparison."""
+    d = inputs.torch_inputs(w.batch, k, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
+                            seed=inputs.seed_of(w.name) + k, with_h0=True)
+    d["prev_B"], d["prev_x"] = d["B"][:, 0].contiguous(), d["x"][:, 0].contiguous()  # any token of the same draw
+    state = d["h0"].clone()
+    y = torch.empty_like(d["x"])
+    res = {}
+    for name, walk in (("token_path", False), ("chunk_walk", True)):
+        fn = lambda: ops.chunked_fwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], h0=state,
+                                     prev_B=d["prev_B"], prev_x=d["prev_x"], chunk=16, chunk_walk=walk, y=y,
+                                     h_final=state)
+        wall, ev = timed(fn, steps, warmup, torch)
+        res[name] = ev
+    b = verify_bytes_per_call(w, k)
+    del d, state, y
+    torch.cuda.empty_cache()
+    ms = res["token_path"]
+    return dict(k=k, ms_per_call=ms, tokens_per_s=w.batch * k / (ms * 1e-3), bytes_per_call=b,
+                gbps=b / (ms * 1e-3) / 1e9, chunk_walk_ms=res["chunk_walk"])
+
+
 def bench_rope(ops, inputs, w, steps, warmup, torch):
     d = inputs.torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
                             seed=inputs.seed_of(w.name))
@@ -271,7 +305,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "rope", "copy", "all"], default="all")
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "rope", "copy", "all"], default="all")
+    ap.add_argument("--verify-k", type=int, default=8, help="tokens per call of the verify workload")
     ap.add_argument("--workload", default="mimo_bf16", choices=["mimo_bf16", "siso_bf16", "long_mimo_bf16"],
                     help="prefill workload timed by --only prefill (profiling); the headline line uses mimo_bf16")
     args = ap.parse_args()
@@ -297,6 +332,10 @@ def main():
         wd = W["decode_mimo_bf16"]
         print(f"[bench] decode {wd.name}: {wd.decode_steps} steps", file=sys.stderr, flush=True)
         out["decode"] = bench_decode(ops, inputs, wd, torch)
+    if args.only in ("verify", "all"):
+        wd = W["decode_mimo_bf16"]
+        print(f"[bench] verify: {args.verify_k} tokens per call on {wd.name} shapes", file=sys.stderr, flush=True)
+        out["verify"] = bench_verify(ops, inputs, wd, args.verify_k, args.steps, args.warmup, torch)
     if args.only in ("rope", "all"):
         print(f"[bench] rope_bc on {w.name} shapes", file=sys.stderr, flush=True)
         out["rope"] = bench_rope(ops, inputs, w, max(3, args.steps // 4), 2, torch)
@@ -334,6 +373,14 @@ def main():
                           "steps_per_s": round(dc["steps_per_s"], 1), "ms_per_step": round(dc["ms_per_step"], 5),
                           "achieved_GBps": round(dc["gbps"], 1), "peak_GBps": HBM_PEAK_GBPS,
                           "frac": round(dc["gbps"] / HBM_PEAK_GBPS, 4), "bytes_per_step": dc["bytes_per_step"]}
+    if "verify" in out:
+        vf = out["verify"]
+        line["verify"] = {"workload": f"verify_mimo_bf16: decode shapes (batch 256, H=64, P=64, N=64, R=4), "
+                                      f"k={vf['k']} tokens per chunked_fwd call on the fp32 state in place",
+                          "ms_per_call": round(vf["ms_per_call"], 5), "tokens_per_s": round(vf["tokens_per_s"], 1),
+                          "achieved_GBps": round(vf["gbps"], 1), "frac": round(vf["gbps"] / HBM_PEAK_GBPS, 4),
+                          "bytes_per_call": vf["bytes_per_call"],
+                          "chunk_walk_ms_per_call": round(vf["chunk_walk_ms"], 5)}
     if "rope" in out:
         line["rope_bc"] = {"ms": round(out["rope"]["ms"], 4), "achieved_GBps": round(out["rope"]["gbps"], 1),
                            "frac": round(out["rope"]["gbps"] / HBM_PEAK_GBPS, 4)}

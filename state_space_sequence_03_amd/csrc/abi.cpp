@@ -8,6 +8,8 @@
 
 #include "m3_launch.hpp"
 
+static_assert(M3_TOKEN_PATH_MAX_L <= m3::TOKENS_MAX, "the short-sequence path stages every token in LDS");
+
 namespace {
 
 bool in_set(int64_t v, std::initializer_list<int64_t> s) {
@@ -129,7 +131,7 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
                                  float* h_final, void* workspace, size_t workspace_bytes, void* stream) {
   m3_status st = check_dims(d, true, true);
   if (st != M3_OK) return st;
-  if ((d->flags & ~0xffff) != 0) return M3_ERR_UNSUPPORTED;
+  if ((d->flags & ~(0xffff | M3_FLAG_CHUNK_WALK)) != 0) return M3_ERR_UNSUPPORTED;
   if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0 &&
       !m3::walk_fast_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) &&
       !m3::subwalk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank, d->nheads))
@@ -154,6 +156,15 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
     if (h_final && h_final != h0)
       return m3::launch_copy_f32(h_final, h0, BH * d->dstate * d->headdim, s) == hipSuccess ? M3_OK : M3_ERR_HIP;
     return M3_OK;
+  }
+  if (d->seqlen <= M3_TOKEN_PATH_MAX_L && sp.S == 1 && !(d->flags & M3_FLAG_CHUNK_WALK)) {
+    // a few tokens: token by token with the state in registers
+    m3::TokensArgs t{};
+    t.h0 = h0; t.h_final = h_final; t.x = x; t.B = B; t.C = C;
+    t.dt = dt; t.A = A; t.lam = lam; t.theta = theta; t.prev_B = prev_B; t.prev_x = prev_x; t.y = y;
+    t.batch = d->batch; t.L = d->seqlen; t.H = d->nheads; t.R = (int)d->rank;
+    return m3::launch_decode_tokens(io_bf16(d), (int)d->dstate, (int)d->headdim, t, s) == hipSuccess ? M3_OK
+                                                                                                : M3_ERR_HIP;
   }
   m3::WalkArgs a{};
   a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.lam = lam; a.theta = theta;

@@ -49,6 +49,15 @@ struct io<float> {
     const float4 v = *(const float4*)((const float*)p + i);
     f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
   }
+  // two consecutive elements, i even (one 8-byte access)
+  __device__ static void load2(const void* p, int64_t i, float& f0, float& f1) {
+    const float2 v = *(const float2*)((const float*)p + i);
+    f0 = v.x; f1 = v.y;
+  }
+  // four consecutive elements, i a multiple of 4 (one 16-byte access)
+  __device__ static void store4(void* p, int64_t i, const float* f) {
+    *(float4*)((float*)p + i) = make_float4(f[0], f[1], f[2], f[3]);
+  }
 };
 
 template <>
@@ -79,6 +88,15 @@ struct io<bf16_t> {
   __device__ static void load4(const void* p, int64_t i, float* f) {
     const uint2 v = *(const uint2*)((const u16*)p + i);
     f[0] = bf_lo(v.x); f[1] = bf_hi(v.x); f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
+  }
+  // two consecutive elements, i even (one 4-byte access)
+  __device__ static void load2(const void* p, int64_t i, float& f0, float& f1) {
+    const uint32_t v = *(const uint32_t*)((const u16*)p + i);
+    f0 = bf_lo(v); f1 = bf_hi(v);
+  }
+  // four consecutive elements, i a multiple of 4 (one 8-byte access)
+  __device__ static void store4(void* p, int64_t i, const float* f) {
+    *(uint2*)((u16*)p + i) = make_uint2(pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3]));
   }
 };
 

@@ -20,6 +20,21 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(int io_bf16, int N, int P, const DecodeArgs& a, hipStream_t s);
 
+// The chunked forward over a short sequence, token by token (state in
+// registers); the ABI layer picks it for short calls.
+struct TokensArgs {
+  const float* h0;   // nullable (B, H, N, P)
+  float* h_final;    // nullable; may alias h0
+  const void *x, *B, *C;
+  const float *dt, *A, *lam, *theta;
+  const void *prev_B, *prev_x;
+  void* y;
+  int64_t batch, L, H;
+  int R;
+};
+constexpr int TOKENS_MAX = 16;  // at most this many tokens (all staged in LDS)
+hipError_t launch_decode_tokens(int io_bf16, int N, int P, const TokensArgs& a, hipStream_t s);
+
 struct RopeArgs {
   const void *B, *C;
   const float *dt, *theta, *angle0;

@@ -39,6 +39,14 @@ def test_exports_every_declared_symbol(L):
     assert lib.mamba3_abi_version() == 1
 
 
+def test_header_constants_match_binding(L):
+    text = open(HEADER).read()
+    for name in ("M3_FLAG_CHUNK_WALK", "M3_TOKEN_PATH_MAX_L"):
+        m = re.search(r"#define\s+" + name + r"\s+(\w+)", text)
+        assert m, name
+        assert int(m.group(1), 0) == getattr(L, name), name
+
+
 def test_status_strings(L):
     for s in range(7):
         assert len(L.status_string(s)) >= 2 and L.status_string(s) != "unknown status"
@@ -69,6 +77,7 @@ def dims(L, **kw):
     (dict(dstate=48), "M3_ERR_UNSUPPORTED"), (dict(headdim=96), "M3_ERR_UNSUPPORTED"),
     (dict(rank=3), "M3_ERR_UNSUPPORTED"), (dict(chunk=128), "M3_ERR_UNSUPPORTED"),
     (dict(io_dtype=7), "M3_ERR_UNSUPPORTED"), (dict(flags=1 << 20), "M3_ERR_UNSUPPORTED"),
+    (dict(flags=1 << 17), "M3_ERR_UNSUPPORTED"),
     (dict(dstate=128, headdim=128, rank=4, chunk=64), "M3_ERR_UNSUPPORTED"),     # tiles exceed LDS
     (dict(io_dtype=0, rank=4, chunk=64), "M3_ERR_UNSUPPORTED"),                # fp32 tiles exceed LDS
 ])

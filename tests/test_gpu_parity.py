@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 from state_space_sequence_03_amd.inputs import numpy_inputs, torch_inputs, WORKLOADS, seed_of
+from state_space_sequence_03_amd.ops import M3_TOKEN_PATH_MAX_L
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -121,6 +122,61 @@ def test_chunked_matches_oracle(ops, case):
     say(f"chunked_fwd {case}")
     inp = numpy_inputs(b, L, H, P, N, R, io=io, seed=zlib.crc32(repr(case).encode()) % 10000, with_h0=h0, with_prev=prev)
     check_fwd(ops, inp, io, Q)
+    if L <= M3_TOKEN_PATH_MAX_L:  # the call above ran token by token: also walk the chunks
+        say("   forced chunk walk")
+        check_fwd(ops, inp, io, Q, chunk_walk=True)
+
+
+# short sequences (at most M3_TOKEN_PATH_MAX_L tokens) run token by token with
+# the state on chip; each case also runs through the chunk walk
+TOKEN_CASES = [
+    # io,    b, L,  H, P,   N,   R, h0,    prev
+    ("f32", 3, 1, 5, 16, 16, 1, True, True),
+    ("f32", 2, 7, 3, 64, 64, 4, True, False),
+    ("f32", 1, 16, 2, 128, 128, 2, False, True),
+    ("f32", 2, 4, 2, 32, 16, 1, False, False),
+    ("bf16", 4, 8, 8, 64, 64, 4, True, True),     # decode shapes, 8 tokens per call
+    ("bf16", 2, 3, 4, 32, 128, 1, False, False),
+    ("bf16", 1, 16, 3, 128, 32, 2, True, True),
+    ("bf16", 2, 2, 2, 16, 64, 4, True, True),
+    ("bf16", 1, 11, 2, 64, 128, 4, True, True),   # long-context head shape
+]
+
+
+@pytest.mark.parametrize("case", TOKEN_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_short_sequence_token_path(ops, case):
+    io, b, L, H, P, N, R, h0, prev = case
+    say(f"token path {case}")
+    inp = numpy_inputs(b, L, H, P, N, R, io=io, seed=zlib.crc32(repr(case).encode()) % 10000, with_h0=h0, with_prev=prev)
+    y_t, h_t = check_fwd(ops, inp, io, 16)
+    y_w, h_w = check_fwd(ops, inp, io, 16, chunk_walk=True)
+    assert slice_err(host(h_t), host(h_w), (0, 1)) < 1e-3
+
+
+def test_verify_step_in_place(ops):
+    """k tokens per call on a decode state: h_final aliases h0 (updated in
+    place) and equals k one-token steps; y matches the oracle."""
+    b, L, H, P, N, R = 4, 8, 8, 64, 64, 4
+    inp = numpy_inputs(b, L, H, P, N, R, io="bf16", seed=21, with_h0=True, with_prev=True)
+    d = to_dev(inp, "bf16")
+    say("verify step in place")
+    state = d["h0"].clone()
+    y, hf = ops.chunked_fwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], h0=state,
+                            prev_B=d["prev_B"], prev_x=d["prev_x"], chunk=16, h_final=state)
+    torch.cuda.synchronize()
+    assert hf.data_ptr() == state.data_ptr()
+    yo, ho = oracle_fwd(inp)
+    assert slice_err(host(y), yo, (0, 2)) < TOL["bf16"]
+    assert slice_err(host(state), ho, (0, 1)) < TOL["bf16"]
+    st = d["h0"].clone()
+    pb, px = d["prev_B"], d["prev_x"]
+    for t in range(L):
+        ops.decode_step(st, d["x"][:, t].contiguous(), d["B"][:, t].contiguous(), d["C"][:, t].contiguous(),
+                        d["dt"][:, t].contiguous(), d["A"][:, t].contiguous(), d["lam"][:, t].contiguous(),
+                        d["theta"][:, t].contiguous(), pb, px)
+        pb, px = d["B"][:, t].contiguous(), d["x"][:, t].contiguous()
+    torch.cuda.synchronize()
+    assert slice_err(host(st), host(state), (0, 1)) < 1e-5
 
 
 @pytest.mark.parametrize("io,N,P,R,Q", [("f32", 16, 32, 2, 32), ("bf16", 64, 64, 4, 64), ("bf16", 128, 64, 4, 64)])
