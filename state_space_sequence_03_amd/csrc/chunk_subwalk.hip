@@ -35,6 +35,8 @@
 //    distinct banks.
 //  * Two barriers per sub-chunk: after the previous sub-chunk's last LDS read
 //    (and the scan exchange), and after staging.
+//  * Wave priorities order the two blocks' waves on a SIMD: matrix phases
+//    first, then staging, then the rest.
 //
 // Precision matches the other bf16 walkers: bf16 MFMA operands with fp32
 // accumulation; the chunk state uses w B~ split into bf16 hi + lo parts.
@@ -319,6 +321,10 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
             make_uint2(pack_bf2(hst[j][pt][0], hst[j][pt][1]), pack_bf2(hst[j][pt][2], hst[j][pt][3]));
     }
 
+    // Wave priorities: the two blocks of a compute unit share its SIMDs; a
+    // wave in the matrix phases (C~, outputs, state) issues first, one in
+    // staging next, then the rest.  Measured: 4 % faster at R = 4, 6 % at R = 1.
+    __builtin_amdgcn_s_setprio(1);
     // ---------- staging ----------
     {
       // prefix over the lower waves (uniform loop) and the sub-chunk's log-decay total
@@ -439,6 +445,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
       }
     }
     __syncthreads();  // B~, X, (w B~)^T, H'^T, the cos/sin table and the scalars are in LDS
+    __builtin_amdgcn_s_setprio(2);
     const bool more = c0 + QS < t1;
     if constexpr (R == 1) {
       if (more) {
@@ -630,6 +637,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
           }
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (more) local_scan();
     if (++kin == spc) {
       kin = 0;
