@@ -521,6 +521,18 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
           for (int ks = 0; ks < NKS; ++ks)
             bfr[sub][ks] = *(const uint4*)(bB[ks] + (kb * 32 + sub * 16) * Ly::BROW);
         const float2* scs = (const float2*)(sSC + kb * 8 + g);  // (log2 decay, q) of the lane's source token (R = 4)
+        // X^T fragments of the slab in the score operand's k order (rows 4g..
+        // and 16 + 4g..), shared by the wave's column tiles
+        uint4 xf[PTW];
+        {
+          const unsigned char* xk = bXt + kb * 32 * Ly::XP;
+#pragma unroll
+          for (int pp = 0; pp < PTW; ++pp) {
+            const uint2 f0 = lds_tr16(xk + pp * 32);
+            const uint2 f1 = lds_tr16(xk + 16 * Ly::XP + pp * 32);
+            xf[pp] = make_uint4(f0.x, f0.y, f1.x, f1.y);
+          }
+        }
 #pragma unroll
         for (int ci = 0; ci < NCW; ++ci) {
           if (ci == 1 && kb >= nkb1) continue;
@@ -551,13 +563,9 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
           }
           const uint4 gfr = make_uint4(pack_bf2(gm[0][0], gm[0][1]), pack_bf2(gm[0][2], gm[0][3]),
                                        pack_bf2(gm[1][0], gm[1][1]), pack_bf2(gm[1][2], gm[1][3]));
-          // X^T fragments in the score operand's k order (rows 4g.. and 16 + 4g.. of the slab)
-          const unsigned char* xk = bXt + kb * 32 * Ly::XP;
 #pragma unroll
           for (int pp = 0; pp < PTW; ++pp) {
-            const uint2 f0 = lds_tr16(xk + pp * 32);
-            const uint2 f1 = lds_tr16(xk + 16 * Ly::XP + pp * 32);
-            yacc[ci][pp] = mfma_bf16(as_bf16x8(make_uint4(f0.x, f0.y, f1.x, f1.y)), as_bf16x8(gfr), yacc[ci][pp]);
+            yacc[ci][pp] = mfma_bf16(as_bf16x8(xf[pp]), as_bf16x8(gfr), yacc[ci][pp]);
           }
         }
       }

@@ -22,14 +22,20 @@ __global__ __launch_bounds__(256) void rope_totals_kernel(RopeArgs a, int64_t nc
   constexpr int TG = 256 / K;
   const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;  // head fastest
   const int k = threadIdx.x % K, tg = threadIdx.x / K;
-  float s = 0.0f;
-  for (int t = tg; t < ROPE_CHUNK; t += TG) {
-    const int64_t tok = c * ROPE_CHUNK + t;
-    if (tok < a.L) {
-      const int64_t idx = (b * a.L + tok) * a.H + h;
-      s += a.dt[idx] * a.theta[idx * K + k];
-    }
+  // every load of the thread is issued before the sum (tokens past L read
+  // token L - 1 with weight 0)
+  constexpr int NT = ROPE_CHUNK / TG;
+  float dv[NT], tv[NT];
+#pragma unroll
+  for (int q = 0; q < NT; ++q) {
+    const int64_t tok = c * ROPE_CHUNK + tg + TG * q;
+    const int64_t idx = (b * a.L + (tok < a.L ? tok : a.L - 1)) * a.H + h;
+    dv[q] = tok < a.L ? a.dt[idx] : 0.0f;
+    tv[q] = a.theta[idx * K + k];
   }
+  float s = 0.0f;
+#pragma unroll
+  for (int q = 0; q < NT; ++q) s += dv[q] * tv[q];
   __shared__ float red[256];
   red[threadIdx.x] = s;
   __syncthreads();
