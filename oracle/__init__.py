@@ -55,6 +55,8 @@ def _lib(mutant: int = 0) -> ctypes.CDLL:
             i64 = ctypes.c_int64
             lib.mamba3_oracle_forward.argtypes = [i64] * 6 + [d] * 12 + [ctypes.c_int]
             lib.mamba3_oracle_forward.restype = ctypes.c_int
+            lib.mamba3_oracle_backward.argtypes = [i64] * 6 + [d] * 22 + [ctypes.c_int]
+            lib.mamba3_oracle_backward.restype = ctypes.c_int
             lib.mamba3_oracle_rope_bc.argtypes = [i64] * 5 + [d] * 8
             lib.mamba3_oracle_rope_bc.restype = ctypes.c_int
             lib.mamba3_oracle_version.restype = ctypes.c_int
@@ -105,6 +107,36 @@ def forward(x, B, C, dt, A, lam, theta, h0=None, prev_B=None, prev_x=None,
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return y, hf
+
+
+def backward(x, B, C, dt, A, lam, theta, dy, h0=None, prev_B=None, prev_x=None, dh_final=None,
+             nthreads: int = 0, mutant: int = 0):
+    """Gradients of  sum_t <dy_t, y_t> + <dh_final, h_final>  for the forward above.
+
+    Returns a dict with dx, dB, dC, ddt, dA, dlam, dtheta (shapes of the
+    inputs), dh0 (b,H,N,P) and, when prev_B is given, dprev_B and dprev_x.
+    """
+    x, B, C, dt, A, lam, theta, dy = (_f64(a) for a in (x, B, C, dt, A, lam, theta, dy))
+    h0, prev_B, prev_x, dh_final = _f64(h0), _f64(prev_B), _f64(prev_x), _f64(dh_final)
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    assert dy.shape == x.shape
+    if (prev_B is None) != (prev_x is None):
+        raise ValueError("prev_B and prev_x go together")
+    out = {k: np.zeros_like(v) for k, v in (("dx", x), ("dB", B), ("dC", C), ("ddt", dt), ("dA", A),
+                                                 ("dlam", lam), ("dtheta", theta))}
+    out["dh0"] = np.zeros((b, H, N, P), dtype=np.float64)
+    if prev_B is not None:
+        out["dprev_B"] = np.zeros_like(prev_B)
+        out["dprev_x"] = np.zeros_like(prev_x)
+    rc = _lib(mutant).mamba3_oracle_backward(
+        b, L, H, P, N, R, _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(lam), _ptr(theta),
+        _ptr(h0), _ptr(prev_B), _ptr(prev_x), _ptr(dy), _ptr(dh_final),
+        *(_ptr(out[k]) for k in ("dx", "dB", "dC", "ddt", "dA", "dlam", "dtheta", "dh0")),
+        _ptr(out.get("dprev_B")), _ptr(out.get("dprev_x")), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return out
 
 
 def decode_step(state, x, B, C, dt, A, lam, theta, prev_B=None, prev_x=None, mutant: int = 0):

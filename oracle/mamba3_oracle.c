@@ -51,6 +51,10 @@
  * quadratic "1-semiseparable x 2-band" form), none of which call this code's
  * formulas.
  *
+ * The backward (gradients of a linear functional of y and h_final) is the
+ * chain rule of this same computation in reverse order; it is pinned against
+ * central finite differences of the forward.
+ *
  * Compile-time switch ORACLE_MUTANT (tests only): plants one known mistake so
  * that a test can show that the pins catch it.  Never set in a normal build.
  */
@@ -230,6 +234,241 @@ int mamba3_oracle_forward(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N,
   }
   for (int i = 1; i < nt; ++i) pthread_create(&tids[i], NULL, fwd_worker, &jobs[i]);
   fwd_worker(&jobs[0]);
+  for (int i = 1; i < nt; ++i) pthread_join(tids[i], NULL);
+  free(jobs); free(tids);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Backward (reverse mode) of the forward above.
+ *
+ * The gradient of the scalar  l = sum_t <dy_t, y_t> + <dh_final, h_final>
+ * with respect to every input, for given dy (B,L,H,R,P) and dh_final (B,H,N,P)
+ * (nullable: zero).  It is the exact derivative of the forward recurrence,
+ * taken step by step in reverse order of the same operations (the chain rule
+ * written out; no other formula is involved):
+ *
+ *   h_final = R(phi_L) ht_L:     g_L = R(-phi_L) dh_final, and phi_L gets
+ *                                <dh_final, J h_final> per pair (J = d/da R(a) R(-a));
+ *   y_t[r] = Ct_t[r]^T ht_t:     dCt_t[r] = ht_t dy_t[r],  g_t += Ct_t[r] dy_t[r]^T;
+ *   ht_t = alpha ht_{t-1} + beta Q_{t-1} + gamma Q_t  (Q_t = sum_r Bt_t[r] x_t[r]^T):
+ *                                dalpha = <g_t, ht_{t-1}>, dbeta = <g_t, Q_{t-1}>,
+ *                                dgamma = <g_t, Q_t>, dQ_t += gamma g_t,
+ *                                dQ_{t-1} += beta g_t, g_{t-1} = alpha g_t;
+ *   Q_t:                         dBt_t[r] = dQ_t x_t[r], dx_t[r] = dQ_t^T Bt_t[r];
+ *   Bt = R(-phi) B, Ct likewise: dB = R(phi) dBt, and phi_t gets
+ *                                dBt[2k] Bt[2k+1] - dBt[2k+1] Bt[2k] (+ the same for C);
+ *   phi_t = phi_{t-1} + dt_t theta_t: the angle adjoint accumulates backwards,
+ *                                dtheta_t = dt_t dphi_t, ddt_t += <theta_t, dphi_t>;
+ *   alpha = exp(dt A), beta = (1 - lam) dt alpha, gamma = lam dt: the scalar
+ *                                chain rule.
+ * The token before the first (prev_B, prev_x) sits at angle 0, so its
+ * gradients need no rotation; dh0 is g_0.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t B, L, H, P, N, R;
+  const double *x, *Bm, *Cm, *dt, *A, *lam, *theta, *h0, *prev_B, *prev_x, *dy, *dhf;
+  double *dx, *dB, *dC, *ddt, *dA, *dlam, *dtheta, *dh0, *dprev_B, *dprev_x;
+  int64_t slice_begin, slice_end;
+} bwd_job;
+
+static void bwd_slice(const bwd_job* j, int64_t bh) {
+  const int64_t L = j->L, H = j->H, P = j->P, N = j->N, R = j->R, K = N / 2, NP = N * P;
+  const int64_t b = bh / H, h = bh % H;
+  /* forward pass, keeping what the reverse pass needs */
+  double* hs = (double*)calloc((size_t)((L + 1) * NP), sizeof(double)); /* ht_0 .. ht_L */
+  double* phi = (double*)calloc((size_t)((L + 1) * K), sizeof(double));  /* phi_0 .. phi_L */
+  double* Bt = (double*)calloc((size_t)((L + 1) * R * N), sizeof(double)); /* row 0: prev_B */
+  double* Ct = (double*)calloc((size_t)((L + 1) * R * N), sizeof(double));
+  double* xs = (double*)calloc((size_t)((L + 1) * R * P), sizeof(double)); /* row 0: prev_x */
+  if (j->h0) memcpy(hs, j->h0 + bh * NP, sizeof(double) * (size_t)NP);
+  if (j->prev_B && j->prev_x) {
+    memcpy(Bt, j->prev_B + bh * R * N, sizeof(double) * (size_t)(R * N));
+    memcpy(xs, j->prev_x + bh * R * P, sizeof(double) * (size_t)(R * P));
+  }
+  for (int64_t t = 1; t <= L; ++t) {
+    const int64_t tok = (b * L + (t - 1)) * H + h;
+    const double dt = j->dt[tok], alpha = exp(dt * j->A[tok]);
+    const double beta = (1.0 - j->lam[tok]) * dt * alpha, gamma = j->lam[tok] * dt;
+    for (int64_t k = 0; k < K; ++k) phi[t * K + k] = phi[(t - 1) * K + k] + dt * j->theta[tok * K + k];
+    memcpy(xs + t * R * P, j->x + tok * R * P, sizeof(double) * (size_t)(R * P));
+    for (int64_t r = 0; r < R; ++r)
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t i = r * N + 2 * k;
+        rot(-phi[t * K + k], j->Bm[tok * R * N + i], j->Bm[tok * R * N + i + 1], &Bt[t * R * N + i], &Bt[t * R * N + i + 1]);
+        rot(-phi[t * K + k], j->Cm[tok * R * N + i], j->Cm[tok * R * N + i + 1], &Ct[t * R * N + i], &Ct[t * R * N + i + 1]);
+      }
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t p = 0; p < P; ++p) {
+        double qp = 0.0, qc = 0.0;
+        for (int64_t r = 0; r < R; ++r) {
+          qp += Bt[(t - 1) * R * N + r * N + n] * xs[(t - 1) * R * P + r * P + p];
+          qc += Bt[t * R * N + r * N + n] * xs[t * R * P + r * P + p];
+        }
+        hs[t * NP + n * P + p] = alpha * hs[(t - 1) * NP + n * P + p] + beta * qp + gamma * qc;
+      }
+  }
+
+  /* reverse pass */
+  double* g = (double*)calloc((size_t)NP, sizeof(double));      /* adjoint of ht_t */
+  double* dQn = (double*)calloc((size_t)NP, sizeof(double));    /* beta_{t+1} g_{t+1}: pending part of dQ_t */
+  double* dQ = (double*)calloc((size_t)NP, sizeof(double));
+  double* dphi = (double*)calloc((size_t)K, sizeof(double));    /* running angle adjoint */
+  double* dBt = (double*)calloc((size_t)(R * N), sizeof(double));
+  double* dCt = (double*)calloc((size_t)(R * N), sizeof(double));
+  if (j->dhf) {
+    const double* dh = j->dhf + bh * NP;
+    for (int64_t k = 0; k < K; ++k) {
+      const double a = phi[L * K + k], c = cos(a), s = sin(a);
+      for (int64_t p = 0; p < P; ++p) {
+        const double du = dh[(2 * k) * P + p], dv = dh[(2 * k + 1) * P + p];
+        const double u = hs[L * NP + (2 * k) * P + p], v = hs[L * NP + (2 * k + 1) * P + p];
+        /* h_final = R(a) (u, v): adjoint R(-a) (du, dv); d/da R(a)(u,v) = (-s u - c v, c u - s v) */
+        g[(2 * k) * P + p] = c * du + s * dv;
+        g[(2 * k + 1) * P + p] = -s * du + c * dv;
+        dphi[k] += du * (-s * u - c * v) + dv * (c * u - s * v);
+      }
+    }
+  }
+  for (int64_t t = L; t >= 1; --t) {
+    const int64_t tok = (b * L + (t - 1)) * H + h;
+    const double dt = j->dt[tok], A = j->A[tok], lam = j->lam[tok], alpha = exp(dt * A);
+    const double beta = (1.0 - lam) * dt * alpha, gamma = lam * dt;
+    const double* dyt = j->dy + tok * R * P;
+    /* y_t */
+    for (int64_t r = 0; r < R; ++r)
+      for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t p = 0; p < P; ++p) acc += hs[t * NP + n * P + p] * dyt[r * P + p];
+        dCt[r * N + n] = acc;
+      }
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t p = 0; p < P; ++p) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < R; ++r) acc += Ct[t * R * N + r * N + n] * dyt[r * P + p];
+        g[n * P + p] += acc;
+      }
+    /* ht_t = alpha ht_{t-1} + beta Q_{t-1} + gamma Q_t */
+    double dalpha = 0.0, dbeta = 0.0, dgamma = 0.0;
+    for (int64_t n = 0; n < N; ++n)
+      for (int64_t p = 0; p < P; ++p) {
+        double qp = 0.0, qc = 0.0;
+        for (int64_t r = 0; r < R; ++r) {
+          qp += Bt[(t - 1) * R * N + r * N + n] * xs[(t - 1) * R * P + r * P + p];
+          qc += Bt[t * R * N + r * N + n] * xs[t * R * P + r * P + p];
+        }
+        const double gg = g[n * P + p];
+        dalpha += gg * hs[(t - 1) * NP + n * P + p];
+        dbeta += gg * qp;
+        dgamma += gg * qc;
+        dQ[n * P + p] = gamma * gg + dQn[n * P + p]; /* complete dQ_t */
+#if ORACLE_MUTANT == 10
+        dQn[n * P + p] = 0.0; /* mutant: the trapezoid term's adjoint is dropped */
+#else
+        dQn[n * P + p] = beta * gg;                  /* pending part of dQ_{t-1} */
+#endif
+        g[n * P + p] = alpha * gg;                   /* becomes g_{t-1} */
+      }
+    /* Q_t = sum_r Bt_t[r] x_t[r]^T */
+    double* dxt = j->dx + tok * R * P;
+    for (int64_t r = 0; r < R; ++r) {
+      for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t p = 0; p < P; ++p) acc += dQ[n * P + p] * xs[t * R * P + r * P + p];
+        dBt[r * N + n] = acc;
+      }
+      for (int64_t p = 0; p < P; ++p) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) acc += dQ[n * P + p] * Bt[t * R * N + r * N + n];
+        dxt[r * P + p] = acc;
+      }
+    }
+    /* rotations of B and C, and the angle adjoint */
+    double* dBo = j->dB + tok * R * N;
+    double* dCo = j->dC + tok * R * N;
+    for (int64_t k = 0; k < K; ++k) {
+      const double a = phi[t * K + k];
+      double dp = 0.0;
+      for (int64_t r = 0; r < R; ++r) {
+        const int64_t i = r * N + 2 * k;
+        rot(a, dBt[i], dBt[i + 1], &dBo[i], &dBo[i + 1]);
+        rot(a, dCt[i], dCt[i + 1], &dCo[i], &dCo[i + 1]);
+#if ORACLE_MUTANT == 11
+        dp -= dBt[i] * Bt[t * R * N + i + 1] - dBt[i + 1] * Bt[t * R * N + i]; /* mutant: sign of B's angle term */
+#else
+        dp += dBt[i] * Bt[t * R * N + i + 1] - dBt[i + 1] * Bt[t * R * N + i];
+#endif
+        dp += dCt[i] * Ct[t * R * N + i + 1] - dCt[i + 1] * Ct[t * R * N + i];
+      }
+      dphi[k] += dp;
+    }
+    /* scalars */
+    double ddt = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      j->dtheta[tok * K + k] = dt * dphi[k];
+      ddt += j->theta[tok * K + k] * dphi[k];
+    }
+    ddt += A * alpha * dalpha + ((1.0 - lam) * alpha + (1.0 - lam) * dt * A * alpha) * dbeta + lam * dgamma;
+    j->ddt[tok] = ddt;
+    j->dA[tok] = dt * alpha * dalpha + (1.0 - lam) * dt * dt * alpha * dbeta;
+    j->dlam[tok] = -dt * alpha * dbeta + dt * dgamma;
+  }
+  if (j->dh0) memcpy(j->dh0 + bh * NP, g, sizeof(double) * (size_t)NP);
+  if (j->dprev_B && j->prev_B) {
+    /* dQ_0 = beta_1 g_1 (the pending part); prev sits at angle 0 */
+    for (int64_t r = 0; r < R; ++r) {
+      for (int64_t n = 0; n < N; ++n) {
+        double acc = 0.0;
+        for (int64_t p = 0; p < P; ++p) acc += dQn[n * P + p] * xs[r * P + p];
+        j->dprev_B[(bh * R + r) * N + n] = acc;
+      }
+      for (int64_t p = 0; p < P; ++p) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) acc += dQn[n * P + p] * Bt[r * N + n];
+        j->dprev_x[(bh * R + r) * P + p] = acc;
+      }
+    }
+  }
+  free(hs); free(phi); free(Bt); free(Ct); free(xs);
+  free(g); free(dQn); free(dQ); free(dphi); free(dBt); free(dCt);
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_job* j = (bwd_job*)arg;
+  for (int64_t bh = j->slice_begin; bh < j->slice_end; ++bh) bwd_slice(j, bh);
+  return NULL;
+}
+
+/* Returns 0 on success, -1 on bad arguments.  dh_final, h0, prev_B/prev_x
+ * nullable; dh0 is written when non-NULL, dprev_B/dprev_x when prev_B is
+ * given and they are non-NULL. */
+int mamba3_oracle_backward(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t R,
+                           const double* x, const double* Bm, const double* Cm,
+                           const double* dt, const double* A, const double* lam, const double* theta,
+                           const double* h0, const double* prev_B, const double* prev_x,
+                           const double* dy, const double* dh_final,
+                           double* dx, double* dB, double* dC, double* ddt, double* dA, double* dlam,
+                           double* dtheta, double* dh0, double* dprev_B, double* dprev_x, int nthreads) {
+  if (B <= 0 || L < 0 || H <= 0 || P <= 0 || N <= 0 || R <= 0 || (N % 2) != 0) return -1;
+  if (L > 0 && (!x || !Bm || !Cm || !dt || !A || !lam || !theta || !dy || !dx || !dB || !dC || !ddt ||
+                !dA || !dlam || !dtheta))
+    return -1;
+  const int64_t slices = B * H;
+  const int nt = pick_threads(nthreads, slices);
+  bwd_job* jobs = (bwd_job*)calloc((size_t)nt, sizeof(bwd_job));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nt, sizeof(pthread_t));
+  for (int i = 0; i < nt; ++i) {
+    bwd_job* j = &jobs[i];
+    j->B = B; j->L = L; j->H = H; j->P = P; j->N = N; j->R = R;
+    j->x = x; j->Bm = Bm; j->Cm = Cm; j->dt = dt; j->A = A; j->lam = lam; j->theta = theta;
+    j->h0 = h0; j->prev_B = prev_B; j->prev_x = prev_x; j->dy = dy; j->dhf = dh_final;
+    j->dx = dx; j->dB = dB; j->dC = dC; j->ddt = ddt; j->dA = dA; j->dlam = dlam; j->dtheta = dtheta;
+    j->dh0 = dh0; j->dprev_B = dprev_B; j->dprev_x = dprev_x;
+    j->slice_begin = slices * i / nt;
+    j->slice_end = slices * (i + 1) / nt;
+  }
+  for (int i = 1; i < nt; ++i) pthread_create(&tids[i], NULL, bwd_worker, &jobs[i]);
+  bwd_worker(&jobs[0]);
   for (int i = 1; i < nt; ++i) pthread_join(tids[i], NULL);
   free(jobs); free(tids);
   return 0;

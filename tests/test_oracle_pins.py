@@ -356,6 +356,84 @@ def test_empty_sequence_returns_h0():
 
 
 # --------------------------------------------------------------------------
+# backward: the gradient of  sum <dy, y> + <dh_final, h_final>  against
+# central finite differences of the forward (an independent computation)
+# --------------------------------------------------------------------------
+
+GRAD_OF = {"x": "dx", "B": "dB", "C": "dC", "dt": "ddt", "A": "dA", "lam": "dlam", "theta": "dtheta",
+           "h0": "dh0", "prev_B": "dprev_B", "prev_x": "dprev_x"}
+
+
+def grad_case(seed, L, R, N, P, with_h0, with_prev, with_dhf, H=2):
+    inp = numpy_inputs(1, L, H, P, N, R, seed=seed, with_h0=with_h0, with_prev=with_prev)
+    inp = {k: np.asarray(v, dtype=np.float64) for k, v in inp.items()}
+    rng = np.random.default_rng(seed + 1)
+    dy = rng.normal(size=inp["x"].shape)
+    dhf = rng.normal(size=(1, H, N, P)) if with_dhf else None
+    return inp, dy, dhf
+
+
+def loss_of(inp, dy, dhf, mutant=0):
+    y, hf = oracle.forward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["lam"], inp["theta"],
+                           h0=inp.get("h0"), prev_B=inp.get("prev_B"), prev_x=inp.get("prev_x"), mutant=mutant)
+    return float((dy * y).sum() + (0.0 if dhf is None else (dhf * hf).sum()))
+
+
+def finite_difference_grads(inp, dy, dhf, eps=1e-6):
+    out = {}
+    for k, v in inp.items():
+        fd = np.zeros_like(v)
+        for idx in np.ndindex(v.shape):
+            hi, lo = dict(inp), dict(inp)
+            hi[k] = v.copy()
+            hi[k][idx] += eps
+            lo[k] = v.copy()
+            lo[k][idx] -= eps
+            fd[idx] = (loss_of(hi, dy, dhf) - loss_of(lo, dy, dhf)) / (2 * eps)
+        out[GRAD_OF[k]] = fd
+    return out
+
+
+def oracle_grads(inp, dy, dhf, mutant=0):
+    return oracle.backward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["lam"], inp["theta"], dy,
+                           h0=inp.get("h0"), prev_B=inp.get("prev_B"), prev_x=inp.get("prev_x"),
+                           dh_final=dhf, mutant=mutant)
+
+
+def grad_errors(g, fd):
+    return {k: float(np.max(np.abs(g[k] - fd[k])) / max(1e-12, np.max(np.abs(fd[k])))) for k in fd}
+
+
+@pytest.mark.parametrize("seed,L,R,N,P,with_h0,with_prev,with_dhf", [
+    (31, 7, 2, 4, 3, True, True, True),
+    (32, 9, 1, 2, 2, False, False, False),
+    (33, 5, 4, 6, 2, True, False, True),
+    (34, 11, 2, 2, 3, False, True, False),
+])
+def test_backward_matches_finite_differences(seed, L, R, N, P, with_h0, with_prev, with_dhf):
+    inp, dy, dhf = grad_case(seed, L, R, N, P, with_h0, with_prev, with_dhf)
+    errs = grad_errors(oracle_grads(inp, dy, dhf), finite_difference_grads(inp, dy, dhf))
+    assert max(errs.values()) < 1e-7, errs
+
+
+def test_backward_is_linear_in_the_cotangents():
+    inp, dy1, dhf1 = grad_case(35, 8, 2, 4, 2, True, True, True)
+    rng = np.random.default_rng(99)
+    dy2, dhf2 = rng.normal(size=dy1.shape), rng.normal(size=dhf1.shape)
+    g1, g2 = oracle_grads(inp, dy1, dhf1), oracle_grads(inp, dy2, dhf2)
+    g12 = oracle_grads(inp, dy1 + 2.0 * dy2, dhf1 + 2.0 * dhf2)
+    for k in g12:
+        assert np.allclose(g12[k], g1[k] + 2.0 * g2[k], rtol=1e-12, atol=1e-12), k
+
+
+@pytest.mark.parametrize("mutant", [10, 11])
+def test_backward_mutants_are_caught(mutant):
+    inp, dy, dhf = grad_case(36, 6, 2, 4, 2, True, True, True)
+    fd = finite_difference_grads(inp, dy, dhf)
+    assert max(grad_errors(oracle_grads(inp, dy, dhf, mutant=mutant), fd).values()) > 1e-3
+
+
+# --------------------------------------------------------------------------
 # planted mistakes (compiled oracle variants, CPU only)
 # --------------------------------------------------------------------------
 
