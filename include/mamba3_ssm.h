@@ -1,10 +1,11 @@
 /*
  * mamba3_ssm.h -- C ABI of the MI355X (gfx950) Mamba-3 SSM layer core.
  *
- * Three operations, all asynchronous on a caller-given HIP stream:
+ * Four operations, all asynchronous on a caller-given HIP stream:
  *
  *   mamba3_ssm_chunked_fwd   whole-sequence forward (prefill / training
  *                            forward) by the chunked parallel form;
+ *   mamba3_ssm_chunked_bwd   its backward (training);
  *   mamba3_ssm_decode_step   one-token state update (generation);
  *   mamba3_rope_bc           the cumulative-angle rotation of B and C.
  *
@@ -137,6 +138,36 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d,
                                  void* y, float* h_final,
                                  void* workspace, size_t workspace_bytes, void* stream);
 size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d);
+
+/* Backward of mamba3_ssm_chunked_fwd: the gradients of
+ *     l = sum_t <dy_t, y_t> + <dh_final, h_final>
+ * with respect to every input of the forward (the chain rule of the chunked
+ * form, chunks walked in reverse order; same pages as the forward).
+ *   dy: (B, L, H, R, P) io dtype.  dh_final: nullable (B, H, N, P) fp32; NULL
+ *       means zero.
+ *   dx (B, L, H, R, P), dB, dC (B, L, H, R, N): io dtype, written.
+ *   ddt, dA, dlam (B, L, H), dtheta (B, L, H, N/2): fp32, written.
+ *   dh0: nullable (B, H, N, P) fp32, written when given (also when h0 is NULL:
+ *        the gradient with respect to a zero initial state).
+ *   dprev_B (B, H, R, N), dprev_x (B, H, R, P): nullable pair, io dtype,
+ *        written when prev_B/prev_x are given.
+ * Supported: N and P in {16, 32, 64}, R in {1, 2, 4}, io fp32 or bf16; d->chunk
+ * must be a supported chunk length but the backward always walks 16-token
+ * chunks.  All products are fp32.  workspace: at least
+ * mamba3_ssm_chunked_bwd_workspace_size(d) bytes (the states at every chunk
+ * start); its contents on entry do not matter.  Outputs must not alias inputs.
+ * Alignment: x, B, C, dy, dx, dB, dC, theta, dtheta and the workspace 16-byte;
+ * the others their element size.  flags must be 0. */
+m3_status mamba3_ssm_chunked_bwd(const m3_dims* d,
+                                 const void* x, const void* B, const void* C,
+                                 const float* dt, const float* A, const float* lam, const float* theta,
+                                 const float* h0, const void* prev_B, const void* prev_x,
+                                 const void* dy, const float* dh_final,
+                                 void* dx, void* dB, void* dC,
+                                 float* ddt, float* dA, float* dlam, float* dtheta,
+                                 float* dh0, void* dprev_B, void* dprev_x,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+size_t mamba3_ssm_chunked_bwd_workspace_size(const m3_dims* d);
 
 /* One-token update, in place on the fp32 true-frame state:
  *   h <- alpha R(dt theta) [h + eps prev_B^T prev_x] + gamma B^T x,

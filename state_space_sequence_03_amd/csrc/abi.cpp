@@ -185,6 +185,62 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
   return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 
+size_t mamba3_ssm_chunked_bwd_workspace_size(const m3_dims* d) {
+  if (check_dims(d, true, true) != M3_OK) return 0;
+  if (d->batch == 0 || d->nheads == 0 || d->seqlen == 0) return 0;
+  const int64_t nch = (d->seqlen + m3::BWD_CHUNK - 1) / m3::BWD_CHUNK;
+  return sizeof(float) * (size_t)(d->batch * d->nheads) * (size_t)(nch + 1) * (size_t)(d->dstate * d->headdim);
+}
+
+m3_status mamba3_ssm_chunked_bwd(const m3_dims* d, const void* x, const void* B, const void* C,
+                                 const float* dt, const float* A, const float* lam, const float* theta,
+                                 const float* h0, const void* prev_B, const void* prev_x,
+                                 const void* dy, const float* dh_final,
+                                 void* dx, void* dB, void* dC,
+                                 float* ddt, float* dA, float* dlam, float* dtheta,
+                                 float* dh0, void* dprev_B, void* dprev_x,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  m3_status st = check_dims(d, true, true);
+  if (st != M3_OK) return st;
+  if (d->flags != 0) return M3_ERR_UNSUPPORTED;
+  if (!m3::bwd_supported((int)d->dstate, (int)d->headdim, (int)d->rank)) return M3_ERR_UNSUPPORTED;
+  const bool empty = d->batch == 0 || d->nheads == 0;
+  const bool has_tokens = !empty && d->seqlen > 0;
+  if ((prev_B == nullptr) != (prev_x == nullptr) || (dprev_B == nullptr) != (dprev_x == nullptr)) return M3_ERR_NULL;
+  if (has_tokens && (!x || !B || !C || !dt || !A || !lam || !theta || !dy || !dx || !dB || !dC || !ddt || !dA ||
+                     !dlam || !dtheta))
+    return M3_ERR_NULL;
+  const uintptr_t esz = d->io_dtype == M3_BF16 ? 2 : 4;
+  if (!all_aligned({x, B, C, dy, dx, dB, dC, workspace}, {prev_B, prev_x, dprev_B, dprev_x}, esz) ||
+      !all_aligned({theta, dtheta}, {dt, A, lam, h0, dh_final, ddt, dA, dlam, dh0}, 4))
+    return M3_ERR_ALIGN;
+  const size_t need = mamba3_ssm_chunked_bwd_workspace_size(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return M3_ERR_WORKSPACE;
+  if (empty) return M3_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t BH = d->batch * d->nheads;
+  if (d->seqlen == 0) {
+    // h_final = h0: dh0 = dh_final; the previous token has no successor
+    hipError_t e = hipSuccess;
+    if (dh0) e = m3::launch_copy_f32(dh0, dh_final, BH * d->dstate * d->headdim, s);
+    if (e == hipSuccess && prev_B && dprev_B) {
+      const int64_t nb = BH * d->rank * d->dstate * (int64_t)esz, nx = BH * d->rank * d->headdim * (int64_t)esz;
+      // zero fill with a kernel (byte sizes are multiples of 4: N and P are even)
+      e = m3::launch_copy_f32((float*)dprev_B, nullptr, nb / 4, s);
+      if (e == hipSuccess) e = m3::launch_copy_f32((float*)dprev_x, nullptr, nx / 4, s);
+    }
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+  }
+  m3::BwdArgs a{};
+  a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.lam = lam; a.theta = theta;
+  a.h0 = h0; a.prev_B = prev_B; a.prev_x = prev_x; a.dy = dy; a.dh_final = dh_final;
+  a.dx = dx; a.dB = dB; a.dC = dC; a.ddt = ddt; a.dA = dA; a.dlam = dlam; a.dtheta = dtheta;
+  a.dh0 = dh0; a.dprev_B = prev_B ? dprev_B : nullptr; a.dprev_x = prev_B ? dprev_x : nullptr;
+  a.ckpt = (float*)workspace;
+  a.batch = d->batch; a.L = d->seqlen; a.H = d->nheads; a.R = (int)d->rank;
+  return m3::launch_chunked_bwd(io_bf16(d), (int)d->dstate, (int)d->headdim, a, s) == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
 m3_status mamba3_ssm_decode_step(const m3_dims* d, float* state, const void* x, const void* B,
                                  const void* C, const float* dt, const float* A, const float* lam,
                                  const float* theta, const void* prev_B, const void* prev_x, void* y,

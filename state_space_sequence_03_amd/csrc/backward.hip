@@ -1,0 +1,699 @@
+// Backward of the chunked forward: the gradients of
+//     l = sum_t <dy_t, y_t> + <dh_final, h_final>
+// with respect to x, B, C, dt, A, lam, theta, h0 and the previous token's B
+// and x.  The forward is the chunked form of the exponential-trapezoidal
+// recurrence with data-dependent RoPE and rank-R inputs (linkstar.cloud/
+// article/869, "第一刀", "第二刀", "第三刀"; chunks computed in parallel
+// inside and passed on in order: yetianai.com/news/16273, "榨干硬件算力").
+// The backward of a chunk is the chain rule of that chunk's forward, run over
+// the chunks in reverse order.
+//
+// Per chunk of Q tokens (V = Q R virtual rows (token, rank)), chunk-local
+// cumulative log-decay Lam_t and angles phi_t, B~ = R(-phi) B, C~ = R(-phi) C,
+// q_s = gamma_s + eps_{s+1}, w_s = e^{Lam_end - Lam_s} q_s and
+// M[t,s] = e^{Lam_t - Lam_s} q_s (s < t), gamma_t (s = t), 0 (s > t):
+//     y_t   = sum_{s<=t} M[t,s] (C~_t . B~_s) x_s + e^{Lam_t} C~_t^T H_in
+//     H_out = R(Theta) (e^{Lam_end} H_in + sum_s w_s B~_s x_s^T)
+// With G = C~ B~^T, dGM = dY X^T (both V x V), dZ = R(-Theta) dH_out:
+//     dX   = (G o M)^T dY + (w B~) dZ
+//     dC~  = (dGM o M) B~ + e^{Lam} dY H_in^T
+//     dB~  = (dGM o M)^T C~ + w X dZ^T
+//     dH_in = e^{Lam_end} dZ + C~^T (e^{Lam} dY)
+// and the scalar adjoints follow from dM = dGM o G (summed over the rank
+// blocks), dw_s = B~_s . (X dZ^T)_s, d e^{Lam_t} = C~_t . (dY H_in^T)_t,
+// <dZ, H_in> and the rotation adjoints of B~, C~ and H_out.
+//
+// Two kernels, one block per (b,h) each:
+//  1. bwd_ckpt_kernel walks the chunks forward and stores the carried state
+//     H' at every chunk start (and the final one) in the workspace;
+//  2. bwd_chunk_kernel walks the chunks backward with dH' in registers.
+// Every product above is a fp32 MFMA (16x16x4) over fp32 tiles in LDS, so
+// the gradients carry fp32 rounding only; the chunk is 16 tokens, V <= 64,
+// and N, P <= 64.
+#include "m3_common.hpp"
+#include "m3_launch.hpp"
+
+namespace m3 {
+
+bool bwd_supported(int N, int P, int R) {
+  const bool np = (N == 16 || N == 32 || N == 64) && (P == 16 || P == 32 || P == 64);
+  return np && (R == 1 || R == 2 || R == 4);
+}
+
+namespace {
+
+constexpr int QB = BWD_CHUNK;
+
+// Shapes of one (N, P, R) instance
+template <int N, int P, int R>
+struct BS {
+  static constexpr int K = N / 2, V = QB * R;
+  static constexpr int LDN = N + 4, LDP = P + 4, LDV = V + 4;  // fp32 row strides in LDS
+  static constexpr int TN = N / 16, TP = P / 16, TV = V / 16;   // 16-wide tiles
+  static constexpr int NPT = TN * TP;                           // tiles of an N x P matrix
+  static constexpr int NPW = (NPT + 3) / 4;                     // ... per wave
+};
+
+// acc[j] += A(tr*16 + m16, k) B(k, tc*16 + m16) over k < KD for the wave's
+// tiles j of a TM x TN grid (tile ti = wave + 4 j, tr = ti / TNC, tc = ti % TNC)
+template <int TM, int TNC, int KD, typename FA, typename FB>
+__device__ __forceinline__ void mm(FA fa, FB fb, f32x4* acc, int wave, int m16, int g) {
+  constexpr int TPW = (TM * TNC + 3) / 4;
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int ti = wave + 4 * j;
+    if (ti < TM * TNC) {
+      const int tr = ti / TNC, tc = ti % TNC;
+#pragma unroll 4
+      for (int k0 = 0; k0 < KD; k0 += 4) acc[j] = mfma_f32(fa(tr * 16 + m16, k0 + g), fb(k0 + g, tc * 16 + m16), acc[j]);
+    }
+  }
+}
+
+// Per-token scalars of a chunk (tokens past L are padding with dt = 0, so
+// that they change no cumulative quantity and carry no weight).
+struct TokScal {
+  float d, A, lam, eps_next;
+};
+
+template <typename T>
+__device__ __forceinline__ float ld_io(const void* p, int64_t i) {
+  return io<T>::load1(p, i);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// 1. forward walk storing H' at every chunk start
+// ---------------------------------------------------------------------------
+template <typename T, int N, int P, int R>
+__global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
+  typedef BS<N, P, R> S;
+  constexpr int K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP;
+  const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
+  const int64_t L = a.L, nch = (L + QB - 1) / QB;
+  auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
+
+  __shared__ float sW[V * LDN], sX[V * LDP];
+  __shared__ float2 sCS[QB][K];
+  __shared__ float sLam[QB], sQ[QB], sDA[QB];
+  __shared__ TokScal sT[QB];
+
+  // H' in the MFMA accumulator layout: tile j holds rows 16 tr + 4g + i, column 16 tc + m16
+  f32x4 Hs[S::NPW];
+  const bool has_prev = a.prev_B != nullptr;
+  const float eps1 = (has_prev && L > 0) ? (1.0f - a.lam[tok_of(0)]) * a.dt[tok_of(0)] : 0.0f;
+#pragma unroll
+  for (int j = 0; j < S::NPW; ++j) {
+    const int ti = wave + 4 * j;
+    Hs[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (ti < S::NPT) {
+      const int tr = ti / S::TP, tc = ti % S::TP, p = tc * 16 + m16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = tr * 16 + 4 * g + i;
+        float v = a.h0 ? a.h0[bh * (int64_t)N * P + n * P + p] : 0.0f;
+        if (has_prev) {
+          float acc = 0.0f;
+          for (int r = 0; r < R; ++r)
+            acc += ld_io<T>(a.prev_B, (bh * R + r) * N + n) * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
+          v += eps1 * acc;
+        }
+        Hs[j][i] = v;
+      }
+    }
+  }
+  float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
+  auto store_state = [&](int64_t c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < S::NPW; ++j) {
+      const int ti = wave + 4 * j;
+      if (ti < S::NPT) {
+        const int tr = ti / S::TP, tc = ti % S::TP, p = tc * 16 + m16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ck[c * (N * P) + (tr * 16 + 4 * g + i) * P + p] = Hs[j][i];
+      }
+    }
+  };
+
+  for (int64_t c = 0; c < nch; ++c) {
+    const int64_t a0 = c * QB;
+    store_state(c);
+    if (tid < QB) {
+      const int64_t t = a0 + tid;
+      TokScal ts{0.0f, 0.0f, 0.0f, 0.0f};
+      if (t < L) {
+        ts.d = a.dt[tok_of(t)];
+        ts.A = a.A[tok_of(t)];
+        ts.lam = a.lam[tok_of(t)];
+        if (t + 1 < L) ts.eps_next = (1.0f - a.lam[tok_of(t + 1)]) * a.dt[tok_of(t + 1)];
+      }
+      sT[tid] = ts;
+      sDA[tid] = ts.d * ts.A;
+    }
+    __syncthreads();
+    if (tid < QB) {
+      float lam_c = 0.0f;
+      for (int j = 0; j <= tid; ++j) lam_c += sDA[j];
+      sLam[tid] = lam_c;
+      sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
+    }
+    for (int e = tid; e < QB * K; e += 256) {
+      const int t = e / K, k = e % K;
+      float ph = 0.0f;
+      for (int j = 0; j <= t; ++j)
+        if (a0 + j < L) ph += sT[j].d * a.theta[tok_of(a0 + j) * K + k];
+      float sn, cs;
+      sincosf(ph, &sn, &cs);
+      sCS[t][k] = make_float2(cs, sn);
+    }
+    __syncthreads();
+    const float lamQ = sLam[QB - 1];
+    // W = w B~ (rows v = t R + r), X
+    for (int e = tid; e < V * (N / 2); e += 256) {
+      const int v = e / K, k = e % K, t = v / R;
+      float b0 = 0.0f, b1 = 0.0f;
+      if (a0 + t < L) {
+        const int64_t base = (tok_of(a0 + t) * R + v % R) * N + 2 * k;
+        b0 = ld_io<T>(a.B, base);
+        b1 = ld_io<T>(a.B, base + 1);
+      }
+      const float2 cs = sCS[t][k];
+      const float w = __expf(lamQ - sLam[t]) * sQ[t];
+      sW[v * LDN + 2 * k] = w * (cs.x * b0 + cs.y * b1);
+      sW[v * LDN + 2 * k + 1] = w * (cs.x * b1 - cs.y * b0);
+    }
+    for (int e = tid; e < V * P; e += 256) {
+      const int v = e / P, p = e % P, t = v / R;
+      sX[v * LDP + p] = (a0 + t < L) ? ld_io<T>(a.x, (tok_of(a0 + t) * R + v % R) * P + p) : 0.0f;
+    }
+    __syncthreads();
+    // S = W^T X, then H' <- R(Theta) (e^{Lam_end} H' + S)
+    f32x4 sacc[S::NPW];
+#pragma unroll
+    for (int j = 0; j < S::NPW; ++j) sacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    mm<S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; }, [&](int v, int p) { return sX[v * LDP + p]; },
+                        sacc, wave, m16, g);
+    const float eQ = __expf(lamQ);
+#pragma unroll
+    for (int j = 0; j < S::NPW; ++j) {
+      const int ti = wave + 4 * j;
+      if (ti < S::NPT) {
+        const int tr = ti / S::TP;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int k = (tr * 16 + 4 * g) / 2 + q;
+          const float2 cs = sCS[QB - 1][k];
+          const float u = eQ * Hs[j][2 * q] + sacc[j][2 * q];
+          const float w = eQ * Hs[j][2 * q + 1] + sacc[j][2 * q + 1];
+          Hs[j][2 * q] = cs.x * u - cs.y * w;
+          Hs[j][2 * q + 1] = cs.y * u + cs.x * w;
+        }
+      }
+    }
+    __syncthreads();  // LDS reads of this chunk done before the next staging
+  }
+  store_state(nch);
+}
+
+// ---------------------------------------------------------------------------
+// 2. backward walk over the chunks in reverse order
+// ---------------------------------------------------------------------------
+template <typename T, int N, int P, int R>
+__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
+  typedef BS<N, P, R> S;
+  constexpr int K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP, LDV = S::LDV;
+  constexpr int TV = S::TV, TN = S::TN, TP = S::TP;
+  constexpr int VVW = (TV * TV + 3) / 4, VNW = (TV * TN + 3) / 4, VPW = (TV * TP + 3) / 4;
+  const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
+  const int64_t L = a.L, nch = (L + QB - 1) / QB;
+  auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
+
+  __shared__ float sX[V * LDP], sDY[V * LDP], sB[V * LDN], sC[V * LDN];
+  __shared__ float sH[N * LDP], sDZ[N * LDP], sGM[V * LDV], sDG[V * LDV];
+  __shared__ float2 sCS[QB][K];
+  __shared__ TokScal sT[QB];
+  __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
+  __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K];
+  __shared__ float sDLam[QB], sDq[QB], sDgam[QB], sDe[V], sDw[V], sDlq[QB], sRed[1];
+
+  const float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
+  // dH' (adjoint of the carried state) in the accumulator layout of an N x P matrix
+  f32x4 Gb[S::NPW];
+#pragma unroll
+  for (int j = 0; j < S::NPW; ++j) {
+    const int ti = wave + 4 * j;
+    Gb[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (ti < S::NPT && a.dh_final) {
+      const int tr = ti / TP, tc = ti % TP;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        Gb[j][i] = a.dh_final[bh * (int64_t)N * P + (tr * 16 + 4 * g + i) * P + tc * 16 + m16];
+    }
+  }
+  // the first token of the chunk processed last time: its dt and lam
+  // gradients wait for the trapezoid weight of the token before it
+  float pend_ddt = 0.0f, pend_dlam = 0.0f;
+
+  for (int64_t c = nch - 1; c >= 0; --c) {
+    const int64_t a0 = c * QB;
+    // ---------------- staging ----------------
+    if (tid < QB) {
+      const int64_t t = a0 + tid;
+      TokScal ts{0.0f, 0.0f, 0.0f, 0.0f};
+      if (t < L) {
+        ts.d = a.dt[tok_of(t)];
+        ts.A = a.A[tok_of(t)];
+        ts.lam = a.lam[tok_of(t)];
+        if (t + 1 < L) ts.eps_next = (1.0f - a.lam[tok_of(t + 1)]) * a.dt[tok_of(t + 1)];
+      }
+      sT[tid] = ts;
+      sDLam[tid] = 0.0f;
+      sDq[tid] = 0.0f;
+      sDgam[tid] = 0.0f;
+    }
+    for (int e = tid; e < V; e += 256) {
+      sDe[e] = 0.0f;
+      sDw[e] = 0.0f;
+    }
+    for (int e = tid; e < K; e += 256) sDTheta[e] = 0.0f;
+    if (tid == 0) sRed[0] = 0.0f;
+    for (int e = tid; e < N * P; e += 256) sH[(e / P) * LDP + e % P] = ck[c * (N * P) + e];
+    __syncthreads();
+    if (tid < QB) {
+      float lam_c = 0.0f;
+      for (int j = 0; j <= tid; ++j) lam_c += sT[j].d * sT[j].A;
+      sLam[tid] = lam_c;
+      sEL[tid] = __expf(lam_c);
+      sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
+    }
+    for (int e = tid; e < QB * K; e += 256) {
+      const int t = e / K, k = e % K;
+      float ph = 0.0f;
+      for (int j = 0; j <= t; ++j)
+        if (a0 + j < L) ph += sT[j].d * a.theta[tok_of(a0 + j) * K + k];
+      float sn, cs;
+      sincosf(ph, &sn, &cs);
+      sCS[t][k] = make_float2(cs, sn);
+    }
+    __syncthreads();
+    const float lamQ = sLam[QB - 1], eQ = sEL[QB - 1];
+    if (tid < QB) sW[tid] = __expf(lamQ - sLam[tid]) * sQ[tid];
+    for (int e = tid; e < V * K; e += 256) {
+      const int v = e / K, k = e % K, t = v / R;
+      float b0 = 0.0f, b1 = 0.0f, c0 = 0.0f, c1 = 0.0f;
+      if (a0 + t < L) {
+        const int64_t base = (tok_of(a0 + t) * R + v % R) * N + 2 * k;
+        b0 = ld_io<T>(a.B, base);
+        b1 = ld_io<T>(a.B, base + 1);
+        c0 = ld_io<T>(a.C, base);
+        c1 = ld_io<T>(a.C, base + 1);
+      }
+      const float2 cs = sCS[t][k];
+      sB[v * LDN + 2 * k] = cs.x * b0 + cs.y * b1;
+      sB[v * LDN + 2 * k + 1] = cs.x * b1 - cs.y * b0;
+      sC[v * LDN + 2 * k] = cs.x * c0 + cs.y * c1;
+      sC[v * LDN + 2 * k + 1] = cs.x * c1 - cs.y * c0;
+    }
+    for (int e = tid; e < V * P; e += 256) {
+      const int v = e / P, p = e % P, t = v / R;
+      const bool ok = a0 + t < L;
+      const int64_t off = (tok_of(ok ? a0 + t : 0) * R + v % R) * P + p;
+      sX[v * LDP + p] = ok ? ld_io<T>(a.x, off) : 0.0f;
+      sDY[v * LDP + p] = ok ? ld_io<T>(a.dy, off) : 0.0f;
+    }
+    // dZ = R(-Theta) dH_out; dTheta = <dH_out, J H_out> per pair; <dZ, H_in>
+    {
+      float part = 0.0f;
+#pragma unroll
+      for (int j = 0; j < S::NPW; ++j) {
+        const int ti = wave + 4 * j;
+        if (ti < S::NPT) {
+          const int tr = ti / TP, tc = ti % TP, p = tc * 16 + m16;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int n0 = tr * 16 + 4 * g + 2 * q, k = n0 / 2;
+            const float2 cs = sCS[QB - 1][k];
+            const float g0 = Gb[j][2 * q], g1 = Gb[j][2 * q + 1];
+            const float z0 = cs.x * g0 + cs.y * g1, z1 = cs.x * g1 - cs.y * g0;
+            sDZ[n0 * LDP + p] = z0;
+            sDZ[(n0 + 1) * LDP + p] = z1;
+            const float o0 = ck[(c + 1) * (N * P) + n0 * P + p], o1 = ck[(c + 1) * (N * P) + (n0 + 1) * P + p];
+            float dth = -g0 * o1 + g1 * o0;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) dth += __shfl_xor(dth, o, 64);
+            if (m16 == 0) atomicAdd(&sDTheta[k], dth);
+            part += z0 * sH[n0 * LDP + p] + z1 * sH[(n0 + 1) * LDP + p];
+            // dH_in starts as e^{Lam_end} dZ
+            Gb[j][2 * q] = eQ * z0;
+            Gb[j][2 * q + 1] = eQ * z1;
+          }
+        }
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
+      if (lane == 0) atomicAdd(&sRed[0], part);
+    }
+    __syncthreads();
+
+    // ---------------- G = C~ B~^T and dGM = dY X^T (V x V), masked ----------------
+    {
+      f32x4 gacc[VVW], dacc[VVW];
+#pragma unroll
+      for (int j = 0; j < VVW; ++j) gacc[j] = dacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      mm<TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
+                    gacc, wave, m16, g);
+      mm<TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
+                    dacc, wave, m16, g);
+#pragma unroll
+      for (int j = 0; j < VVW; ++j) {
+        const int ti = wave + 4 * j;
+        if (ti < TV * TV) {
+          const int tr = ti / TV, tc = ti % TV;
+          const int vc = tc * 16 + m16, s = vc / R;
+          float pr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int vr = tr * 16 + 4 * g + i, t = vr / R;
+            float m = 0.0f;
+            if (s < t) m = __expf(fminf(sLam[t] - sLam[s], 0.0f)) * sQ[s];
+            else if (s == t) m = sT[t].lam * sT[t].d;
+            sGM[vr * LDV + vc] = gacc[j][i] * m;
+            sDG[vr * LDV + vc] = dacc[j][i] * m;
+            pr[i] = gacc[j][i] * dacc[j][i];
+          }
+          // dM[t][s]: sum over the R x R rank block (rows R-groups of i, columns R lanes)
+#pragma unroll
+          for (int i0 = 0; i0 < 4; i0 += R) {
+            float v = 0.0f;
+#pragma unroll
+            for (int i = 0; i < R; ++i) v += pr[i0 + i];
+#pragma unroll
+            for (int o = 1; o < R; o <<= 1) v += __shfl_xor(v, o, 64);
+            if (m16 % R == 0) sDM[(tr * 16 + 4 * g + i0) / R][s] = v;
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---------------- products on the masked matrices ----------------
+    {
+      // dX = GM^T dY + (w B~) dZ
+      f32x4 xacc[VPW];
+#pragma unroll
+      for (int j = 0; j < VPW; ++j) xacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      mm<TV, TP, V>([&](int vr, int vk) { return sGM[vk * LDV + vr]; }, [&](int vk, int p) { return sDY[vk * LDP + p]; },
+                    xacc, wave, m16, g);
+      mm<TV, TP, N>([&](int v, int n) { return sW[v / R] * sB[v * LDN + n]; }, [&](int n, int p) { return sDZ[n * LDP + p]; },
+                    xacc, wave, m16, g);
+#pragma unroll
+      for (int j = 0; j < VPW; ++j) {
+        const int ti = wave + 4 * j;
+        if (ti < TV * TP) {
+          const int tr = ti / TP, tc = ti % TP, p = tc * 16 + m16;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = tr * 16 + 4 * g + i, t = v / R;
+            if (a0 + t < L) io<T>::store1(a.dx, (tok_of(a0 + t) * R + v % R) * P + p, xacc[j][i]);
+          }
+        }
+      }
+    }
+    {
+      // dC~ = DGM B~ + e^{Lam} E, E = dY H_in^T;  dB~ = DGM^T C~ + w F, F = X dZ^T
+      f32x4 cacc[VNW], eacc[VNW], bacc[VNW], facc[VNW];
+#pragma unroll
+      for (int j = 0; j < VNW; ++j) cacc[j] = eacc[j] = bacc[j] = facc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      mm<TV, TN, V>([&](int vr, int vk) { return sDG[vr * LDV + vk]; }, [&](int vk, int n) { return sB[vk * LDN + n]; },
+                    cacc, wave, m16, g);
+      mm<TV, TN, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int n) { return sH[n * LDP + p]; },
+                    eacc, wave, m16, g);
+      mm<TV, TN, V>([&](int vr, int vk) { return sDG[vk * LDV + vr]; }, [&](int vk, int n) { return sC[vk * LDN + n]; },
+                    bacc, wave, m16, g);
+      mm<TV, TN, P>([&](int v, int p) { return sX[v * LDP + p]; }, [&](int p, int n) { return sDZ[n * LDP + p]; },
+                    facc, wave, m16, g);
+#pragma unroll
+      for (int j = 0; j < VNW; ++j) {
+        const int ti = wave + 4 * j;
+        if (ti < TV * TN) {
+          const int tr = ti / TN, tc = ti % TN, n = tc * 16 + m16, k = n / 2;
+          float dCt[4], dBt[4], de[4], dw[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = tr * 16 + 4 * g + i, t = v / R;
+            dCt[i] = cacc[j][i] + sEL[t] * eacc[j][i];
+            dBt[i] = bacc[j][i] + sW[t] * facc[j][i];
+            de[i] = sC[v * LDN + n] * eacc[j][i];
+            dw[i] = sB[v * LDN + n] * facc[j][i];
+          }
+          // row sums over n (16 lanes of the tile) for d e^{Lam} and dw
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+              de[i] += __shfl_xor(de[i], o, 64);
+              dw[i] += __shfl_xor(dw[i], o, 64);
+            }
+          }
+          if (m16 == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              atomicAdd(&sDe[tr * 16 + 4 * g + i], de[i]);
+              atomicAdd(&sDw[tr * 16 + 4 * g + i], dw[i]);
+            }
+          }
+          // angle adjoint of the pair (n even: this lane and the next) and the
+          // un-rotated gradients dB = R(phi) dB~, dC = R(phi) dC~
+          const bool even = (m16 & 1) == 0;
+          float dph[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int v = tr * 16 + 4 * g + i, t = v / R;
+            const float dCo = __shfl_xor(dCt[i], 1, 64), dBo = __shfl_xor(dBt[i], 1, 64);
+            const float bS = sB[v * LDN + n], bO = sB[v * LDN + (n ^ 1)];
+            const float cS = sC[v * LDN + n], cO = sC[v * LDN + (n ^ 1)];
+            // pair (u, w) = (even, odd) columns: dphi += du w - dw u
+            dph[i] = even ? (dBt[i] * bO - dBo * bS + dCt[i] * cO - dCo * cS) : 0.0f;
+            const float2 cs = sCS[t][k];
+            // R(phi) (du, dw) = (c du - s dw, s du + c dw)
+            const float gB = even ? (cs.x * dBt[i] - cs.y * dBo) : (cs.y * dBo + cs.x * dBt[i]);
+            const float gC = even ? (cs.x * dCt[i] - cs.y * dCo) : (cs.y * dCo + cs.x * dCt[i]);
+            if (a0 + t < L) {
+              const int64_t off = (tok_of(a0 + t) * R + v % R) * N + n;
+              io<T>::store1(a.dB, off, gB);
+              io<T>::store1(a.dC, off, gC);
+            }
+          }
+          // sum the ranks of each token (groups of R rows) into the token's angle adjoint
+#pragma unroll
+          for (int i0 = 0; i0 < 4; i0 += R) {
+            float v = 0.0f;
+#pragma unroll
+            for (int i = 0; i < R; ++i) v += dph[i0 + i];
+            if (even) sDphi[(tr * 16 + 4 * g + i0) / R][k] = v;
+          }
+        }
+      }
+    }
+    {
+      // dH_in += C~^T (e^{Lam} dY)
+      mm<TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; }, [&](int v, int p) { return sEL[v / R] * sDY[v * LDP + p]; },
+                    Gb, wave, m16, g);
+    }
+    __syncthreads();
+
+    // ---------------- scalar adjoints of the chunk ----------------
+    {
+      // the masked decay: dM on s < t and the diagonal
+      const int t = tid / QB, s = tid % QB;
+      const float dm = sDM[t][s];
+      if (s < t) {
+        const float e = __expf(fminf(sLam[t] - sLam[s], 0.0f));
+        const float dmm = dm * e * sQ[s];
+        atomicAdd(&sDLam[t], dmm);
+        atomicAdd(&sDLam[s], -dmm);
+        atomicAdd(&sDq[s], dm * e);
+      } else if (s == t) {
+        atomicAdd(&sDgam[t], dm);
+      }
+    }
+    __syncthreads();
+    if (tid < QB) {
+      const int t = tid;
+      float dwt = 0.0f, det = 0.0f;
+      for (int r = 0; r < R; ++r) {
+        dwt += sDw[t * R + r];
+        det += sDe[t * R + r];
+      }
+      // w_t = e^{Lam_end - Lam_t} q_t; e^{Lam_t} of the inter-chunk output
+      sDLam[t] += det * sEL[t] - dwt * sW[t];
+      sDq[t] += dwt * __expf(lamQ - sLam[t]);
+      sDlq[t] = dwt * sW[t];  // this token's share of d Lam_end
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float dlq = eQ * sRed[0];  // e^{Lam_end} <dZ, H_in>
+      for (int t = 0; t < QB; ++t) dlq += sDlq[t];
+      sDLam[QB - 1] += dlq;
+    }
+    __syncthreads();
+    if (tid < QB) {
+      const int t = tid;
+      const TokScal ts = sT[t];
+      // d(dt A)_t = sum_{i >= t} dLam_i
+      float dda = 0.0f;
+      for (int i = t; i < QB; ++i) dda += sDLam[i];
+      const float dgam = sDgam[t] + sDq[t];  // q_t = gamma_t + eps_{t+1}
+      const float deps = t > 0 ? sDq[t - 1] : 0.0f;  // eps_t weighs the previous token
+      float ddt = ts.A * dda + ts.lam * dgam + (1.0f - ts.lam) * deps;
+      float dlam = ts.d * dgam - ts.d * deps;
+      // angles: d omega_t = sum_{i >= t} dphi_i + dTheta
+      float dth_dot = 0.0f;
+      const int64_t tk = a0 + t < L ? tok_of(a0 + t) : 0;
+      for (int k = 0; k < K; ++k) {
+        float dom = sDTheta[k];
+        for (int i = t; i < QB; ++i) dom += sDphi[i][k];
+        if (a0 + t < L) {
+          a.dtheta[tk * K + k] = ts.d * dom;
+          dth_dot += a.theta[tk * K + k] * dom;
+        }
+      }
+      ddt += dth_dot;
+      if (a0 + t < L) {
+        a.dA[tk] = ts.d * dda;
+        if (t > 0) {
+          a.ddt[tk] = ddt;
+          a.dlam[tk] = dlam;
+        }
+      }
+      if (t == 0) {
+        // finish the first token of the chunk processed before (it follows
+        // this chunk's last token, whose q carries its eps), then hold this one
+        if (c + 1 < nch) {
+          const float de_next = sDq[QB - 1];
+          const int64_t tn = tok_of(a0 + QB);
+          const float dn = a.dt[tn], ln = a.lam[tn];
+          a.ddt[tn] = pend_ddt + (1.0f - ln) * de_next;
+          a.dlam[tn] = pend_dlam - dn * de_next;
+        }
+        pend_ddt = ddt;
+        pend_dlam = dlam;
+      }
+    }
+    __syncthreads();  // LDS reads of this chunk done before the next staging
+  }
+
+  // ---------------- the state before the first token ----------------
+  // H'_0 = h0 + eps_1 prev_B^T prev_x
+  const bool has_prev = a.prev_B != nullptr;
+  if (a.dh0) {
+#pragma unroll
+    for (int j = 0; j < S::NPW; ++j) {
+      const int ti = wave + 4 * j;
+      if (ti < S::NPT) {
+        const int tr = ti / TP, tc = ti % TP;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.dh0[bh * (int64_t)N * P + (tr * 16 + 4 * g + i) * P + tc * 16 + m16] = Gb[j][i];
+      }
+    }
+  }
+  // dH'_0 to LDS for the prev products
+#pragma unroll
+  for (int j = 0; j < S::NPW; ++j) {
+    const int ti = wave + 4 * j;
+    if (ti < S::NPT) {
+      const int tr = ti / TP, tc = ti % TP;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sDZ[(tr * 16 + 4 * g + i) * LDP + tc * 16 + m16] = Gb[j][i];
+    }
+  }
+  if (tid == 0) sRed[0] = 0.0f;
+  __syncthreads();
+  if (L > 0) {
+    const float d1 = a.dt[tok_of(0)], l1 = a.lam[tok_of(0)];
+    const float eps1 = has_prev ? (1.0f - l1) * d1 : 0.0f;
+    if (has_prev) {
+      // d eps_1 = <dH'_0, prev_B^T prev_x>; dprev_B = eps_1 dH'_0 prev_x; dprev_x = eps_1 dH'_0^T prev_B
+      float part = 0.0f;
+      for (int e = tid; e < N * P; e += 256) {
+        const int n = e / P, p = e % P;
+        float q0 = 0.0f;
+        for (int r = 0; r < R; ++r)
+          q0 += ld_io<T>(a.prev_B, (bh * R + r) * N + n) * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
+        part += sDZ[n * LDP + p] * q0;
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
+      if (lane == 0) atomicAdd(&sRed[0], part);
+      if (a.dprev_B) {
+        for (int e = tid; e < R * N; e += 256) {
+          const int r = e / N, n = e % N;
+          float acc = 0.0f;
+          for (int p = 0; p < P; ++p) acc += sDZ[n * LDP + p] * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
+          io<T>::store1(a.dprev_B, (bh * R + r) * N + n, eps1 * acc);
+        }
+        for (int e = tid; e < R * P; e += 256) {
+          const int r = e / P, p = e % P;
+          float acc = 0.0f;
+          for (int n = 0; n < N; ++n) acc += sDZ[n * LDP + p] * ld_io<T>(a.prev_B, (bh * R + r) * N + n);
+          io<T>::store1(a.dprev_x, (bh * R + r) * P + p, eps1 * acc);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const float de1 = sRed[0];
+      a.ddt[tok_of(0)] = pend_ddt + (1.0f - l1) * de1;
+      a.dlam[tok_of(0)] = pend_dlam - d1 * de1;
+    }
+  }
+}
+
+template <typename T, int N, int P, int R>
+static hipError_t bwd_run(const BwdArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.batch * a.H)), block(256);
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, N, P, R>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((bwd_chunk_kernel<T, N, P, R>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename T, int N, int P>
+static hipError_t bwd_r(const BwdArgs& a, hipStream_t s) {
+  switch (a.R) {
+    case 1: return bwd_run<T, N, P, 1>(a, s);
+    case 2: return bwd_run<T, N, P, 2>(a, s);
+    case 4: return bwd_run<T, N, P, 4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T, int N>
+static hipError_t bwd_p(int P, const BwdArgs& a, hipStream_t s) {
+  switch (P) {
+    case 16: return bwd_r<T, N, 16>(a, s);
+    case 32: return bwd_r<T, N, 32>(a, s);
+    case 64: return bwd_r<T, N, 64>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename T>
+static hipError_t bwd_n(int N, int P, const BwdArgs& a, hipStream_t s) {
+  switch (N) {
+    case 16: return bwd_p<T, 16>(P, a, s);
+    case 32: return bwd_p<T, 32>(P, a, s);
+    case 64: return bwd_p<T, 64>(P, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_chunked_bwd(int io_bf16, int N, int P, const BwdArgs& a, hipStream_t s) {
+  if (a.batch * a.H == 0 || a.L == 0) return hipSuccess;
+  if (!bwd_supported(N, P, a.R)) return hipErrorInvalidValue;
+  return io_bf16 ? bwd_n<bf16_t>(N, P, a, s) : bwd_n<float>(N, P, a, s);
+}
+
+}  // namespace m3

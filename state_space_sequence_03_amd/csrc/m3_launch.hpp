@@ -76,6 +76,26 @@ hipError_t launch_subwalk(int N, const WalkArgs& a, hipStream_t s);
 // applies, the general walker otherwise.
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
 
+// Backward of the chunked forward: gradients of <dy, y> + <dh_final, h_final>.
+struct BwdArgs {
+  const void *x, *B, *C;
+  const float *dt, *A, *lam, *theta;
+  const float* h0;              // nullable
+  const void *prev_B, *prev_x;  // nullable pair
+  const void* dy;               // (B, L, H, R, P) io dtype
+  const float* dh_final;        // nullable (B, H, N, P)
+  void *dx, *dB, *dC;           // io dtype
+  float *ddt, *dA, *dlam, *dtheta;
+  float* dh0;                   // nullable
+  void *dprev_B, *dprev_x;      // nullable pair (written when prev is given)
+  float* ckpt;                  // workspace: (B*H, nchunks + 1, N, P) fp32 states at chunk starts
+  int64_t batch, L, H;
+  int R;
+};
+constexpr int BWD_CHUNK = 16;  // tokens per chunk of the backward walk
+bool bwd_supported(int N, int P, int R);
+hipError_t launch_chunked_bwd(int io_bf16, int N, int P, const BwdArgs& a, hipStream_t s);
+
 // After a walk with S > 1 segments: segment scan (true incoming states and
 // h_final) and the output fix-up of segments 1..S-1 (bf16 io).
 hipError_t launch_segment_fixups(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);

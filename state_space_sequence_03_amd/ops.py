@@ -21,7 +21,8 @@ M3_OK, M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_UNSUPPORTED, M3_ERR_ALIGN, M3_ERR_WORKS
 M3_F32, M3_BF16 = 0, 1
 M3_FLAG_CHUNK_WALK = 0x10000   # chunked_fwd: walk chunks even for short sequences
 M3_TOKEN_PATH_MAX_L = 16      # chunked_fwd runs token by token up to this many tokens
-ABI_SYMBOLS = ("mamba3_ssm_chunked_fwd", "mamba3_ssm_chunked_fwd_workspace_size", "mamba3_ssm_decode_step",
+ABI_SYMBOLS = ("mamba3_ssm_chunked_fwd", "mamba3_ssm_chunked_fwd_workspace_size", "mamba3_ssm_chunked_bwd",
+               "mamba3_ssm_chunked_bwd_workspace_size", "mamba3_ssm_decode_step",
                "mamba3_rope_bc", "mamba3_rope_bc_workspace_size", "mamba3_status_string", "mamba3_abi_version")
 
 
@@ -54,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.mamba3_ssm_chunked_fwd.restype = ctypes.c_int
         L.mamba3_ssm_chunked_fwd_workspace_size.argtypes = [dp]
         L.mamba3_ssm_chunked_fwd_workspace_size.restype = sz
+        L.mamba3_ssm_chunked_bwd.argtypes = [dp] + [vp] * 22 + [vp, sz, vp]
+        L.mamba3_ssm_chunked_bwd.restype = ctypes.c_int
+        L.mamba3_ssm_chunked_bwd_workspace_size.argtypes = [dp]
+        L.mamba3_ssm_chunked_bwd_workspace_size.restype = sz
         L.mamba3_ssm_decode_step.argtypes = [dp] + [vp] * 11 + [vp]
         L.mamba3_ssm_decode_step.restype = ctypes.c_int
         L.mamba3_rope_bc.argtypes = [dp] + [vp] * 8 + [vp, sz, vp]
@@ -145,6 +150,41 @@ def mamba3_ssm_chunked_fwd(x, B, C, dt, A, lam, theta, h0=None, prev_B=None, pre
     return y, h_final
 
 
+def chunked_bwd_workspace_size(dims: Dims) -> int:
+    return int(lib().mamba3_ssm_chunked_bwd_workspace_size(ctypes.byref(dims)))
+
+
+def mamba3_ssm_chunked_bwd(x, B, C, dt, A, lam, theta, dy, h0=None, prev_B=None, prev_x=None, dh_final=None, *,
+                           chunk=64, want_dh0=True, workspace=None, stream=None):
+    """Backward of the chunked forward.  Returns a dict with dx, dB, dC (io dtype),
+    ddt, dA, dlam, dtheta (fp32), dh0 (fp32, if wanted) and, when prev is given,
+    dprev_B and dprev_x (io dtype)."""
+    torch = _torch()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x))
+    out = {"dx": torch.empty_like(x), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
+           "ddt": torch.empty_like(dt), "dA": torch.empty_like(A), "dlam": torch.empty_like(lam),
+           "dtheta": torch.empty_like(theta)}
+    if want_dh0:
+        out["dh0"] = torch.empty((b, H, N, P), device=x.device, dtype=torch.float32)
+    if prev_B is not None:
+        out["dprev_B"] = torch.empty_like(prev_B)
+        out["dprev_x"] = torch.empty_like(prev_x)
+    ws_bytes = chunked_bwd_workspace_size(dims)
+    if ws_bytes > 0 and workspace is None:
+        workspace = torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
+    st = lib().mamba3_ssm_chunked_bwd(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A), _ptr(lam),
+                                      _ptr(theta), _ptr(h0), _ptr(prev_B), _ptr(prev_x), _ptr(dy), _ptr(dh_final),
+                                      _ptr(out["dx"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["ddt"]),
+                                      _ptr(out["dA"]), _ptr(out["dlam"]), _ptr(out["dtheta"]), _ptr(out.get("dh0")),
+                                      _ptr(out.get("dprev_B")), _ptr(out.get("dprev_x")), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+                                      _stream(stream))
+    _check(st, "mamba3_ssm_chunked_bwd")
+    return out
+
+
 def mamba3_ssm_decode_step(state, x, B, C, dt, A, lam, theta, prev_B=None, prev_x=None, *, y=None, stream=None):
     """One token, state updated in place.  Shapes: state (b,H,N,P) fp32, x (b,H,R,P),
     B/C (b,H,R,N), dt/A/lam (b,H), theta (b,H,N/2).  Returns y (b,H,R,P)."""
@@ -185,5 +225,6 @@ def mamba3_rope_bc(B, C, dt, theta, angle0=None, *, B_rot=None, C_rot=None, angl
 
 
 chunked_fwd = mamba3_ssm_chunked_fwd
+chunked_bwd = mamba3_ssm_chunked_bwd
 decode_step = mamba3_ssm_decode_step
 rope_bc = mamba3_rope_bc

@@ -1,0 +1,128 @@
+"""Parity of the HIP backward (mamba3_ssm_chunked_bwd) with the fp64 oracle
+backward, itself pinned against finite differences of the oracle forward
+(tests/test_oracle_pins.py).  Needs an MI355X.
+
+Metric as for the forward: for each (b, h) slice, max|gpu - ref| / max|ref|,
+maximised over slices; bounds 1e-4 for fp32 io and 2e-2 for bf16 io (the
+gradients of x, B, C are rounded to bf16 there).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from state_space_sequence_03_amd.inputs import numpy_inputs, round_bf16_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+BH_AXES = {"dx": (0, 2), "dB": (0, 2), "dC": (0, 2), "ddt": (0, 2), "dA": (0, 2), "dlam": (0, 2),
+           "dtheta": (0, 2), "dh0": (0, 1), "dprev_B": (0, 1), "dprev_x": (0, 1)}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from state_space_sequence_03_amd import ops as o
+    o.lib()
+    return o
+
+
+def slice_err(gpu, ref, bh_axes):
+    g = np.moveaxis(gpu, bh_axes, (0, 1))
+    r = np.moveaxis(ref, bh_axes, (0, 1))
+    worst = 0.0
+    for i in range(g.shape[0]):
+        for j in range(g.shape[1]):
+            den = np.max(np.abs(r[i, j]))
+            den = den if den > 0 else 1.0
+            worst = max(worst, float(np.max(np.abs(g[i, j] - r[i, j])) / den))
+    return worst
+
+
+def dev(a, io, key):
+    t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    if key in ("x", "B", "C", "prev_B", "prev_x", "dy") and io == "bf16":
+        return t.to(torch.bfloat16)
+    return t.float()
+
+
+def run_case(ops, b, L, H, P, N, R, io, h0, prev, dhf, seed):
+    inp = numpy_inputs(b, L, H, P, N, R, io=io, seed=seed, with_h0=h0, with_prev=prev)
+    rng = np.random.default_rng(seed + 7)
+    dy = rng.standard_normal((b, L, H, R, P)).astype(np.float32)
+    if io == "bf16":
+        dy = round_bf16_np(dy)
+    dh = rng.standard_normal((b, H, N, P)).astype(np.float32) if dhf else None
+    d = {k: dev(v, io, k) for k, v in inp.items()}
+    g = ops.chunked_bwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], dev(dy, io, "dy"),
+                        h0=d.get("h0"), prev_B=d.get("prev_B"), prev_x=d.get("prev_x"),
+                        dh_final=None if dh is None else dev(dh, io, "dh"))
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["lam"], inp["theta"], dy,
+                          h0=inp.get("h0"), prev_B=inp.get("prev_B"), prev_x=inp.get("prev_x"), dh_final=dh)
+    errs = {}
+    for k, v in g.items():
+        errs[k] = slice_err(v.float().cpu().numpy().astype(np.float64), ref[k], BH_AXES[k])
+    say("   " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()))
+    return errs
+
+
+BWD_CASES = [
+    # io,    b, L,   H, P,  N,  R, h0,    prev,  dh_final
+    ("f32", 1, 64, 2, 16, 16, 1, False, False, False),
+    ("f32", 2, 37, 2, 32, 32, 2, True, True, True),
+    ("f32", 1, 100, 3, 64, 64, 4, True, True, True),
+    ("f32", 1, 16, 1, 64, 16, 4, False, True, False),
+    ("f32", 2, 5, 2, 16, 64, 2, True, False, True),
+    ("f32", 1, 1, 2, 32, 64, 1, True, True, True),
+    ("bf16", 2, 75, 2, 64, 64, 4, True, True, True),
+    ("bf16", 1, 130, 2, 64, 64, 1, False, False, True),
+    ("bf16", 1, 33, 3, 32, 64, 2, True, True, False),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_matches_oracle(ops, case):
+    io, b, L, H, P, N, R, h0, prev, dhf = case
+    say(f"chunked_bwd {case}")
+    errs = run_case(ops, b, L, H, P, N, R, io, h0, prev, dhf, zlib.crc32(repr(case).encode()) % 10000)
+    assert max(errs.values()) < TOL[io], errs
+
+
+def test_backward_slow_decay(ops):
+    """A in [-1e-2, 0]: gradients reach back across many chunks."""
+    say("chunked_bwd slow decay")
+    b, L, H, P, N, R = 1, 300, 2, 32, 32, 2
+    inp = numpy_inputs(b, L, H, P, N, R, io="f32", seed=5, with_h0=True, with_prev=True, a_range=(-30.0, np.log(1e-2)))
+    rng = np.random.default_rng(6)
+    dy = rng.standard_normal((b, L, H, R, P)).astype(np.float32)
+    dh = rng.standard_normal((b, H, N, P)).astype(np.float32)
+    d = {k: dev(v, "f32", k) for k, v in inp.items()}
+    g = ops.chunked_bwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], dev(dy, "f32", "dy"),
+                        h0=d["h0"], prev_B=d["prev_B"], prev_x=d["prev_x"], dh_final=dev(dh, "f32", "dh"))
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["lam"], inp["theta"], dy,
+                          h0=inp["h0"], prev_B=inp["prev_B"], prev_x=inp["prev_x"], dh_final=dh)
+    errs = {k: slice_err(v.float().cpu().numpy().astype(np.float64), ref[k], BH_AXES[k]) for k, v in g.items()}
+    say("   " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()))
+    assert max(errs.values()) < 1e-3, errs
+
+
+def test_backward_workspace_and_rejections(ops):
+    d = ops.make_dims(2, 100, 3, 64, 64, 4, 64, ops.M3_BF16)
+    assert ops.chunked_bwd_workspace_size(d) == 4 * 6 * (7 + 1) * 64 * 64
+    x = torch.zeros((1, 8, 1, 1, 128), device="cuda")
+    B = torch.zeros((1, 8, 1, 1, 16), device="cuda")
+    s = torch.zeros((1, 8, 1), device="cuda")
+    th = torch.zeros((1, 8, 1, 8), device="cuda")
+    with pytest.raises(ops.Mamba3Error) as e:
+        ops.chunked_bwd(x, B, B, s, s, s, th, x)   # P = 128 is not covered by the backward
+    assert e.value.status == ops.M3_ERR_UNSUPPORTED
