@@ -213,6 +213,53 @@ def bench_verify(ops, inputs, w, k, steps, warmup, torch):
                 gbps=b / (ms * 1e-3) / 1e9, chunk_walk_ms=res["chunk_walk"])
 
 
+BWD_CHUNK = 16
+FP32_MFMA_TFLOPS = 157.3
+
+
+def backward_flops_per_token_head(w):
+    """Dense fp32 MFMA flops of the backward per token-head: per 16-token
+    chunk (V = 16 R rows) the checkpoint walk's state product W^T X and the
+    reverse walk's nine products (G, dGM, two for dX, two for dC~, two for dB~
+    and dH_in), each 2 M N K."""
+    V, N, P = BWD_CHUNK * w.rank, w.dstate, w.headdim
+    per_chunk = 2 * (N * P * V) + 2 * (V * V * N + V * V * P + V * P * V + V * P * N + V * N * V + V * N * P
+                                       + V * N * V + V * N * P + N * P * V)
+    return per_chunk / BWD_CHUNK
+
+
+def backward_bytes_per_token_head(w, s_io=2):
+    """Algorithmic HBM bytes: x, B, C, dy, dt, A, lam, theta read; dx, dB,
+    dC, ddt, dA, dlam, dtheta written; the chunk-start states written once
+    and read once."""
+    R, N, P = w.rank, w.dstate, w.headdim
+    io_in = s_io * R * (2 * P + 2 * N) + 12 + 2 * N
+    io_out = s_io * R * (P + 2 * N) + 12 + 2 * N
+    states = 2 * N * P * 4 / BWD_CHUNK
+    return io_in + io_out + states
+
+
+def bench_backward(ops, inputs, w, steps, warmup, torch):
+    """mamba3_ssm_chunked_bwd on the prefill workload with dy ~ N(0, 1)."""
+    d = inputs.torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
+                            seed=inputs.seed_of(w.name) + 1)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(inputs.seed_of(w.name) + 2)
+    dy = torch.randn(d["x"].shape, generator=g, device="cuda", dtype=torch.float32).to(d["x"].dtype)
+    dims = ops.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk, ops._io_code(d["x"]))
+    ws = torch.empty(ops.chunked_bwd_workspace_size(dims), device="cuda", dtype=torch.uint8)
+    fn = lambda: ops.chunked_bwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], dy, chunk=w.chunk,
+                                 want_dh0=False, workspace=ws)
+    wall, ev = timed(fn, steps, warmup, torch)
+    th = w.batch * w.seqlen * w.nheads
+    flops = th * backward_flops_per_token_head(w)
+    bytes_ = th * backward_bytes_per_token_head(w)
+    del d, dy, ws
+    torch.cuda.empty_cache()
+    return dict(ms=ev, tokens_per_s=w.tokens / (ev * 1e-3), tflops=flops / (ev * 1e-3) / 1e12, flops=flops,
+                gbps=bytes_ / (ev * 1e-3) / 1e9, bytes=bytes_)
+
+
 def bench_rope(ops, inputs, w, steps, warmup, torch):
     d = inputs.torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
                             seed=inputs.seed_of(w.name))
@@ -305,7 +352,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify", "rope", "copy", "all"], default="all")
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "rope", "copy", "all"], default="all")
     ap.add_argument("--verify-k", type=int, default=8, help="tokens per call of the verify workload")
     ap.add_argument("--workload", default="mimo_bf16", choices=["mimo_bf16", "siso_bf16", "long_mimo_bf16"],
                     help="prefill workload timed by --only prefill (profiling); the headline line uses mimo_bf16")
@@ -336,6 +383,9 @@ def main():
         wd = W["decode_mimo_bf16"]
         print(f"[bench] verify: {args.verify_k} tokens per call on {wd.name} shapes", file=sys.stderr, flush=True)
         out["verify"] = bench_verify(ops, inputs, wd, args.verify_k, args.steps, args.warmup, torch)
+    if args.only in ("backward", "all"):
+        print(f"[bench] backward on {w.name}", file=sys.stderr, flush=True)
+        out["backward"] = bench_backward(ops, inputs, w, max(3, args.steps // 4), 2, torch)
     if args.only in ("rope", "all"):
         print(f"[bench] rope_bc on {w.name} shapes", file=sys.stderr, flush=True)
         out["rope"] = bench_rope(ops, inputs, w, max(3, args.steps // 4), 2, torch)
@@ -381,6 +431,14 @@ def main():
                           "achieved_GBps": round(vf["gbps"], 1), "frac": round(vf["gbps"] / HBM_PEAK_GBPS, 4),
                           "bytes_per_call": vf["bytes_per_call"],
                           "chunk_walk_ms_per_call": round(vf["chunk_walk_ms"], 5)}
+    if "backward" in out:
+        bw = out["backward"]
+        line["backward"] = {"workload": f"{w.name} backward (mamba3_ssm_chunked_bwd, dy ~ N(0,1), fp32 products)",
+                            "ms": round(bw["ms"], 4), "tokens_per_s": round(bw["tokens_per_s"], 1),
+                            "bound": "mfma", "achieved_TFLOPs": round(bw["tflops"], 1),
+                            "peak_TFLOPs": FP32_MFMA_TFLOPS, "frac": round(bw["tflops"] / FP32_MFMA_TFLOPS, 4),
+                            "flops_per_call": bw["flops"], "achieved_GBps": round(bw["gbps"], 1),
+                            "bytes_per_call": round(bw["bytes"])}
     if "rope" in out:
         line["rope_bc"] = {"ms": round(out["rope"]["ms"], 4), "achieved_GBps": round(out["rope"]["gbps"], 1),
                            "frac": round(out["rope"]["gbps"] / HBM_PEAK_GBPS, 4)}

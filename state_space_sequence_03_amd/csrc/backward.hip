@@ -56,16 +56,29 @@ struct BS {
 
 // acc[j] += A(tr*16 + m16, k) B(k, tc*16 + m16) over k < KD for the wave's
 // tiles j of a TM x TN grid (tile ti = wave + 4 j, tr = ti / TNC, tc = ti % TNC)
+// The k loop is outside the tile loop, so the wave's tiles form independent
+// MFMA chains that are issued interleaved.
 template <int TM, int TNC, int KD, typename FA, typename FB>
 __device__ __forceinline__ void mm(FA fa, FB fb, f32x4* acc, int wave, int m16, int g) {
-  constexpr int TPW = (TM * TNC + 3) / 4;
+  constexpr int NT = TM * TNC, TPW = (NT + 3) / 4;
+  if constexpr (NT % 4 == 0) {
+#pragma unroll 2
+    for (int k0 = 0; k0 < KD; k0 += 4) {
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    const int ti = wave + 4 * j;
-    if (ti < TM * TNC) {
-      const int tr = ti / TNC, tc = ti % TNC;
+      for (int j = 0; j < TPW; ++j) {
+        const int ti = wave + 4 * j, tr = ti / TNC, tc = ti % TNC;
+        acc[j] = mfma_f32(fa(tr * 16 + m16, k0 + g), fb(k0 + g, tc * 16 + m16), acc[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int ti = wave + 4 * j;
+      if (ti < NT) {
+        const int tr = ti / TNC, tc = ti % TNC;
 #pragma unroll 4
-      for (int k0 = 0; k0 < KD; k0 += 4) acc[j] = mfma_f32(fa(tr * 16 + m16, k0 + g), fb(k0 + g, tc * 16 + m16), acc[j]);
+        for (int k0 = 0; k0 < KD; k0 += 4) acc[j] = mfma_f32(fa(tr * 16 + m16, k0 + g), fb(k0 + g, tc * 16 + m16), acc[j]);
+      }
     }
   }
 }
@@ -80,6 +93,26 @@ template <typename T>
 __device__ __forceinline__ float ld_io(const void* p, int64_t i) {
   return io<T>::load1(p, i);
 }
+
+// Raw rows of a chunk held in registers: item e of a thread covers row
+// v = e / (W / VEC) (token v / R, rank v % R) and the VEC elements from
+// column (e % (W / VEC)) VEC of a row W elements wide; tokens past L read as 0.
+template <typename T, int W, int V>
+struct RowVecs {
+  static constexpr int VEC = io<T>::VEC, PERROW = W / VEC, ITEMS = V * PERROW;
+  static constexpr int PER = (ITEMS + 255) / 256;
+  typename io<T>::vec r[PER];
+  template <typename TokOf>
+  __device__ __forceinline__ void load(const void* base, int tid, int R, int64_t a0, int64_t L, TokOf tok_of) {
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const int e = tid + 256 * q;
+      const int v = e / PERROW, c = e % PERROW, t = v / R;
+      if (e < ITEMS && a0 + t < L) r[q] = ldg16<T>(base, (tok_of(a0 + t) * R + v % R) * W + c * VEC);
+      else r[q] = typename io<T>::vec{};
+    }
+  }
+};
 
 }  // namespace
 
@@ -97,7 +130,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
 
   __shared__ float sW[V * LDN], sX[V * LDP];
   __shared__ float2 sCS[QB][K];
-  __shared__ float sLam[QB], sQ[QB], sDA[QB];
+  __shared__ float sLam[QB], sQ[QB], sDA[QB], sOm[QB][K];
   __shared__ TokScal sT[QB];
 
   // H' in the MFMA accumulator layout: tile j holds rows 16 tr + 4g + i, column 16 tc + m16
@@ -140,6 +173,10 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   for (int64_t c = 0; c < nch; ++c) {
     const int64_t a0 = c * QB;
     store_state(c);
+    RowVecs<T, N, V> rb;
+    RowVecs<T, P, V> rx;
+    rb.load(a.B, tid, R, a0, L, tok_of);
+    rx.load(a.x, tid, R, a0, L, tok_of);
     if (tid < QB) {
       const int64_t t = a0 + tid;
       TokScal ts{0.0f, 0.0f, 0.0f, 0.0f};
@@ -152,6 +189,10 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
       sT[tid] = ts;
       sDA[tid] = ts.d * ts.A;
     }
+    for (int e = tid; e < QB * K; e += 256) {
+      const int t = e / K, k = e % K;
+      sOm[t][k] = a0 + t < L ? a.dt[tok_of(a0 + t)] * a.theta[tok_of(a0 + t) * K + k] : 0.0f;
+    }
     __syncthreads();
     if (tid < QB) {
       float lam_c = 0.0f;
@@ -162,8 +203,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     for (int e = tid; e < QB * K; e += 256) {
       const int t = e / K, k = e % K;
       float ph = 0.0f;
-      for (int j = 0; j <= t; ++j)
-        if (a0 + j < L) ph += sT[j].d * a.theta[tok_of(a0 + j) * K + k];
+      for (int j = 0; j <= t; ++j) ph += sOm[j][k];
       float sn, cs;
       sincosf(ph, &sn, &cs);
       sCS[t][k] = make_float2(cs, sn);
@@ -171,22 +211,35 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     __syncthreads();
     const float lamQ = sLam[QB - 1];
     // W = w B~ (rows v = t R + r), X
-    for (int e = tid; e < V * (N / 2); e += 256) {
-      const int v = e / K, k = e % K, t = v / R;
-      float b0 = 0.0f, b1 = 0.0f;
-      if (a0 + t < L) {
-        const int64_t base = (tok_of(a0 + t) * R + v % R) * N + 2 * k;
-        b0 = ld_io<T>(a.B, base);
-        b1 = ld_io<T>(a.B, base + 1);
+    {
+      constexpr int VEC = io<T>::VEC;
+#pragma unroll
+      for (int q = 0; q < RowVecs<T, N, V>::PER; ++q) {
+        const int e = tid + 256 * q;
+        if (e < RowVecs<T, N, V>::ITEMS) {
+          const int v = e / (N / VEC), n0 = (e % (N / VEC)) * VEC, t = v / R;
+          float f[VEC];
+          io<T>::unpack(rb.r[q], f);
+          const float w = __expf(lamQ - sLam[t]) * sQ[t];
+#pragma unroll
+          for (int j = 0; j < VEC / 2; ++j) {
+            const float2 cs = sCS[t][n0 / 2 + j];
+            sW[v * LDN + n0 + 2 * j] = w * (cs.x * f[2 * j] + cs.y * f[2 * j + 1]);
+            sW[v * LDN + n0 + 2 * j + 1] = w * (cs.x * f[2 * j + 1] - cs.y * f[2 * j]);
+          }
+        }
       }
-      const float2 cs = sCS[t][k];
-      const float w = __expf(lamQ - sLam[t]) * sQ[t];
-      sW[v * LDN + 2 * k] = w * (cs.x * b0 + cs.y * b1);
-      sW[v * LDN + 2 * k + 1] = w * (cs.x * b1 - cs.y * b0);
-    }
-    for (int e = tid; e < V * P; e += 256) {
-      const int v = e / P, p = e % P, t = v / R;
-      sX[v * LDP + p] = (a0 + t < L) ? ld_io<T>(a.x, (tok_of(a0 + t) * R + v % R) * P + p) : 0.0f;
+#pragma unroll
+      for (int q = 0; q < RowVecs<T, P, V>::PER; ++q) {
+        const int e = tid + 256 * q;
+        if (e < RowVecs<T, P, V>::ITEMS) {
+          const int v = e / (P / VEC), p0 = (e % (P / VEC)) * VEC;
+          float f[VEC];
+          io<T>::unpack(rx.r[q], f);
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) sX[v * LDP + p0 + j] = f[j];
+        }
+      }
     }
     __syncthreads();
     // S = W^T X, then H' <- R(Theta) (e^{Lam_end} H' + S)
@@ -236,7 +289,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ float2 sCS[QB][K];
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
-  __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K];
+  __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K], sTh[QB][K], sThDot[QB];
   __shared__ float sDLam[QB], sDq[QB], sDgam[QB], sDe[V], sDw[V], sDlq[QB], sRed[1];
 
   const float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
@@ -260,6 +313,16 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   for (int64_t c = nch - 1; c >= 0; --c) {
     const int64_t a0 = c * QB;
     // ---------------- staging ----------------
+    RowVecs<T, N, V> rb, rc;
+    RowVecs<T, P, V> rx, rdy;
+    rb.load(a.B, tid, R, a0, L, tok_of);
+    rc.load(a.C, tid, R, a0, L, tok_of);
+    rx.load(a.x, tid, R, a0, L, tok_of);
+    rdy.load(a.dy, tid, R, a0, L, tok_of);
+    for (int e = tid; e < QB * K; e += 256) {
+      const int t = e / K, k = e % K;
+      sTh[t][k] = a0 + t < L ? a.theta[tok_of(a0 + t) * K + k] : 0.0f;
+    }
     if (tid < QB) {
       const int64_t t = a0 + tid;
       TokScal ts{0.0f, 0.0f, 0.0f, 0.0f};
@@ -280,7 +343,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     }
     for (int e = tid; e < K; e += 256) sDTheta[e] = 0.0f;
     if (tid == 0) sRed[0] = 0.0f;
-    for (int e = tid; e < N * P; e += 256) sH[(e / P) * LDP + e % P] = ck[c * (N * P) + e];
+    for (int e = tid; e < N * P / 4; e += 256) {
+      const float4 hv = *(const float4*)(ck + c * (N * P) + 4 * e);
+      float* dst = &sH[((4 * e) / P) * LDP + (4 * e) % P];
+      dst[0] = hv.x; dst[1] = hv.y; dst[2] = hv.z; dst[3] = hv.w;
+    }
     __syncthreads();
     if (tid < QB) {
       float lam_c = 0.0f;
@@ -292,8 +359,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     for (int e = tid; e < QB * K; e += 256) {
       const int t = e / K, k = e % K;
       float ph = 0.0f;
-      for (int j = 0; j <= t; ++j)
-        if (a0 + j < L) ph += sT[j].d * a.theta[tok_of(a0 + j) * K + k];
+      for (int j = 0; j <= t; ++j) ph += sT[j].d * sTh[j][k];
       float sn, cs;
       sincosf(ph, &sn, &cs);
       sCS[t][k] = make_float2(cs, sn);
@@ -301,28 +367,41 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     __syncthreads();
     const float lamQ = sLam[QB - 1], eQ = sEL[QB - 1];
     if (tid < QB) sW[tid] = __expf(lamQ - sLam[tid]) * sQ[tid];
-    for (int e = tid; e < V * K; e += 256) {
-      const int v = e / K, k = e % K, t = v / R;
-      float b0 = 0.0f, b1 = 0.0f, c0 = 0.0f, c1 = 0.0f;
-      if (a0 + t < L) {
-        const int64_t base = (tok_of(a0 + t) * R + v % R) * N + 2 * k;
-        b0 = ld_io<T>(a.B, base);
-        b1 = ld_io<T>(a.B, base + 1);
-        c0 = ld_io<T>(a.C, base);
-        c1 = ld_io<T>(a.C, base + 1);
+    {
+      constexpr int VEC = io<T>::VEC;
+#pragma unroll
+      for (int q = 0; q < RowVecs<T, N, V>::PER; ++q) {
+        const int e = tid + 256 * q;
+        if (e < RowVecs<T, N, V>::ITEMS) {
+          const int v = e / (N / VEC), n0 = (e % (N / VEC)) * VEC, t = v / R;
+          float fb[VEC], fc[VEC];
+          io<T>::unpack(rb.r[q], fb);
+          io<T>::unpack(rc.r[q], fc);
+#pragma unroll
+          for (int j = 0; j < VEC / 2; ++j) {
+            const float2 cs = sCS[t][n0 / 2 + j];
+            sB[v * LDN + n0 + 2 * j] = cs.x * fb[2 * j] + cs.y * fb[2 * j + 1];
+            sB[v * LDN + n0 + 2 * j + 1] = cs.x * fb[2 * j + 1] - cs.y * fb[2 * j];
+            sC[v * LDN + n0 + 2 * j] = cs.x * fc[2 * j] + cs.y * fc[2 * j + 1];
+            sC[v * LDN + n0 + 2 * j + 1] = cs.x * fc[2 * j + 1] - cs.y * fc[2 * j];
+          }
+        }
       }
-      const float2 cs = sCS[t][k];
-      sB[v * LDN + 2 * k] = cs.x * b0 + cs.y * b1;
-      sB[v * LDN + 2 * k + 1] = cs.x * b1 - cs.y * b0;
-      sC[v * LDN + 2 * k] = cs.x * c0 + cs.y * c1;
-      sC[v * LDN + 2 * k + 1] = cs.x * c1 - cs.y * c0;
-    }
-    for (int e = tid; e < V * P; e += 256) {
-      const int v = e / P, p = e % P, t = v / R;
-      const bool ok = a0 + t < L;
-      const int64_t off = (tok_of(ok ? a0 + t : 0) * R + v % R) * P + p;
-      sX[v * LDP + p] = ok ? ld_io<T>(a.x, off) : 0.0f;
-      sDY[v * LDP + p] = ok ? ld_io<T>(a.dy, off) : 0.0f;
+#pragma unroll
+      for (int q = 0; q < RowVecs<T, P, V>::PER; ++q) {
+        const int e = tid + 256 * q;
+        if (e < RowVecs<T, P, V>::ITEMS) {
+          const int v = e / (P / VEC), p0 = (e % (P / VEC)) * VEC;
+          float fx[VEC], fd[VEC];
+          io<T>::unpack(rx.r[q], fx);
+          io<T>::unpack(rdy.r[q], fd);
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) {
+            sX[v * LDP + p0 + j] = fx[j];
+            sDY[v * LDP + p0 + j] = fd[j];
+          }
+        }
+      }
     }
     // dZ = R(-Theta) dH_out; dTheta = <dH_out, J H_out> per pair; <dZ, H_in>
     {
@@ -539,6 +618,17 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       for (int t = 0; t < QB; ++t) dlq += sDlq[t];
       sDLam[QB - 1] += dlq;
     }
+    // angles: d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega
+    for (int e = tid; e < QB * K; e += 256) {
+      const int t = e / K, k = e % K;
+      float dom = sDTheta[k];
+      for (int i = t; i < QB; ++i) dom += sDphi[i][k];
+      if (a0 + t < L) a.dtheta[tok_of(a0 + t) * K + k] = sT[t].d * dom;
+      float v = sTh[t][k] * dom;  // the K pairs of a token are K consecutive lanes
+#pragma unroll
+      for (int o = 1; o < K; o <<= 1) v += __shfl_xor(v, o, 64);
+      if (k == 0) sThDot[t] = v;
+    }
     __syncthreads();
     if (tid < QB) {
       const int t = tid;
@@ -550,18 +640,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       const float deps = t > 0 ? sDq[t - 1] : 0.0f;  // eps_t weighs the previous token
       float ddt = ts.A * dda + ts.lam * dgam + (1.0f - ts.lam) * deps;
       float dlam = ts.d * dgam - ts.d * deps;
-      // angles: d omega_t = sum_{i >= t} dphi_i + dTheta
-      float dth_dot = 0.0f;
+      ddt += sThDot[t];  // theta_t . d omega_t
       const int64_t tk = a0 + t < L ? tok_of(a0 + t) : 0;
-      for (int k = 0; k < K; ++k) {
-        float dom = sDTheta[k];
-        for (int i = t; i < QB; ++i) dom += sDphi[i][k];
-        if (a0 + t < L) {
-          a.dtheta[tk * K + k] = ts.d * dom;
-          dth_dot += a.theta[tk * K + k] * dom;
-        }
-      }
-      ddt += dth_dot;
       if (a0 + t < L) {
         a.dA[tk] = ts.d * dda;
         if (t > 0) {
