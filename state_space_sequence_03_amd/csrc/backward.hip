@@ -51,29 +51,28 @@ struct BS {
   static constexpr int LDN = N + 4, LDP = P + 4, LDV = V + 4;  // fp32 row strides in LDS
   static constexpr int TN = N / 16, TP = P / 16, TV = V / 16;   // 16-wide tiles
   static constexpr int NPT = TN * TP;                           // tiles of an N x P matrix
-  static constexpr int NPW = (NPT + 3) / 4;                     // ... per wave
 };
 
 // acc[j] += A(tr*16 + m16, k) B(k, tc*16 + m16) over k < KD for the wave's
-// tiles j of a TM x TN grid (tile ti = wave + 4 j, tr = ti / TNC, tc = ti % TNC)
+// tiles j of a TM x TN grid (tile ti = wave + NW j, tr = ti / TNC, tc = ti % TNC)
 // The k loop is outside the tile loop, so the wave's tiles form independent
 // MFMA chains that are issued interleaved.
-template <int TM, int TNC, int KD, typename FA, typename FB>
+template <int NW, int TM, int TNC, int KD, typename FA, typename FB>
 __device__ __forceinline__ void mm(FA fa, FB fb, f32x4* acc, int wave, int m16, int g) {
-  constexpr int NT = TM * TNC, TPW = (NT + 3) / 4;
-  if constexpr (NT % 4 == 0) {
+  constexpr int NT = TM * TNC, TPW = (NT + NW - 1) / NW;
+  if constexpr (NT % NW == 0) {
 #pragma unroll 2
     for (int k0 = 0; k0 < KD; k0 += 4) {
 #pragma unroll
       for (int j = 0; j < TPW; ++j) {
-        const int ti = wave + 4 * j, tr = ti / TNC, tc = ti % TNC;
+        const int ti = wave + NW * j, tr = ti / TNC, tc = ti % TNC;
         acc[j] = mfma_f32(fa(tr * 16 + m16, k0 + g), fb(k0 + g, tc * 16 + m16), acc[j]);
       }
     }
   } else {
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
-      const int ti = wave + 4 * j;
+      const int ti = wave + NW * j;
       if (ti < NT) {
         const int tr = ti / TNC, tc = ti % TNC;
 #pragma unroll 4
@@ -97,16 +96,16 @@ __device__ __forceinline__ float ld_io(const void* p, int64_t i) {
 // Raw rows of a chunk held in registers: item e of a thread covers row
 // v = e / (W / VEC) (token v / R, rank v % R) and the VEC elements from
 // column (e % (W / VEC)) VEC of a row W elements wide; tokens past L read as 0.
-template <typename T, int W, int V>
+template <typename T, int W, int V, int TH>
 struct RowVecs {
   static constexpr int VEC = io<T>::VEC, PERROW = W / VEC, ITEMS = V * PERROW;
-  static constexpr int PER = (ITEMS + 255) / 256;
+  static constexpr int PER = (ITEMS + TH - 1) / TH;
   typename io<T>::vec r[PER];
   template <typename TokOf>
   __device__ __forceinline__ void load(const void* base, int tid, int R, int64_t a0, int64_t L, TokOf tok_of) {
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
-      const int e = tid + 256 * q;
+      const int e = tid + TH * q;
       const int v = e / PERROW, c = e % PERROW, t = v / R;
       if (e < ITEMS && a0 + t < L) r[q] = ldg16<T>(base, (tok_of(a0 + t) * R + v % R) * W + c * VEC);
       else r[q] = typename io<T>::vec{};
@@ -123,6 +122,7 @@ template <typename T, int N, int P, int R>
 __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   typedef BS<N, P, R> S;
   constexpr int K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP;
+  constexpr int NW = 4, TH = 64 * NW, NPW = (S::NPT + NW - 1) / NW;
   const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
@@ -134,12 +134,12 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   __shared__ TokScal sT[QB];
 
   // H' in the MFMA accumulator layout: tile j holds rows 16 tr + 4g + i, column 16 tc + m16
-  f32x4 Hs[S::NPW];
+  f32x4 Hs[NPW];
   const bool has_prev = a.prev_B != nullptr;
   const float eps1 = (has_prev && L > 0) ? (1.0f - a.lam[tok_of(0)]) * a.dt[tok_of(0)] : 0.0f;
 #pragma unroll
-  for (int j = 0; j < S::NPW; ++j) {
-    const int ti = wave + 4 * j;
+  for (int j = 0; j < NPW; ++j) {
+    const int ti = wave + NW * j;
     Hs[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (ti < S::NPT) {
       const int tr = ti / S::TP, tc = ti % S::TP, p = tc * 16 + m16;
@@ -160,8 +160,8 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
   auto store_state = [&](int64_t c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < S::NPW; ++j) {
-      const int ti = wave + 4 * j;
+    for (int j = 0; j < NPW; ++j) {
+      const int ti = wave + NW * j;
       if (ti < S::NPT) {
         const int tr = ti / S::TP, tc = ti % S::TP, p = tc * 16 + m16;
 #pragma unroll
@@ -173,8 +173,8 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   for (int64_t c = 0; c < nch; ++c) {
     const int64_t a0 = c * QB;
     store_state(c);
-    RowVecs<T, N, V> rb;
-    RowVecs<T, P, V> rx;
+    RowVecs<T, N, V, TH> rb;
+    RowVecs<T, P, V, TH> rx;
     rb.load(a.B, tid, R, a0, L, tok_of);
     rx.load(a.x, tid, R, a0, L, tok_of);
     if (tid < QB) {
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
       sT[tid] = ts;
       sDA[tid] = ts.d * ts.A;
     }
-    for (int e = tid; e < QB * K; e += 256) {
+    for (int e = tid; e < QB * K; e += TH) {
       const int t = e / K, k = e % K;
       sOm[t][k] = a0 + t < L ? a.dt[tok_of(a0 + t)] * a.theta[tok_of(a0 + t) * K + k] : 0.0f;
     }
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
       sLam[tid] = lam_c;
       sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
     }
-    for (int e = tid; e < QB * K; e += 256) {
+    for (int e = tid; e < QB * K; e += TH) {
       const int t = e / K, k = e % K;
       float ph = 0.0f;
       for (int j = 0; j <= t; ++j) ph += sOm[j][k];
@@ -214,9 +214,9 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     {
       constexpr int VEC = io<T>::VEC;
 #pragma unroll
-      for (int q = 0; q < RowVecs<T, N, V>::PER; ++q) {
-        const int e = tid + 256 * q;
-        if (e < RowVecs<T, N, V>::ITEMS) {
+      for (int q = 0; q < RowVecs<T, N, V, TH>::PER; ++q) {
+        const int e = tid + TH * q;
+        if (e < RowVecs<T, N, V, TH>::ITEMS) {
           const int v = e / (N / VEC), n0 = (e % (N / VEC)) * VEC, t = v / R;
           float f[VEC];
           io<T>::unpack(rb.r[q], f);
@@ -230,9 +230,9 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int q = 0; q < RowVecs<T, P, V>::PER; ++q) {
-        const int e = tid + 256 * q;
-        if (e < RowVecs<T, P, V>::ITEMS) {
+      for (int q = 0; q < RowVecs<T, P, V, TH>::PER; ++q) {
+        const int e = tid + TH * q;
+        if (e < RowVecs<T, P, V, TH>::ITEMS) {
           const int v = e / (P / VEC), p0 = (e % (P / VEC)) * VEC;
           float f[VEC];
           io<T>::unpack(rx.r[q], f);
@@ -243,15 +243,15 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     }
     __syncthreads();
     // S = W^T X, then H' <- R(Theta) (e^{Lam_end} H' + S)
-    f32x4 sacc[S::NPW];
+    f32x4 sacc[NPW];
 #pragma unroll
-    for (int j = 0; j < S::NPW; ++j) sacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    mm<S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; }, [&](int v, int p) { return sX[v * LDP + p]; },
+    for (int j = 0; j < NPW; ++j) sacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    mm<NW, S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; }, [&](int v, int p) { return sX[v * LDP + p]; },
                         sacc, wave, m16, g);
     const float eQ = __expf(lamQ);
 #pragma unroll
-    for (int j = 0; j < S::NPW; ++j) {
-      const int ti = wave + 4 * j;
+    for (int j = 0; j < NPW; ++j) {
+      const int ti = wave + NW * j;
       if (ti < S::NPT) {
         const int tr = ti / S::TP;
 #pragma unroll
@@ -274,11 +274,12 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
 // 2. backward walk over the chunks in reverse order
 // ---------------------------------------------------------------------------
 template <typename T, int N, int P, int R>
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   typedef BS<N, P, R> S;
   constexpr int K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP, LDV = S::LDV;
   constexpr int TV = S::TV, TN = S::TN, TP = S::TP;
-  constexpr int VVW = (TV * TV + 3) / 4, VNW = (TV * TN + 3) / 4, VPW = (TV * TP + 3) / 4;
+  constexpr int NW = 8, TH = 64 * NW, NPW = (S::NPT + NW - 1) / NW;
+  constexpr int VVW = (TV * TV + NW - 1) / NW, VNW = (TV * TN + NW - 1) / NW, VPW = (TV * TP + NW - 1) / NW;
   const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
@@ -294,10 +295,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
 
   const float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
   // dH' (adjoint of the carried state) in the accumulator layout of an N x P matrix
-  f32x4 Gb[S::NPW];
+  f32x4 Gb[NPW];
 #pragma unroll
-  for (int j = 0; j < S::NPW; ++j) {
-    const int ti = wave + 4 * j;
+  for (int j = 0; j < NPW; ++j) {
+    const int ti = wave + NW * j;
     Gb[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if (ti < S::NPT && a.dh_final) {
       const int tr = ti / TP, tc = ti % TP;
@@ -313,13 +314,13 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   for (int64_t c = nch - 1; c >= 0; --c) {
     const int64_t a0 = c * QB;
     // ---------------- staging ----------------
-    RowVecs<T, N, V> rb, rc;
-    RowVecs<T, P, V> rx, rdy;
+    RowVecs<T, N, V, TH> rb, rc;
+    RowVecs<T, P, V, TH> rx, rdy;
     rb.load(a.B, tid, R, a0, L, tok_of);
     rc.load(a.C, tid, R, a0, L, tok_of);
     rx.load(a.x, tid, R, a0, L, tok_of);
     rdy.load(a.dy, tid, R, a0, L, tok_of);
-    for (int e = tid; e < QB * K; e += 256) {
+    for (int e = tid; e < QB * K; e += TH) {
       const int t = e / K, k = e % K;
       sTh[t][k] = a0 + t < L ? a.theta[tok_of(a0 + t) * K + k] : 0.0f;
     }
@@ -337,13 +338,13 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       sDq[tid] = 0.0f;
       sDgam[tid] = 0.0f;
     }
-    for (int e = tid; e < V; e += 256) {
+    for (int e = tid; e < V; e += TH) {
       sDe[e] = 0.0f;
       sDw[e] = 0.0f;
     }
-    for (int e = tid; e < K; e += 256) sDTheta[e] = 0.0f;
+    for (int e = tid; e < K; e += TH) sDTheta[e] = 0.0f;
     if (tid == 0) sRed[0] = 0.0f;
-    for (int e = tid; e < N * P / 4; e += 256) {
+    for (int e = tid; e < N * P / 4; e += TH) {
       const float4 hv = *(const float4*)(ck + c * (N * P) + 4 * e);
       float* dst = &sH[((4 * e) / P) * LDP + (4 * e) % P];
       dst[0] = hv.x; dst[1] = hv.y; dst[2] = hv.z; dst[3] = hv.w;
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       sEL[tid] = __expf(lam_c);
       sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
     }
-    for (int e = tid; e < QB * K; e += 256) {
+    for (int e = tid; e < QB * K; e += TH) {
       const int t = e / K, k = e % K;
       float ph = 0.0f;
       for (int j = 0; j <= t; ++j) ph += sT[j].d * sTh[j][k];
@@ -370,9 +371,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     {
       constexpr int VEC = io<T>::VEC;
 #pragma unroll
-      for (int q = 0; q < RowVecs<T, N, V>::PER; ++q) {
-        const int e = tid + 256 * q;
-        if (e < RowVecs<T, N, V>::ITEMS) {
+      for (int q = 0; q < RowVecs<T, N, V, TH>::PER; ++q) {
+        const int e = tid + TH * q;
+        if (e < RowVecs<T, N, V, TH>::ITEMS) {
           const int v = e / (N / VEC), n0 = (e % (N / VEC)) * VEC, t = v / R;
           float fb[VEC], fc[VEC];
           io<T>::unpack(rb.r[q], fb);
@@ -388,9 +389,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
         }
       }
 #pragma unroll
-      for (int q = 0; q < RowVecs<T, P, V>::PER; ++q) {
-        const int e = tid + 256 * q;
-        if (e < RowVecs<T, P, V>::ITEMS) {
+      for (int q = 0; q < RowVecs<T, P, V, TH>::PER; ++q) {
+        const int e = tid + TH * q;
+        if (e < RowVecs<T, P, V, TH>::ITEMS) {
           const int v = e / (P / VEC), p0 = (e % (P / VEC)) * VEC;
           float fx[VEC], fd[VEC];
           io<T>::unpack(rx.r[q], fx);
@@ -407,8 +408,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     {
       float part = 0.0f;
 #pragma unroll
-      for (int j = 0; j < S::NPW; ++j) {
-        const int ti = wave + 4 * j;
+      for (int j = 0; j < NPW; ++j) {
+        const int ti = wave + NW * j;
         if (ti < S::NPT) {
           const int tr = ti / TP, tc = ti % TP, p = tc * 16 + m16;
 #pragma unroll
@@ -442,13 +443,13 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       f32x4 gacc[VVW], dacc[VVW];
 #pragma unroll
       for (int j = 0; j < VVW; ++j) gacc[j] = dacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
+      mm<NW, TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
                     gacc, wave, m16, g);
-      mm<TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
+      mm<NW, TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
                     dacc, wave, m16, g);
 #pragma unroll
       for (int j = 0; j < VVW; ++j) {
-        const int ti = wave + 4 * j;
+        const int ti = wave + NW * j;
         if (ti < TV * TV) {
           const int tr = ti / TV, tc = ti % TV;
           const int vc = tc * 16 + m16, s = vc / R;
@@ -484,13 +485,13 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       f32x4 xacc[VPW];
 #pragma unroll
       for (int j = 0; j < VPW; ++j) xacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<TV, TP, V>([&](int vr, int vk) { return sGM[vk * LDV + vr]; }, [&](int vk, int p) { return sDY[vk * LDP + p]; },
+      mm<NW, TV, TP, V>([&](int vr, int vk) { return sGM[vk * LDV + vr]; }, [&](int vk, int p) { return sDY[vk * LDP + p]; },
                     xacc, wave, m16, g);
-      mm<TV, TP, N>([&](int v, int n) { return sW[v / R] * sB[v * LDN + n]; }, [&](int n, int p) { return sDZ[n * LDP + p]; },
+      mm<NW, TV, TP, N>([&](int v, int n) { return sW[v / R] * sB[v * LDN + n]; }, [&](int n, int p) { return sDZ[n * LDP + p]; },
                     xacc, wave, m16, g);
 #pragma unroll
       for (int j = 0; j < VPW; ++j) {
-        const int ti = wave + 4 * j;
+        const int ti = wave + NW * j;
         if (ti < TV * TP) {
           const int tr = ti / TP, tc = ti % TP, p = tc * 16 + m16;
 #pragma unroll
@@ -506,17 +507,17 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       f32x4 cacc[VNW], eacc[VNW], bacc[VNW], facc[VNW];
 #pragma unroll
       for (int j = 0; j < VNW; ++j) cacc[j] = eacc[j] = bacc[j] = facc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<TV, TN, V>([&](int vr, int vk) { return sDG[vr * LDV + vk]; }, [&](int vk, int n) { return sB[vk * LDN + n]; },
+      mm<NW, TV, TN, V>([&](int vr, int vk) { return sDG[vr * LDV + vk]; }, [&](int vk, int n) { return sB[vk * LDN + n]; },
                     cacc, wave, m16, g);
-      mm<TV, TN, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int n) { return sH[n * LDP + p]; },
+      mm<NW, TV, TN, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int n) { return sH[n * LDP + p]; },
                     eacc, wave, m16, g);
-      mm<TV, TN, V>([&](int vr, int vk) { return sDG[vk * LDV + vr]; }, [&](int vk, int n) { return sC[vk * LDN + n]; },
+      mm<NW, TV, TN, V>([&](int vr, int vk) { return sDG[vk * LDV + vr]; }, [&](int vk, int n) { return sC[vk * LDN + n]; },
                     bacc, wave, m16, g);
-      mm<TV, TN, P>([&](int v, int p) { return sX[v * LDP + p]; }, [&](int p, int n) { return sDZ[n * LDP + p]; },
+      mm<NW, TV, TN, P>([&](int v, int p) { return sX[v * LDP + p]; }, [&](int p, int n) { return sDZ[n * LDP + p]; },
                     facc, wave, m16, g);
 #pragma unroll
       for (int j = 0; j < VNW; ++j) {
-        const int ti = wave + 4 * j;
+        const int ti = wave + NW * j;
         if (ti < TV * TN) {
           const int tr = ti / TN, tc = ti % TN, n = tc * 16 + m16, k = n / 2;
           float dCt[4], dBt[4], de[4], dw[4];
@@ -579,7 +580,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     }
     {
       // dH_in += C~^T (e^{Lam} dY)
-      mm<TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; }, [&](int v, int p) { return sEL[v / R] * sDY[v * LDP + p]; },
+      mm<NW, TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; }, [&](int v, int p) { return sEL[v / R] * sDY[v * LDP + p]; },
                     Gb, wave, m16, g);
     }
     __syncthreads();
@@ -588,8 +589,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     {
       // the masked decay: dM on s < t and the diagonal
       const int t = tid / QB, s = tid % QB;
-      const float dm = sDM[t][s];
-      if (s < t) {
+      const float dm = tid < QB * QB ? sDM[t % QB][s] : 0.0f;
+      if (tid >= QB * QB) {
+      } else if (s < t) {
         const float e = __expf(fminf(sLam[t] - sLam[s], 0.0f));
         const float dmm = dm * e * sQ[s];
         atomicAdd(&sDLam[t], dmm);
@@ -619,7 +621,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       sDLam[QB - 1] += dlq;
     }
     // angles: d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega
-    for (int e = tid; e < QB * K; e += 256) {
+    for (int e = tid; e < QB * K; e += TH) {
       const int t = e / K, k = e % K;
       float dom = sDTheta[k];
       for (int i = t; i < QB; ++i) dom += sDphi[i][k];
@@ -671,8 +673,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   const bool has_prev = a.prev_B != nullptr;
   if (a.dh0) {
 #pragma unroll
-    for (int j = 0; j < S::NPW; ++j) {
-      const int ti = wave + 4 * j;
+    for (int j = 0; j < NPW; ++j) {
+      const int ti = wave + NW * j;
       if (ti < S::NPT) {
         const int tr = ti / TP, tc = ti % TP;
 #pragma unroll
@@ -682,8 +684,8 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
   }
   // dH'_0 to LDS for the prev products
 #pragma unroll
-  for (int j = 0; j < S::NPW; ++j) {
-    const int ti = wave + 4 * j;
+  for (int j = 0; j < NPW; ++j) {
+    const int ti = wave + NW * j;
     if (ti < S::NPT) {
       const int tr = ti / TP, tc = ti % TP;
 #pragma unroll
@@ -698,7 +700,7 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
     if (has_prev) {
       // d eps_1 = <dH'_0, prev_B^T prev_x>; dprev_B = eps_1 dH'_0 prev_x; dprev_x = eps_1 dH'_0^T prev_B
       float part = 0.0f;
-      for (int e = tid; e < N * P; e += 256) {
+      for (int e = tid; e < N * P; e += TH) {
         const int n = e / P, p = e % P;
         float q0 = 0.0f;
         for (int r = 0; r < R; ++r)
@@ -709,13 +711,13 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
       for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
       if (lane == 0) atomicAdd(&sRed[0], part);
       if (a.dprev_B) {
-        for (int e = tid; e < R * N; e += 256) {
+        for (int e = tid; e < R * N; e += TH) {
           const int r = e / N, n = e % N;
           float acc = 0.0f;
           for (int p = 0; p < P; ++p) acc += sDZ[n * LDP + p] * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
           io<T>::store1(a.dprev_B, (bh * R + r) * N + n, eps1 * acc);
         }
-        for (int e = tid; e < R * P; e += 256) {
+        for (int e = tid; e < R * P; e += TH) {
           const int r = e / P, p = e % P;
           float acc = 0.0f;
           for (int n = 0; n < N; ++n) acc += sDZ[n * LDP + p] * ld_io<T>(a.prev_B, (bh * R + r) * N + n);
@@ -734,9 +736,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(BwdArgs a) {
 
 template <typename T, int N, int P, int R>
 static hipError_t bwd_run(const BwdArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.batch * a.H)), block(256);
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, N, P, R>), grid, block, 0, s, a);
-  hipLaunchKernelGGL((bwd_chunk_kernel<T, N, P, R>), grid, block, 0, s, a);
+  const dim3 grid((unsigned)(a.batch * a.H));
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, N, P, R>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_chunk_kernel<T, N, P, R>), grid, dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
