@@ -119,6 +119,38 @@ def test_workspace_sizes(L):
     assert L.rope_bc_workspace_size(dims(L, dstate=7)) == 0
 
 
+BWD_PTRS = ("x", "B", "C", "dt", "A", "lam", "theta", "h0", "prev_B", "prev_x", "dy", "dh_final",
+            "dx", "dB", "dC", "ddt", "dA", "dlam", "dtheta", "dh0", "dprev_B", "dprev_x")
+
+
+def call_bwd(L, d, ws_bytes=None, **over):
+    p = {k: ctypes.c_void_p(FAKE) for k in BWD_PTRS}
+    p.update(h0=None, prev_B=None, prev_x=None, dh_final=None, dh0=None, dprev_B=None, dprev_x=None, ws=ctypes.c_void_p(FAKE))
+    p.update(over)
+    need = L.chunked_bwd_workspace_size(d) if ws_bytes is None else ws_bytes
+    return L.lib().mamba3_ssm_chunked_bwd(ctypes.byref(d), *(p[k] for k in BWD_PTRS), p["ws"], ctypes.c_size_t(need), None)
+
+
+def test_backward_validation(L):
+    d = dims(L)  # batch 2, L 100, H 3, P 64, N 64, R 4, bf16
+    assert L.chunked_bwd_workspace_size(d) == 4 * 6 * ((100 + 15) // 16 + 1) * 64 * 64
+    assert call_bwd(L, dims(L, dstate=15)) == L.M3_ERR_SHAPE
+    assert call_bwd(L, dims(L, headdim=128)) == L.M3_ERR_UNSUPPORTED   # the backward covers N, P <= 64
+    assert call_bwd(L, dims(L, dstate=128)) == L.M3_ERR_UNSUPPORTED
+    assert call_bwd(L, dims(L, flags=1)) == L.M3_ERR_UNSUPPORTED
+    assert call_bwd(L, d, dy=None) == L.M3_ERR_NULL
+    assert call_bwd(L, d, dtheta=None) == L.M3_ERR_NULL
+    assert call_bwd(L, d, prev_B=ctypes.c_void_p(FAKE)) == L.M3_ERR_NULL          # prev_x missing
+    assert call_bwd(L, d, dprev_B=ctypes.c_void_p(FAKE)) == L.M3_ERR_NULL         # dprev_x missing
+    assert call_bwd(L, d, dx=ctypes.c_void_p(FAKE + 8)) == L.M3_ERR_ALIGN
+    assert call_bwd(L, d, dtheta=ctypes.c_void_p(FAKE + 4)) == L.M3_ERR_ALIGN
+    assert call_bwd(L, d, ddt=ctypes.c_void_p(FAKE + 2)) == L.M3_ERR_ALIGN
+    assert call_bwd(L, d, ws_bytes=1024) == L.M3_ERR_WORKSPACE
+    assert call_bwd(L, d, ws=None) == L.M3_ERR_WORKSPACE
+    e = dims(L, batch=0)
+    assert L.lib().mamba3_ssm_chunked_bwd(ctypes.byref(e), *([None] * 22), None, ctypes.c_size_t(0), None) == L.M3_OK
+
+
 def call_decode(L, d, **over):
     p = {k: ctypes.c_void_p(FAKE) for k in ("state", "x", "B", "C", "dt", "A", "lam", "theta", "y")}
     p.update(prev_B=None, prev_x=None)
