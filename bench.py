@@ -201,8 +201,8 @@ def bench_verify(ops, inputs, w, k, steps, warmup, torch):
     res = {}
     for name, walk in (("token_path", False), ("chunk_walk", True)):
         fn = lambda: ops.chunked_fwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], h0=state,
-                                     prev_B=d["prev_B"], prev_x=d["prev_x"], chunk=w.chunk, chunk_walk=walk, y=y,
-                                     h_final=state)
+                                     prev_B=d["prev_B"], prev_x=d["prev_x"], chunk=w.chunk, chunk_walk=walk,
+                                     token_path=not walk, y=y, h_final=state)
         wall, ev = timed(fn, steps, warmup, torch)
         res[name] = ev
     b = verify_bytes_per_call(w, k)

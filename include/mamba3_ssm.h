@@ -103,18 +103,25 @@ typedef struct {
   int32_t flags;    /* chunked_fwd: bits 0..15 = number of sequence segments
                        walked in parallel per (b,h) (0 = chosen by the
                        library: more than one only for bf16 io when B*H <
-                       256); M3_FLAG_CHUNK_WALK; other bits must be 0.
+                       256); M3_FLAG_CHUNK_WALK or M3_FLAG_TOKEN_PATH;
+                       other bits must be 0.
                        Segments > 1 need bf16 io and B*H <= 65535.  Other
                        entry points: must be 0. */
 } m3_dims;
 
-/* chunked_fwd: walk chunks even when seqlen <= M3_TOKEN_PATH_MAX_L.  Without
- * this flag such short calls (e.g. verifying k draft tokens of a decoder, with
+/* chunked_fwd: short calls (e.g. verifying k draft tokens of a decoder, with
  * the decode state as h0 and h_final) run token by token with the state held
  * on chip: the one-token update of decode_step applied to each token, the
- * state read once and written once.  Both paths compute the same function. */
+ * state read once and written once.  The library takes that path for
+ * seqlen <= M3_TOKEN_PATH_SUBWALK_L when the sub-chunk walker covers the sizes
+ * (bf16 io, P = 64, N = 64 or 128) and for seqlen <= M3_TOKEN_PATH_MAX_L
+ * otherwise.  M3_FLAG_CHUNK_WALK forces the chunk walk; M3_FLAG_TOKEN_PATH
+ * forces the token path (seqlen <= M3_TOKEN_PATH_MAX_L, else
+ * M3_ERR_UNSUPPORTED); not both.  Both paths compute the same function. */
 #define M3_FLAG_CHUNK_WALK 0x10000
+#define M3_FLAG_TOKEN_PATH 0x20000
 #define M3_TOKEN_PATH_MAX_L 16
+#define M3_TOKEN_PATH_SUBWALK_L 8
 
 /* Whole-sequence forward.
  *   y_t = C_t^T h_t for every token, and h_final = h_L.

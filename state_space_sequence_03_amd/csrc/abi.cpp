@@ -131,7 +131,9 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
                                  float* h_final, void* workspace, size_t workspace_bytes, void* stream) {
   m3_status st = check_dims(d, true, true);
   if (st != M3_OK) return st;
-  if ((d->flags & ~(0xffff | M3_FLAG_CHUNK_WALK)) != 0) return M3_ERR_UNSUPPORTED;
+  if ((d->flags & ~(0xffff | M3_FLAG_CHUNK_WALK | M3_FLAG_TOKEN_PATH)) != 0) return M3_ERR_UNSUPPORTED;
+  if ((d->flags & M3_FLAG_CHUNK_WALK) && (d->flags & M3_FLAG_TOKEN_PATH)) return M3_ERR_UNSUPPORTED;
+  if ((d->flags & M3_FLAG_TOKEN_PATH) && d->seqlen > M3_TOKEN_PATH_MAX_L) return M3_ERR_UNSUPPORTED;
   if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0 &&
       !m3::walk_fast_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) &&
       !m3::subwalk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank, d->nheads))
@@ -157,7 +159,15 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
       return m3::launch_copy_f32(h_final, h0, BH * d->dstate * d->headdim, s) == hipSuccess ? M3_OK : M3_ERR_HIP;
     return M3_OK;
   }
-  if (d->seqlen <= M3_TOKEN_PATH_MAX_L && sp.S == 1 && !(d->flags & M3_FLAG_CHUNK_WALK)) {
+  // the token path wins up to ~8 tokens against the sub-chunk walker and up to
+  // 16 against the other walkers (measured at the 1.5B decode shapes)
+  const int64_t tok_max =
+      m3::subwalk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank, d->nheads)
+          ? M3_TOKEN_PATH_SUBWALK_L
+          : M3_TOKEN_PATH_MAX_L;
+  const bool token_path = (d->flags & M3_FLAG_TOKEN_PATH) ||
+                          (d->seqlen <= tok_max && sp.S == 1 && !(d->flags & M3_FLAG_CHUNK_WALK));
+  if (token_path) {
     // a few tokens: token by token with the state in registers
     m3::TokensArgs t{};
     t.h0 = h0; t.h_final = h_final; t.x = x; t.B = B; t.C = C;

@@ -20,7 +20,9 @@ LIB_PATH = os.path.join(HERE, "libmamba3_ssm.so")
 M3_OK, M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_UNSUPPORTED, M3_ERR_ALIGN, M3_ERR_WORKSPACE, M3_ERR_HIP = range(7)
 M3_F32, M3_BF16 = 0, 1
 M3_FLAG_CHUNK_WALK = 0x10000   # chunked_fwd: walk chunks even for short sequences
-M3_TOKEN_PATH_MAX_L = 16      # chunked_fwd runs token by token up to this many tokens
+M3_FLAG_TOKEN_PATH = 0x20000   # chunked_fwd: token by token (at most M3_TOKEN_PATH_MAX_L tokens)
+M3_TOKEN_PATH_MAX_L = 16       # longest call the token path takes
+M3_TOKEN_PATH_SUBWALK_L = 8    # ... chosen by default when the sub-chunk walker covers the sizes
 ABI_SYMBOLS = ("mamba3_ssm_chunked_fwd", "mamba3_ssm_chunked_fwd_workspace_size", "mamba3_ssm_chunked_bwd",
                "mamba3_ssm_chunked_bwd_workspace_size", "mamba3_ssm_decode_step",
                "mamba3_rope_bc", "mamba3_rope_bc_workspace_size", "mamba3_status_string", "mamba3_abi_version")
@@ -126,14 +128,16 @@ def rope_bc_workspace_size(dims: Dims) -> int:
 
 
 def mamba3_ssm_chunked_fwd(x, B, C, dt, A, lam, theta, h0=None, prev_B=None, prev_x=None, *, chunk=64,
-                           segments=0, chunk_walk=False, y=None, h_final=None, want_final=True, workspace=None,
-                           stream=None):
+                           segments=0, chunk_walk=False, token_path=False, y=None, h_final=None, want_final=True,
+                           workspace=None, stream=None):
     """Whole-sequence forward.  Returns (y, h_final) (h_final None if not wanted).
-    chunk_walk: walk chunks even for sequences of at most M3_TOKEN_PATH_MAX_L tokens."""
+    chunk_walk / token_path force one of the two paths for short calls (the
+    library picks one by default)."""
     torch = _torch()
     b, L, H, R, P = x.shape
     N = B.shape[-1]
-    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x), flags=segments | (M3_FLAG_CHUNK_WALK if chunk_walk else 0))
+    flags = segments | (M3_FLAG_CHUNK_WALK if chunk_walk else 0) | (M3_FLAG_TOKEN_PATH if token_path else 0)
+    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x), flags=flags)
     if y is None:
         y = torch.empty_like(x)
     if h_final is None and want_final:

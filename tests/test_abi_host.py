@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_header_constants_match_binding(L):
     text = open(HEADER).read()
-    for name in ("M3_FLAG_CHUNK_WALK", "M3_TOKEN_PATH_MAX_L"):
+    for name in ("M3_FLAG_CHUNK_WALK", "M3_FLAG_TOKEN_PATH", "M3_TOKEN_PATH_MAX_L", "M3_TOKEN_PATH_SUBWALK_L"):
         m = re.search(r"#define\s+" + name + r"\s+(\w+)", text)
         assert m, name
         assert int(m.group(1), 0) == getattr(L, name), name
@@ -77,7 +77,9 @@ def dims(L, **kw):
     (dict(dstate=48), "M3_ERR_UNSUPPORTED"), (dict(headdim=96), "M3_ERR_UNSUPPORTED"),
     (dict(rank=3), "M3_ERR_UNSUPPORTED"), (dict(chunk=128), "M3_ERR_UNSUPPORTED"),
     (dict(io_dtype=7), "M3_ERR_UNSUPPORTED"), (dict(flags=1 << 20), "M3_ERR_UNSUPPORTED"),
-    (dict(flags=1 << 17), "M3_ERR_UNSUPPORTED"),
+    (dict(flags=1 << 18), "M3_ERR_UNSUPPORTED"),
+    (dict(flags=0x30000), "M3_ERR_UNSUPPORTED"),                                # both path flags
+    (dict(flags=0x20000, seqlen=17), "M3_ERR_UNSUPPORTED"),                     # token path too long
     (dict(dstate=128, headdim=128, rank=4, chunk=64), "M3_ERR_UNSUPPORTED"),     # tiles exceed LDS
     (dict(io_dtype=0, rank=4, chunk=64), "M3_ERR_UNSUPPORTED"),                # fp32 tiles exceed LDS
 ])

@@ -122,9 +122,10 @@ def test_chunked_matches_oracle(ops, case):
     say(f"chunked_fwd {case}")
     inp = numpy_inputs(b, L, H, P, N, R, io=io, seed=zlib.crc32(repr(case).encode()) % 10000, with_h0=h0, with_prev=prev)
     check_fwd(ops, inp, io, Q)
-    if L <= M3_TOKEN_PATH_MAX_L:  # the call above ran token by token: also walk the chunks
-        say("   forced chunk walk")
+    if L <= M3_TOKEN_PATH_MAX_L:  # short: both paths
+        say("   forced chunk walk, forced token path")
         check_fwd(ops, inp, io, Q, chunk_walk=True)
+        check_fwd(ops, inp, io, Q, token_path=True)
 
 
 # short sequences (at most M3_TOKEN_PATH_MAX_L tokens) run token by token with
@@ -148,8 +149,9 @@ def test_short_sequence_token_path(ops, case):
     io, b, L, H, P, N, R, h0, prev = case
     say(f"token path {case}")
     inp = numpy_inputs(b, L, H, P, N, R, io=io, seed=zlib.crc32(repr(case).encode()) % 10000, with_h0=h0, with_prev=prev)
-    y_t, h_t = check_fwd(ops, inp, io, 16)
+    y_t, h_t = check_fwd(ops, inp, io, 16, token_path=True)
     y_w, h_w = check_fwd(ops, inp, io, 16, chunk_walk=True)
+    check_fwd(ops, inp, io, 16)  # the library's own choice
     assert slice_err(host(h_t), host(h_w), (0, 1)) < 1e-3
 
 
@@ -162,7 +164,7 @@ def test_verify_step_in_place(ops):
     say("verify step in place")
     state = d["h0"].clone()
     y, hf = ops.chunked_fwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], h0=state,
-                            prev_B=d["prev_B"], prev_x=d["prev_x"], chunk=16, h_final=state)
+                            prev_B=d["prev_B"], prev_x=d["prev_x"], chunk=16, h_final=state, token_path=True)
     torch.cuda.synchronize()
     assert hf.data_ptr() == state.data_ptr()
     yo, ho = oracle_fwd(inp)
