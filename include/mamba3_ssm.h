@@ -158,9 +158,10 @@ size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d);
  *        the gradient with respect to a zero initial state).
  *   dprev_B (B, H, R, N), dprev_x (B, H, R, P): nullable pair, io dtype,
  *        written when prev_B/prev_x are given.
- * Supported: N and P in {16, 32, 64}, R in {1, 2, 4}, io fp32 or bf16; d->chunk
- * must be a supported chunk length but the backward always walks 16-token
- * chunks.  All products are fp32.  workspace: at least
+ * Supported: N and P in {16, 32, 64, 128} but not both 128, R in {1, 2, 4},
+ * io fp32 or bf16; d->chunk must be a supported chunk length but the backward
+ * walks chunks of its own: 16 tokens, 8 when N or P is 128 and R = 4.  All
+ * products are fp32.  workspace: at least
  * mamba3_ssm_chunked_bwd_workspace_size(d) bytes (the states at every chunk
  * start); its contents on entry do not matter.  Outputs must not alias inputs.
  * Alignment: x, B, C, dy, dx, dB, dC, theta, dtheta and the workspace 16-byte;

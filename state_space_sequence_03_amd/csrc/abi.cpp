@@ -198,7 +198,8 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
 size_t mamba3_ssm_chunked_bwd_workspace_size(const m3_dims* d) {
   if (check_dims(d, true, true) != M3_OK) return 0;
   if (d->batch == 0 || d->nheads == 0 || d->seqlen == 0) return 0;
-  const int64_t nch = (d->seqlen + m3::BWD_CHUNK - 1) / m3::BWD_CHUNK;
+  const int64_t q = m3::bwd_chunk_len((int)d->dstate, (int)d->headdim, (int)d->rank);
+  const int64_t nch = (d->seqlen + q - 1) / q;
   return sizeof(float) * (size_t)(d->batch * d->nheads) * (size_t)(nch + 1) * (size_t)(d->dstate * d->headdim);
 }
 

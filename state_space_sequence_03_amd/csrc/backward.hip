@@ -28,25 +28,24 @@
 //     H' at every chunk start (and the final one) in the workspace;
 //  2. bwd_chunk_kernel walks the chunks backward with dH' in registers.
 // Every product above is a fp32 MFMA (16x16x4) over fp32 tiles in LDS, so
-// the gradients carry fp32 rounding only; the chunk is 16 tokens, V <= 64,
-// and N, P <= 64.
+// the gradients carry fp32 rounding only; the chunk is 16 tokens (8 when N
+// or P is 128 and R = 4, to fit LDS), V <= 64, N, P <= 128, not both 128.
 #include "m3_common.hpp"
 #include "m3_launch.hpp"
 
 namespace m3 {
 
 bool bwd_supported(int N, int P, int R) {
-  const bool np = (N == 16 || N == 32 || N == 64) && (P == 16 || P == 32 || P == 64);
-  return np && (R == 1 || R == 2 || R == 4);
+  const bool n = N == 16 || N == 32 || N == 64 || N == 128, p = P == 16 || P == 32 || P == 64 || P == 128;
+  return n && p && !(N == 128 && P == 128) && (R == 1 || R == 2 || R == 4);
 }
 
 namespace {
 
-constexpr int QB = BWD_CHUNK;
-
 // Shapes of one (N, P, R) instance
 template <int N, int P, int R>
 struct BS {
+  static constexpr int QB = bwd_chunk_len(N, P, R);
   static constexpr int K = N / 2, V = QB * R;
   static constexpr int LDN = N + 4, LDP = P + 4, LDV = V + 4;  // fp32 row strides in LDS
   static constexpr int TN = N / 16, TP = P / 16, TV = V / 16;   // 16-wide tiles
@@ -121,7 +120,7 @@ struct RowVecs {
 template <typename T, int N, int P, int R>
 __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   typedef BS<N, P, R> S;
-  constexpr int K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP;
+  constexpr int QB = S::QB, K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP;
   constexpr int NW = 4, TH = 64 * NW, NPW = (S::NPT + NW - 1) / NW;
   const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
@@ -276,7 +275,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
 template <typename T, int N, int P, int R>
 __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   typedef BS<N, P, R> S;
-  constexpr int K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP, LDV = S::LDV;
+  constexpr int QB = S::QB, K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP, LDV = S::LDV;
   constexpr int TV = S::TV, TN = S::TN, TP = S::TP;
   constexpr int NW = 8, TH = 64 * NW, NPW = (S::NPT + NW - 1) / NW;
   constexpr int VVW = (TV * TV + NW - 1) / NW, VNW = (TV * TN + NW - 1) / NW, VPW = (TV * TP + NW - 1) / NW;
@@ -758,6 +757,9 @@ static hipError_t bwd_p(int P, const BwdArgs& a, hipStream_t s) {
     case 16: return bwd_r<T, N, 16>(a, s);
     case 32: return bwd_r<T, N, 32>(a, s);
     case 64: return bwd_r<T, N, 64>(a, s);
+    case 128:
+      if constexpr (N < 128) return bwd_r<T, N, 128>(a, s);
+      else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -768,6 +770,7 @@ static hipError_t bwd_n(int N, int P, const BwdArgs& a, hipStream_t s) {
     case 16: return bwd_p<T, 16>(P, a, s);
     case 32: return bwd_p<T, 32>(P, a, s);
     case 64: return bwd_p<T, 64>(P, a, s);
+    case 128: return bwd_p<T, 128>(P, a, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -92,7 +92,9 @@ struct BwdArgs {
   int64_t batch, L, H;
   int R;
 };
-constexpr int BWD_CHUNK = 16;  // tokens per chunk of the backward walk
+// tokens per chunk of the backward walk: 16, or 8 when N or P is 128 and
+// R = 4 (so that the chunk's tiles fit LDS)
+constexpr int bwd_chunk_len(int N, int P, int R) { return ((N > 64 || P > 64) && R == 4) ? 8 : 16; }
 bool bwd_supported(int N, int P, int R);
 hipError_t launch_chunked_bwd(int io_bf16, int N, int P, const BwdArgs& a, hipStream_t s);
 

@@ -137,8 +137,9 @@ def test_backward_validation(L):
     d = dims(L)  # batch 2, L 100, H 3, P 64, N 64, R 4, bf16
     assert L.chunked_bwd_workspace_size(d) == 4 * 6 * ((100 + 15) // 16 + 1) * 64 * 64
     assert call_bwd(L, dims(L, dstate=15)) == L.M3_ERR_SHAPE
-    assert call_bwd(L, dims(L, headdim=128)) == L.M3_ERR_UNSUPPORTED   # the backward covers N, P <= 64
-    assert call_bwd(L, dims(L, dstate=128)) == L.M3_ERR_UNSUPPORTED
+    assert call_bwd(L, dims(L, headdim=128, dstate=128)) == L.M3_ERR_UNSUPPORTED   # not both 128
+    long = dims(L, batch=1, seqlen=100, nheads=2, dstate=128)                      # 8-token chunks at R = 4
+    assert L.chunked_bwd_workspace_size(long) == 4 * 2 * ((100 + 7) // 8 + 1) * 128 * 64
     assert call_bwd(L, dims(L, flags=1)) == L.M3_ERR_UNSUPPORTED
     assert call_bwd(L, d, dy=None) == L.M3_ERR_NULL
     assert call_bwd(L, d, dtheta=None) == L.M3_ERR_NULL

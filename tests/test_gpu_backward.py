@@ -86,6 +86,11 @@ BWD_CASES = [
     ("bf16", 2, 75, 2, 64, 64, 4, True, True, True),
     ("bf16", 1, 130, 2, 64, 64, 1, False, False, True),
     ("bf16", 1, 33, 3, 32, 64, 2, True, True, False),
+    # N or P = 128 (8-token chunks when R = 4): the long-context head shape among them
+    ("bf16", 1, 70, 2, 64, 128, 4, True, True, True),
+    ("f32", 1, 33, 2, 128, 32, 2, True, False, True),
+    ("f32", 1, 19, 1, 64, 128, 1, False, True, True),
+    ("f32", 2, 25, 1, 128, 64, 4, True, True, False),
 ]
 
 
@@ -120,9 +125,9 @@ def test_backward_workspace_and_rejections(ops):
     d = ops.make_dims(2, 100, 3, 64, 64, 4, 64, ops.M3_BF16)
     assert ops.chunked_bwd_workspace_size(d) == 4 * 6 * (7 + 1) * 64 * 64
     x = torch.zeros((1, 8, 1, 1, 128), device="cuda")
-    B = torch.zeros((1, 8, 1, 1, 16), device="cuda")
+    B = torch.zeros((1, 8, 1, 1, 128), device="cuda")
     s = torch.zeros((1, 8, 1), device="cuda")
-    th = torch.zeros((1, 8, 1, 8), device="cuda")
+    th = torch.zeros((1, 8, 1, 64), device="cuda")
     with pytest.raises(ops.Mamba3Error) as e:
-        ops.chunked_bwd(x, B, B, s, s, s, th, x)   # P = 128 is not covered by the backward
+        ops.chunked_bwd(x, B, B, s, s, s, th, x)   # N = P = 128 is not covered by the backward
     assert e.value.status == ops.M3_ERR_UNSUPPORTED
