@@ -364,7 +364,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the (b,h) slices of this "
-              "workload shard with no communication, see DESIGN.md", file=sys.stderr)
+              "workload shard over batch x heads with no communication", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -33,7 +33,7 @@
  *   y_t[r]     = Ct_t[r]^T ht_t
  *   h_final    = R(+phi_L) ht_L    (back to the un-rotated, "true" frame)
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *  - the token before the first one (prev_B, prev_x) sits at angle 0, i.e.
  *    in the starting frame; absent, it is zero;
  *  - h0 is given in the true frame, which equals the rotated frame at angle 0;
