@@ -310,29 +310,65 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // gradients wait for the trapezoid weight of the token before it
   float pend_ddt = 0.0f, pend_dlam = 0.0f;
 
-  for (int64_t c = nch - 1; c >= 0; --c) {
+  // Global inputs of a chunk are fetched into registers one chunk ahead, so
+  // that their latency overlaps the previous chunk's products.
+  constexpr int THP = (QB * K + TH - 1) / TH, HP = (N * P / 4 + TH - 1) / TH;
+  RowVecs<T, N, V, TH> rb, rc;
+  RowVecs<T, P, V, TH> rx, rdy;
+  float thv[THP];
+  float4 hv[HP];
+  TokScal tsv{0.0f, 0.0f, 0.0f, 0.0f};
+  auto fetch = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t a0 = c * QB;
-    // ---------------- staging ----------------
-    RowVecs<T, N, V, TH> rb, rc;
-    RowVecs<T, P, V, TH> rx, rdy;
     rb.load(a.B, tid, R, a0, L, tok_of);
     rc.load(a.C, tid, R, a0, L, tok_of);
     rx.load(a.x, tid, R, a0, L, tok_of);
     rdy.load(a.dy, tid, R, a0, L, tok_of);
-    for (int e = tid; e < QB * K; e += TH) {
-      const int t = e / K, k = e % K;
-      sTh[t][k] = a0 + t < L ? a.theta[tok_of(a0 + t) * K + k] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < THP; ++q) {
+      const int e = tid + TH * q, t = e / K, k = e % K;
+      thv[q] = (e < QB * K && a0 + t < L) ? a.theta[tok_of(a0 + t) * K + k] : 0.0f;
     }
     if (tid < QB) {
       const int64_t t = a0 + tid;
-      TokScal ts{0.0f, 0.0f, 0.0f, 0.0f};
+      tsv = TokScal{0.0f, 0.0f, 0.0f, 0.0f};
       if (t < L) {
-        ts.d = a.dt[tok_of(t)];
-        ts.A = a.A[tok_of(t)];
-        ts.lam = a.lam[tok_of(t)];
-        if (t + 1 < L) ts.eps_next = (1.0f - a.lam[tok_of(t + 1)]) * a.dt[tok_of(t + 1)];
+        tsv.d = a.dt[tok_of(t)];
+        tsv.A = a.A[tok_of(t)];
+        tsv.lam = a.lam[tok_of(t)];
+        if (t + 1 < L) tsv.eps_next = (1.0f - a.lam[tok_of(t + 1)]) * a.dt[tok_of(t + 1)];
       }
-      sT[tid] = ts;
+    }
+#pragma unroll
+    for (int q = 0; q < HP; ++q) {
+      const int e = tid + TH * q;
+      if (e < N * P / 4) hv[q] = *(const float4*)(ck + c * (N * P) + 4 * e);
+    }
+  };
+  // H_out of the chunk (the carried state after it) in the layout of Gb: the
+  // stored final state for the last chunk, then the H_in of the chunk after
+  float ho[NPW][4];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const int ti = wave + NW * j;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ho[j][i] = ti < S::NPT ? ck[nch * (N * P) + ((ti / TP) * 16 + 4 * g + i) * P + (ti % TP) * 16 + m16] : 0.0f;
+  }
+  // dt and lam of the first token of the chunk processed last time
+  float pend_d = 0.0f, pend_l = 0.0f;
+  if (nch > 0) fetch(nch - 1);
+
+  for (int64_t c = nch - 1; c >= 0; --c) {
+    const int64_t a0 = c * QB;
+    // ---------------- staging (from the registers fetched ahead) ----------------
+#pragma unroll
+    for (int q = 0; q < THP; ++q) {
+      const int e = tid + TH * q;
+      if (e < QB * K) sTh[e / K][e % K] = thv[q];
+    }
+    if (tid < QB) {
+      sT[tid] = tsv;
       sDLam[tid] = 0.0f;
       sDq[tid] = 0.0f;
       sDgam[tid] = 0.0f;
@@ -343,10 +379,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
     for (int e = tid; e < K; e += TH) sDTheta[e] = 0.0f;
     if (tid == 0) sRed[0] = 0.0f;
-    for (int e = tid; e < N * P / 4; e += TH) {
-      const float4 hv = *(const float4*)(ck + c * (N * P) + 4 * e);
-      float* dst = &sH[((4 * e) / P) * LDP + (4 * e) % P];
-      dst[0] = hv.x; dst[1] = hv.y; dst[2] = hv.z; dst[3] = hv.w;
+#pragma unroll
+    for (int q = 0; q < HP; ++q) {
+      const int e = tid + TH * q;
+      if (e < N * P / 4) {
+        float* dst = &sH[((4 * e) / P) * LDP + (4 * e) % P];
+        dst[0] = hv[q].x; dst[1] = hv[q].y; dst[2] = hv[q].z; dst[3] = hv[q].w;
+      }
     }
     __syncthreads();
     if (tid < QB) {
@@ -419,7 +458,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             const float z0 = cs.x * g0 + cs.y * g1, z1 = cs.x * g1 - cs.y * g0;
             sDZ[n0 * LDP + p] = z0;
             sDZ[(n0 + 1) * LDP + p] = z1;
-            const float o0 = ck[(c + 1) * (N * P) + n0 * P + p], o1 = ck[(c + 1) * (N * P) + (n0 + 1) * P + p];
+            const float o0 = ho[j][2 * q], o1 = ho[j][2 * q + 1];
             float dth = -g0 * o1 + g1 * o0;
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) dth += __shfl_xor(dth, o, 64);
@@ -434,6 +473,18 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
       if (lane == 0) atomicAdd(&sRed[0], part);
+    }
+    if (c > 0) {
+      // this chunk's H_in is the H_out of the chunk processed next
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        const int ti = wave + NW * j;
+        if (ti < S::NPT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ho[j][i] = sH[((ti / TP) * 16 + 4 * g + i) * LDP + (ti % TP) * 16 + m16];
+        }
+      }
+      fetch(c - 1);
     }
     __syncthreads();
 
@@ -656,12 +707,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         if (c + 1 < nch) {
           const float de_next = sDq[QB - 1];
           const int64_t tn = tok_of(a0 + QB);
-          const float dn = a.dt[tn], ln = a.lam[tn];
-          a.ddt[tn] = pend_ddt + (1.0f - ln) * de_next;
-          a.dlam[tn] = pend_dlam - dn * de_next;
+          a.ddt[tn] = pend_ddt + (1.0f - pend_l) * de_next;
+          a.dlam[tn] = pend_dlam - pend_d * de_next;
         }
         pend_ddt = ddt;
         pend_dlam = dlam;
+        pend_d = ts.d;
+        pend_l = ts.lam;
       }
     }
     __syncthreads();  // LDS reads of this chunk done before the next staging
