@@ -223,14 +223,15 @@ FP32_MFMA_TFLOPS = 157.3
 
 
 def backward_flops_per_token_head(w):
-    """Dense fp32 MFMA flops of the backward per token-head: per 16-token
-    chunk (V = 16 R rows) the checkpoint walk's state product W^T X and the
-    reverse walk's nine products (G, dGM, two for dX, two for dC~, two for dB~
-    and dH_in), each 2 M N K."""
+    """Dense MFMA flops of the backward per token-head, as (fp32, bf16): per
+    16-token chunk (V = 16 R rows) the checkpoint walk's state product W^T X
+    (fp32 operands) and the reverse walk's nine products (G, dGM, two for dX,
+    two for dC~, two for dB~ and dH_in; bf16 operands for bf16 io), each 2 M N K."""
     V, N, P = BWD_CHUNK * w.rank, w.dstate, w.headdim
-    per_chunk = 2 * (N * P * V) + 2 * (V * V * N + V * V * P + V * P * V + V * P * N + V * N * V + V * N * P
-                                       + V * N * V + V * N * P + N * P * V)
-    return per_chunk / BWD_CHUNK
+    ckpt = 2 * (N * P * V)
+    walk = 2 * (V * V * N + V * V * P + V * P * V + V * P * N + V * N * V + V * N * P + V * N * V + V * N * P
+                + N * P * V)
+    return ckpt / BWD_CHUNK, walk / BWD_CHUNK
 
 
 def backward_bytes_per_token_head(w, s_io=2):
@@ -257,12 +258,16 @@ def bench_backward(ops, inputs, w, steps, warmup, torch):
                                  want_dh0=False, workspace=ws)
     wall, ev = timed(fn, steps, warmup, torch)
     th = w.batch * w.seqlen * w.nheads
-    flops = th * backward_flops_per_token_head(w)
+    f32_fl, bf_fl = (th * f for f in backward_flops_per_token_head(w))
+    flops = f32_fl + bf_fl
     bytes_ = th * backward_bytes_per_token_head(w)
+    # time floors: the products at the dense MFMA peaks of their operand types, the bytes at the HBM peak
+    mfma_floor_ms = (f32_fl / (FP32_MFMA_TFLOPS * 1e12) + bf_fl / (BF16_DENSE_TFLOPS * 1e12)) * 1e3
+    hbm_floor_ms = bytes_ / (HBM_PEAK_GBPS * 1e9) * 1e3
     del d, dy, ws
     torch.cuda.empty_cache()
     return dict(ms=ev, tokens_per_s=w.tokens / (ev * 1e-3), tflops=flops / (ev * 1e-3) / 1e12, flops=flops,
-                gbps=bytes_ / (ev * 1e-3) / 1e9, bytes=bytes_)
+                gbps=bytes_ / (ev * 1e-3) / 1e9, bytes=bytes_, mfma_floor_ms=mfma_floor_ms, hbm_floor_ms=hbm_floor_ms)
 
 
 def bench_rope(ops, inputs, w, steps, warmup, torch):
@@ -440,12 +445,15 @@ def main():
                           "chunk_walk_ms_per_call": round(vf["chunk_walk_ms"], 5)}
     if "backward" in out:
         bw = out["backward"]
-        line["backward"] = {"workload": f"{w.name} backward (mamba3_ssm_chunked_bwd, dy ~ N(0,1), fp32 products)",
+        line["backward"] = {"workload": f"{w.name} backward (mamba3_ssm_chunked_bwd, dy ~ N(0,1); bf16 operands "
+                                        f"in the reverse walk's products, fp32 in the checkpoint walk)",
                             "ms": round(bw["ms"], 4), "tokens_per_s": round(bw["tokens_per_s"], 1),
-                            "bound": "mfma", "achieved_TFLOPs": round(bw["tflops"], 1),
-                            "peak_TFLOPs": FP32_MFMA_TFLOPS, "frac": round(bw["tflops"] / FP32_MFMA_TFLOPS, 4),
-                            "flops_per_call": bw["flops"], "achieved_GBps": round(bw["gbps"], 1),
-                            "bytes_per_call": round(bw["bytes"])}
+                            "bound": "hbm" if bw["hbm_floor_ms"] >= bw["mfma_floor_ms"] else "mfma",
+                            "achieved_GBps": round(bw["gbps"], 1), "peak_GBps": HBM_PEAK_GBPS,
+                            "frac": round(max(bw["hbm_floor_ms"], bw["mfma_floor_ms"]) / bw["ms"], 4),
+                            "bytes_per_call": round(bw["bytes"]), "achieved_TFLOPs": round(bw["tflops"], 1),
+                            "flops_per_call": bw["flops"], "hbm_floor_ms": round(bw["hbm_floor_ms"], 4),
+                            "mfma_floor_ms": round(bw["mfma_floor_ms"], 4)}
     if "rope" in out:
         line["rope_bc"] = {"ms": round(out["rope"]["ms"], 4), "achieved_GBps": round(out["rope"]["gbps"], 1),
                            "frac": round(out["rope"]["gbps"] / HBM_PEAK_GBPS, 4)}

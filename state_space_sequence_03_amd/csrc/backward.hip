@@ -27,9 +27,13 @@
 //  1. bwd_ckpt_kernel walks the chunks forward and stores the carried state
 //     H' at every chunk start (and the final one) in the workspace;
 //  2. bwd_chunk_kernel walks the chunks backward with dH' in registers.
-// Every product above is a fp32 MFMA (16x16x4) over fp32 tiles in LDS, so
-// the gradients carry fp32 rounding only; the chunk is 16 tokens (8 when N
-// or P is 128 and R = 4, to fit LDS), V <= 64, N, P <= 128, not both 128.
+// The products read fp32 tiles in LDS. For fp32 io they are fp32 MFMAs
+// (16x16x4), so those gradients carry fp32 rounding only; for bf16 io the
+// reverse walk rounds both operands of each product to bf16 and uses the bf16
+// MFMA (16x16x32) with fp32 accumulation, the precision the forward's products
+// have (the checkpoint walk stays fp32: its states accumulate over the whole
+// sequence). The chunk is 16 tokens (8 when N or P is 128 and R = 4, to fit
+// LDS), V <= 64, N, P <= 128, not both 128.
 #include "m3_common.hpp"
 #include "m3_launch.hpp"
 
@@ -52,14 +56,58 @@ struct BS {
   static constexpr int NPT = TN * TP;                           // tiles of an N x P matrix
 };
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
 // acc[j] += A(tr*16 + m16, k) B(k, tc*16 + m16) over k < KD for the wave's
-// tiles j of a TM x TN grid (tile ti = wave + NW j, tr = ti / TNC, tc = ti % TNC)
-// The k loop is outside the tile loop, so the wave's tiles form independent
-// MFMA chains that are issued interleaved.
-template <int NW, int TM, int TNC, int KD, typename FA, typename FB>
+// tiles j of a TM x TN grid (tile ti = wave + NW j, tr = ti / TNC, tc = ti % TNC).
+// BF = false: fp32 MFMA 16x16x4, the k loop outside the tile loop, so the
+// wave's tiles form independent MFMA chains that are issued interleaved.
+// BF = true: the fp32 operands are rounded to bf16 (nearest even) and
+// multiplied with the bf16 MFMA 16x16x32 (16x16x16 for a last k block of 16),
+// fp32 accumulation; lane group g takes the k range [8g, 8g + 8) of each
+// 32-wide block in both operands.
+template <bool BF, int NW, int TM, int TNC, int KD, typename FA, typename FB>
 __device__ __forceinline__ void mm(FA fa, FB fb, f32x4* acc, int wave, int m16, int g) {
   constexpr int NT = TM * TNC, TPW = (NT + NW - 1) / NW;
-  if constexpr (NT % NW == 0) {
+  if constexpr (BF) {
+    static_assert(KD % 16 == 0, "k in steps of 16");
+    constexpr int K32 = KD / 32 * 32;
+#pragma unroll 1
+    for (int k0 = 0; k0 < K32; k0 += 32) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const int ti = wave + NW * j;
+        if (NT % NW == 0 || ti < NT) {
+          const int tr = ti / TNC, tc = ti % TNC, kk = k0 + 8 * g;
+          f32x8 av, bv;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            av[e] = fa(tr * 16 + m16, kk + e);
+            bv[e] = fb(kk + e, tc * 16 + m16);
+          }
+          acc[j] = mfma_bf16(__builtin_convertvector(av, bf16x8), __builtin_convertvector(bv, bf16x8), acc[j]);
+        }
+      }
+    }
+    if constexpr (KD % 32 == 16) {
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const int ti = wave + NW * j;
+        if (NT % NW == 0 || ti < NT) {
+          const int tr = ti / TNC, tc = ti % TNC, kk = K32 + 4 * g;
+          f32x4 av, bv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            av[e] = fa(tr * 16 + m16, kk + e);
+            bv[e] = fb(kk + e, tc * 16 + m16);
+          }
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_convertvector(av, bf16x4),
+                                                               __builtin_convertvector(bv, bf16x4), acc[j], 0, 0, 0);
+        }
+      }
+    }
+  } else if constexpr (NT % NW == 0) {
 #pragma unroll 2
     for (int k0 = 0; k0 < KD; k0 += 4) {
 #pragma unroll
@@ -169,28 +217,44 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     }
   };
 
-  for (int64_t c = 0; c < nch; ++c) {
+  // the inputs of a chunk are fetched into registers one chunk ahead
+  constexpr int OMP = (QB * K + TH - 1) / TH;
+  RowVecs<T, N, V, TH> rb;
+  RowVecs<T, P, V, TH> rx;
+  float omv[OMP];
+  TokScal tsv{0.0f, 0.0f, 0.0f, 0.0f};
+  auto fetch = [&](int64_t c) __attribute__((always_inline)) {
     const int64_t a0 = c * QB;
-    store_state(c);
-    RowVecs<T, N, V, TH> rb;
-    RowVecs<T, P, V, TH> rx;
     rb.load(a.B, tid, R, a0, L, tok_of);
     rx.load(a.x, tid, R, a0, L, tok_of);
     if (tid < QB) {
       const int64_t t = a0 + tid;
-      TokScal ts{0.0f, 0.0f, 0.0f, 0.0f};
+      tsv = TokScal{0.0f, 0.0f, 0.0f, 0.0f};
       if (t < L) {
-        ts.d = a.dt[tok_of(t)];
-        ts.A = a.A[tok_of(t)];
-        ts.lam = a.lam[tok_of(t)];
-        if (t + 1 < L) ts.eps_next = (1.0f - a.lam[tok_of(t + 1)]) * a.dt[tok_of(t + 1)];
+        tsv.d = a.dt[tok_of(t)];
+        tsv.A = a.A[tok_of(t)];
+        tsv.lam = a.lam[tok_of(t)];
+        if (t + 1 < L) tsv.eps_next = (1.0f - a.lam[tok_of(t + 1)]) * a.dt[tok_of(t + 1)];
       }
-      sT[tid] = ts;
-      sDA[tid] = ts.d * ts.A;
     }
-    for (int e = tid; e < QB * K; e += TH) {
-      const int t = e / K, k = e % K;
-      sOm[t][k] = a0 + t < L ? a.dt[tok_of(a0 + t)] * a.theta[tok_of(a0 + t) * K + k] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < OMP; ++q) {
+      const int e = tid + TH * q, t = e / K, k = e % K;
+      omv[q] = (e < QB * K && a0 + t < L) ? a.dt[tok_of(a0 + t)] * a.theta[tok_of(a0 + t) * K + k] : 0.0f;
+    }
+  };
+  if (nch > 0) fetch(0);
+
+  for (int64_t c = 0; c < nch; ++c) {
+    store_state(c);
+    if (tid < QB) {
+      sT[tid] = tsv;
+      sDA[tid] = tsv.d * tsv.A;
+    }
+#pragma unroll
+    for (int q = 0; q < OMP; ++q) {
+      const int e = tid + TH * q;
+      if (e < QB * K) sOm[e / K][e % K] = omv[q];
     }
     __syncthreads();
     if (tid < QB) {
@@ -240,12 +304,13 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
         }
       }
     }
+    if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
     // S = W^T X, then H' <- R(Theta) (e^{Lam_end} H' + S)
     f32x4 sacc[NPW];
 #pragma unroll
     for (int j = 0; j < NPW; ++j) sacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    mm<NW, S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; }, [&](int v, int p) { return sX[v * LDP + p]; },
+    mm<false, NW, S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; }, [&](int v, int p) { return sX[v * LDP + p]; },
                         sacc, wave, m16, g);
     const float eQ = __expf(lamQ);
 #pragma unroll
@@ -278,6 +343,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   constexpr int QB = S::QB, K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP, LDV = S::LDV;
   constexpr int TV = S::TV, TN = S::TN, TP = S::TP;
   constexpr int NW = 8, TH = 64 * NW, NPW = (S::NPT + NW - 1) / NW;
+  // bf16 io: products with bf16 operands (the gradients are rounded to bf16
+  // anyway); fp32 io: fp32 products
+  constexpr bool BFO = sizeof(T) == 2;
   constexpr int VVW = (TV * TV + NW - 1) / NW, VNW = (TV * TN + NW - 1) / NW, VPW = (TV * TP + NW - 1) / NW;
   const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
@@ -493,9 +561,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       f32x4 gacc[VVW], dacc[VVW];
 #pragma unroll
       for (int j = 0; j < VVW; ++j) gacc[j] = dacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<NW, TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
+      mm<BFO, NW, TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
                     gacc, wave, m16, g);
-      mm<NW, TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
+      mm<BFO, NW, TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
                     dacc, wave, m16, g);
 #pragma unroll
       for (int j = 0; j < VVW; ++j) {
@@ -535,9 +603,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       f32x4 xacc[VPW];
 #pragma unroll
       for (int j = 0; j < VPW; ++j) xacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<NW, TV, TP, V>([&](int vr, int vk) { return sGM[vk * LDV + vr]; }, [&](int vk, int p) { return sDY[vk * LDP + p]; },
+      mm<BFO, NW, TV, TP, V>([&](int vr, int vk) { return sGM[vk * LDV + vr]; }, [&](int vk, int p) { return sDY[vk * LDP + p]; },
                     xacc, wave, m16, g);
-      mm<NW, TV, TP, N>([&](int v, int n) { return sW[v / R] * sB[v * LDN + n]; }, [&](int n, int p) { return sDZ[n * LDP + p]; },
+      mm<BFO, NW, TV, TP, N>([&](int v, int n) { return sW[v / R] * sB[v * LDN + n]; }, [&](int n, int p) { return sDZ[n * LDP + p]; },
                     xacc, wave, m16, g);
 #pragma unroll
       for (int j = 0; j < VPW; ++j) {
@@ -557,13 +625,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       f32x4 cacc[VNW], eacc[VNW], bacc[VNW], facc[VNW];
 #pragma unroll
       for (int j = 0; j < VNW; ++j) cacc[j] = eacc[j] = bacc[j] = facc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<NW, TV, TN, V>([&](int vr, int vk) { return sDG[vr * LDV + vk]; }, [&](int vk, int n) { return sB[vk * LDN + n]; },
+      mm<BFO, NW, TV, TN, V>([&](int vr, int vk) { return sDG[vr * LDV + vk]; }, [&](int vk, int n) { return sB[vk * LDN + n]; },
                     cacc, wave, m16, g);
-      mm<NW, TV, TN, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int n) { return sH[n * LDP + p]; },
+      mm<BFO, NW, TV, TN, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int n) { return sH[n * LDP + p]; },
                     eacc, wave, m16, g);
-      mm<NW, TV, TN, V>([&](int vr, int vk) { return sDG[vk * LDV + vr]; }, [&](int vk, int n) { return sC[vk * LDN + n]; },
+      mm<BFO, NW, TV, TN, V>([&](int vr, int vk) { return sDG[vk * LDV + vr]; }, [&](int vk, int n) { return sC[vk * LDN + n]; },
                     bacc, wave, m16, g);
-      mm<NW, TV, TN, P>([&](int v, int p) { return sX[v * LDP + p]; }, [&](int p, int n) { return sDZ[n * LDP + p]; },
+      mm<BFO, NW, TV, TN, P>([&](int v, int p) { return sX[v * LDP + p]; }, [&](int p, int n) { return sDZ[n * LDP + p]; },
                     facc, wave, m16, g);
 #pragma unroll
       for (int j = 0; j < VNW; ++j) {
@@ -630,7 +698,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
     {
       // dH_in += C~^T (e^{Lam} dY)
-      mm<NW, TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; }, [&](int v, int p) { return sEL[v / R] * sDY[v * LDP + p]; },
+      mm<BFO, NW, TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; }, [&](int v, int p) { return sEL[v / R] * sDY[v * LDP + p]; },
                     Gb, wave, m16, g);
     }
     __syncthreads();
