@@ -215,6 +215,7 @@ m3_status mamba3_ssm_chunked_bwd(const m3_dims* d, const void* x, const void* B,
   if (st != M3_OK) return st;
   if (d->flags != 0) return M3_ERR_UNSUPPORTED;
   if (!m3::bwd_supported((int)d->dstate, (int)d->headdim, (int)d->rank)) return M3_ERR_UNSUPPORTED;
+  if (d->nheads > 65536) return M3_ERR_UNSUPPORTED;  // 32-bit offsets inside a chunk
   const bool empty = d->batch == 0 || d->nheads == 0;
   const bool has_tokens = !empty && d->seqlen > 0;
   if ((prev_B == nullptr) != (prev_x == nullptr) || (dprev_B == nullptr) != (dprev_x == nullptr)) return M3_ERR_NULL;

@@ -140,24 +140,40 @@ __device__ __forceinline__ float ld_io(const void* p, int64_t i) {
   return io<T>::load1(p, i);
 }
 
+// An empty asm makes a per-thread offset look new at every use, so that the
+// compiler adds it to the block-uniform base (scalar-base addressing with a
+// 32-bit offset) instead of hoisting a 64-bit per-thread address out of the
+// chunk loop, where it would occupy (or spill) vector register pairs.
+__device__ __forceinline__ void fresh(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
 // Raw rows of a chunk held in registers: item e of a thread covers row
 // v = e / (W / VEC) (token v / R, rank v % R) and the VEC elements from
-// column (e % (W / VEC)) VEC of a row W elements wide; tokens past L read as 0.
+// column (e % (W / VEC)) VEC of a row W elements wide. `base` points at the
+// chunk's first token (block-uniform), tokens are `tstride` elements apart
+// (32-bit offsets), and tokens from `nvalid` on (past L) read as 0.
 template <typename T, int W, int V, int TH>
 struct RowVecs {
   static constexpr int VEC = io<T>::VEC, PERROW = W / VEC, ITEMS = V * PERROW;
   static constexpr int PER = (ITEMS + TH - 1) / TH;
   typename io<T>::vec r[PER];
-  template <typename TokOf>
-  __device__ __forceinline__ void load(const void* base, int tid, int R, int64_t a0, int64_t L, TokOf tok_of) {
+  __device__ __forceinline__ void load(const void* base, int tid, int R, uint32_t tstride, int nvalid) {
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int e = tid + TH * q;
       const int v = e / PERROW, c = e % PERROW, t = v / R;
-      if (e < ITEMS && a0 + t < L) r[q] = ldg16<T>(base, (tok_of(a0 + t) * R + v % R) * W + c * VEC);
+      uint32_t off = (uint32_t)t * tstride + (uint32_t)((v % R) * W + c * VEC);
+      fresh(off);
+      if (e < ITEMS && t < nvalid) r[q] = *(const typename io<T>::vec*)((const char*)base + off * io<T>::BYTES);
       else r[q] = typename io<T>::vec{};
     }
   }
+};
+
+// Scalars of a token and of the one after it as loaded (dn = ln = 0 past L);
+// the trapezoid weight of the next token is formed when the chunk is staged.
+struct TokRaw {
+  float d, A, lam, dn, ln;
+  __device__ __forceinline__ TokScal scal() const { return TokScal{d, A, lam, (1.0f - ln) * dn}; }
 };
 
 }  // namespace
@@ -174,6 +190,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
   auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
+  const uint32_t Hu = (uint32_t)a.H;
 
   __shared__ float sW[V * LDN], sX[V * LDP];
   __shared__ float2 sCS[QB][K];
@@ -217,30 +234,42 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     }
   };
 
-  // the inputs of a chunk are fetched into registers one chunk ahead
+  // The inputs of a chunk are fetched into registers one chunk ahead, as
+  // loaded: nothing consumes them before the chunk is staged, so their
+  // latency overlaps the current chunk's work.
   constexpr int OMP = (QB * K + TH - 1) / TH;
   RowVecs<T, N, V, TH> rb;
   RowVecs<T, P, V, TH> rx;
-  float omv[OMP];
-  TokScal tsv{0.0f, 0.0f, 0.0f, 0.0f};
+  float omd[OMP], omt[OMP];
+  TokRaw tsv{0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   auto fetch = [&](int64_t c) __attribute__((always_inline)) {
-    const int64_t a0 = c * QB;
-    rb.load(a.B, tid, R, a0, L, tok_of);
-    rx.load(a.x, tid, R, a0, L, tok_of);
+    const int64_t a0 = c * QB, t0 = tok_of(a0);
+    const int nv = (int)(L - a0 < QB ? L - a0 : QB), nv1 = (int)(L - a0 < QB + 1 ? L - a0 : QB + 1);
+    rb.load((const char*)a.B + t0 * (R * N * io<T>::BYTES), tid, R, Hu * (R * N), nv);
+    rx.load((const char*)a.x + t0 * (R * P * io<T>::BYTES), tid, R, Hu * (R * P), nv);
     if (tid < QB) {
-      const int64_t t = a0 + tid;
-      tsv = TokScal{0.0f, 0.0f, 0.0f, 0.0f};
-      if (t < L) {
-        tsv.d = a.dt[tok_of(t)];
-        tsv.A = a.A[tok_of(t)];
-        tsv.lam = a.lam[tok_of(t)];
-        if (t + 1 < L) tsv.eps_next = (1.0f - a.lam[tok_of(t + 1)]) * a.dt[tok_of(t + 1)];
+      tsv = TokRaw{0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      uint32_t o = (uint32_t)tid * Hu;
+      fresh(o);
+      if (tid < nv) {
+        tsv.d = (a.dt + t0)[o];
+        tsv.A = (a.A + t0)[o];
+        tsv.lam = (a.lam + t0)[o];
+        if (tid + 1 < nv1) {
+          tsv.dn = (a.dt + t0)[o + Hu];
+          tsv.ln = (a.lam + t0)[o + Hu];
+        }
       }
     }
 #pragma unroll
     for (int q = 0; q < OMP; ++q) {
       const int e = tid + TH * q, t = e / K, k = e % K;
-      omv[q] = (e < QB * K && a0 + t < L) ? a.dt[tok_of(a0 + t)] * a.theta[tok_of(a0 + t) * K + k] : 0.0f;
+      const bool ok = e < QB * K && t < nv;
+      uint32_t od = (uint32_t)t * Hu, ot = od * K + k;
+      fresh(od);
+      fresh(ot);
+      omd[q] = ok ? (a.dt + t0)[od] : 0.0f;
+      omt[q] = ok ? (a.theta + t0 * K)[ot] : 0.0f;
     }
   };
   if (nch > 0) fetch(0);
@@ -248,13 +277,13 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   for (int64_t c = 0; c < nch; ++c) {
     store_state(c);
     if (tid < QB) {
-      sT[tid] = tsv;
+      sT[tid] = tsv.scal();
       sDA[tid] = tsv.d * tsv.A;
     }
 #pragma unroll
     for (int q = 0; q < OMP; ++q) {
       const int e = tid + TH * q;
-      if (e < QB * K) sOm[e / K][e % K] = omv[q];
+      if (e < QB * K) sOm[e / K][e % K] = omd[q] * omt[q];
     }
     __syncthreads();
     if (tid < QB) {
@@ -351,6 +380,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
   auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
+  const uint32_t Hu = (uint32_t)a.H;
 
   __shared__ float sX[V * LDP], sDY[V * LDP], sB[V * LDN], sC[V * LDN];
   __shared__ float sH[N * LDP], sDZ[N * LDP], sGM[V * LDV], sDG[V * LDV];
@@ -385,32 +415,41 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   RowVecs<T, P, V, TH> rx, rdy;
   float thv[THP];
   float4 hv[HP];
-  TokScal tsv{0.0f, 0.0f, 0.0f, 0.0f};
+  TokRaw tsv{0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   auto fetch = [&](int64_t c) __attribute__((always_inline)) {
-    const int64_t a0 = c * QB;
-    rb.load(a.B, tid, R, a0, L, tok_of);
-    rc.load(a.C, tid, R, a0, L, tok_of);
-    rx.load(a.x, tid, R, a0, L, tok_of);
-    rdy.load(a.dy, tid, R, a0, L, tok_of);
+    const int64_t a0 = c * QB, t0 = tok_of(a0);
+    const int nv = (int)(L - a0 < QB ? L - a0 : QB), nv1 = (int)(L - a0 < QB + 1 ? L - a0 : QB + 1);
+    rb.load((const char*)a.B + t0 * (R * N * io<T>::BYTES), tid, R, Hu * (R * N), nv);
+    rc.load((const char*)a.C + t0 * (R * N * io<T>::BYTES), tid, R, Hu * (R * N), nv);
+    rx.load((const char*)a.x + t0 * (R * P * io<T>::BYTES), tid, R, Hu * (R * P), nv);
+    rdy.load((const char*)a.dy + t0 * (R * P * io<T>::BYTES), tid, R, Hu * (R * P), nv);
 #pragma unroll
     for (int q = 0; q < THP; ++q) {
       const int e = tid + TH * q, t = e / K, k = e % K;
-      thv[q] = (e < QB * K && a0 + t < L) ? a.theta[tok_of(a0 + t) * K + k] : 0.0f;
+      uint32_t ot = (uint32_t)t * Hu * K + k;
+      fresh(ot);
+      thv[q] = (e < QB * K && t < nv) ? (a.theta + t0 * K)[ot] : 0.0f;
     }
     if (tid < QB) {
-      const int64_t t = a0 + tid;
-      tsv = TokScal{0.0f, 0.0f, 0.0f, 0.0f};
-      if (t < L) {
-        tsv.d = a.dt[tok_of(t)];
-        tsv.A = a.A[tok_of(t)];
-        tsv.lam = a.lam[tok_of(t)];
-        if (t + 1 < L) tsv.eps_next = (1.0f - a.lam[tok_of(t + 1)]) * a.dt[tok_of(t + 1)];
+      tsv = TokRaw{0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      uint32_t o = (uint32_t)tid * Hu;
+      fresh(o);
+      if (tid < nv) {
+        tsv.d = (a.dt + t0)[o];
+        tsv.A = (a.A + t0)[o];
+        tsv.lam = (a.lam + t0)[o];
+        if (tid + 1 < nv1) {
+          tsv.dn = (a.dt + t0)[o + Hu];
+          tsv.ln = (a.lam + t0)[o + Hu];
+        }
       }
     }
 #pragma unroll
     for (int q = 0; q < HP; ++q) {
       const int e = tid + TH * q;
-      if (e < N * P / 4) hv[q] = *(const float4*)(ck + c * (N * P) + 4 * e);
+      uint32_t o = 4 * e;
+      fresh(o);
+      if (e < N * P / 4) hv[q] = *(const float4*)(ck + c * (N * P) + o);
     }
   };
   // H_out of the chunk (the carried state after it) in the layout of Gb: the
@@ -428,7 +467,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   if (nch > 0) fetch(nch - 1);
 
   for (int64_t c = nch - 1; c >= 0; --c) {
-    const int64_t a0 = c * QB;
+    const int64_t a0 = c * QB, t0c = tok_of(a0);  // block-uniform
+    // the chunk's outputs: uniform bases at its first token, 32-bit offsets
+    void* const odx = (char*)a.dx + t0c * (R * P * io<T>::BYTES);
+    void* const odB = (char*)a.dB + t0c * (R * N * io<T>::BYTES);
+    void* const odC = (char*)a.dC + t0c * (R * N * io<T>::BYTES);
     // ---------------- staging (from the registers fetched ahead) ----------------
 #pragma unroll
     for (int q = 0; q < THP; ++q) {
@@ -436,7 +479,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       if (e < QB * K) sTh[e / K][e % K] = thv[q];
     }
     if (tid < QB) {
-      sT[tid] = tsv;
+      sT[tid] = tsv.scal();
       sDLam[tid] = 0.0f;
       sDq[tid] = 0.0f;
       sDgam[tid] = 0.0f;
@@ -615,7 +658,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int v = tr * 16 + 4 * g + i, t = v / R;
-            if (a0 + t < L) io<T>::store1(a.dx, (tok_of(a0 + t) * R + v % R) * P + p, xacc[j][i]);
+            uint32_t off = (uint32_t)t * Hu * (R * P) + (uint32_t)((v % R) * P + p);
+            fresh(off);
+            if (a0 + t < L) io<T>::store1(odx, off, xacc[j][i]);
           }
         }
       }
@@ -680,9 +725,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             const float gB = even ? (cs.x * dBt[i] - cs.y * dBo) : (cs.y * dBo + cs.x * dBt[i]);
             const float gC = even ? (cs.x * dCt[i] - cs.y * dCo) : (cs.y * dCo + cs.x * dCt[i]);
             if (a0 + t < L) {
-              const int64_t off = (tok_of(a0 + t) * R + v % R) * N + n;
-              io<T>::store1(a.dB, off, gB);
-              io<T>::store1(a.dC, off, gC);
+              uint32_t off = (uint32_t)t * Hu * (R * N) + (uint32_t)((v % R) * N + n);
+              fresh(off);
+              io<T>::store1(odB, off, gB);
+              io<T>::store1(odC, off, gC);
             }
           }
           // sum the ranks of each token (groups of R rows) into the token's angle adjoint
@@ -743,7 +789,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       const int t = e / K, k = e % K;
       float dom = sDTheta[k];
       for (int i = t; i < QB; ++i) dom += sDphi[i][k];
-      if (a0 + t < L) a.dtheta[tok_of(a0 + t) * K + k] = sT[t].d * dom;
+      uint32_t ot = (uint32_t)t * Hu * K + k;
+      fresh(ot);
+      if (a0 + t < L) (a.dtheta + t0c * K)[ot] = sT[t].d * dom;
       float v = sTh[t][k] * dom;  // the K pairs of a token are K consecutive lanes
 #pragma unroll
       for (int o = 1; o < K; o <<= 1) v += __shfl_xor(v, o, 64);
@@ -761,12 +809,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       float ddt = ts.A * dda + ts.lam * dgam + (1.0f - ts.lam) * deps;
       float dlam = ts.d * dgam - ts.d * deps;
       ddt += sThDot[t];  // theta_t . d omega_t
-      const int64_t tk = a0 + t < L ? tok_of(a0 + t) : 0;
+      uint32_t tk = (uint32_t)t * Hu;
+      fresh(tk);
       if (a0 + t < L) {
-        a.dA[tk] = ts.d * dda;
+        (a.dA + t0c)[tk] = ts.d * dda;
         if (t > 0) {
-          a.ddt[tk] = ddt;
-          a.dlam[tk] = dlam;
+          (a.ddt + t0c)[tk] = ddt;
+          (a.dlam + t0c)[tk] = dlam;
         }
       }
       if (t == 0) {
@@ -774,9 +823,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         // this chunk's last token, whose q carries its eps), then hold this one
         if (c + 1 < nch) {
           const float de_next = sDq[QB - 1];
-          const int64_t tn = tok_of(a0 + QB);
-          a.ddt[tn] = pend_ddt + (1.0f - pend_l) * de_next;
-          a.dlam[tn] = pend_dlam - pend_d * de_next;
+          const uint32_t tn = (uint32_t)QB * Hu;
+          (a.ddt + t0c)[tn] = pend_ddt + (1.0f - pend_l) * de_next;
+          (a.dlam + t0c)[tn] = pend_dlam - pend_d * de_next;
         }
         pend_ddt = ddt;
         pend_dlam = dlam;

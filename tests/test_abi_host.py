@@ -141,6 +141,7 @@ def test_backward_validation(L):
     long = dims(L, batch=1, seqlen=100, nheads=2, dstate=128)                      # 8-token chunks at R = 4
     assert L.chunked_bwd_workspace_size(long) == 4 * 2 * ((100 + 7) // 8 + 1) * 128 * 64
     assert call_bwd(L, dims(L, flags=1)) == L.M3_ERR_UNSUPPORTED
+    assert call_bwd(L, dims(L, batch=1, seqlen=16, nheads=65537)) == L.M3_ERR_UNSUPPORTED  # 32-bit chunk offsets
     assert call_bwd(L, d, dy=None) == L.M3_ERR_NULL
     assert call_bwd(L, d, dtheta=None) == L.M3_ERR_NULL
     assert call_bwd(L, d, prev_B=ctypes.c_void_p(FAKE)) == L.M3_ERR_NULL          # prev_x missing
