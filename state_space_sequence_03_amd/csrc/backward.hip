@@ -288,16 +288,21 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     __syncthreads();
     if (tid < QB) {
       float lam_c = 0.0f;
-      for (int j = 0; j <= tid; ++j) lam_c += sDA[j];
+#pragma unroll
+      for (int j = 0; j < QB; ++j) lam_c += j <= tid ? sDA[j] : 0.0f;  // all reads issued at once
       sLam[tid] = lam_c;
       sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
     }
     for (int e = tid; e < QB * K; e += TH) {
       const int t = e / K, k = e % K;
       float ph = 0.0f;
-      for (int j = 0; j <= t; ++j) ph += sOm[j][k];
+#pragma unroll
+      for (int j = 0; j < QB; ++j) ph += j <= t ? sOm[j][k] : 0.0f;
       float sn, cs;
-      sincosf(ph, &sn, &cs);
+      // the chunk-local angle: the hardware sine/cosine (in revolutions) for
+      // bf16 io, the full-precision library routine for fp32 io
+      if constexpr (sizeof(T) == 2) sincos_rev(ph, &sn, &cs);
+      else sincosf(ph, &sn, &cs);
       sCS[t][k] = make_float2(cs, sn);
     }
     __syncthreads();
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
   __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K], sTh[QB][K], sThDot[QB];
-  __shared__ float sDLam[QB], sDq[QB], sDgam[QB], sDe[V], sDw[V], sDlq[QB], sRed[1];
+  __shared__ float sDLam[QB], sDq[QB], sDgam[QB], sDe[V], sDw[V], sRed[1];
 
   const float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
   // dH' (adjoint of the carried state) in the accumulator layout of an N x P matrix
@@ -468,6 +473,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 
   for (int64_t c = nch - 1; c >= 0; --c) {
     const int64_t a0 = c * QB, t0c = tok_of(a0);  // block-uniform
+    // The lane coordinates are made opaque once per chunk: the compiler then
+    // computes LDS addresses next to their uses instead of hoisting dozens of
+    // them out of the loop into registers (where they spill).
+    uint32_t tid_f = tid;
+    fresh(tid_f);
+    {
+    const int tid = (int)tid_f, lane = tid & 63, m16 = lane & 15, g = lane >> 4;
     // the chunk's outputs: uniform bases at its first token, 32-bit offsets
     void* const odx = (char*)a.dx + t0c * (R * P * io<T>::BYTES);
     void* const odB = (char*)a.dB + t0c * (R * N * io<T>::BYTES);
@@ -501,7 +513,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     __syncthreads();
     if (tid < QB) {
       float lam_c = 0.0f;
-      for (int j = 0; j <= tid; ++j) lam_c += sT[j].d * sT[j].A;
+#pragma unroll
+      for (int j = 0; j < QB; ++j) lam_c += j <= tid ? sT[j].d * sT[j].A : 0.0f;  // all reads issued at once
       sLam[tid] = lam_c;
       sEL[tid] = __expf(lam_c);
       sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
@@ -509,9 +522,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     for (int e = tid; e < QB * K; e += TH) {
       const int t = e / K, k = e % K;
       float ph = 0.0f;
-      for (int j = 0; j <= t; ++j) ph += sT[j].d * sTh[j][k];
+#pragma unroll
+      for (int j = 0; j < QB; ++j) ph += j <= t ? sT[j].d * sTh[j][k] : 0.0f;
       float sn, cs;
-      sincosf(ph, &sn, &cs);
+      // the chunk-local angle: the hardware sine/cosine (in revolutions) for
+      // bf16 io, the full-precision library routine for fp32 io
+      if constexpr (sizeof(T) == 2) sincos_rev(ph, &sn, &cs);
+      else sincosf(ph, &sn, &cs);
       sCS[t][k] = make_float2(cs, sn);
     }
     __syncthreads();
@@ -750,8 +767,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     __syncthreads();
 
     // ---------------- scalar adjoints of the chunk ----------------
-    {
-      // the masked decay: dM on s < t and the diagonal
+    // Waves 0-3: the masked decay's adjoints; waves 4-7: the angle adjoints.
+    if (tid < 256) {
+      // dM on s < t and the diagonal
       const int t = tid / QB, s = tid % QB;
       const float dm = tid < QB * QB ? sDM[t % QB][s] : 0.0f;
       if (tid >= QB * QB) {
@@ -764,76 +782,84 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       } else if (s == t) {
         atomicAdd(&sDgam[t], dm);
       }
+    } else {
+      // d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega
+      for (int e = tid - 256; e < QB * K; e += TH - 256) {
+        const int t = e / K, k = e % K;
+        float dom = sDTheta[k];
+#pragma unroll
+        for (int i = 0; i < QB; ++i) dom += i >= t ? sDphi[i][k] : 0.0f;  // all reads issued at once
+        uint32_t ot = (uint32_t)t * Hu * K + k;
+        fresh(ot);
+        if (a0 + t < L) (a.dtheta + t0c * K)[ot] = sT[t].d * dom;
+        float v = sTh[t][k] * dom;  // the K pairs of a token are K consecutive lanes
+#pragma unroll
+        for (int o = 1; o < K; o <<= 1) v += __shfl_xor(v, o, 64);
+        if (k == 0) sThDot[t] = v;
+      }
     }
     __syncthreads();
-    if (tid < QB) {
+    // Per-token gradients: lane t < QB of wave 0, sums across tokens with
+    // shuffles (no further barrier).
+    if (tid < 64) {
       const int t = tid;
+      const bool ok = t < QB;
+      const int tt = ok ? t : 0;
       float dwt = 0.0f, det = 0.0f;
       for (int r = 0; r < R; ++r) {
-        dwt += sDw[t * R + r];
-        det += sDe[t * R + r];
+        dwt += sDw[tt * R + r];
+        det += sDe[tt * R + r];
       }
       // w_t = e^{Lam_end - Lam_t} q_t; e^{Lam_t} of the inter-chunk output
-      sDLam[t] += det * sEL[t] - dwt * sW[t];
-      sDq[t] += dwt * __expf(lamQ - sLam[t]);
-      sDlq[t] = dwt * sW[t];  // this token's share of d Lam_end
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float dlq = eQ * sRed[0];  // e^{Lam_end} <dZ, H_in>
-      for (int t = 0; t < QB; ++t) dlq += sDlq[t];
-      sDLam[QB - 1] += dlq;
-    }
-    // angles: d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega
-    for (int e = tid; e < QB * K; e += TH) {
-      const int t = e / K, k = e % K;
-      float dom = sDTheta[k];
-      for (int i = t; i < QB; ++i) dom += sDphi[i][k];
-      uint32_t ot = (uint32_t)t * Hu * K + k;
-      fresh(ot);
-      if (a0 + t < L) (a.dtheta + t0c * K)[ot] = sT[t].d * dom;
-      float v = sTh[t][k] * dom;  // the K pairs of a token are K consecutive lanes
+      float dlam_t = ok ? sDLam[tt] + det * sEL[tt] - dwt * sW[tt] : 0.0f;
+      const float dq_t = ok ? sDq[tt] + dwt * __expf(lamQ - sLam[tt]) : 0.0f;
+      // d Lam_end: e^{Lam_end} <dZ, H_in> plus every token's share through w
+      float dlq = ok ? dwt * sW[tt] : 0.0f;
 #pragma unroll
-      for (int o = 1; o < K; o <<= 1) v += __shfl_xor(v, o, 64);
-      if (k == 0) sThDot[t] = v;
-    }
-    __syncthreads();
-    if (tid < QB) {
-      const int t = tid;
-      const TokScal ts = sT[t];
+      for (int o = 1; o < 16; o <<= 1) dlq += __shfl_xor(dlq, o, 64);
+      if (t == QB - 1) dlam_t += dlq + eQ * sRed[0];
       // d(dt A)_t = sum_{i >= t} dLam_i
-      float dda = 0.0f;
-      for (int i = t; i < QB; ++i) dda += sDLam[i];
-      const float dgam = sDgam[t] + sDq[t];  // q_t = gamma_t + eps_{t+1}
-      const float deps = t > 0 ? sDq[t - 1] : 0.0f;  // eps_t weighs the previous token
-      float ddt = ts.A * dda + ts.lam * dgam + (1.0f - ts.lam) * deps;
-      float dlam = ts.d * dgam - ts.d * deps;
-      ddt += sThDot[t];  // theta_t . d omega_t
-      uint32_t tk = (uint32_t)t * Hu;
-      fresh(tk);
-      if (a0 + t < L) {
-        (a.dA + t0c)[tk] = ts.d * dda;
-        if (t > 0) {
-          (a.ddt + t0c)[tk] = ddt;
-          (a.dlam + t0c)[tk] = dlam;
-        }
+      float dda = dlam_t;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float u = __shfl_down(dda, o, 64);
+        if (t + o < QB) dda += u;
       }
-      if (t == 0) {
-        // finish the first token of the chunk processed before (it follows
-        // this chunk's last token, whose q carries its eps), then hold this one
-        if (c + 1 < nch) {
-          const float de_next = sDq[QB - 1];
-          const uint32_t tn = (uint32_t)QB * Hu;
-          (a.ddt + t0c)[tn] = pend_ddt + (1.0f - pend_l) * de_next;
-          (a.dlam + t0c)[tn] = pend_dlam - pend_d * de_next;
+      const float dq_prev = __shfl_up(dq_t, 1, 64);
+      const float de_next = __shfl(dq_t, QB - 1, 64);  // d eps of the token after this chunk
+      if (ok) {
+        const TokScal ts = sT[t];
+        const float dgam = sDgam[t] + dq_t;         // q_t = gamma_t + eps_{t+1}
+        const float deps = t > 0 ? dq_prev : 0.0f;  // eps_t weighs the previous token
+        float ddt = ts.A * dda + ts.lam * dgam + (1.0f - ts.lam) * deps;
+        const float dlam = ts.d * dgam - ts.d * deps;
+        ddt += sThDot[t];  // theta_t . d omega_t
+        uint32_t tk = (uint32_t)t * Hu;
+        fresh(tk);
+        if (a0 + t < L) {
+          (a.dA + t0c)[tk] = ts.d * dda;
+          if (t > 0) {
+            (a.ddt + t0c)[tk] = ddt;
+            (a.dlam + t0c)[tk] = dlam;
+          }
         }
-        pend_ddt = ddt;
-        pend_dlam = dlam;
-        pend_d = ts.d;
-        pend_l = ts.lam;
+        if (t == 0) {
+          // finish the first token of the chunk processed before (it follows
+          // this chunk's last token, whose q carries its eps), then hold this one
+          if (c + 1 < nch) {
+            const uint32_t tn = (uint32_t)QB * Hu;
+            (a.ddt + t0c)[tn] = pend_ddt + (1.0f - pend_l) * de_next;
+            (a.dlam + t0c)[tn] = pend_dlam - pend_d * de_next;
+          }
+          pend_ddt = ddt;
+          pend_dlam = dlam;
+          pend_d = ts.d;
+          pend_l = ts.lam;
+        }
       }
     }
     __syncthreads();  // LDS reads of this chunk done before the next staging
+    }
   }
 
   // ---------------- the state before the first token ----------------
