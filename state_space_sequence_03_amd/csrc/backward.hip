@@ -129,6 +129,79 @@ __device__ __forceinline__ void mm(FA fa, FB fb, f32x4* acc, int wave, int m16, 
   }
 }
 
+// Operand readers for mmv: IC<E> selects E = 8 (16x16x32) or 4 (16x16x16).
+template <int E>
+struct IC {
+  static constexpr int value = E;
+};
+template <int E>
+struct BV;
+template <>
+struct BV<8> {
+  typedef bf16x8 t;
+  typedef f32x8 f;
+  typedef uint4 u;
+};
+template <>
+struct BV<4> {
+  typedef bf16x4 t;
+  typedef f32x4 f;
+  typedef uint2 u;
+};
+// E consecutive bf16 from LDS (one 16- or 8-byte read)
+template <int E>
+__device__ __forceinline__ typename BV<E>::t lds_bf(const u16* p) {
+  return __builtin_bit_cast(typename BV<E>::t, *(const typename BV<E>::u*)p);
+}
+// E consecutive fp32 from LDS (16-byte reads) times s, rounded to bf16
+template <int E>
+__device__ __forceinline__ typename BV<E>::t lds_f2bf(const float* p, float s) {
+  typename BV<E>::f v;
+#pragma unroll
+  for (int e = 0; e < E; e += 4) {
+    const float4 q = *(const float4*)(p + e);
+    v[e] = q.x * s;
+    v[e + 1] = q.y * s;
+    v[e + 2] = q.z * s;
+    v[e + 3] = q.w * s;
+  }
+  return __builtin_convertvector(v, typename BV<E>::t);
+}
+
+// acc[j] += A(tr*16 + m16, k) B(k, tc*16 + m16) over k < KD with bf16
+// operands and fp32 accumulation, the operands given as vectors along k:
+// fa(row, kk, IC<E>) = A(row, kk .. kk+E-1), fb(col, kk, IC<E>) =
+// B(kk .. kk+E-1, col). Lane group g takes k in [8g, 8g + 8) of each 32-wide
+// block (16x16x32), or [4g, 4g + 4) of a last block of 16 (16x16x16).
+template <int NW, int TM, int TNC, int KD, typename FA, typename FB>
+__device__ __forceinline__ void mmv(FA fa, FB fb, f32x4* acc, int wave, int m16, int g) {
+  constexpr int NT = TM * TNC, TPW = (NT + NW - 1) / NW;
+  static_assert(KD % 16 == 0, "k in steps of 16");
+  constexpr int K32 = KD / 32 * 32;
+#pragma unroll
+  for (int k0 = 0; k0 < K32; k0 += 32) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int ti = wave + NW * j;
+      if (NT % NW == 0 || ti < NT) {
+        const int tr = ti / TNC, tc = ti % TNC, kk = k0 + 8 * g;
+        acc[j] = mfma_bf16(fa(tr * 16 + m16, kk, IC<8>{}), fb(tc * 16 + m16, kk, IC<8>{}), acc[j]);
+      }
+    }
+  }
+  if constexpr (KD % 32 == 16) {
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int ti = wave + NW * j;
+      if (NT % NW == 0 || ti < NT) {
+        const int tr = ti / TNC, tc = ti % TNC, kk = K32 + 4 * g;
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(fa(tr * 16 + m16, kk, IC<4>{}), fb(tc * 16 + m16, kk, IC<4>{}),
+                                                             acc[j], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // Per-token scalars of a chunk (tokens past L are padding with dt = 0, so
 // that they change no cumulative quantity and carry no weight).
 struct TokScal {
@@ -387,8 +460,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
   const uint32_t Hu = (uint32_t)a.H;
 
-  __shared__ float sX[V * LDP], sDY[V * LDP], sB[V * LDN], sC[V * LDN];
-  __shared__ float sH[N * LDP], sDZ[N * LDP], sGM[V * LDV], sDG[V * LDV];
+  // fp32 tiles (rows padded by 4 floats). With bf16 io (TL) the MFMA
+  // operands are bf16 tiles in natural row order (16-byte row padding): an
+  // operand that runs along a tile's rows is read 16 bytes at a time, one that
+  // runs down its columns with two transpose reads (ds_read_b64_tr_b16); B~,
+  // C~ and H_in are also kept in fp32 for the element-wise adjoints. Where
+  // that layout does not fit the LDS, the fp32 tiles are read element by
+  // element and rounded.
+  constexpr int LBV = V + 8, LBN = N + 8, LBP = P + 8;
+  constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + K * 4 + QB * 16 + V * 8 + 4 + 512;
+  constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 2 * V * LBN + N * LBP) + SMALL;
+  constexpr bool TL = BFO && TL_BYTES <= 160 * 1024;
+  __shared__ float sX[TL ? 4 : V * LDP], sDY[TL ? 4 : V * LDP], sB[V * LDN], sC[V * LDN];
+  __shared__ float sH[N * LDP], sDZ[TL ? 4 : N * LDP], sGM[TL ? 4 : V * LDV], sDG[TL ? 4 : V * LDV];
+  __shared__ __attribute__((aligned(16))) u16 tGM[TL ? V * LBV : 8];  // G o M
+  __shared__ __attribute__((aligned(16))) u16 tDG[TL ? V * LBV : 8];  // dGM o M
+  __shared__ __attribute__((aligned(16))) u16 tDY[TL ? V * LBP : 8];  // dY
+  __shared__ __attribute__((aligned(16))) u16 tX[TL ? V * LBP : 8];   // X
+  __shared__ __attribute__((aligned(16))) u16 tB[TL ? V * LBN : 8];   // B~
+  __shared__ __attribute__((aligned(16))) u16 tC[TL ? V * LBN : 8];   // C~
+  __shared__ __attribute__((aligned(16))) u16 tDZ[TL ? N * LBP : 8];  // dZ
   __shared__ float2 sCS[QB][K];
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
@@ -542,15 +633,24 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         if (e < RowVecs<T, N, V, TH>::ITEMS) {
           const int v = e / (N / VEC), n0 = (e % (N / VEC)) * VEC, t = v / R;
           float fb[VEC], fc[VEC];
+          uint32_t pb[VEC / 2], pc[VEC / 2];
           io<T>::unpack(rb.r[q], fb);
           io<T>::unpack(rc.r[q], fc);
 #pragma unroll
           for (int j = 0; j < VEC / 2; ++j) {
             const float2 cs = sCS[t][n0 / 2 + j];
-            sB[v * LDN + n0 + 2 * j] = cs.x * fb[2 * j] + cs.y * fb[2 * j + 1];
-            sB[v * LDN + n0 + 2 * j + 1] = cs.x * fb[2 * j + 1] - cs.y * fb[2 * j];
-            sC[v * LDN + n0 + 2 * j] = cs.x * fc[2 * j] + cs.y * fc[2 * j + 1];
-            sC[v * LDN + n0 + 2 * j + 1] = cs.x * fc[2 * j + 1] - cs.y * fc[2 * j];
+            const float b0 = cs.x * fb[2 * j] + cs.y * fb[2 * j + 1], b1 = cs.x * fb[2 * j + 1] - cs.y * fb[2 * j];
+            const float c0 = cs.x * fc[2 * j] + cs.y * fc[2 * j + 1], c1 = cs.x * fc[2 * j + 1] - cs.y * fc[2 * j];
+            sB[v * LDN + n0 + 2 * j] = b0;
+            sB[v * LDN + n0 + 2 * j + 1] = b1;
+            sC[v * LDN + n0 + 2 * j] = c0;
+            sC[v * LDN + n0 + 2 * j + 1] = c1;
+            pb[j] = pack_bf2(b0, b1);
+            pc[j] = pack_bf2(c0, c1);
+          }
+          if constexpr (TL) {
+            *(uint4*)&tB[v * LBN + n0] = make_uint4(pb[0], pb[1], pb[2], pb[3]);
+            *(uint4*)&tC[v * LBN + n0] = make_uint4(pc[0], pc[1], pc[2], pc[3]);
           }
         }
       }
@@ -559,13 +659,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         const int e = tid + TH * q;
         if (e < RowVecs<T, P, V, TH>::ITEMS) {
           const int v = e / (P / VEC), p0 = (e % (P / VEC)) * VEC;
-          float fx[VEC], fd[VEC];
-          io<T>::unpack(rx.r[q], fx);
-          io<T>::unpack(rdy.r[q], fd);
+          if constexpr (TL) {
+            // the raw bf16 rows as they came
+            *(uint4*)&tX[v * LBP + p0] = rx.r[q];
+            *(uint4*)&tDY[v * LBP + p0] = rdy.r[q];
+          } else {
+            float fx[VEC], fd[VEC];
+            io<T>::unpack(rx.r[q], fx);
+            io<T>::unpack(rdy.r[q], fd);
 #pragma unroll
-          for (int j = 0; j < VEC; ++j) {
-            sX[v * LDP + p0 + j] = fx[j];
-            sDY[v * LDP + p0 + j] = fd[j];
+            for (int j = 0; j < VEC; ++j) {
+              sX[v * LDP + p0 + j] = fx[j];
+              sDY[v * LDP + p0 + j] = fd[j];
+            }
           }
         }
       }
@@ -584,8 +690,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             const float2 cs = sCS[QB - 1][k];
             const float g0 = Gb[j][2 * q], g1 = Gb[j][2 * q + 1];
             const float z0 = cs.x * g0 + cs.y * g1, z1 = cs.x * g1 - cs.y * g0;
-            sDZ[n0 * LDP + p] = z0;
-            sDZ[(n0 + 1) * LDP + p] = z1;
+            if constexpr (TL) {
+              tDZ[n0 * LBP + p] = f2bf(z0);
+              tDZ[(n0 + 1) * LBP + p] = f2bf(z1);
+            } else {
+              sDZ[n0 * LDP + p] = z0;
+              sDZ[(n0 + 1) * LDP + p] = z1;
+            }
             const float o0 = ho[j][2 * q], o1 = ho[j][2 * q + 1];
             float dth = -g0 * o1 + g1 * o0;
 #pragma unroll
@@ -616,31 +727,82 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
 
+    // bf16 io: operand readers along k for mmv (row or column index, first k, IC<E>)
+    // (an operand index r = 16 * tile + m16 is a row of the operand's tile
+    // for rdT, a column for rdTr)
+    auto rdWB = [&](int v, int kk, auto e) { return lds_f2bf<decltype(e)::value>(&sB[v * LDN + kk], sW[v / R]); };
+    auto rdH = [&](int n, int kk, auto e) { return lds_f2bf<decltype(e)::value>(&sH[n * LDP + kk], 1.0f); };
+    // along a row: elements (r, kk .. kk+E-1)
+    auto rdT = [&](const u16* base, int ld) {
+      return [=](int r, int kk, auto e) { return lds_bf<decltype(e)::value>(base + r * ld + kk); };
+    };
+    // down a column: elements (kk .. kk+E-1, r). Within a 16-lane group, the
+    // transpose read gives lane i element (i mod 4) of the 8 bytes that lane
+    // 4j + i/4 addresses, as its element j: lane m16 addresses row kk + m16/4
+    // at columns 16 * tile + 4 (m16 mod 4) .. + 3, so lane m16 receives rows
+    // kk .. kk+3 of column 16 * tile + m16 (a second read gives kk+4 .. kk+7).
+    auto tr_at = [&](const u16* base, int ld, int r, int kk) {
+      return base + (kk + ((r & 15) >> 2)) * ld + (r & ~15) + 4 * (r & 3);
+    };
+    auto rdTr = [&](const u16* base, int ld) {
+      return [=](int r, int kk, auto e) {
+        constexpr int E = decltype(e)::value;
+        const uint2 f0 = lds_tr16(tr_at(base, ld, r, kk));
+        if constexpr (E == 4) {
+          return __builtin_bit_cast(bf16x4, f0);
+        } else {
+          const uint2 f1 = lds_tr16(tr_at(base, ld, r, kk + 4));
+          return __builtin_bit_cast(bf16x8, make_uint4(f0.x, f0.y, f1.x, f1.y));
+        }
+      };
+    };
+    // e^{Lam_v} dY(v, p) down column p: the k range holds E / R whole tokens (R | E)
+    auto rdELDY = [&](int p, int kk, auto e) {
+      constexpr int E = decltype(e)::value;
+      const typename BV<E>::t raw = rdTr(tDY, LBP)(p, kk, e);
+      typename BV<E>::f f;
+#pragma unroll
+      for (int q = 0; q < E; ++q) f[q] = (float)raw[q] * sEL[kk / R + q / R];
+      return __builtin_convertvector(f, typename BV<E>::t);
+    };
+
     // ---------------- G = C~ B~^T and dGM = dY X^T (V x V), masked ----------------
     {
       f32x4 gacc[VVW], dacc[VVW];
 #pragma unroll
       for (int j = 0; j < VVW; ++j) gacc[j] = dacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<BFO, NW, TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
-                    gacc, wave, m16, g);
-      mm<BFO, NW, TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
-                    dacc, wave, m16, g);
+      if constexpr (TL) {
+        mmv<NW, TV, TV, N>(rdT(tC, LBN), rdT(tB, LBN), gacc, wave, m16, g);
+        mmv<NW, TV, TV, P>(rdT(tDY, LBP), rdT(tX, LBP), dacc, wave, m16, g);
+      } else {
+        mm<BFO, NW, TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
+                                 gacc, wave, m16, g);
+        mm<BFO, NW, TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
+                                 dacc, wave, m16, g);
+      }
 #pragma unroll
       for (int j = 0; j < VVW; ++j) {
         const int ti = wave + NW * j;
         if (ti < TV * TV) {
           const int tr = ti / TV, tc = ti % TV;
-          const int vc = tc * 16 + m16, s = vc / R;
-          float pr[4];
+          const int vc = tc * 16 + m16, s = vc / R, vr0 = tr * 16 + 4 * g;
+          float pr[4], gm[4], dg[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int vr = tr * 16 + 4 * g + i, t = vr / R;
+            const int vr = vr0 + i, t = vr / R;
             float m = 0.0f;
             if (s < t) m = __expf(fminf(sLam[t] - sLam[s], 0.0f)) * sQ[s];
             else if (s == t) m = sT[t].lam * sT[t].d;
-            sGM[vr * LDV + vc] = gacc[j][i] * m;
-            sDG[vr * LDV + vc] = dacc[j][i] * m;
+            gm[i] = gacc[j][i] * m;
+            dg[i] = dacc[j][i] * m;
             pr[i] = gacc[j][i] * dacc[j][i];
+            if constexpr (TL) {
+              tGM[vr * LBV + vc] = f2bf(gm[i]);
+              tDG[vr * LBV + vc] = f2bf(dg[i]);
+            } else {
+              sGM[vr * LDV + vc] = gm[i];
+              sDG[vr * LDV + vc] = dg[i];
+            }
           }
           // dM[t][s]: sum over the R x R rank block (rows R-groups of i, columns R lanes)
 #pragma unroll
@@ -663,10 +825,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       f32x4 xacc[VPW];
 #pragma unroll
       for (int j = 0; j < VPW; ++j) xacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<BFO, NW, TV, TP, V>([&](int vr, int vk) { return sGM[vk * LDV + vr]; }, [&](int vk, int p) { return sDY[vk * LDP + p]; },
-                    xacc, wave, m16, g);
-      mm<BFO, NW, TV, TP, N>([&](int v, int n) { return sW[v / R] * sB[v * LDN + n]; }, [&](int n, int p) { return sDZ[n * LDP + p]; },
-                    xacc, wave, m16, g);
+      if constexpr (TL) {
+        mmv<NW, TV, TP, V>(rdTr(tGM, LBV), rdTr(tDY, LBP), xacc, wave, m16, g);
+        mmv<NW, TV, TP, N>(rdWB, rdTr(tDZ, LBP), xacc, wave, m16, g);
+      } else {
+        mm<BFO, NW, TV, TP, V>([&](int vr, int vk) { return sGM[vk * LDV + vr]; },
+                                 [&](int vk, int p) { return sDY[vk * LDP + p]; }, xacc, wave, m16, g);
+        mm<BFO, NW, TV, TP, N>([&](int v, int n) { return sW[v / R] * sB[v * LDN + n]; },
+                                 [&](int n, int p) { return sDZ[n * LDP + p]; }, xacc, wave, m16, g);
+      }
 #pragma unroll
       for (int j = 0; j < VPW; ++j) {
         const int ti = wave + NW * j;
@@ -687,14 +854,21 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       f32x4 cacc[VNW], eacc[VNW], bacc[VNW], facc[VNW];
 #pragma unroll
       for (int j = 0; j < VNW; ++j) cacc[j] = eacc[j] = bacc[j] = facc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      mm<BFO, NW, TV, TN, V>([&](int vr, int vk) { return sDG[vr * LDV + vk]; }, [&](int vk, int n) { return sB[vk * LDN + n]; },
-                    cacc, wave, m16, g);
-      mm<BFO, NW, TV, TN, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int n) { return sH[n * LDP + p]; },
-                    eacc, wave, m16, g);
-      mm<BFO, NW, TV, TN, V>([&](int vr, int vk) { return sDG[vk * LDV + vr]; }, [&](int vk, int n) { return sC[vk * LDN + n]; },
-                    bacc, wave, m16, g);
-      mm<BFO, NW, TV, TN, P>([&](int v, int p) { return sX[v * LDP + p]; }, [&](int p, int n) { return sDZ[n * LDP + p]; },
-                    facc, wave, m16, g);
+      if constexpr (TL) {
+        mmv<NW, TV, TN, V>(rdT(tDG, LBV), rdTr(tB, LBN), cacc, wave, m16, g);
+        mmv<NW, TV, TN, P>(rdT(tDY, LBP), rdH, eacc, wave, m16, g);
+        mmv<NW, TV, TN, V>(rdTr(tDG, LBV), rdTr(tC, LBN), bacc, wave, m16, g);
+        mmv<NW, TV, TN, P>(rdT(tX, LBP), rdT(tDZ, LBP), facc, wave, m16, g);
+      } else {
+        mm<BFO, NW, TV, TN, V>([&](int vr, int vk) { return sDG[vr * LDV + vk]; },
+                                 [&](int vk, int n) { return sB[vk * LDN + n]; }, cacc, wave, m16, g);
+        mm<BFO, NW, TV, TN, P>([&](int v, int p) { return sDY[v * LDP + p]; },
+                                 [&](int p, int n) { return sH[n * LDP + p]; }, eacc, wave, m16, g);
+        mm<BFO, NW, TV, TN, V>([&](int vr, int vk) { return sDG[vk * LDV + vr]; },
+                                 [&](int vk, int n) { return sC[vk * LDN + n]; }, bacc, wave, m16, g);
+        mm<BFO, NW, TV, TN, P>([&](int v, int p) { return sX[v * LDP + p]; },
+                                 [&](int p, int n) { return sDZ[n * LDP + p]; }, facc, wave, m16, g);
+      }
 #pragma unroll
       for (int j = 0; j < VNW; ++j) {
         const int ti = wave + NW * j;
@@ -761,8 +935,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
     {
       // dH_in += C~^T (e^{Lam} dY)
-      mm<BFO, NW, TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; }, [&](int v, int p) { return sEL[v / R] * sDY[v * LDP + p]; },
-                    Gb, wave, m16, g);
+      if constexpr (TL) {
+        mmv<NW, TN, TP, V>(rdTr(tC, LBN), rdELDY, Gb, wave, m16, g);
+      } else {
+        mm<BFO, NW, TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; },
+                                 [&](int v, int p) { return sEL[v / R] * sDY[v * LDP + p]; }, Gb, wave, m16, g);
+      }
     }
     __syncthreads();
 
@@ -883,7 +1061,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     if (ti < S::NPT) {
       const int tr = ti / TP, tc = ti % TP;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sDZ[(tr * 16 + 4 * g + i) * LDP + tc * 16 + m16] = Gb[j][i];
+      for (int i = 0; i < 4; ++i) sH[(tr * 16 + 4 * g + i) * LDP + tc * 16 + m16] = Gb[j][i];
     }
   }
   if (tid == 0) sRed[0] = 0.0f;
@@ -899,7 +1077,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         float q0 = 0.0f;
         for (int r = 0; r < R; ++r)
           q0 += ld_io<T>(a.prev_B, (bh * R + r) * N + n) * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
-        part += sDZ[n * LDP + p] * q0;
+        part += sH[n * LDP + p] * q0;
       }
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
@@ -908,13 +1086,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         for (int e = tid; e < R * N; e += TH) {
           const int r = e / N, n = e % N;
           float acc = 0.0f;
-          for (int p = 0; p < P; ++p) acc += sDZ[n * LDP + p] * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
+          for (int p = 0; p < P; ++p) acc += sH[n * LDP + p] * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
           io<T>::store1(a.dprev_B, (bh * R + r) * N + n, eps1 * acc);
         }
         for (int e = tid; e < R * P; e += TH) {
           const int r = e / P, p = e % P;
           float acc = 0.0f;
-          for (int n = 0; n < N; ++n) acc += sDZ[n * LDP + p] * ld_io<T>(a.prev_B, (bh * R + r) * N + n);
+          for (int n = 0; n < N; ++n) acc += sH[n * LDP + p] * ld_io<T>(a.prev_B, (bh * R + r) * N + n);
           io<T>::store1(a.dprev_x, (bh * R + r) * P + p, eps1 * acc);
         }
       }
