@@ -471,8 +471,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + K * 4 + QB * 16 + V * 8 + 4 + 512;
   constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 2 * V * LBN + N * LBP) + SMALL;
   constexpr bool TL = BFO && TL_BYTES <= 160 * 1024;
-  __shared__ float sX[TL ? 4 : V * LDP], sDY[TL ? 4 : V * LDP], sB[V * LDN], sC[V * LDN];
-  __shared__ float sH[N * LDP], sDZ[TL ? 4 : N * LDP], sGM[TL ? 4 : V * LDV], sDG[TL ? 4 : V * LDV];
+  __shared__ __attribute__((aligned(16))) float sB[V * LDN], sC[V * LDN], sH[N * LDP];  // 16-byte reads
+  __shared__ float sX[TL ? 4 : V * LDP], sDY[TL ? 4 : V * LDP];
+  __shared__ float sDZ[TL ? 4 : N * LDP], sGM[TL ? 4 : V * LDV], sDG[TL ? 4 : V * LDV];
   __shared__ __attribute__((aligned(16))) u16 tGM[TL ? V * LBV : 8];  // G o M
   __shared__ __attribute__((aligned(16))) u16 tDG[TL ? V * LBV : 8];  // dGM o M
   __shared__ __attribute__((aligned(16))) u16 tDY[TL ? V * LBP : 8];  // dY
@@ -480,7 +481,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 tB[TL ? V * LBN : 8];   // B~
   __shared__ __attribute__((aligned(16))) u16 tC[TL ? V * LBN : 8];   // C~
   __shared__ __attribute__((aligned(16))) u16 tDZ[TL ? N * LBP : 8];  // dZ
-  __shared__ float2 sCS[QB][K];
+  __shared__ __attribute__((aligned(16))) float2 sCS[QB][K];
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
   __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K], sTh[QB][K], sThDot[QB];
@@ -820,115 +821,112 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     __syncthreads();
 
     // ---------------- products on the masked matrices ----------------
+    // dX, dC~ and dB~ are computed transposed (feature rows, virtual-row
+    // columns): a lane then holds 4 consecutive features of one (token, rank)
+    // row, so each rotation pair sits in one lane and the row is stored with
+    // one 8-byte write.
     {
-      // dX = GM^T dY + (w B~) dZ
+      // dX^T = dY^T GM + dZ^T (w B~)^T  (P x V)
       f32x4 xacc[VPW];
 #pragma unroll
       for (int j = 0; j < VPW; ++j) xacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (TL) {
-        mmv<NW, TV, TP, V>(rdTr(tGM, LBV), rdTr(tDY, LBP), xacc, wave, m16, g);
-        mmv<NW, TV, TP, N>(rdWB, rdTr(tDZ, LBP), xacc, wave, m16, g);
+        mmv<NW, TP, TV, V>(rdTr(tDY, LBP), rdTr(tGM, LBV), xacc, wave, m16, g);
+        mmv<NW, TP, TV, N>(rdTr(tDZ, LBP), rdWB, xacc, wave, m16, g);
       } else {
-        mm<BFO, NW, TV, TP, V>([&](int vr, int vk) { return sGM[vk * LDV + vr]; },
-                                 [&](int vk, int p) { return sDY[vk * LDP + p]; }, xacc, wave, m16, g);
-        mm<BFO, NW, TV, TP, N>([&](int v, int n) { return sW[v / R] * sB[v * LDN + n]; },
-                                 [&](int n, int p) { return sDZ[n * LDP + p]; }, xacc, wave, m16, g);
+        mm<BFO, NW, TP, TV, V>([&](int p, int t) { return sDY[t * LDP + p]; },
+                               [&](int t, int s) { return sGM[t * LDV + s]; }, xacc, wave, m16, g);
+        mm<BFO, NW, TP, TV, N>([&](int p, int n) { return sDZ[n * LDP + p]; },
+                               [&](int n, int v) { return sW[v / R] * sB[v * LDN + n]; }, xacc, wave, m16, g);
       }
 #pragma unroll
       for (int j = 0; j < VPW; ++j) {
         const int ti = wave + NW * j;
-        if (ti < TV * TP) {
-          const int tr = ti / TP, tc = ti % TP, p = tc * 16 + m16;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int v = tr * 16 + 4 * g + i, t = v / R;
-            uint32_t off = (uint32_t)t * Hu * (R * P) + (uint32_t)((v % R) * P + p);
-            fresh(off);
-            if (a0 + t < L) io<T>::store1(odx, off, xacc[j][i]);
-          }
+        if (ti < TP * TV) {
+          const int tr = ti / TV, tc = ti % TV, v = tc * 16 + m16, t = v / R, p0 = tr * 16 + 4 * g;
+          uint32_t off = (uint32_t)t * Hu * (R * P) + (uint32_t)((v % R) * P + p0);
+          fresh(off);
+          const float f[4] = {xacc[j][0], xacc[j][1], xacc[j][2], xacc[j][3]};
+          if (a0 + t < L) io<T>::store4(odx, off, f);
         }
       }
     }
     {
-      // dC~ = DGM B~ + e^{Lam} E, E = dY H_in^T;  dB~ = DGM^T C~ + w F, F = X dZ^T
+      // dC~^T = B~^T DGM^T + e^{Lam} E^T, E^T = H_in dY^T;  dB~^T = C~^T DGM + w F^T, F^T = dZ X^T  (N x V)
       f32x4 cacc[VNW], eacc[VNW], bacc[VNW], facc[VNW];
 #pragma unroll
       for (int j = 0; j < VNW; ++j) cacc[j] = eacc[j] = bacc[j] = facc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (TL) {
-        mmv<NW, TV, TN, V>(rdT(tDG, LBV), rdTr(tB, LBN), cacc, wave, m16, g);
-        mmv<NW, TV, TN, P>(rdT(tDY, LBP), rdH, eacc, wave, m16, g);
-        mmv<NW, TV, TN, V>(rdTr(tDG, LBV), rdTr(tC, LBN), bacc, wave, m16, g);
-        mmv<NW, TV, TN, P>(rdT(tX, LBP), rdT(tDZ, LBP), facc, wave, m16, g);
+        mmv<NW, TN, TV, V>(rdTr(tB, LBN), rdT(tDG, LBV), cacc, wave, m16, g);
+        mmv<NW, TN, TV, P>(rdH, rdT(tDY, LBP), eacc, wave, m16, g);
+        mmv<NW, TN, TV, V>(rdTr(tC, LBN), rdTr(tDG, LBV), bacc, wave, m16, g);
+        mmv<NW, TN, TV, P>(rdT(tDZ, LBP), rdT(tX, LBP), facc, wave, m16, g);
       } else {
-        mm<BFO, NW, TV, TN, V>([&](int vr, int vk) { return sDG[vr * LDV + vk]; },
-                                 [&](int vk, int n) { return sB[vk * LDN + n]; }, cacc, wave, m16, g);
-        mm<BFO, NW, TV, TN, P>([&](int v, int p) { return sDY[v * LDP + p]; },
-                                 [&](int p, int n) { return sH[n * LDP + p]; }, eacc, wave, m16, g);
-        mm<BFO, NW, TV, TN, V>([&](int vr, int vk) { return sDG[vk * LDV + vr]; },
-                                 [&](int vk, int n) { return sC[vk * LDN + n]; }, bacc, wave, m16, g);
-        mm<BFO, NW, TV, TN, P>([&](int v, int p) { return sX[v * LDP + p]; },
-                                 [&](int p, int n) { return sDZ[n * LDP + p]; }, facc, wave, m16, g);
+        mm<BFO, NW, TN, TV, V>([&](int n, int s) { return sB[s * LDN + n]; },
+                               [&](int s, int v) { return sDG[v * LDV + s]; }, cacc, wave, m16, g);
+        mm<BFO, NW, TN, TV, P>([&](int n, int p) { return sH[n * LDP + p]; },
+                               [&](int p, int v) { return sDY[v * LDP + p]; }, eacc, wave, m16, g);
+        mm<BFO, NW, TN, TV, V>([&](int n, int t) { return sC[t * LDN + n]; },
+                               [&](int t, int s) { return sDG[t * LDV + s]; }, bacc, wave, m16, g);
+        mm<BFO, NW, TN, TV, P>([&](int n, int p) { return sDZ[n * LDP + p]; },
+                               [&](int p, int v) { return sX[v * LDP + p]; }, facc, wave, m16, g);
       }
 #pragma unroll
       for (int j = 0; j < VNW; ++j) {
         const int ti = wave + NW * j;
-        if (ti < TV * TN) {
-          const int tr = ti / TN, tc = ti % TN, n = tc * 16 + m16, k = n / 2;
-          float dCt[4], dBt[4], de[4], dw[4];
+        if (ti < TN * TV) {
+          const int tr = ti / TV, tc = ti % TV, v = tc * 16 + m16, t = v / R, n0 = tr * 16 + 4 * g, k0 = n0 / 2;
+          const float el = sEL[t], wt = sW[t];
+          const float4 bq = *(const float4*)&sB[v * LDN + n0], cq = *(const float4*)&sC[v * LDN + n0];
+          const float bS[4] = {bq.x, bq.y, bq.z, bq.w}, cS[4] = {cq.x, cq.y, cq.z, cq.w};
+          float dCt[4], dBt[4], de = 0.0f, dw = 0.0f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int v = tr * 16 + 4 * g + i, t = v / R;
-            dCt[i] = cacc[j][i] + sEL[t] * eacc[j][i];
-            dBt[i] = bacc[j][i] + sW[t] * facc[j][i];
-            de[i] = sC[v * LDN + n] * eacc[j][i];
-            dw[i] = sB[v * LDN + n] * facc[j][i];
+            dCt[i] = cacc[j][i] + el * eacc[j][i];
+            dBt[i] = bacc[j][i] + wt * facc[j][i];
+            de += cS[i] * eacc[j][i];
+            dw += bS[i] * facc[j][i];
           }
-          // row sums over n (16 lanes of the tile) for d e^{Lam} and dw
+          // sums over n: the lane's 4 features, then the 4 lane groups
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-              de[i] += __shfl_xor(de[i], o, 64);
-              dw[i] += __shfl_xor(dw[i], o, 64);
-            }
+          for (int o = 16; o < 64; o <<= 1) {
+            de += __shfl_xor(de, o, 64);
+            dw += __shfl_xor(dw, o, 64);
           }
-          if (m16 == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              atomicAdd(&sDe[tr * 16 + 4 * g + i], de[i]);
-              atomicAdd(&sDw[tr * 16 + 4 * g + i], dw[i]);
-            }
+          if (g == 0) {
+            atomicAdd(&sDe[v], de);
+            atomicAdd(&sDw[v], dw);
           }
-          // angle adjoint of the pair (n even: this lane and the next) and the
-          // un-rotated gradients dB = R(phi) dB~, dC = R(phi) dC~
-          const bool even = (m16 & 1) == 0;
-          float dph[4];
+          // per pair (u, w) = features (n0 + 2q, n0 + 2q + 1): the angle
+          // adjoint du w - dw u, and the un-rotated gradients
+          // R(phi) (du, dw) = (c du - s dw, s du + c dw)
+          const float4 csq = *(const float4*)&sCS[t][k0];
+          const float cs[2][2] = {{csq.x, csq.y}, {csq.z, csq.w}};
+          float gB[4], gC[4], dph[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int v = tr * 16 + 4 * g + i, t = v / R;
-            const float dCo = __shfl_xor(dCt[i], 1, 64), dBo = __shfl_xor(dBt[i], 1, 64);
-            const float bS = sB[v * LDN + n], bO = sB[v * LDN + (n ^ 1)];
-            const float cS = sC[v * LDN + n], cO = sC[v * LDN + (n ^ 1)];
-            // pair (u, w) = (even, odd) columns: dphi += du w - dw u
-            dph[i] = even ? (dBt[i] * bO - dBo * bS + dCt[i] * cO - dCo * cS) : 0.0f;
-            const float2 cs = sCS[t][k];
-            // R(phi) (du, dw) = (c du - s dw, s du + c dw)
-            const float gB = even ? (cs.x * dBt[i] - cs.y * dBo) : (cs.y * dBo + cs.x * dBt[i]);
-            const float gC = even ? (cs.x * dCt[i] - cs.y * dCo) : (cs.y * dCo + cs.x * dCt[i]);
-            if (a0 + t < L) {
-              uint32_t off = (uint32_t)t * Hu * (R * N) + (uint32_t)((v % R) * N + n);
-              fresh(off);
-              io<T>::store1(odB, off, gB);
-              io<T>::store1(odC, off, gC);
-            }
+          for (int q = 0; q < 2; ++q) {
+            const int u = 2 * q, w = 2 * q + 1;
+            dph[q] = dBt[u] * bS[w] - dBt[w] * bS[u] + dCt[u] * cS[w] - dCt[w] * cS[u];
+            gB[u] = cs[q][0] * dBt[u] - cs[q][1] * dBt[w];
+            gB[w] = cs[q][1] * dBt[u] + cs[q][0] * dBt[w];
+            gC[u] = cs[q][0] * dCt[u] - cs[q][1] * dCt[w];
+            gC[w] = cs[q][1] * dCt[u] + cs[q][0] * dCt[w];
           }
-          // sum the ranks of each token (groups of R rows) into the token's angle adjoint
+          if (a0 + t < L) {
+            uint32_t off = (uint32_t)t * Hu * (R * N) + (uint32_t)((v % R) * N + n0);
+            fresh(off);
+            io<T>::store4(odB, off, gB);
+            io<T>::store4(odC, off, gC);
+          }
+          // the token's angle adjoint sums its R ranks (R adjacent lanes)
 #pragma unroll
-          for (int i0 = 0; i0 < 4; i0 += R) {
-            float v = 0.0f;
+          for (int q = 0; q < 2; ++q) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) v += dph[i0 + i];
-            if (even) sDphi[(tr * 16 + 4 * g + i0) / R][k] = v;
+            for (int o = 1; o < R; o <<= 1) dph[q] += __shfl_xor(dph[q], o, 64);
+          }
+          if (m16 % R == 0) {
+            sDphi[t][k0] = dph[0];
+            sDphi[t][k0 + 1] = dph[1];
           }
         }
       }
