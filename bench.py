@@ -219,14 +219,15 @@ def bench_verify(ops, inputs, w, k, steps, warmup, torch):
 
 
 BWD_CHUNK = 16
-FP32_MFMA_TFLOPS = 157.3
 
 
 def backward_flops_per_token_head(w):
-    """Dense MFMA flops of the backward per token-head, as (fp32, bf16): per
-    16-token chunk (V = 16 R rows) the checkpoint walk's state product W^T X
-    (fp32 operands) and the reverse walk's nine products (G, dGM, two for dX,
-    two for dC~, two for dB~ and dH_in; bf16 operands for bf16 io), each 2 M N K."""
+    """Dense MFMA flops of the backward per token-head, as (checkpoint walk,
+    reverse walk): per 16-token chunk (V = 16 R rows) the checkpoint walk's
+    state product W^T X and the reverse walk's nine products (G, dGM, two for
+    dX, two for dC~, two for dB~ and dH_in), each 2 M N K. With bf16 io all of
+    them run on bf16 MFMAs, the checkpoint product twice (bf16 hi and lo parts
+    of W)."""
     V, N, P = BWD_CHUNK * w.rank, w.dstate, w.headdim
     ckpt = 2 * (N * P * V)
     walk = 2 * (V * V * N + V * V * P + V * P * V + V * P * N + V * N * V + V * N * P + V * N * V + V * N * P
@@ -258,11 +259,11 @@ def bench_backward(ops, inputs, w, steps, warmup, torch):
                                  want_dh0=False, workspace=ws)
     wall, ev = timed(fn, steps, warmup, torch)
     th = w.batch * w.seqlen * w.nheads
-    f32_fl, bf_fl = (th * f for f in backward_flops_per_token_head(w))
-    flops = f32_fl + bf_fl
+    ck_fl, walk_fl = (th * f for f in backward_flops_per_token_head(w))
+    flops = ck_fl + walk_fl
     bytes_ = th * backward_bytes_per_token_head(w)
-    # time floors: the products at the dense MFMA peaks of their operand types, the bytes at the HBM peak
-    mfma_floor_ms = (f32_fl / (FP32_MFMA_TFLOPS * 1e12) + bf_fl / (BF16_DENSE_TFLOPS * 1e12)) * 1e3
+    # time floors: the issued products at the dense bf16 MFMA peak, the bytes at the HBM peak
+    mfma_floor_ms = (2 * ck_fl + walk_fl) / (BF16_DENSE_TFLOPS * 1e12) * 1e3
     hbm_floor_ms = bytes_ / (HBM_PEAK_GBPS * 1e9) * 1e3
     del d, dy, ws
     torch.cuda.empty_cache()
@@ -445,8 +446,8 @@ def main():
                           "chunk_walk_ms_per_call": round(vf["chunk_walk_ms"], 5)}
     if "backward" in out:
         bw = out["backward"]
-        line["backward"] = {"workload": f"{w.name} backward (mamba3_ssm_chunked_bwd, dy ~ N(0,1); bf16 operands "
-                                        f"in the reverse walk's products, fp32 in the checkpoint walk)",
+        line["backward"] = {"workload": f"{w.name} backward (mamba3_ssm_chunked_bwd, dy ~ N(0,1); bf16 MFMA "
+                                        f"operands with fp32 accumulation, the checkpoint walk's in hi + lo parts)",
                             "ms": round(bw["ms"], 4), "tokens_per_s": round(bw["tokens_per_s"], 1),
                             "bound": "hbm" if bw["hbm_floor_ms"] >= bw["mfma_floor_ms"] else "mfma",
                             "achieved_GBps": round(bw["gbps"], 1), "peak_GBps": HBM_PEAK_GBPS,

@@ -162,9 +162,10 @@ size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d);
  * io fp32 or bf16; d->chunk must be a supported chunk length but the backward
  * walks chunks of its own: 16 tokens, 8 when N or P is 128 and R = 4; nheads
  * at most 65536 (M3_ERR_UNSUPPORTED otherwise: offsets inside a chunk are
- * 32-bit).  Products: fp32 for fp32 io; for bf16 io the reverse walk rounds
- * the operands of its products to bf16 (fp32 accumulation) and the state
- * checkpoints stay fp32.  workspace: at least
+ * 32-bit).  Products: fp32 for fp32 io; bf16 MFMAs with fp32 accumulation
+ * for bf16 io (operands rounded to bf16; the state product of the checkpoint
+ * walk takes w B~ as bf16 hi + lo parts), with fp32 state checkpoints.
+ * workspace: at least
  * mamba3_ssm_chunked_bwd_workspace_size(d) bytes (the states at every chunk
  * start); its contents on entry do not matter.  Outputs must not alias inputs.
  * Alignment: x, B, C, dy, dx, dB, dC, theta, dtheta and the workspace 16-byte;

@@ -27,13 +27,14 @@
 //  1. bwd_ckpt_kernel walks the chunks forward and stores the carried state
 //     H' at every chunk start (and the final one) in the workspace;
 //  2. bwd_chunk_kernel walks the chunks backward with dH' in registers.
-// The products read fp32 tiles in LDS. For fp32 io they are fp32 MFMAs
-// (16x16x4), so those gradients carry fp32 rounding only; for bf16 io the
-// reverse walk rounds both operands of each product to bf16 and uses the bf16
-// MFMA (16x16x32) with fp32 accumulation, the precision the forward's products
-// have (the checkpoint walk stays fp32: its states accumulate over the whole
-// sequence). The chunk is 16 tokens (8 when N or P is 128 and R = 4, to fit
-// LDS), V <= 64, N, P <= 128, not both 128.
+// For fp32 io every product is a fp32 MFMA (16x16x4) over fp32 tiles in LDS,
+// so those gradients carry fp32 rounding only. For bf16 io the products are
+// bf16 MFMAs (16x16x32) with fp32 accumulation, the precision the forward's
+// products have: the reverse walk rounds each operand to bf16, and the
+// checkpoint walk, whose states accumulate over the whole sequence, splits
+// w B~ into bf16 hi and lo parts (two MFMAs, accurate to ~2^-17). The chunk is
+// 16 tokens (8 when N or P is 128 and R = 4, to fit LDS), V <= 64,
+// N, P <= 128, not both 128.
 #include "m3_common.hpp"
 #include "m3_launch.hpp"
 
@@ -168,6 +169,24 @@ __device__ __forceinline__ typename BV<E>::t lds_f2bf(const float* p, float s) {
   return __builtin_convertvector(v, typename BV<E>::t);
 }
 
+// Elements (kk .. kk+E-1, r) down column r of a bf16 tile with row stride ld
+// (r = 16 * tile + m16 for lane m16 of a 16-lane group). The transpose read
+// gives lane i element (i mod 4) of the 8 bytes that lane 4j + i/4 of its
+// group addresses, as its element j: lane m16 addresses row kk + m16/4 at
+// columns 16 * tile + 4 (m16 mod 4) .. + 3, so lane m16 receives rows
+// kk .. kk+3 of column 16 * tile + m16; a second read gives kk+4 .. kk+7.
+template <int E>
+__device__ __forceinline__ typename BV<E>::t lds_col(const u16* base, int ld, int r, int kk) {
+  auto at = [&](int k) { return base + (k + ((r & 15) >> 2)) * ld + (r & ~15) + 4 * (r & 3); };
+  const uint2 f0 = lds_tr16(at(kk));
+  if constexpr (E == 4) {
+    return __builtin_bit_cast(bf16x4, f0);
+  } else {
+    const uint2 f1 = lds_tr16(at(kk + 4));
+    return __builtin_bit_cast(bf16x8, make_uint4(f0.x, f0.y, f1.x, f1.y));
+  }
+}
+
 // acc[j] += A(tr*16 + m16, k) B(k, tc*16 + m16) over k < KD with bf16
 // operands and fp32 accumulation, the operands given as vectors along k:
 // fa(row, kk, IC<E>) = A(row, kk .. kk+E-1), fb(col, kk, IC<E>) =
@@ -265,7 +284,12 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
   const uint32_t Hu = (uint32_t)a.H;
 
-  __shared__ float sW[V * LDN], sX[V * LDP];
+  // bf16 io: W = w B~ as bf16 hi + lo parts (fp32 accuracy to ~2^-17) and X
+  // as loaded, for bf16 MFMAs; fp32 io: fp32 tiles and fp32 MFMAs
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int LBN = N + 8, LBP = P + 8;
+  __shared__ float sW[BF ? 4 : V * LDN], sX[BF ? 4 : V * LDP];
+  __shared__ __attribute__((aligned(16))) u16 tWh[BF ? V * LBN : 8], tWl[BF ? V * LBN : 8], tX[BF ? V * LBP : 8];
   __shared__ float2 sCS[QB][K];
   __shared__ float sLam[QB], sQ[QB], sDA[QB], sOm[QB][K];
   __shared__ TokScal sT[QB];
@@ -391,11 +415,23 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
           float f[VEC];
           io<T>::unpack(rb.r[q], f);
           const float w = __expf(lamQ - sLam[t]) * sQ[t];
+          uint32_t hi[VEC / 2], lo[VEC / 2];
 #pragma unroll
           for (int j = 0; j < VEC / 2; ++j) {
             const float2 cs = sCS[t][n0 / 2 + j];
-            sW[v * LDN + n0 + 2 * j] = w * (cs.x * f[2 * j] + cs.y * f[2 * j + 1]);
-            sW[v * LDN + n0 + 2 * j + 1] = w * (cs.x * f[2 * j + 1] - cs.y * f[2 * j]);
+            const float w0 = w * (cs.x * f[2 * j] + cs.y * f[2 * j + 1]);
+            const float w1 = w * (cs.x * f[2 * j + 1] - cs.y * f[2 * j]);
+            if constexpr (BF) {
+              hi[j] = pack_bf2(w0, w1);
+              lo[j] = pack_bf2(w0 - bf_lo(hi[j]), w1 - bf_hi(hi[j]));  // the differences are exact in fp32
+            } else {
+              sW[v * LDN + n0 + 2 * j] = w0;
+              sW[v * LDN + n0 + 2 * j + 1] = w1;
+            }
+          }
+          if constexpr (BF) {
+            *(uint4*)&tWh[v * LBN + n0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *(uint4*)&tWl[v * LBN + n0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
           }
         }
       }
@@ -404,10 +440,14 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
         const int e = tid + TH * q;
         if (e < RowVecs<T, P, V, TH>::ITEMS) {
           const int v = e / (P / VEC), p0 = (e % (P / VEC)) * VEC;
-          float f[VEC];
-          io<T>::unpack(rx.r[q], f);
+          if constexpr (BF) {
+            *(uint4*)&tX[v * LBP + p0] = rx.r[q];
+          } else {
+            float f[VEC];
+            io<T>::unpack(rx.r[q], f);
 #pragma unroll
-          for (int j = 0; j < VEC; ++j) sX[v * LDP + p0 + j] = f[j];
+            for (int j = 0; j < VEC; ++j) sX[v * LDP + p0 + j] = f[j];
+          }
         }
       }
     }
@@ -417,8 +457,17 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     f32x4 sacc[NPW];
 #pragma unroll
     for (int j = 0; j < NPW; ++j) sacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    mm<false, NW, S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; }, [&](int v, int p) { return sX[v * LDP + p]; },
-                        sacc, wave, m16, g);
+    if constexpr (BF) {
+      // S(n, p) = sum_v W(v, n) X(v, p): both operands run down tile columns
+      auto rX = [&](int p, int kk, auto e) { return lds_col<decltype(e)::value>(tX, LBP, p, kk); };
+      mmv<NW, S::TN, S::TP, V>([&](int n, int kk, auto e) { return lds_col<decltype(e)::value>(tWh, LBN, n, kk); }, rX,
+                               sacc, wave, m16, g);
+      mmv<NW, S::TN, S::TP, V>([&](int n, int kk, auto e) { return lds_col<decltype(e)::value>(tWl, LBN, n, kk); }, rX,
+                               sacc, wave, m16, g);
+    } else {
+      mm<false, NW, S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; },
+                                     [&](int v, int p) { return sX[v * LDP + p]; }, sacc, wave, m16, g);
+    }
     const float eQ = __expf(lamQ);
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
@@ -737,25 +786,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     auto rdT = [&](const u16* base, int ld) {
       return [=](int r, int kk, auto e) { return lds_bf<decltype(e)::value>(base + r * ld + kk); };
     };
-    // down a column: elements (kk .. kk+E-1, r). Within a 16-lane group, the
-    // transpose read gives lane i element (i mod 4) of the 8 bytes that lane
-    // 4j + i/4 addresses, as its element j: lane m16 addresses row kk + m16/4
-    // at columns 16 * tile + 4 (m16 mod 4) .. + 3, so lane m16 receives rows
-    // kk .. kk+3 of column 16 * tile + m16 (a second read gives kk+4 .. kk+7).
-    auto tr_at = [&](const u16* base, int ld, int r, int kk) {
-      return base + (kk + ((r & 15) >> 2)) * ld + (r & ~15) + 4 * (r & 3);
-    };
+    // down a column: elements (kk .. kk+E-1, r)
     auto rdTr = [&](const u16* base, int ld) {
-      return [=](int r, int kk, auto e) {
-        constexpr int E = decltype(e)::value;
-        const uint2 f0 = lds_tr16(tr_at(base, ld, r, kk));
-        if constexpr (E == 4) {
-          return __builtin_bit_cast(bf16x4, f0);
-        } else {
-          const uint2 f1 = lds_tr16(tr_at(base, ld, r, kk + 4));
-          return __builtin_bit_cast(bf16x8, make_uint4(f0.x, f0.y, f1.x, f1.y));
-        }
-      };
+      return [=](int r, int kk, auto e) { return lds_col<decltype(e)::value>(base, ld, r, kk); };
     };
     // e^{Lam_v} dY(v, p) down column p: the k range holds E / R whole tokens (R | E)
     auto rdELDY = [&](int p, int kk, auto e) {
