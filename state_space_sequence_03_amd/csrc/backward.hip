@@ -534,7 +534,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
   __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K], sTh[QB][K], sThDot[QB];
-  __shared__ float sDLam[QB], sDq[QB], sDgam[QB], sDe[V], sDw[V], sRed[1];
+  __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDe[V], sDw[V], sRed[1];
 
   const float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
   // dH' (adjoint of the carried state) in the accumulator layout of an N x P matrix
@@ -633,9 +633,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
     if (tid < QB) {
       sT[tid] = tsv.scal();
-      sDLam[tid] = 0.0f;
-      sDq[tid] = 0.0f;
-      sDgam[tid] = 0.0f;
     }
     for (int e = tid; e < V; e += TH) {
       sDe[e] = 0.0f;
@@ -978,18 +975,34 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     // ---------------- scalar adjoints of the chunk ----------------
     // Waves 0-3: the masked decay's adjoints; waves 4-7: the angle adjoints.
     if (tid < 256) {
-      // dM on s < t and the diagonal
+      // dM on s < t and the diagonal; lane (t, s) = t QB + s. Row sums over s
+      // (the QB lanes of a row) and partial column sums over the rows a wave
+      // holds are formed with shuffles; the waves' column partials are added
+      // by the per-token phase below.
       const int t = tid / QB, s = tid % QB;
-      const float dm = tid < QB * QB ? sDM[t % QB][s] : 0.0f;
-      if (tid >= QB * QB) {
-      } else if (s < t) {
-        const float e = __expf(fminf(sLam[t] - sLam[s], 0.0f));
-        const float dmm = dm * e * sQ[s];
-        atomicAdd(&sDLam[t], dmm);
-        atomicAdd(&sDLam[s], -dmm);
-        atomicAdd(&sDq[s], dm * e);
-      } else if (s == t) {
-        atomicAdd(&sDgam[t], dm);
+      float dmm = 0.0f, dme = 0.0f;
+      if (tid < QB * QB) {
+        const float dm = sDM[t][s];
+        if (s < t) {
+          const float e = __expf(fminf(sLam[t] - sLam[s], 0.0f));
+          dme = dm * e;
+          dmm = dme * sQ[s];
+        } else if (s == t) {
+          sDgam[t] = dm;
+        }
+      }
+      float row = dmm, colL = dmm, colQ = dme;
+#pragma unroll
+      for (int o = 1; o < QB; o <<= 1) row += __shfl_xor(row, o, 64);
+#pragma unroll
+      for (int o = QB; o < 64; o <<= 1) {
+        colL += __shfl_xor(colL, o, 64);
+        colQ += __shfl_xor(colQ, o, 64);
+      }
+      if (tid < QB * QB && s == 0) sDLam[t] = row;
+      if (lane < QB) {
+        sColL[wave][s] = colL;
+        sColQ[wave][s] = colQ;
       }
     } else {
       // d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega
@@ -1020,8 +1033,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         det += sDe[tt * R + r];
       }
       // w_t = e^{Lam_end - Lam_t} q_t; e^{Lam_t} of the inter-chunk output
-      float dlam_t = ok ? sDLam[tt] + det * sEL[tt] - dwt * sW[tt] : 0.0f;
-      const float dq_t = ok ? sDq[tt] + dwt * __expf(lamQ - sLam[tt]) : 0.0f;
+      float cl = 0.0f, cq = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        cl += sColL[w][tt];
+        cq += sColQ[w][tt];
+      }
+      float dlam_t = ok ? sDLam[tt] - cl + det * sEL[tt] - dwt * sW[tt] : 0.0f;
+      const float dq_t = ok ? cq + dwt * __expf(lamQ - sLam[tt]) : 0.0f;
       // d Lam_end: e^{Lam_end} <dZ, H_in> plus every token's share through w
       float dlq = ok ? dwt * sW[tt] : 0.0f;
 #pragma unroll
