@@ -533,7 +533,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float2 sCS[QB][K];
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
-  __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K], sTh[QB][K], sThDot[QB];
+  __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K], sTh[QB][K], sThP[4][QB];
   __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDe[V], sDw[V], sRed[1];
 
   const float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
@@ -1005,20 +1005,28 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         sColQ[wave][s] = colQ;
       }
     } else {
-      // d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega
-      for (int e = tid - 256; e < QB * K; e += TH - 256) {
-        const int t = e / K, k = e % K;
-        float dom = sDTheta[k];
+      // d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega.
+      // Lane e = k QB + t: the suffix sum over t runs within QB lanes with
+      // shuffles; theta_t . d omega_t is summed over the wave's pairs k here
+      // and over the four waves by the per-token phase.
+      float thd = 0.0f;
+      for (int e = tid - 256; e < QB * K; e += TH - 256) {  // QB K is a multiple of 64: whole waves
+        const int t = e % QB, k = e / QB;
+        float dom = sDphi[t][k];
 #pragma unroll
-        for (int i = 0; i < QB; ++i) dom += i >= t ? sDphi[i][k] : 0.0f;  // all reads issued at once
+        for (int o = 1; o < QB; o <<= 1) {
+          const float u = __shfl_down(dom, o, 64);
+          if (t + o < QB) dom += u;
+        }
+        dom += sDTheta[k];
         uint32_t ot = (uint32_t)t * Hu * K + k;
         fresh(ot);
         if (a0 + t < L) (a.dtheta + t0c * K)[ot] = sT[t].d * dom;
-        float v = sTh[t][k] * dom;  // the K pairs of a token are K consecutive lanes
-#pragma unroll
-        for (int o = 1; o < K; o <<= 1) v += __shfl_xor(v, o, 64);
-        if (k == 0) sThDot[t] = v;
+        thd += sTh[t][k] * dom;
       }
+#pragma unroll
+      for (int o = QB; o < 64; o <<= 1) thd += __shfl_xor(thd, o, 64);
+      if (lane < QB) sThP[wave - 4][lane] = thd;
     }
     __syncthreads();
     // Per-token gradients: lane t < QB of wave 0, sums across tokens with
@@ -1061,7 +1069,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         const float deps = t > 0 ? dq_prev : 0.0f;  // eps_t weighs the previous token
         float ddt = ts.A * dda + ts.lam * dgam + (1.0f - ts.lam) * deps;
         const float dlam = ts.d * dgam - ts.d * deps;
-        ddt += sThDot[t];  // theta_t . d omega_t
+        ddt += sThP[0][t] + sThP[1][t] + sThP[2][t] + sThP[3][t];  // theta_t . d omega_t
         uint32_t tk = (uint32_t)t * Hu;
         fresh(tk);
         if (a0 + t < L) {
