@@ -518,7 +518,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // element and rounded.
   constexpr int LBV = V + 8, LBN = N + 8, LBP = P + 8;
   constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + K * 4 + QB * 16 + V * 8 + 4 + 512;
-  constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 2 * V * LBN + N * LBP) + SMALL;
+  constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 4 * V * LBN + N * LBP) + SMALL;
   constexpr bool TL = BFO && TL_BYTES <= 160 * 1024;
   __shared__ __attribute__((aligned(16))) float sB[V * LDN], sC[V * LDN], sH[N * LDP];  // 16-byte reads
   __shared__ float sX[TL ? 4 : V * LDP], sDY[TL ? 4 : V * LDP];
@@ -527,8 +527,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 tDG[TL ? V * LBV : 8];  // dGM o M
   __shared__ __attribute__((aligned(16))) u16 tDY[TL ? V * LBP : 8];  // dY
   __shared__ __attribute__((aligned(16))) u16 tX[TL ? V * LBP : 8];   // X
-  __shared__ __attribute__((aligned(16))) u16 tB[TL ? V * LBN : 8];   // B~
-  __shared__ __attribute__((aligned(16))) u16 tC[TL ? V * LBN : 8];   // C~
+  __shared__ __attribute__((aligned(16))) u16 tB[TL ? V * LBN : 8];   // B~ (bf16 hi part)
+  __shared__ __attribute__((aligned(16))) u16 tC[TL ? V * LBN : 8];   // C~ (bf16 hi part)
+  __shared__ __attribute__((aligned(16))) u16 tBl[TL ? V * LBN : 8];  // B~ - hi (lo part)
+  __shared__ __attribute__((aligned(16))) u16 tCl[TL ? V * LBN : 8];  // C~ - hi (lo part)
   __shared__ __attribute__((aligned(16))) u16 tDZ[TL ? N * LBP : 8];  // dZ
   __shared__ __attribute__((aligned(16))) float2 sCS[QB][K];
   __shared__ TokScal sT[QB];
@@ -680,7 +682,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         if (e < RowVecs<T, N, V, TH>::ITEMS) {
           const int v = e / (N / VEC), n0 = (e % (N / VEC)) * VEC, t = v / R;
           float fb[VEC], fc[VEC];
-          uint32_t pb[VEC / 2], pc[VEC / 2];
+          uint32_t pb[VEC / 2], pc[VEC / 2], lb[VEC / 2], lc[VEC / 2];
           io<T>::unpack(rb.r[q], fb);
           io<T>::unpack(rc.r[q], fc);
 #pragma unroll
@@ -694,10 +696,14 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             sC[v * LDN + n0 + 2 * j + 1] = c1;
             pb[j] = pack_bf2(b0, b1);
             pc[j] = pack_bf2(c0, c1);
+            lb[j] = pack_bf2(b0 - bf_lo(pb[j]), b1 - bf_hi(pb[j]));  // the differences are exact in fp32
+            lc[j] = pack_bf2(c0 - bf_lo(pc[j]), c1 - bf_hi(pc[j]));
           }
           if constexpr (TL) {
             *(uint4*)&tB[v * LBN + n0] = make_uint4(pb[0], pb[1], pb[2], pb[3]);
             *(uint4*)&tC[v * LBN + n0] = make_uint4(pc[0], pc[1], pc[2], pc[3]);
+            *(uint4*)&tBl[v * LBN + n0] = make_uint4(lb[0], lb[1], lb[2], lb[3]);
+            *(uint4*)&tCl[v * LBN + n0] = make_uint4(lc[0], lc[1], lc[2], lc[3]);
           }
         }
       }
@@ -887,17 +893,23 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < VNW; ++j) cacc[j] = eacc[j] = bacc[j] = facc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (TL) {
+        // B~ and C~ enter as bf16 hi + lo parts here: the angle adjoints take
+        // differences of products that cancel to first order, and one bf16
+        // rounding of B~, C~ would leave ~1e-2 relative error in dtheta
         mmv<NW, TN, TV, V>(rdTr(tB, LBN), rdT(tDG, LBV), cacc, wave, m16, g);
+        mmv<NW, TN, TV, V>(rdTr(tBl, LBN), rdT(tDG, LBV), cacc, wave, m16, g);
         mmv<NW, TN, TV, P>(rdH, rdT(tDY, LBP), eacc, wave, m16, g);
         mmv<NW, TN, TV, V>(rdTr(tC, LBN), rdTr(tDG, LBV), bacc, wave, m16, g);
+        mmv<NW, TN, TV, V>(rdTr(tCl, LBN), rdTr(tDG, LBV), bacc, wave, m16, g);
         mmv<NW, TN, TV, P>(rdT(tDZ, LBP), rdT(tX, LBP), facc, wave, m16, g);
       } else {
-        mm<BFO, NW, TN, TV, V>([&](int n, int s) { return sB[s * LDN + n]; },
-                               [&](int s, int v) { return sDG[v * LDV + s]; }, cacc, wave, m16, g);
+        // (fp32 products for dC~, dB~ here: see the bf16 tile path above)
+        mm<false, NW, TN, TV, V>([&](int n, int s) { return sB[s * LDN + n]; },
+                                 [&](int s, int v) { return sDG[v * LDV + s]; }, cacc, wave, m16, g);
         mm<BFO, NW, TN, TV, P>([&](int n, int p) { return sH[n * LDP + p]; },
                                [&](int p, int v) { return sDY[v * LDP + p]; }, eacc, wave, m16, g);
-        mm<BFO, NW, TN, TV, V>([&](int n, int t) { return sC[t * LDN + n]; },
-                               [&](int t, int s) { return sDG[t * LDV + s]; }, bacc, wave, m16, g);
+        mm<false, NW, TN, TV, V>([&](int n, int t) { return sC[t * LDN + n]; },
+                                 [&](int t, int s) { return sDG[t * LDV + s]; }, bacc, wave, m16, g);
         mm<BFO, NW, TN, TV, P>([&](int n, int p) { return sDZ[n * LDP + p]; },
                                [&](int p, int v) { return sX[v * LDP + p]; }, facc, wave, m16, g);
       }
