@@ -536,7 +536,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
   __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K], sTh[QB][K], sThP[4][QB];
-  __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDe[V], sDw[V], sRed[1];
+  __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDe[V], sDw[V], sRedW[NW];
+  __shared__ double sRedD[NW];
 
   const float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
   // dH' (adjoint of the carried state) in the accumulator layout of an N x P matrix
@@ -641,7 +642,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       sDw[e] = 0.0f;
     }
     for (int e = tid; e < K; e += TH) sDTheta[e] = 0.0f;
-    if (tid == 0) sRed[0] = 0.0f;
 #pragma unroll
     for (int q = 0; q < HP; ++q) {
       const int e = tid + TH * q;
@@ -764,7 +764,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
-      if (lane == 0) atomicAdd(&sRed[0], part);
+      if (lane == 0) sRedW[wave] = part;  // summed over the waves in a fixed order below
     }
     if (c > 0) {
       // this chunk's H_in is the H_out of the chunk processed next
@@ -1065,7 +1065,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       float dlq = ok ? dwt * sW[tt] : 0.0f;
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) dlq += __shfl_xor(dlq, o, 64);
-      if (t == QB - 1) dlam_t += dlq + eQ * sRed[0];
+      float dzh = 0.0f;  // <dZ, H_in>
+#pragma unroll
+      for (int w = 0; w < NW; ++w) dzh += sRedW[w];
+      if (t == QB - 1) dlam_t += dlq + eQ * dzh;
       // d(dt A)_t = sum_{i >= t} dLam_i
       float dda = dlam_t;
 #pragma unroll
@@ -1134,24 +1137,25 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       for (int i = 0; i < 4; ++i) sH[(tr * 16 + 4 * g + i) * LDP + tc * 16 + m16] = Gb[j][i];
     }
   }
-  if (tid == 0) sRed[0] = 0.0f;
   __syncthreads();
   if (L > 0) {
     const float d1 = a.dt[tok_of(0)], l1 = a.lam[tok_of(0)];
     const float eps1 = has_prev ? (1.0f - l1) * d1 : 0.0f;
     if (has_prev) {
-      // d eps_1 = <dH'_0, prev_B^T prev_x>; dprev_B = eps_1 dH'_0 prev_x; dprev_x = eps_1 dH'_0^T prev_B
-      float part = 0.0f;
+      // d eps_1 = <dH'_0, prev_B^T prev_x>; dprev_B = eps_1 dH'_0 prev_x; dprev_x = eps_1 dH'_0^T prev_B.
+      // d eps_1 is summed in fp64 and in a fixed order (it can nearly cancel
+      // against the first token's other dt and lam terms).
+      double part = 0.0;
       for (int e = tid; e < N * P; e += TH) {
         const int n = e / P, p = e % P;
         float q0 = 0.0f;
         for (int r = 0; r < R; ++r)
           q0 += ld_io<T>(a.prev_B, (bh * R + r) * N + n) * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
-        part += sH[n * LDP + p] * q0;
+        part += (double)sH[n * LDP + p] * (double)q0;
       }
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
-      if (lane == 0) atomicAdd(&sRed[0], part);
+      if (lane == 0) sRedD[wave] = part;
       if (a.dprev_B) {
         for (int e = tid; e < R * N; e += TH) {
           const int r = e / N, n = e % N;
@@ -1169,7 +1173,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
     if (tid == 0) {
-      const float de1 = sRed[0];
+      double de1d = 0.0;
+      if (has_prev)
+        for (int w = 0; w < NW; ++w) de1d += sRedD[w];
+      const float de1 = (float)de1d;
       a.ddt[tok_of(0)] = pend_ddt + (1.0f - l1) * de1;
       a.dlam[tok_of(0)] = pend_dlam - d1 * de1;
     }
