@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from state_space_sequence_03_amd.inputs import numpy_inputs, round_bf16_np
+from state_space_sequence_03_amd.inputs import WORKLOADS, numpy_inputs, round_bf16_np, seed_of, torch_inputs
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -119,6 +119,36 @@ def test_backward_slow_decay(ops):
     errs = {k: slice_err(v.float().cpu().numpy().astype(np.float64), ref[k], BH_AXES[k]) for k, v in g.items()}
     say("   " + "  ".join(f"{k} {e:.2e}" for k, e in errs.items()))
     assert max(errs.values()) < 1e-3, errs
+
+
+def test_backward_full_workload_sampled(ops):
+    """The mimo_bf16 workload at full size (batch 8, L=4096, H=64, P=N=64, R=4,
+    bf16) with dy ~ N(0, 1), as the benchmark runs it; four (b,h) slices
+    checked against the oracle backward."""
+    w = WORKLOADS["mimo_bf16"]
+    say("backward full workload: generating")
+    d = torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io, seed=seed_of(w.name) + 1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed_of(w.name) + 2)
+    dy = torch.randn(d["x"].shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    say("backward full workload: chunked_bwd")
+    g = ops.chunked_bwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], dy, chunk=w.chunk)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.nheads))) for _ in range(4)]
+    say(f"backward full workload: oracle on slices {pairs}")
+    host = lambda t: t.float().cpu().numpy().astype(np.float64)
+    sl = lambda t, bi, hi: host(t[bi:bi + 1, :, hi:hi + 1])
+    cat = lambda t: np.concatenate([sl(t, bi, hi) for bi, hi in pairs], 0)
+    ref = oracle.backward(cat(d["x"]), cat(d["B"]), cat(d["C"]), cat(d["dt"]), cat(d["A"]), cat(d["lam"]),
+                          cat(d["theta"]), cat(dy))
+    for k in ("dx", "dB", "dC", "ddt", "dA", "dlam", "dtheta"):
+        e = slice_err(cat(g[k]), ref[k], (0, 2))
+        say(f"   {k} {e:.2e}")
+        assert e < TOL["bf16"], (k, e)
+    e = slice_err(np.concatenate([host(g["dh0"][bi:bi + 1, hi:hi + 1]) for bi, hi in pairs], 0), ref["dh0"], (0, 1))
+    say(f"   dh0 {e:.2e}")
+    assert e < TOL["bf16"]
 
 
 def test_backward_workspace_and_rejections(ops):
