@@ -500,7 +500,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   constexpr int TV = S::TV, TN = S::TN, TP = S::TP;
   constexpr int NW = 8, TH = 64 * NW, NPW = (S::NPT + NW - 1) / NW;
   // bf16 io: products with bf16 operands (the gradients are rounded to bf16
-  // anyway); fp32 io: fp32 products
+  // anyway); fp32 io: fp32 products throughout
   constexpr bool BFO = sizeof(T) == 2;
   constexpr int VVW = (TV * TV + NW - 1) / NW, VNW = (TV * TN + NW - 1) / NW, VPW = (TV * TP + NW - 1) / NW;
   const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
