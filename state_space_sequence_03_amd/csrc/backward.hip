@@ -221,6 +221,58 @@ __device__ __forceinline__ void mmv(FA fa, FB fb, f32x4* acc, int wave, int m16,
   }
 }
 
+// Cross-lane sums and scans on the VALU (DPP and the gfx950 row swaps)
+// rather than LDS permutes. dpp<CTRL>(v) is v of the lane the DPP control
+// names; lanes outside the 16-lane row read 0 (bound_ctrl).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+// The row swaps exchange rows between their two register operands. Both the
+// copy going in and the two results pass through empty asm: without that the
+// compiler was seen to treat the two results as one value (the sum came out
+// as twice this lane's own value).
+__device__ __forceinline__ float swap_sum16(float v) {  // v of lane l plus v of lane l ^ 16
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  asm volatile("" : "+v"(b));
+  const auto s = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = s[0];
+  b = s[1];
+  asm volatile("" : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float swap_sum32(float v) {  // v of lane l plus v of lane l ^ 32
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  asm volatile("" : "+v"(b));
+  const auto s = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = s[0];
+  b = s[1];
+  asm volatile("" : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+// Sum over the lanes whose index differs from this lane's only in bits
+// [log2 LO, log2 HI); every lane of such a group receives the group's sum.
+// Each step pairs every lane with one holding the sum over the other half of
+// its aligned group: lane ^ 1 and lane ^ 2 (quad permutes), the other quad
+// of the 8-lane half-row (its mirror, valid once the quads are summed),
+// lane ^ 8 (row rotation by 8), lane ^ 16 and lane ^ 32 (row swaps).
+template <int LO, int HI>
+__device__ __forceinline__ float lane_sum(float v) {
+  static_assert(LO == 1 || LO >= 8, "the half-row mirror needs the quads summed first");
+  if constexpr (LO <= 1 && HI > 1) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (LO <= 2 && HI > 2) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (LO <= 4 && HI > 4) v += dpp<0x141>(v);  // row_half_mirror
+  if constexpr (LO <= 8 && HI > 8) v += dpp<0x128>(v);  // row_ror:8
+  if constexpr (LO <= 16 && HI > 16) v = swap_sum16(v);
+  if constexpr (LO <= 32 && HI > 32) v = swap_sum32(v);
+  return v;
+}
+// v of lane l + O within the 16-lane row (0 past its end), and of lane l - O
+template <int O>
+__device__ __forceinline__ float row_down(float v) { return dpp<0x100 + O>(v); }  // row_shl:O
+template <int O>
+__device__ __forceinline__ float row_up(float v) { return dpp<0x110 + O>(v); }    // row_shr:O
+
 // Per-token scalars of a chunk (tokens past L are padding with dt = 0, so
 // that they change no cumulative quantity and carry no weight).
 struct TokScal {
@@ -752,8 +804,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             }
             const float o0 = ho[j][2 * q], o1 = ho[j][2 * q + 1];
             float dth = -g0 * o1 + g1 * o0;
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) dth += __shfl_xor(dth, o, 64);
+            dth = lane_sum<1, 16>(dth);
             if (m16 == 0) atomicAdd(&sDTheta[k], dth);
             part += z0 * sH[n0 * LDP + p] + z1 * sH[(n0 + 1) * LDP + p];
             // dH_in starts as e^{Lam_end} dZ
@@ -762,8 +813,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
           }
         }
       }
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
+      part = lane_sum<1, 64>(part);
       if (lane == 0) sRedW[wave] = part;  // summed over the waves in a fixed order below
     }
     if (c > 0) {
@@ -847,8 +897,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             float v = 0.0f;
 #pragma unroll
             for (int i = 0; i < R; ++i) v += pr[i0 + i];
-#pragma unroll
-            for (int o = 1; o < R; o <<= 1) v += __shfl_xor(v, o, 64);
+            v = lane_sum<1, R>(v);
             if (m16 % R == 0) sDM[(tr * 16 + 4 * g + i0) / R][s] = v;
           }
         }
@@ -930,11 +979,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             dw += bS[i] * facc[j][i];
           }
           // sums over n: the lane's 4 features, then the 4 lane groups
-#pragma unroll
-          for (int o = 16; o < 64; o <<= 1) {
-            de += __shfl_xor(de, o, 64);
-            dw += __shfl_xor(dw, o, 64);
-          }
+          de = lane_sum<16, 64>(de);
+          dw = lane_sum<16, 64>(dw);
           if (g == 0) {
             atomicAdd(&sDe[v], de);
             atomicAdd(&sDw[v], dw);
@@ -961,11 +1007,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             io<T>::store4(odC, off, gC);
           }
           // the token's angle adjoint sums its R ranks (R adjacent lanes)
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-#pragma unroll
-            for (int o = 1; o < R; o <<= 1) dph[q] += __shfl_xor(dph[q], o, 64);
-          }
+          dph[0] = lane_sum<1, R>(dph[0]);
+          dph[1] = lane_sum<1, R>(dph[1]);
           if (m16 % R == 0) {
             sDphi[t][k0] = dph[0];
             sDphi[t][k0 + 1] = dph[1];
@@ -1004,13 +1047,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         }
       }
       float row = dmm, colL = dmm, colQ = dme;
-#pragma unroll
-      for (int o = 1; o < QB; o <<= 1) row += __shfl_xor(row, o, 64);
-#pragma unroll
-      for (int o = QB; o < 64; o <<= 1) {
-        colL += __shfl_xor(colL, o, 64);
-        colQ += __shfl_xor(colQ, o, 64);
-      }
+      row = lane_sum<1, QB>(row);
+      colL = lane_sum<QB, 64>(colL);
+      colQ = lane_sum<QB, 64>(colQ);
       if (tid < QB * QB && s == 0) sDLam[t] = row;
       if (lane < QB) {
         sColL[wave][s] = colL;
@@ -1025,10 +1064,18 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       for (int e = tid - 256; e < QB * K; e += TH - 256) {  // QB K is a multiple of 64: whole waves
         const int t = e % QB, k = e / QB;
         float dom = sDphi[t][k];
-#pragma unroll
-        for (int o = 1; o < QB; o <<= 1) {
-          const float u = __shfl_down(dom, o, 64);
-          if (t + o < QB) dom += u;
+        // suffix sum over the token's QB-lane group
+        {
+          float u = row_down<1>(dom);
+          if (t + 1 < QB) dom += u;
+          u = row_down<2>(dom);
+          if (t + 2 < QB) dom += u;
+          u = row_down<4>(dom);
+          if (t + 4 < QB) dom += u;
+          if constexpr (QB > 8) {
+            u = row_down<8>(dom);
+            if (t + 8 < QB) dom += u;
+          }
         }
         dom += sDTheta[k];
         uint32_t ot = (uint32_t)t * Hu * K + k;
@@ -1036,8 +1083,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         if (a0 + t < L) (a.dtheta + t0c * K)[ot] = sT[t].d * dom;
         thd += sTh[t][k] * dom;
       }
-#pragma unroll
-      for (int o = QB; o < 64; o <<= 1) thd += __shfl_xor(thd, o, 64);
+      thd = lane_sum<QB, 64>(thd);
       if (lane < QB) sThP[wave - 4][lane] = thd;
     }
     __syncthreads();
@@ -1063,21 +1109,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       const float dq_t = ok ? cq + dwt * __expf(lamQ - sLam[tt]) : 0.0f;
       // d Lam_end: e^{Lam_end} <dZ, H_in> plus every token's share through w
       float dlq = ok ? dwt * sW[tt] : 0.0f;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) dlq += __shfl_xor(dlq, o, 64);
+      dlq = lane_sum<1, 16>(dlq);
       float dzh = 0.0f;  // <dZ, H_in>
 #pragma unroll
       for (int w = 0; w < NW; ++w) dzh += sRedW[w];
       if (t == QB - 1) dlam_t += dlq + eQ * dzh;
       // d(dt A)_t = sum_{i >= t} dLam_i
       float dda = dlam_t;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float u = __shfl_down(dda, o, 64);
-        if (t + o < QB) dda += u;
+      {
+        float u = row_down<1>(dda);
+        if (t + 1 < QB) dda += u;
+        u = row_down<2>(dda);
+        if (t + 2 < QB) dda += u;
+        u = row_down<4>(dda);
+        if (t + 4 < QB) dda += u;
+        u = row_down<8>(dda);
+        if (t + 8 < QB) dda += u;
       }
-      const float dq_prev = __shfl_up(dq_t, 1, 64);
-      const float de_next = __shfl(dq_t, QB - 1, 64);  // d eps of the token after this chunk
+      const float dq_prev = row_up<1>(dq_t);
+      // d eps of the token after this chunk
+      const float de_next = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dq_t), QB - 1));
       if (ok) {
         const TokScal ts = sT[t];
         const float dgam = sDgam[t] + dq_t;         // q_t = gamma_t + eps_{t+1}
