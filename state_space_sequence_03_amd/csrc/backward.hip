@@ -36,6 +36,7 @@
 // 16 tokens (8 when N or P is 128 and R = 4, to fit LDS), V <= 64,
 // N, P <= 128, not both 128.
 #include "m3_common.hpp"
+#include "m3_lanes.hpp"
 #include "m3_launch.hpp"
 
 namespace m3 {
@@ -220,58 +221,6 @@ __device__ __forceinline__ void mmv(FA fa, FB fb, f32x4* acc, int wave, int m16,
     }
   }
 }
-
-// Cross-lane sums and scans on the VALU (DPP and the gfx950 row swaps)
-// rather than LDS permutes. dpp<CTRL>(v) is v of the lane the DPP control
-// names; lanes outside the 16-lane row read 0 (bound_ctrl).
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
-}
-// The row swaps exchange rows between their two register operands. Both the
-// copy going in and the two results pass through empty asm: without that the
-// compiler was seen to treat the two results as one value (the sum came out
-// as twice this lane's own value).
-__device__ __forceinline__ float swap_sum16(float v) {  // v of lane l plus v of lane l ^ 16
-  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
-  asm volatile("" : "+v"(b));
-  const auto s = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-  a = s[0];
-  b = s[1];
-  asm volatile("" : "+v"(a), "+v"(b));
-  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-__device__ __forceinline__ float swap_sum32(float v) {  // v of lane l plus v of lane l ^ 32
-  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
-  asm volatile("" : "+v"(b));
-  const auto s = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-  a = s[0];
-  b = s[1];
-  asm volatile("" : "+v"(a), "+v"(b));
-  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-// Sum over the lanes whose index differs from this lane's only in bits
-// [log2 LO, log2 HI); every lane of such a group receives the group's sum.
-// Each step pairs every lane with one holding the sum over the other half of
-// its aligned group: lane ^ 1 and lane ^ 2 (quad permutes), the other quad
-// of the 8-lane half-row (its mirror, valid once the quads are summed),
-// lane ^ 8 (row rotation by 8), lane ^ 16 and lane ^ 32 (row swaps).
-template <int LO, int HI>
-__device__ __forceinline__ float lane_sum(float v) {
-  static_assert(LO == 1 || LO >= 8, "the half-row mirror needs the quads summed first");
-  if constexpr (LO <= 1 && HI > 1) v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-  if constexpr (LO <= 2 && HI > 2) v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-  if constexpr (LO <= 4 && HI > 4) v += dpp<0x141>(v);  // row_half_mirror
-  if constexpr (LO <= 8 && HI > 8) v += dpp<0x128>(v);  // row_ror:8
-  if constexpr (LO <= 16 && HI > 16) v = swap_sum16(v);
-  if constexpr (LO <= 32 && HI > 32) v = swap_sum32(v);
-  return v;
-}
-// v of lane l + O within the 16-lane row (0 past its end), and of lane l - O
-template <int O>
-__device__ __forceinline__ float row_down(float v) { return dpp<0x100 + O>(v); }  // row_shl:O
-template <int O>
-__device__ __forceinline__ float row_up(float v) { return dpp<0x110 + O>(v); }    // row_shr:O
 
 // Per-token scalars of a chunk (tokens past L are padding with dt = 0, so
 // that they change no cumulative quantity and carry no weight).
