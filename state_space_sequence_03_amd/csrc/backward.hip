@@ -652,19 +652,36 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    if (tid < QB) {
-      float lam_c = 0.0f;
-#pragma unroll
-      for (int j = 0; j < QB; ++j) lam_c += j <= tid ? sT[j].d * sT[j].A : 0.0f;  // all reads issued at once
-      sLam[tid] = lam_c;
-      sEL[tid] = __expf(lam_c);
-      sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
+    // chunk-local prefix sums over the QB tokens, as 16-lane row scans:
+    // the log-decay in wave 0, the angles with lane e = k QB + t
+    if (tid < 64) {
+      const TokScal ts = sT[tid < QB ? tid : 0];
+      float lam_c = tid < QB ? ts.d * ts.A : 0.0f;
+      lam_c += row_up<1>(lam_c);
+      lam_c += row_up<2>(lam_c);
+      lam_c += row_up<4>(lam_c);
+      if constexpr (QB > 8) lam_c += row_up<8>(lam_c);
+      if (tid < QB) {
+        sLam[tid] = lam_c;
+        sEL[tid] = __expf(lam_c);
+        sQ[tid] = ts.lam * ts.d + ts.eps_next;
+      }
     }
-    for (int e = tid; e < QB * K; e += TH) {
-      const int t = e / K, k = e % K;
-      float ph = 0.0f;
-#pragma unroll
-      for (int j = 0; j < QB; ++j) ph += j <= t ? sT[j].d * sTh[j][k] : 0.0f;
+    for (int e = tid; e < QB * K; e += TH) {  // QB K is a multiple of 64: whole waves
+      const int t = e % QB, k = e / QB;
+      float ph = sT[t].d * sTh[t][k];
+      {
+        float u = row_up<1>(ph);
+        if (t >= 1) ph += u;
+        u = row_up<2>(ph);
+        if (t >= 2) ph += u;
+        u = row_up<4>(ph);
+        if (t >= 4) ph += u;
+        if constexpr (QB > 8) {
+          u = row_up<8>(ph);
+          if (t >= 8) ph += u;
+        }
+      }
       float sn, cs;
       // the chunk-local angle: the hardware sine/cosine (in revolutions) for
       // bf16 io, the full-precision library routine for fp32 io
