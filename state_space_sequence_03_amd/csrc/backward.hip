@@ -519,20 +519,20 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // element and rounded.
   constexpr int LBV = V + 8, LBN = N + 8, LBP = P + 8;
   constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + K * 4 + QB * 16 + V * 8 + 4 + 512;
-  constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 4 * V * LBN + N * LBP) + SMALL;
+  constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 4 * V * LBN + P * LBN) + SMALL;
   constexpr bool TL = BFO && TL_BYTES <= 160 * 1024;
   __shared__ __attribute__((aligned(16))) float sB[V * LDN], sC[V * LDN], sH[N * LDP];  // 16-byte reads
   __shared__ float sX[TL ? 4 : V * LDP], sDY[TL ? 4 : V * LDP];
   __shared__ float sDZ[TL ? 4 : N * LDP], sGM[TL ? 4 : V * LDV], sDG[TL ? 4 : V * LDV];
-  __shared__ __attribute__((aligned(16))) u16 tGM[TL ? V * LBV : 8];  // G o M
-  __shared__ __attribute__((aligned(16))) u16 tDG[TL ? V * LBV : 8];  // dGM o M
+  __shared__ __attribute__((aligned(16))) u16 tGMt[TL ? V * LBV : 8];  // (G o M)^T
+  __shared__ __attribute__((aligned(16))) u16 tDGt[TL ? V * LBV : 8];  // (dGM o M)^T
   __shared__ __attribute__((aligned(16))) u16 tDY[TL ? V * LBP : 8];  // dY
   __shared__ __attribute__((aligned(16))) u16 tX[TL ? V * LBP : 8];   // X
   __shared__ __attribute__((aligned(16))) u16 tB[TL ? V * LBN : 8];   // B~ (bf16 hi part)
   __shared__ __attribute__((aligned(16))) u16 tC[TL ? V * LBN : 8];   // C~ (bf16 hi part)
   __shared__ __attribute__((aligned(16))) u16 tBl[TL ? V * LBN : 8];  // B~ - hi (lo part)
   __shared__ __attribute__((aligned(16))) u16 tCl[TL ? V * LBN : 8];  // C~ - hi (lo part)
-  __shared__ __attribute__((aligned(16))) u16 tDZ[TL ? N * LBP : 8];  // dZ
+  __shared__ __attribute__((aligned(16))) u16 tDZt[TL ? P * LBN : 8];  // dZ^T
   __shared__ __attribute__((aligned(16))) float2 sCS[QB][K];
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
@@ -762,8 +762,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             const float g0 = Gb[j][2 * q], g1 = Gb[j][2 * q + 1];
             const float z0 = cs.x * g0 + cs.y * g1, z1 = cs.x * g1 - cs.y * g0;
             if constexpr (TL) {
-              tDZ[n0 * LBP + p] = f2bf(z0);
-              tDZ[(n0 + 1) * LBP + p] = f2bf(z1);
+              *(uint32_t*)&tDZt[p * LBN + n0] = pack_bf2(z0, z1);  // features n0, n0 + 1 of column p
             } else {
               sDZ[n0 * LDP + p] = z0;
               sDZ[(n0 + 1) * LDP + p] = z1;
@@ -849,13 +848,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             gm[i] = gacc[j][i] * m;
             dg[i] = dacc[j][i] * m;
             pr[i] = gacc[j][i] * dacc[j][i];
-            if constexpr (TL) {
-              tGM[vr * LBV + vc] = f2bf(gm[i]);
-              tDG[vr * LBV + vc] = f2bf(dg[i]);
-            } else {
+            if constexpr (!TL) {
               sGM[vr * LDV + vc] = gm[i];
               sDG[vr * LDV + vc] = dg[i];
             }
+          }
+          if constexpr (TL) {
+            // rows vr0 .. vr0+3 of column vc are consecutive in the transposed tiles
+            *(uint2*)&tGMt[vc * LBV + vr0] = make_uint2(pack_bf2(gm[0], gm[1]), pack_bf2(gm[2], gm[3]));
+            *(uint2*)&tDGt[vc * LBV + vr0] = make_uint2(pack_bf2(dg[0], dg[1]), pack_bf2(dg[2], dg[3]));
           }
           // dM[t][s]: sum over the R x R rank block (rows R-groups of i, columns R lanes)
 #pragma unroll
@@ -882,8 +883,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < VPW; ++j) xacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (TL) {
-        mmv<NW, TP, TV, V>(rdTr(tDY, LBP), rdTr(tGM, LBV), xacc, wave, m16, g);
-        mmv<NW, TP, TV, N>(rdTr(tDZ, LBP), rdWB, xacc, wave, m16, g);
+        mmv<NW, TP, TV, V>(rdTr(tDY, LBP), rdT(tGMt, LBV), xacc, wave, m16, g);
+        mmv<NW, TP, TV, N>(rdT(tDZt, LBN), rdWB, xacc, wave, m16, g);
       } else {
         mm<BFO, NW, TP, TV, V>([&](int p, int t) { return sDY[t * LDP + p]; },
                                [&](int t, int s) { return sGM[t * LDV + s]; }, xacc, wave, m16, g);
@@ -911,12 +912,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         // B~ and C~ enter as bf16 hi + lo parts here: the angle adjoints take
         // differences of products that cancel to first order, and one bf16
         // rounding of B~, C~ would leave ~1e-2 relative error in dtheta
-        mmv<NW, TN, TV, V>(rdTr(tB, LBN), rdT(tDG, LBV), cacc, wave, m16, g);
-        mmv<NW, TN, TV, V>(rdTr(tBl, LBN), rdT(tDG, LBV), cacc, wave, m16, g);
+        mmv<NW, TN, TV, V>(rdTr(tB, LBN), rdTr(tDGt, LBV), cacc, wave, m16, g);
+        mmv<NW, TN, TV, V>(rdTr(tBl, LBN), rdTr(tDGt, LBV), cacc, wave, m16, g);
         mmv<NW, TN, TV, P>(rdH, rdT(tDY, LBP), eacc, wave, m16, g);
-        mmv<NW, TN, TV, V>(rdTr(tC, LBN), rdTr(tDG, LBV), bacc, wave, m16, g);
-        mmv<NW, TN, TV, V>(rdTr(tCl, LBN), rdTr(tDG, LBV), bacc, wave, m16, g);
-        mmv<NW, TN, TV, P>(rdT(tDZ, LBP), rdT(tX, LBP), facc, wave, m16, g);
+        mmv<NW, TN, TV, V>(rdTr(tC, LBN), rdT(tDGt, LBV), bacc, wave, m16, g);
+        mmv<NW, TN, TV, V>(rdTr(tCl, LBN), rdT(tDGt, LBV), bacc, wave, m16, g);
+        mmv<NW, TN, TV, P>(rdTr(tDZt, LBN), rdT(tX, LBP), facc, wave, m16, g);
       } else {
         // (fp32 products for dC~, dB~ here: see the bf16 tile path above)
         mm<false, NW, TN, TV, V>([&](int n, int s) { return sB[s * LDN + n]; },
