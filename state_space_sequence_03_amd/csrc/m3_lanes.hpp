@@ -61,4 +61,17 @@ __device__ __forceinline__ float row_down(float v) { return dpp<0x100 + O>(v); }
 template <int O>
 __device__ __forceinline__ float row_up(float v) { return dpp<0x110 + O>(v); }    // row_shr:O
 
+// Inclusive prefix sum over the 64 lanes of a wave: row shifts inside each
+// 16-lane row, then the last lane of a row added to the rows after it (row
+// broadcasts 15 and 31, masked to the receiving rows).
+__device__ __forceinline__ float wave_scan_dpp(float v) {
+  v += row_up<1>(v);
+  v += row_up<2>(v);
+  v += row_up<4>(v);
+  v += row_up<8>(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
+  return v;
+}
+
 }  // namespace m3

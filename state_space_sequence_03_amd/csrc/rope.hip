@@ -12,6 +12,7 @@
 // Launch 3 moves almost all the bytes (B, C in and out); 1 and 2 read only
 // dt and theta once more.
 #include "m3_common.hpp"
+#include "m3_lanes.hpp"
 #include "m3_launch.hpp"
 
 namespace m3 {
@@ -114,9 +115,12 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
   __syncthreads();
   const float* offs = a.totals + ((b * a.H + h) * nchunks + c) * K;
   for (int k = wave; k < K; k += 4) {
-    const float v = wave_incl_scan(om[lane][k]) + offs[k];
+    const float v = wave_scan_dpp(om[lane][k]) + offs[k];
     float s, co;
-    sincosf(v, &s, &co);
+    // bf16 io: the hardware sine/cosine (in revolutions; the reduction by the
+    // nearest whole revolution is exact); fp32 io: the library routine
+    if constexpr (sizeof(T) == 2) sincos_rev(v, &s, &co);
+    else sincosf(v, &s, &co);
     cs[lane][k] = make_float2(co, s);
   }
   __syncthreads();
