@@ -62,54 +62,14 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 // acc[j] += A(tr*16 + m16, k) B(k, tc*16 + m16) over k < KD for the wave's
-// tiles j of a TM x TN grid (tile ti = wave + NW j, tr = ti / TNC, tc = ti % TNC).
-// BF = false: fp32 MFMA 16x16x4, the k loop outside the tile loop, so the
-// wave's tiles form independent MFMA chains that are issued interleaved.
-// BF = true: the fp32 operands are rounded to bf16 (nearest even) and
-// multiplied with the bf16 MFMA 16x16x32 (16x16x16 for a last k block of 16),
-// fp32 accumulation; lane group g takes the k range [8g, 8g + 8) of each
-// 32-wide block in both operands.
-template <bool BF, int NW, int TM, int TNC, int KD, typename FA, typename FB>
+// tiles j of a TM x TN grid (tile ti = wave + NW j, tr = ti / TNC, tc = ti % TNC),
+// fp32 MFMA 16x16x4 with scalar operand readers fa(row, k), fb(k, col). The k
+// loop is outside the tile loop, so the wave's tiles form independent MFMA
+// chains that are issued interleaved.
+template <int NW, int TM, int TNC, int KD, typename FA, typename FB>
 __device__ __forceinline__ void mm(FA fa, FB fb, f32x4* acc, int wave, int m16, int g) {
   constexpr int NT = TM * TNC, TPW = (NT + NW - 1) / NW;
-  if constexpr (BF) {
-    static_assert(KD % 16 == 0, "k in steps of 16");
-    constexpr int K32 = KD / 32 * 32;
-#pragma unroll 1
-    for (int k0 = 0; k0 < K32; k0 += 32) {
-#pragma unroll
-      for (int j = 0; j < TPW; ++j) {
-        const int ti = wave + NW * j;
-        if (NT % NW == 0 || ti < NT) {
-          const int tr = ti / TNC, tc = ti % TNC, kk = k0 + 8 * g;
-          f32x8 av, bv;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            av[e] = fa(tr * 16 + m16, kk + e);
-            bv[e] = fb(kk + e, tc * 16 + m16);
-          }
-          acc[j] = mfma_bf16(__builtin_convertvector(av, bf16x8), __builtin_convertvector(bv, bf16x8), acc[j]);
-        }
-      }
-    }
-    if constexpr (KD % 32 == 16) {
-#pragma unroll
-      for (int j = 0; j < TPW; ++j) {
-        const int ti = wave + NW * j;
-        if (NT % NW == 0 || ti < NT) {
-          const int tr = ti / TNC, tc = ti % TNC, kk = K32 + 4 * g;
-          f32x4 av, bv;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            av[e] = fa(tr * 16 + m16, kk + e);
-            bv[e] = fb(kk + e, tc * 16 + m16);
-          }
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_convertvector(av, bf16x4),
-                                                               __builtin_convertvector(bv, bf16x4), acc[j], 0, 0, 0);
-        }
-      }
-    }
-  } else if constexpr (NT % NW == 0) {
+  if constexpr (NT % NW == 0) {
 #pragma unroll 2
     for (int k0 = 0; k0 < KD; k0 += 4) {
 #pragma unroll
@@ -466,7 +426,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
       mmv<NW, S::TN, S::TP, V>([&](int n, int kk, auto e) { return lds_col<decltype(e)::value>(tWl, LBN, n, kk); }, rX,
                                sacc, wave, m16, g);
     } else {
-      mm<false, NW, S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; },
+      mm<NW, S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; },
                                      [&](int v, int p) { return sX[v * LDP + p]; }, sacc, wave, m16, g);
     }
     const float eQ = __expf(lamQ);
@@ -510,17 +470,16 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
   const uint32_t Hu = (uint32_t)a.H;
 
-  // fp32 tiles (rows padded by 4 floats). With bf16 io (TL) the MFMA
-  // operands are bf16 tiles in natural row order (16-byte row padding): an
-  // operand that runs along a tile's rows is read 16 bytes at a time, one that
+  // fp32 io: fp32 tiles (rows padded by 4 floats) and fp32 MFMAs. bf16 io
+  // (TL): the MFMA operands are bf16 tiles with 16-byte row padding, an
+  // operand that runs along a tile's rows read 16 bytes at a time, one that
   // runs down its columns with two transpose reads (ds_read_b64_tr_b16); B~,
-  // C~ and H_in are also kept in fp32 for the element-wise adjoints. Where
-  // that layout does not fit the LDS, the fp32 tiles are read element by
-  // element and rounded.
+  // C~ and H_in are also kept in fp32 for the element-wise adjoints.
   constexpr int LBV = V + 8, LBN = N + 8, LBP = P + 8;
   constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + K * 4 + QB * 16 + V * 8 + 4 + 512;
   constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 4 * V * LBN + P * LBN) + SMALL;
   constexpr bool TL = BFO && TL_BYTES <= 160 * 1024;
+  static_assert(TL || !BFO, "bf16 io takes the bf16 tile layout at every supported size");
   __shared__ __attribute__((aligned(16))) float sB[V * LDN], sC[V * LDN], sH[N * LDP];  // 16-byte reads
   __shared__ float sX[TL ? 4 : V * LDP], sDY[TL ? 4 : V * LDP];
   __shared__ float sDZ[TL ? 4 : N * LDP], sGM[TL ? 4 : V * LDV], sDG[TL ? 4 : V * LDV];
@@ -827,9 +786,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         mmv<NW, TV, TV, N>(rdT(tC, LBN), rdT(tB, LBN), gacc, wave, m16, g);
         mmv<NW, TV, TV, P>(rdT(tDY, LBP), rdT(tX, LBP), dacc, wave, m16, g);
       } else {
-        mm<BFO, NW, TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
+        mm<NW, TV, TV, N>([&](int v, int n) { return sC[v * LDN + n]; }, [&](int n, int v) { return sB[v * LDN + n]; },
                                  gacc, wave, m16, g);
-        mm<BFO, NW, TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
+        mm<NW, TV, TV, P>([&](int v, int p) { return sDY[v * LDP + p]; }, [&](int p, int v) { return sX[v * LDP + p]; },
                                  dacc, wave, m16, g);
       }
 #pragma unroll
@@ -886,9 +845,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         mmv<NW, TP, TV, V>(rdTr(tDY, LBP), rdT(tGMt, LBV), xacc, wave, m16, g);
         mmv<NW, TP, TV, N>(rdT(tDZt, LBN), rdWB, xacc, wave, m16, g);
       } else {
-        mm<BFO, NW, TP, TV, V>([&](int p, int t) { return sDY[t * LDP + p]; },
+        mm<NW, TP, TV, V>([&](int p, int t) { return sDY[t * LDP + p]; },
                                [&](int t, int s) { return sGM[t * LDV + s]; }, xacc, wave, m16, g);
-        mm<BFO, NW, TP, TV, N>([&](int p, int n) { return sDZ[n * LDP + p]; },
+        mm<NW, TP, TV, N>([&](int p, int n) { return sDZ[n * LDP + p]; },
                                [&](int n, int v) { return sW[v / R] * sB[v * LDN + n]; }, xacc, wave, m16, g);
       }
 #pragma unroll
@@ -919,14 +878,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         mmv<NW, TN, TV, V>(rdTr(tCl, LBN), rdT(tDGt, LBV), bacc, wave, m16, g);
         mmv<NW, TN, TV, P>(rdTr(tDZt, LBN), rdT(tX, LBP), facc, wave, m16, g);
       } else {
-        // (fp32 products for dC~, dB~ here: see the bf16 tile path above)
-        mm<false, NW, TN, TV, V>([&](int n, int s) { return sB[s * LDN + n]; },
+        mm<NW, TN, TV, V>([&](int n, int s) { return sB[s * LDN + n]; },
                                  [&](int s, int v) { return sDG[v * LDV + s]; }, cacc, wave, m16, g);
-        mm<BFO, NW, TN, TV, P>([&](int n, int p) { return sH[n * LDP + p]; },
+        mm<NW, TN, TV, P>([&](int n, int p) { return sH[n * LDP + p]; },
                                [&](int p, int v) { return sDY[v * LDP + p]; }, eacc, wave, m16, g);
-        mm<false, NW, TN, TV, V>([&](int n, int t) { return sC[t * LDN + n]; },
+        mm<NW, TN, TV, V>([&](int n, int t) { return sC[t * LDN + n]; },
                                  [&](int t, int s) { return sDG[t * LDV + s]; }, bacc, wave, m16, g);
-        mm<BFO, NW, TN, TV, P>([&](int n, int p) { return sDZ[n * LDP + p]; },
+        mm<NW, TN, TV, P>([&](int n, int p) { return sDZ[n * LDP + p]; },
                                [&](int p, int v) { return sX[v * LDP + p]; }, facc, wave, m16, g);
       }
 #pragma unroll
@@ -988,7 +946,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       if constexpr (TL) {
         mmv<NW, TN, TP, V>(rdTr(tC, LBN), rdELDY, Gb, wave, m16, g);
       } else {
-        mm<BFO, NW, TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; },
+        mm<NW, TN, TP, V>([&](int n, int v) { return sC[v * LDN + n]; },
                                  [&](int v, int p) { return sEL[v / R] * sDY[v * LDP + p]; }, Gb, wave, m16, g);
       }
     }
