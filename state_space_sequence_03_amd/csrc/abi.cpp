@@ -80,6 +80,56 @@ SegPlan seg_plan(const m3_dims* d) {
   return sp;
 }
 
+// Segments of the backward: each (b,h) walked as S runs of whole backward
+// chunks by separate blocks. Requested through the low 16 bits of flags, else
+// chosen so that ~512 blocks exist when B*H is small (each segment keeps at
+// least 4 chunks).
+struct BwdSegPlan {
+  int64_t S, cps, nch;
+};
+BwdSegPlan bwd_seg_plan(const m3_dims* d) {
+  BwdSegPlan sp{1, 0, 0};
+  const int64_t q = m3::bwd_chunk_len((int)d->dstate, (int)d->headdim, (int)d->rank);
+  sp.nch = d->seqlen > 0 ? (d->seqlen + q - 1) / q : 0;
+  int64_t S = d->flags & 0xffff;
+  const int64_t BH = d->batch * d->nheads;
+  if (S == 0) {
+    S = 1;
+    if (BH > 0 && BH < 256) {
+      S = (512 + BH - 1) / BH;
+      if (S > sp.nch / 4) S = sp.nch / 4;
+      if (S < 1) S = 1;
+    }
+  }
+  if (S > sp.nch) S = sp.nch > 0 ? sp.nch : 1;
+  sp.cps = sp.nch > 0 ? (sp.nch + S - 1) / S : 1;
+  sp.S = sp.nch > 0 ? (sp.nch + sp.cps - 1) / sp.cps : 1;
+  return sp;
+}
+// Workspace of the backward: the checkpoints, then (S > 1) the segment arrays,
+// each 256-byte aligned.
+struct BwdWs {
+  size_t ckpt, seg_end, seg_in, dh_loc, dh_end, seg_tot, bnd, bytes;
+};
+BwdWs bwd_ws(const m3_dims* d, const BwdSegPlan& sp) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t BH = (size_t)(d->batch * d->nheads), NP = (size_t)(d->dstate * d->headdim), K1 = (size_t)(1 + d->dstate / 2);
+  BwdWs w{};
+  w.ckpt = 0;
+  size_t o = up(sizeof(float) * BH * (size_t)(sp.nch + 1) * NP);
+  if (sp.S > 1) {
+    const size_t st = up(sizeof(float) * BH * (size_t)sp.S * NP);
+    w.seg_end = o; o += st;
+    w.seg_in = o; o += st;
+    w.dh_loc = o; o += st;
+    w.dh_end = o; o += st;
+    w.seg_tot = o; o += up(sizeof(float) * BH * (size_t)sp.S * K1);
+    w.bnd = o; o += up(sizeof(float) * BH * (size_t)sp.S * 4);
+  }
+  w.bytes = o;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -198,9 +248,7 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
 size_t mamba3_ssm_chunked_bwd_workspace_size(const m3_dims* d) {
   if (check_dims(d, true, true) != M3_OK) return 0;
   if (d->batch == 0 || d->nheads == 0 || d->seqlen == 0) return 0;
-  const int64_t q = m3::bwd_chunk_len((int)d->dstate, (int)d->headdim, (int)d->rank);
-  const int64_t nch = (d->seqlen + q - 1) / q;
-  return sizeof(float) * (size_t)(d->batch * d->nheads) * (size_t)(nch + 1) * (size_t)(d->dstate * d->headdim);
+  return bwd_ws(d, bwd_seg_plan(d)).bytes;
 }
 
 m3_status mamba3_ssm_chunked_bwd(const m3_dims* d, const void* x, const void* B, const void* C,
@@ -213,7 +261,7 @@ m3_status mamba3_ssm_chunked_bwd(const m3_dims* d, const void* x, const void* B,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   m3_status st = check_dims(d, true, true);
   if (st != M3_OK) return st;
-  if (d->flags != 0) return M3_ERR_UNSUPPORTED;
+  if ((d->flags & ~0xffff) != 0) return M3_ERR_UNSUPPORTED;
   if (!m3::bwd_supported((int)d->dstate, (int)d->headdim, (int)d->rank)) return M3_ERR_UNSUPPORTED;
   if (d->nheads > 65536) return M3_ERR_UNSUPPORTED;  // 32-bit offsets inside a chunk
   const bool empty = d->batch == 0 || d->nheads == 0;
@@ -250,6 +298,19 @@ m3_status mamba3_ssm_chunked_bwd(const m3_dims* d, const void* x, const void* B,
   a.dh0 = dh0; a.dprev_B = prev_B ? dprev_B : nullptr; a.dprev_x = prev_B ? dprev_x : nullptr;
   a.ckpt = (float*)workspace;
   a.batch = d->batch; a.L = d->seqlen; a.H = d->nheads; a.R = (int)d->rank;
+  const BwdSegPlan sp = bwd_seg_plan(d);
+  a.S = (int)sp.S;
+  a.cps = sp.cps;
+  if (sp.S > 1) {
+    const BwdWs w = bwd_ws(d, sp);
+    char* base = (char*)workspace;
+    a.seg_end = (float*)(base + w.seg_end);
+    a.seg_in = (float*)(base + w.seg_in);
+    a.dh_loc = (float*)(base + w.dh_loc);
+    a.dh_end = (float*)(base + w.dh_end);
+    a.seg_tot = (float*)(base + w.seg_tot);
+    a.bnd = (float*)(base + w.bnd);
+  }
   return m3::launch_chunked_bwd(io_bf16(d), (int)d->dstate, (int)d->headdim, a, s) == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 

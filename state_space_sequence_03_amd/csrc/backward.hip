@@ -239,9 +239,17 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   typedef BS<N, P, R> S;
   constexpr int QB = S::QB, K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP;
   constexpr int NW = 4, TH = 64 * NW, NPW = (S::NPT + NW - 1) / NW;
-  const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  // block (bh, seg): the chunks [c_begin, c_end) of one segment of a (b,h)
+  // sequence (one segment spanning all chunks when NS = 1)
+  const int NS = a.S > 1 ? a.S : 1;
+  const int64_t bh = blockIdx.x / NS, seg = blockIdx.x % NS, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
+  const int64_t c_begin = NS > 1 ? seg * a.cps : 0, c_end = NS > 1 ? (c_begin + a.cps < nch ? c_begin + a.cps : nch) : nch;
+  // local pass: segments from a zero state (the first from the true one), end
+  // states and totals only; otherwise the checkpoints, segments entering with
+  // the states of the segment scan
+  const bool local = NS > 1 && a.ckpt_local;
   auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
   const uint32_t Hu = (uint32_t)a.H;
 
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
 
   // H' in the MFMA accumulator layout: tile j holds rows 16 tr + 4g + i, column 16 tc + m16
   f32x4 Hs[NPW];
-  const bool has_prev = a.prev_B != nullptr;
+  const bool has_prev = a.prev_B != nullptr && seg == 0;
   const float eps1 = (has_prev && L > 0) ? (1.0f - a.lam[tok_of(0)]) * a.dt[tok_of(0)] : 0.0f;
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
@@ -268,7 +276,12 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = tr * 16 + 4 * g + i;
-        float v = a.h0 ? a.h0[bh * (int64_t)N * P + n * P + p] : 0.0f;
+        float v = 0.0f;
+        if (seg == 0) {
+          if (a.h0) v = a.h0[bh * (int64_t)N * P + n * P + p];
+        } else if (!local) {
+          v = a.seg_in[(bh * NS + seg) * (int64_t)N * P + n * P + p];
+        }
         if (has_prev) {
           float acc = 0.0f;
           for (int r = 0; r < R; ++r)
@@ -330,10 +343,13 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
       omt[q] = ok ? (a.theta + t0 * K)[ot] : 0.0f;
     }
   };
-  if (nch > 0) fetch(0);
+  if (c_begin < c_end) fetch(c_begin);
+  float seg_lam = 0.0f, seg_th[OMP];  // segment totals (local pass)
+#pragma unroll
+  for (int q = 0; q < OMP; ++q) seg_th[q] = 0.0f;
 
-  for (int64_t c = 0; c < nch; ++c) {
-    store_state(c);
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    if (!local) store_state(c);
     if (tid < QB) {
       sT[tid] = tsv.scal();
       sDA[tid] = tsv.d * tsv.A;
@@ -351,20 +367,25 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
       sLam[tid] = lam_c;
       sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
     }
-    for (int e = tid; e < QB * K; e += TH) {
-      const int t = e / K, k = e % K;
-      float ph = 0.0f;
 #pragma unroll
-      for (int j = 0; j < QB; ++j) ph += j <= t ? sOm[j][k] : 0.0f;
-      float sn, cs;
-      // the chunk-local angle: the hardware sine/cosine (in revolutions) for
-      // bf16 io, the full-precision library routine for fp32 io
-      if constexpr (sizeof(T) == 2) sincos_rev(ph, &sn, &cs);
-      else sincosf(ph, &sn, &cs);
-      sCS[t][k] = make_float2(cs, sn);
+    for (int q = 0; q < OMP; ++q) {
+      const int e = tid + TH * q, t = e / K, k = e % K;
+      if (e < QB * K) {
+        float ph = 0.0f;
+#pragma unroll
+        for (int j = 0; j < QB; ++j) ph += j <= t ? sOm[j][k] : 0.0f;
+        float sn, cs;
+        // the chunk-local angle: the hardware sine/cosine (in revolutions) for
+        // bf16 io, the full-precision library routine for fp32 io
+        if constexpr (sizeof(T) == 2) sincos_rev(ph, &sn, &cs);
+        else sincosf(ph, &sn, &cs);
+        sCS[t][k] = make_float2(cs, sn);
+        if (t == QB - 1) seg_th[q] += ph;  // the chunk's total angle of pair k
+      }
     }
     __syncthreads();
     const float lamQ = sLam[QB - 1];
+    seg_lam += lamQ;
     // W = w B~ (rows v = t R + r), X
     {
       constexpr int VEC = io<T>::VEC;
@@ -412,7 +433,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
         }
       }
     }
-    if (c + 1 < nch) fetch(c + 1);
+    if (c + 1 < c_end) fetch(c + 1);
     __syncthreads();
     // S = W^T X, then H' <- R(Theta) (e^{Lam_end} H' + S)
     f32x4 sacc[NPW];
@@ -448,7 +469,231 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
     }
     __syncthreads();  // LDS reads of this chunk done before the next staging
   }
-  store_state(nch);
+  if (!local) {
+    if (seg == NS - 1) store_state(nch);
+  } else {
+    float* E = a.seg_end + (bh * NS + seg) * (int64_t)(N * P);
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+      const int ti = wave + NW * j;
+      if (ti < S::NPT) {
+        const int tr = ti / S::TP, tc = ti % S::TP, p = tc * 16 + m16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) E[(tr * 16 + 4 * g + i) * P + p] = Hs[j][i];
+      }
+    }
+    float* tot = a.seg_tot + (bh * NS + seg) * (int64_t)(1 + K);
+    if (tid == 0) tot[0] = seg_lam;
+#pragma unroll
+    for (int q = 0; q < OMP; ++q) {
+      const int e = tid + TH * q, t = e / K, k = e % K;
+      if (e < QB * K && t == QB - 1) tot[1 + k] = seg_th[q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1b. (segments) the state adjoint alone, walked backward over one segment
+//     from zero at its end: dH' <- e^{Lam_end} R(-Theta) dH' + C~^T (e^{Lam} dY)
+// ---------------------------------------------------------------------------
+template <typename T, int N, int P, int R>
+__global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
+  typedef BS<N, P, R> S;
+  constexpr int QB = S::QB, K = S::K, V = S::V, LDN = S::LDN, LDP = S::LDP;
+  constexpr int NW = 4, TH = 64 * NW, NPW = (S::NPT + NW - 1) / NW;
+  // block (bh, seg): the chunks [c_begin, c_end) of one segment of a (b,h)
+  // sequence (one segment spanning all chunks when NS = 1)
+  const int NS = a.S > 1 ? a.S : 1;
+  const int64_t bh = blockIdx.x / NS, seg = blockIdx.x % NS, b = bh / a.H, h = bh % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
+  const int64_t L = a.L, nch = (L + QB - 1) / QB;
+  const int64_t c_begin = NS > 1 ? seg * a.cps : 0, c_end = NS > 1 ? (c_begin + a.cps < nch ? c_begin + a.cps : nch) : nch;
+  if (seg == 0) return;  // the first segment's start adjoint is not needed
+  auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
+  const uint32_t Hu = (uint32_t)a.H;
+
+  // bf16 io: W = e^{Lam} C~ as bf16 hi + lo parts (fp32 accuracy to ~2^-17)
+  // and dY as loaded, for bf16 MFMAs; fp32 io: fp32 tiles and fp32 MFMAs
+  constexpr bool BF = sizeof(T) == 2;
+  constexpr int LBN = N + 8, LBP = P + 8;
+  __shared__ float sW[BF ? 4 : V * LDN], sX[BF ? 4 : V * LDP];
+  __shared__ __attribute__((aligned(16))) u16 tWh[BF ? V * LBN : 8], tWl[BF ? V * LBN : 8], tX[BF ? V * LBP : 8];
+  __shared__ float2 sCS[QB][K];
+  __shared__ float sLam[QB], sQ[QB], sDA[QB], sOm[QB][K];
+  __shared__ TokScal sT[QB];
+
+  // dH' in the MFMA accumulator layout, zero at the segment end (dh_final
+  // enters through the segment scan, with the last segment's transition)
+  f32x4 Hs[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) Hs[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // The inputs of a chunk are fetched into registers one chunk ahead, as
+  // loaded: nothing consumes them before the chunk is staged, so their
+  // latency overlaps the current chunk's work.
+  constexpr int OMP = (QB * K + TH - 1) / TH;
+  RowVecs<T, N, V, TH> rb;
+  RowVecs<T, P, V, TH> rx;
+  float omd[OMP], omt[OMP];
+  TokRaw tsv{0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  auto fetch = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t a0 = c * QB, t0 = tok_of(a0);
+    const int nv = (int)(L - a0 < QB ? L - a0 : QB), nv1 = (int)(L - a0 < QB + 1 ? L - a0 : QB + 1);
+    rb.load((const char*)a.C + t0 * (R * N * io<T>::BYTES), tid, R, Hu * (R * N), nv);
+    rx.load((const char*)a.dy + t0 * (R * P * io<T>::BYTES), tid, R, Hu * (R * P), nv);
+    if (tid < QB) {
+      tsv = TokRaw{0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      uint32_t o = (uint32_t)tid * Hu;
+      fresh(o);
+      if (tid < nv) {
+        tsv.d = (a.dt + t0)[o];
+        tsv.A = (a.A + t0)[o];
+        tsv.lam = (a.lam + t0)[o];
+        if (tid + 1 < nv1) {
+          tsv.dn = (a.dt + t0)[o + Hu];
+          tsv.ln = (a.lam + t0)[o + Hu];
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < OMP; ++q) {
+      const int e = tid + TH * q, t = e / K, k = e % K;
+      const bool ok = e < QB * K && t < nv;
+      uint32_t od = (uint32_t)t * Hu, ot = od * K + k;
+      fresh(od);
+      fresh(ot);
+      omd[q] = ok ? (a.dt + t0)[od] : 0.0f;
+      omt[q] = ok ? (a.theta + t0 * K)[ot] : 0.0f;
+    }
+  };
+  if (c_begin < c_end) fetch(c_end - 1);
+
+  for (int64_t c = c_end - 1; c >= c_begin; --c) {
+    if (tid < QB) {
+      sT[tid] = tsv.scal();
+      sDA[tid] = tsv.d * tsv.A;
+    }
+#pragma unroll
+    for (int q = 0; q < OMP; ++q) {
+      const int e = tid + TH * q;
+      if (e < QB * K) sOm[e / K][e % K] = omd[q] * omt[q];
+    }
+    __syncthreads();
+    if (tid < QB) {
+      float lam_c = 0.0f;
+#pragma unroll
+      for (int j = 0; j < QB; ++j) lam_c += j <= tid ? sDA[j] : 0.0f;  // all reads issued at once
+      sLam[tid] = lam_c;
+      sQ[tid] = sT[tid].lam * sT[tid].d + sT[tid].eps_next;
+    }
+#pragma unroll
+    for (int q = 0; q < OMP; ++q) {
+      const int e = tid + TH * q, t = e / K, k = e % K;
+      if (e < QB * K) {
+        float ph = 0.0f;
+#pragma unroll
+        for (int j = 0; j < QB; ++j) ph += j <= t ? sOm[j][k] : 0.0f;
+        float sn, cs;
+        // the chunk-local angle: the hardware sine/cosine (in revolutions) for
+        // bf16 io, the full-precision library routine for fp32 io
+        if constexpr (sizeof(T) == 2) sincos_rev(ph, &sn, &cs);
+        else sincosf(ph, &sn, &cs);
+        sCS[t][k] = make_float2(cs, sn);
+      }
+    }
+    __syncthreads();
+    const float lamQ = sLam[QB - 1];
+    // W = e^{Lam} C~ (rows v = t R + r), dY
+    {
+      constexpr int VEC = io<T>::VEC;
+#pragma unroll
+      for (int q = 0; q < RowVecs<T, N, V, TH>::PER; ++q) {
+        const int e = tid + TH * q;
+        if (e < RowVecs<T, N, V, TH>::ITEMS) {
+          const int v = e / (N / VEC), n0 = (e % (N / VEC)) * VEC, t = v / R;
+          float f[VEC];
+          io<T>::unpack(rb.r[q], f);
+          const float w = __expf(sLam[t]);
+          uint32_t hi[VEC / 2], lo[VEC / 2];
+#pragma unroll
+          for (int j = 0; j < VEC / 2; ++j) {
+            const float2 cs = sCS[t][n0 / 2 + j];
+            const float w0 = w * (cs.x * f[2 * j] + cs.y * f[2 * j + 1]);
+            const float w1 = w * (cs.x * f[2 * j + 1] - cs.y * f[2 * j]);
+            if constexpr (BF) {
+              hi[j] = pack_bf2(w0, w1);
+              lo[j] = pack_bf2(w0 - bf_lo(hi[j]), w1 - bf_hi(hi[j]));  // the differences are exact in fp32
+            } else {
+              sW[v * LDN + n0 + 2 * j] = w0;
+              sW[v * LDN + n0 + 2 * j + 1] = w1;
+            }
+          }
+          if constexpr (BF) {
+            *(uint4*)&tWh[v * LBN + n0] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *(uint4*)&tWl[v * LBN + n0] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < RowVecs<T, P, V, TH>::PER; ++q) {
+        const int e = tid + TH * q;
+        if (e < RowVecs<T, P, V, TH>::ITEMS) {
+          const int v = e / (P / VEC), p0 = (e % (P / VEC)) * VEC;
+          if constexpr (BF) {
+            *(uint4*)&tX[v * LBP + p0] = rx.r[q];
+          } else {
+            float f[VEC];
+            io<T>::unpack(rx.r[q], f);
+#pragma unroll
+            for (int j = 0; j < VEC; ++j) sX[v * LDP + p0 + j] = f[j];
+          }
+        }
+      }
+    }
+    if (c > c_begin) fetch(c - 1);
+    __syncthreads();
+    // S = W^T dY = C~^T (e^{Lam} dY), then dH' <- e^{Lam_end} R(-Theta) dH' + S
+    f32x4 sacc[NPW];
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) sacc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (BF) {
+      // S(n, p) = sum_v W(v, n) dY(v, p): both operands run down tile columns
+      auto rX = [&](int p, int kk, auto e) { return lds_col<decltype(e)::value>(tX, LBP, p, kk); };
+      mmv<NW, S::TN, S::TP, V>([&](int n, int kk, auto e) { return lds_col<decltype(e)::value>(tWh, LBN, n, kk); }, rX,
+                               sacc, wave, m16, g);
+      mmv<NW, S::TN, S::TP, V>([&](int n, int kk, auto e) { return lds_col<decltype(e)::value>(tWl, LBN, n, kk); }, rX,
+                               sacc, wave, m16, g);
+    } else {
+      mm<NW, S::TN, S::TP, V>([&](int n, int v) { return sW[v * LDN + n]; },
+                                     [&](int v, int p) { return sX[v * LDP + p]; }, sacc, wave, m16, g);
+    }
+    const float eQ = __expf(lamQ);
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+      const int ti = wave + NW * j;
+      if (ti < S::NPT) {
+        const int tr = ti / S::TP;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int k = (tr * 16 + 4 * g) / 2 + q;
+          const float2 cs = sCS[QB - 1][k];
+          const float g0 = Hs[j][2 * q], g1 = Hs[j][2 * q + 1];
+          Hs[j][2 * q] = eQ * (cs.x * g0 + cs.y * g1) + sacc[j][2 * q];
+          Hs[j][2 * q + 1] = eQ * (cs.x * g1 - cs.y * g0) + sacc[j][2 * q + 1];
+        }
+      }
+    }
+    __syncthreads();  // LDS reads of this chunk done before the next staging
+  }
+  float* E = a.dh_loc + (bh * NS + seg) * (int64_t)(N * P);
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const int ti = wave + NW * j;
+    if (ti < S::NPT) {
+      const int tr = ti / S::TP, tc = ti % S::TP, p = tc * 16 + m16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) E[(tr * 16 + 4 * g + i) * P + p] = Hs[j][i];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -464,9 +709,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // anyway); fp32 io: fp32 products throughout
   constexpr bool BFO = sizeof(T) == 2;
   constexpr int VVW = (TV * TV + NW - 1) / NW, VNW = (TV * TN + NW - 1) / NW, VPW = (TV * TP + NW - 1) / NW;
-  const int64_t bh = blockIdx.x, b = bh / a.H, h = bh % a.H;
+  // block (bh, seg): the chunks [c_begin, c_end) of one segment, entered with
+  // the true state adjoint at the segment end (one segment when NS = 1)
+  const int NS = a.S > 1 ? a.S : 1;
+  const int64_t bh = blockIdx.x / NS, seg = blockIdx.x % NS, b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
+  const int64_t c_begin = NS > 1 ? seg * a.cps : 0, c_end = NS > 1 ? (c_begin + a.cps < nch ? c_begin + a.cps : nch) : nch;
   auto tok_of = [&](int64_t t) { return (b * L + t) * a.H + h; };
   const uint32_t Hu = (uint32_t)a.H;
 
@@ -506,11 +755,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   for (int j = 0; j < NPW; ++j) {
     const int ti = wave + NW * j;
     Gb[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    if (ti < S::NPT && a.dh_final) {
+    const float* g0 = seg == NS - 1 ? a.dh_final : a.dh_end + (bh * NS + seg) * (int64_t)N * P;
+    if (ti < S::NPT && g0) {
       const int tr = ti / TP, tc = ti % TP;
+      if (seg == NS - 1) g0 += bh * (int64_t)N * P;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        Gb[j][i] = a.dh_final[bh * (int64_t)N * P + (tr * 16 + 4 * g + i) * P + tc * 16 + m16];
+      for (int i = 0; i < 4; ++i) Gb[j][i] = g0[(tr * 16 + 4 * g + i) * P + tc * 16 + m16];
     }
   }
   // the first token of the chunk processed last time: its dt and lam
@@ -569,13 +819,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     const int ti = wave + NW * j;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      ho[j][i] = ti < S::NPT ? ck[nch * (N * P) + ((ti / TP) * 16 + 4 * g + i) * P + (ti % TP) * 16 + m16] : 0.0f;
+      ho[j][i] = ti < S::NPT ? ck[c_end * (N * P) + ((ti / TP) * 16 + 4 * g + i) * P + (ti % TP) * 16 + m16] : 0.0f;
   }
   // dt and lam of the first token of the chunk processed last time
   float pend_d = 0.0f, pend_l = 0.0f;
-  if (nch > 0) fetch(nch - 1);
+  if (c_begin < c_end) fetch(c_end - 1);
 
-  for (int64_t c = nch - 1; c >= 0; --c) {
+  for (int64_t c = c_end - 1; c >= c_begin; --c) {
     const int64_t a0 = c * QB, t0c = tok_of(a0);  // block-uniform
     // The lane coordinates are made opaque once per chunk: the compiler then
     // computes LDS addresses next to their uses instead of hoisting dozens of
@@ -740,7 +990,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       part = lane_sum<1, 64>(part);
       if (lane == 0) sRedW[wave] = part;  // summed over the waves in a fixed order below
     }
-    if (c > 0) {
+    if (c > c_begin) {
       // this chunk's H_in is the H_out of the chunk processed next
 #pragma unroll
       for (int j = 0; j < NPW; ++j) {
@@ -1073,10 +1323,17 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         if (t == 0) {
           // finish the first token of the chunk processed before (it follows
           // this chunk's last token, whose q carries its eps), then hold this one
-          if (c + 1 < nch) {
-            const uint32_t tn = (uint32_t)QB * Hu;
+          const uint32_t tn = (uint32_t)QB * Hu;
+          if (c + 1 < c_end) {
             (a.ddt + t0c)[tn] = pend_ddt + (1.0f - pend_l) * de_next;
             (a.dlam + t0c)[tn] = pend_dlam - pend_d * de_next;
+          } else if (c + 1 < nch) {
+            // that token opens the next segment, walked by another block: its
+            // share from here goes to the boundary record
+            const float dn = (a.dt + t0c)[tn], ln = (a.lam + t0c)[tn];
+            float* bd = a.bnd + (bh * NS + seg + 1) * 4;
+            bd[0] = (1.0f - ln) * de_next;
+            bd[1] = -dn * de_next;
           }
           pend_ddt = ddt;
           pend_dlam = dlam;
@@ -1089,6 +1346,16 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
   }
 
+  if (seg > 0) {
+    // the segment's first token: its parts without the trapezoid weight it
+    // gets from the segment before
+    if (tid == 0) {
+      float* bd = a.bnd + (bh * NS + seg) * 4;
+      bd[2] = pend_ddt;
+      bd[3] = pend_dlam;
+    }
+    return;
+  }
   // ---------------- the state before the first token ----------------
   // H'_0 = h0 + eps_1 prev_B^T prev_x
   const bool has_prev = a.prev_B != nullptr;
@@ -1159,11 +1426,84 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 3. (segments) scan of the state adjoint over the segments, last to first:
+//    the adjoint at the end of segment j-1 is the one at the start of j, i.e.
+//    its local start adjoint plus e^{Lam_j} R(-Theta_j) (adjoint at its end),
+//    with Lam_j, Theta_j the segment's total log-decay and angle per pair.
+//    One thread per (b,h, pair k, column p).
+// ---------------------------------------------------------------------------
+template <int N>
+__global__ __launch_bounds__(256) void bwd_seg_scan_kernel(BwdArgs a, int P) {
+  constexpr int K = N / 2;
+  const int64_t NS = a.S;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= a.batch * a.H * K * P) return;
+  const int p = (int)(i % P), k = (int)((i / P) % K);
+  const int64_t bh = i / ((int64_t)P * K), NP = (int64_t)N * P;
+  const int64_t r0 = (int64_t)(2 * k) * P + p, r1 = r0 + P;
+  float u = a.dh_final ? a.dh_final[bh * NP + r0] : 0.0f, v = a.dh_final ? a.dh_final[bh * NP + r1] : 0.0f;
+  for (int64_t j = NS - 1; j >= 1; --j) {
+    const float* tot = a.seg_tot + (bh * NS + j) * (1 + K);
+    const float dec = expf(tot[0]);
+    float sn, cs;
+    sincosf(tot[1 + k], &sn, &cs);
+    const float* D = a.dh_loc + (bh * NS + j) * NP;
+    const float nu = D[r0] + dec * (cs * u + sn * v);
+    const float nv = D[r1] + dec * (cs * v - sn * u);
+    u = nu;
+    v = nv;
+    float* E = a.dh_end + (bh * NS + j - 1) * NP;
+    E[r0] = u;
+    E[r1] = v;
+  }
+}
+
+// 4. (segments) the first token of every segment j >= 1: its dt and lam
+//    gradients from its own segment plus the part of the segment before.
+__global__ __launch_bounds__(256) void bwd_bnd_kernel(BwdArgs a, int QB) {
+  const int64_t NS = a.S;
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= a.batch * a.H * (NS - 1)) return;
+  const int64_t bh = i / (NS - 1), seg = 1 + i % (NS - 1), b = bh / a.H, h = bh % a.H;
+  const int64_t t = seg * a.cps * QB;
+  if (t >= a.L) return;
+  const float* bd = a.bnd + (bh * NS + seg) * 4;
+  const int64_t tk = (b * a.L + t) * a.H + h;
+  a.ddt[tk] = bd[2] + bd[0];
+  a.dlam[tk] = bd[3] + bd[1];
+}
+
 template <typename T, int N, int P, int R>
 static hipError_t bwd_run(const BwdArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.batch * a.H));
-  hipLaunchKernelGGL((bwd_ckpt_kernel<T, N, P, R>), grid, dim3(256), 0, s, a);
-  hipLaunchKernelGGL((bwd_chunk_kernel<T, N, P, R>), grid, dim3(512), 0, s, a);
+  const int64_t BH = a.batch * a.H;
+  if (a.S <= 1) {
+    const dim3 grid((unsigned)BH);
+    hipLaunchKernelGGL((bwd_ckpt_kernel<T, N, P, R>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_chunk_kernel<T, N, P, R>), grid, dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
+  // segments: the forward states at segment starts (local walks and a scan),
+  // the checkpoints, the state adjoint at segment ends (local reverse walks
+  // and a scan), then every segment's reverse walk and the boundary tokens
+  const dim3 grid((unsigned)(BH * a.S));
+  BwdArgs l = a;
+  l.ckpt_local = 1;
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, N, P, R>), grid, dim3(256), 0, s, l);
+  WalkArgs w{};
+  w.batch = a.batch; w.H = a.H; w.S = a.S;
+  w.seg_end = a.seg_end; w.seg_tot = a.seg_tot; w.seg_in = a.seg_in; w.h_final = nullptr;
+  hipError_t e = launch_seg_scan(N, P, w, s);
+  if (e != hipSuccess) return e;
+  BwdArgs f = a;
+  f.ckpt_local = 0;
+  hipLaunchKernelGGL((bwd_ckpt_kernel<T, N, P, R>), grid, dim3(256), 0, s, f);
+  hipLaunchKernelGGL((bwd_dh_kernel<T, N, P, R>), grid, dim3(256), 0, s, f);
+  const int64_t nt = BH * (N / 2) * P;
+  hipLaunchKernelGGL((bwd_seg_scan_kernel<N>), dim3((unsigned)((nt + 255) / 256)), dim3(256), 0, s, f, P);
+  hipLaunchKernelGGL((bwd_chunk_kernel<T, N, P, R>), grid, dim3(512), 0, s, f);
+  const int64_t nb = BH * (a.S - 1);
+  hipLaunchKernelGGL(bwd_bnd_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, f, BS<N, P, R>::QB);
   return hipGetLastError();
 }
 

@@ -91,6 +91,17 @@ struct BwdArgs {
   float* ckpt;                  // workspace: (B*H, nchunks + 1, N, P) fp32 states at chunk starts
   int64_t batch, L, H;
   int R;
+  // sequence segments (S > 1: each (b,h) walked as S runs of cps chunks by
+  // separate blocks; the workspace arrays below are then set)
+  int S;
+  int64_t cps;
+  float* seg_end;  // (B*H*S, N, P) segment end states walked from a zero state
+  float* seg_tot;  // (B*H*S, 1 + N/2) segment log-decay and angle totals
+  float* seg_in;   // (B*H*S, N, P) true states entering the segments
+  float* dh_loc;   // (B*H*S, N, P) state adjoint at each segment start, walked from zero at its end
+  float* dh_end;   // (B*H*S, N, P) true state adjoint at each segment end
+  float* bnd;      // (B*H*S, 4) first-token dt / lam gradient parts across segment boundaries
+  int ckpt_local;  // checkpoint walk: 1 = end states and totals only (segments from zero)
 };
 // tokens per chunk of the backward walk: 16, or 8 when N or P is 128 and
 // R = 4 (so that the chunk's tiles fit LDS)
@@ -101,6 +112,8 @@ hipError_t launch_chunked_bwd(int io_bf16, int N, int P, const BwdArgs& a, hipSt
 // After a walk with S > 1 segments: segment scan (true incoming states and
 // h_final) and the output fix-up of segments 1..S-1 (bf16 io).
 hipError_t launch_segment_fixups(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
+// The segment scan alone (seg_end, seg_tot -> seg_in and h_final when set).
+hipError_t launch_seg_scan(int N, int P, const WalkArgs& a, hipStream_t s);
 
 // Fill n floats of dst with src (or zeros when src is NULL).
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s);

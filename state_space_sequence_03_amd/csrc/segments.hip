@@ -327,6 +327,23 @@ static hipError_t seg_p(int io_bf16, int P, const WalkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int N>
+static hipError_t seg_scan_only(int P, const WalkArgs& a, hipStream_t s) {
+  const int64_t total = a.batch * a.H * (N / 2) * P;
+  hipLaunchKernelGGL((seg_scan_kernel<N>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_scan(int N, int P, const WalkArgs& a, hipStream_t s) {
+  switch (N) {
+    case 16: return seg_scan_only<16>(P, a, s);
+    case 32: return seg_scan_only<32>(P, a, s);
+    case 64: return seg_scan_only<64>(P, a, s);
+    case 128: return seg_scan_only<128>(P, a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_segment_fixups(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s) {
   switch (N) {
     case 16: return seg_p<16>(io_bf16, P, a, s);

@@ -159,14 +159,15 @@ def chunked_bwd_workspace_size(dims: Dims) -> int:
 
 
 def mamba3_ssm_chunked_bwd(x, B, C, dt, A, lam, theta, dy, h0=None, prev_B=None, prev_x=None, dh_final=None, *,
-                           chunk=64, want_dh0=True, workspace=None, stream=None):
+                           chunk=64, segments=0, want_dh0=True, workspace=None, stream=None):
     """Backward of the chunked forward.  Returns a dict with dx, dB, dC (io dtype),
     ddt, dA, dlam, dtheta (fp32), dh0 (fp32, if wanted) and, when prev is given,
-    dprev_B and dprev_x (io dtype)."""
+    dprev_B and dprev_x (io dtype).  segments: 0 = the library's choice, else
+    the number of sequence segments walked in parallel (flags' low 16 bits)."""
     torch = _torch()
     b, L, H, R, P = x.shape
     N = B.shape[-1]
-    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x))
+    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x), flags=segments)
     out = {"dx": torch.empty_like(x), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
            "ddt": torch.empty_like(dt), "dA": torch.empty_like(A), "dlam": torch.empty_like(lam),
            "dtheta": torch.empty_like(theta)}

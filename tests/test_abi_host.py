@@ -138,9 +138,15 @@ def test_backward_validation(L):
     assert L.chunked_bwd_workspace_size(d) == 4 * 6 * ((100 + 15) // 16 + 1) * 64 * 64
     assert call_bwd(L, dims(L, dstate=15)) == L.M3_ERR_SHAPE
     assert call_bwd(L, dims(L, headdim=128, dstate=128)) == L.M3_ERR_UNSUPPORTED   # not both 128
-    long = dims(L, batch=1, seqlen=100, nheads=2, dstate=128)                      # 8-token chunks at R = 4
+    long = dims(L, batch=1, seqlen=100, nheads=2, dstate=128, flags=1)             # 8-token chunks at R = 4, one segment
     assert L.chunked_bwd_workspace_size(long) == 4 * 2 * ((100 + 7) // 8 + 1) * 128 * 64
-    assert call_bwd(L, dims(L, flags=1)) == L.M3_ERR_UNSUPPORTED
+    # segments: 13 chunks of 8 tokens at B*H = 2 -> 3 segments of 5, 5, 3 chunks; checkpoints + four
+    # (B*H*S, N, P) state arrays + totals + boundary records, each rounded up to 256 bytes
+    up = lambda v: (v + 255) // 256 * 256
+    seg = dims(L, batch=1, seqlen=100, nheads=2, dstate=128)
+    st = up(4 * 2 * 3 * 128 * 64)
+    assert L.chunked_bwd_workspace_size(seg) == up(4 * 2 * 14 * 128 * 64) + 4 * st + up(4 * 2 * 3 * 65) + up(4 * 2 * 3 * 4)
+    assert call_bwd(L, dims(L, flags=1 << 16)) == L.M3_ERR_UNSUPPORTED
     assert call_bwd(L, dims(L, batch=1, seqlen=16, nheads=65537)) == L.M3_ERR_UNSUPPORTED  # 32-bit chunk offsets
     assert call_bwd(L, d, dy=None) == L.M3_ERR_NULL
     assert call_bwd(L, d, dtheta=None) == L.M3_ERR_NULL

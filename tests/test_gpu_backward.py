@@ -54,8 +54,9 @@ def dev(a, io, key):
     return t.float()
 
 
-def run_case(ops, b, L, H, P, N, R, io, h0, prev, dhf, seed):
-    inp = numpy_inputs(b, L, H, P, N, R, io=io, seed=seed, with_h0=h0, with_prev=prev)
+def run_case(ops, b, L, H, P, N, R, io, h0, prev, dhf, seed, segments=0, a_range=None):
+    kw = {} if a_range is None else {"a_range": a_range}
+    inp = numpy_inputs(b, L, H, P, N, R, io=io, seed=seed, with_h0=h0, with_prev=prev, **kw)
     rng = np.random.default_rng(seed + 7)
     dy = rng.standard_normal((b, L, H, R, P)).astype(np.float32)
     if io == "bf16":
@@ -64,7 +65,7 @@ def run_case(ops, b, L, H, P, N, R, io, h0, prev, dhf, seed):
     d = {k: dev(v, io, k) for k, v in inp.items()}
     g = ops.chunked_bwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], dev(dy, io, "dy"),
                         h0=d.get("h0"), prev_B=d.get("prev_B"), prev_x=d.get("prev_x"),
-                        dh_final=None if dh is None else dev(dh, io, "dh"))
+                        dh_final=None if dh is None else dev(dh, io, "dh"), segments=segments)
     torch.cuda.synchronize()
     ref = oracle.backward(inp["x"], inp["B"], inp["C"], inp["dt"], inp["A"], inp["lam"], inp["theta"], dy,
                           h0=inp.get("h0"), prev_B=inp.get("prev_B"), prev_x=inp.get("prev_x"), dh_final=dh)
@@ -100,6 +101,33 @@ def test_backward_matches_oracle(ops, case):
     say(f"chunked_bwd {case}")
     errs = run_case(ops, b, L, H, P, N, R, io, h0, prev, dhf, zlib.crc32(repr(case).encode()) % 10000)
     assert max(errs.values()) < TOL[io], errs
+
+
+# sequence segments walked by separate blocks (forced counts; ragged last
+# segments and chunks; one-chunk segments)
+SEG_CASES = [
+    # io,    b, L,   H, P,  N,   R, h0,    prev,  dh_final, segments
+    ("f32", 1, 300, 2, 32, 32, 2, True, True, True, 3),
+    ("bf16", 1, 200, 2, 64, 64, 4, True, True, True, 4),
+    ("bf16", 2, 150, 1, 64, 128, 4, False, True, True, 5),
+    ("f32", 1, 64, 2, 16, 16, 1, False, False, False, 4),
+    ("bf16", 1, 129, 3, 64, 64, 1, True, False, False, 2),
+]
+
+
+@pytest.mark.parametrize("case", SEG_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_backward_segments_match_oracle(ops, case):
+    io, b, L, H, P, N, R, h0, prev, dhf, segs = case
+    say(f"chunked_bwd segments {case}")
+    errs = run_case(ops, b, L, H, P, N, R, io, h0, prev, dhf, zlib.crc32(repr(case).encode()) % 10000, segments=segs)
+    assert max(errs.values()) < TOL[io], errs
+
+
+def test_backward_segments_slow_decay(ops):
+    """A in [-1e-2, 0], four segments: the adjoint reaches back across them."""
+    say("chunked_bwd segments slow decay")
+    errs = run_case(ops, 1, 300, 2, 32, 32, 2, "f32", True, True, True, 11, segments=4, a_range=(-30.0, np.log(1e-2)))
+    assert max(errs.values()) < 1e-3, errs
 
 
 def test_backward_slow_decay(ops):
