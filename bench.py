@@ -218,21 +218,26 @@ def bench_verify(ops, inputs, w, k, steps, warmup, torch):
                 gbps=b / (ms * 1e-3) / 1e9, chunk_walk_ms=res["chunk_walk"])
 
 
-BWD_CHUNK = 16
+def bwd_chunk(w):
+    """Tokens per chunk of the backward walk: 16, or 8 when N or P is 128
+    and R = 4."""
+    return 8 if (w.dstate > 64 or w.headdim > 64) and w.rank == 4 else 16
 
 
 def backward_flops_per_token_head(w):
     """Dense MFMA flops of the backward per token-head, as (checkpoint walk,
-    reverse walk): per 16-token chunk (V = 16 R rows) the checkpoint walk's
+    reverse walk): per chunk of Q = 16 tokens (8 when N or P is 128 and
+    R = 4; V = Q R rows) the checkpoint walk's
     state product W^T X and the reverse walk's nine products (G, dGM, two for
     dX, two for dC~, two for dB~ and dH_in), each 2 M N K. With bf16 io all of
     them run on bf16 MFMAs, the checkpoint product twice (bf16 hi and lo parts
     of W)."""
-    V, N, P = BWD_CHUNK * w.rank, w.dstate, w.headdim
+    Q = bwd_chunk(w)
+    V, N, P = Q * w.rank, w.dstate, w.headdim
     ckpt = 2 * (N * P * V)
     walk = 2 * (V * V * N + V * V * P + V * P * V + V * P * N + V * N * V + V * N * P + V * N * V + V * N * P
                 + N * P * V)
-    return ckpt / BWD_CHUNK, walk / BWD_CHUNK
+    return ckpt / Q, walk / Q
 
 
 def backward_bytes_per_token_head(w, s_io=2):
@@ -242,7 +247,7 @@ def backward_bytes_per_token_head(w, s_io=2):
     R, N, P = w.rank, w.dstate, w.headdim
     io_in = s_io * R * (2 * P + 2 * N) + 12 + 2 * N
     io_out = s_io * R * (P + 2 * N) + 12 + 2 * N
-    states = 2 * N * P * 4 / BWD_CHUNK
+    states = 2 * N * P * 4 / bwd_chunk(w)
     return io_in + io_out + states
 
 
@@ -297,8 +302,10 @@ def cpu_baseline(inputs, w, budget_s=12.0):
     t0 = time.perf_counter()
     oracle.forward(one["x"], one["B"], one["C"], one["dt"], one["A"], one["lam"], one["theta"], nthreads=1)
     t_one = time.perf_counter() - t0
-    # whole multiples of the core count, for about budget_s of wall time
-    nsl = cores * max(1, min(16, int(round(budget_s / max(t_one, 1e-3)))))
+    # whole multiples of the core count, for about budget_s of wall time; at
+    # most the whole workload (all B*H slices)
+    total = w.batch * w.nheads
+    nsl = min(total, cores * max(1, int(round(budget_s / max(t_one, 1e-3)))))
     batch = draw(nsl, 6)
     t0 = time.perf_counter()
     oracle.forward(batch["x"], batch["B"], batch["C"], batch["dt"], batch["A"], batch["lam"], batch["theta"],
@@ -306,7 +313,7 @@ def cpu_baseline(inputs, w, budget_s=12.0):
     dt = time.perf_counter() - t0
     token_heads_per_s = nsl * w.seqlen / dt
     return dict(value=token_heads_per_s / w.nheads, unit="tokens/s", cores=min(cores, nsl), kind="oracle",
-                sample=f"{nsl} (b,h) slices x L={w.seqlen} of the {w.name} workload "
+                sample=f"{nsl} of the {total} (b,h) slices x L={w.seqlen} of the {w.name} workload "
                        f"({nsl * w.seqlen} token-heads in {dt:.1f} s); tokens/s = token-heads/s / H={w.nheads}")
 
 
@@ -404,6 +411,8 @@ def main():
         for name in ("siso_bf16", "long_mimo_bf16"):
             print(f"[bench] prefill {name} (context)", file=sys.stderr, flush=True)
             out[name] = bench_prefill(ops, inputs, W[name], 3, 1, torch)
+        print("[bench] backward long_mimo_bf16 (context)", file=sys.stderr, flush=True)
+        out["backward_long"] = bench_backward(ops, inputs, W["long_mimo_bf16"], 3, 1, torch)
 
     line = {"metric": "SSM prefill tokens/s + %MFMA peak (R=4); decode steps/s + HBM GB/s",
             "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -444,17 +453,23 @@ def main():
                           "achieved_GBps": round(vf["gbps"], 1), "frac": round(vf["gbps"] / HBM_PEAK_GBPS, 4),
                           "bytes_per_call": vf["bytes_per_call"],
                           "chunk_walk_ms_per_call": round(vf["chunk_walk_ms"], 5)}
+    def backward_entry(bw, workload):
+        return {"workload": workload, "ms": round(bw["ms"], 4), "tokens_per_s": round(bw["tokens_per_s"], 1),
+                "bound": "hbm" if bw["hbm_floor_ms"] >= bw["mfma_floor_ms"] else "mfma",
+                "achieved_GBps": round(bw["gbps"], 1), "peak_GBps": HBM_PEAK_GBPS,
+                "frac": round(max(bw["hbm_floor_ms"], bw["mfma_floor_ms"]) / bw["ms"], 4),
+                "bytes_per_call": round(bw["bytes"]), "achieved_TFLOPs": round(bw["tflops"], 1),
+                "flops_per_call": bw["flops"], "hbm_floor_ms": round(bw["hbm_floor_ms"], 4),
+                "mfma_floor_ms": round(bw["mfma_floor_ms"], 4)}
+
     if "backward" in out:
-        bw = out["backward"]
-        line["backward"] = {"workload": f"{w.name} backward (mamba3_ssm_chunked_bwd, dy ~ N(0,1); bf16 MFMA "
-                                        f"operands with fp32 accumulation, the checkpoint walk's in hi + lo parts)",
-                            "ms": round(bw["ms"], 4), "tokens_per_s": round(bw["tokens_per_s"], 1),
-                            "bound": "hbm" if bw["hbm_floor_ms"] >= bw["mfma_floor_ms"] else "mfma",
-                            "achieved_GBps": round(bw["gbps"], 1), "peak_GBps": HBM_PEAK_GBPS,
-                            "frac": round(max(bw["hbm_floor_ms"], bw["mfma_floor_ms"]) / bw["ms"], 4),
-                            "bytes_per_call": round(bw["bytes"]), "achieved_TFLOPs": round(bw["tflops"], 1),
-                            "flops_per_call": bw["flops"], "hbm_floor_ms": round(bw["hbm_floor_ms"], 4),
-                            "mfma_floor_ms": round(bw["mfma_floor_ms"], 4)}
+        line["backward"] = backward_entry(out["backward"],
+                                          f"{w.name} backward (mamba3_ssm_chunked_bwd, dy ~ N(0,1); bf16 MFMA "
+                                          f"operands with fp32 accumulation, the checkpoint walk's in hi + lo parts)")
+    if "backward_long" in out:
+        line["backward_long_mimo_bf16"] = backward_entry(
+            out["backward_long"], "long_mimo_bf16 backward: batch 1, L=65536, H=32, P=64, N=128, R=4, 8-token "
+                                  "chunks, each sequence walked as segments (library default)")
     if "rope" in out:
         line["rope_bc"] = {"ms": round(out["rope"]["ms"], 4), "achieved_GBps": round(out["rope"]["gbps"], 1),
                            "frac": round(out["rope"]["gbps"] / HBM_PEAK_GBPS, 4)}

@@ -105,7 +105,10 @@ typedef struct {
                        library: more than one only for bf16 io when B*H <
                        256); M3_FLAG_CHUNK_WALK or M3_FLAG_TOKEN_PATH;
                        other bits must be 0.
-                       Segments > 1 need bf16 io and B*H <= 65535.  Other
+                       Segments > 1 need bf16 io and B*H <= 65535.
+                       chunked_bwd: bits 0..15 = number of sequence
+                       segments (0 = chosen by the library: more than one
+                       only when B*H < 256); other bits must be 0.  Other
                        entry points: must be 0. */
 } m3_dims;
 
@@ -165,11 +168,23 @@ size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d);
  * 32-bit).  Products: fp32 for fp32 io; bf16 MFMAs with fp32 accumulation
  * for bf16 io (operands rounded to bf16; the state product of the checkpoint
  * walk takes w B~ as bf16 hi + lo parts), with fp32 state checkpoints.
+ * Segments (flags bits 0..15, for few long sequences): each sequence is cut
+ * into runs of whole chunks that separate blocks walk at once.  The states at
+ * segment starts come from walks from a zero state and the forward's segment
+ * scan; the state adjoints at segment ends from walks of the adjoint from zero
+ * and a reverse scan (the adjoint recurrence is linear too); the first token
+ * of each segment takes the parts of its dt and lam gradients that the
+ * previous segment computes.  The result is the same function; only rounding
+ * differs.  The library picks ceil(512 / (B*H)) segments (at most a quarter
+ * of the chunks) when B*H < 256 and one otherwise; a count above the number
+ * of chunks is clamped to it.
  * workspace: at least
  * mamba3_ssm_chunked_bwd_workspace_size(d) bytes (the states at every chunk
- * start); its contents on entry do not matter.  Outputs must not alias inputs.
+ * start, and with segments four (B, H, S, N, P) fp32 arrays and small
+ * per-segment records); its contents on entry do not matter.  Outputs must
+ * not alias inputs.
  * Alignment: x, B, C, dy, dx, dB, dC, theta, dtheta and the workspace 16-byte;
- * the others their element size.  flags must be 0. */
+ * the others their element size. */
 m3_status mamba3_ssm_chunked_bwd(const m3_dims* d,
                                  const void* x, const void* B, const void* C,
                                  const float* dt, const float* A, const float* lam, const float* theta,

@@ -179,6 +179,39 @@ def test_backward_full_workload_sampled(ops):
     assert e < TOL["bf16"]
 
 
+def test_backward_long_workload_sampled(ops):
+    """The long_mimo_bf16 workload at full size (batch 1, L=65536, H=32, P=64,
+    N=128, R=4, bf16) with dy ~ N(0, 1) and the library's default sequence
+    segments, as the benchmark runs it; two heads checked against the oracle
+    backward over the whole sequence."""
+    w = WORKLOADS["long_mimo_bf16"]
+    say("backward long workload: generating")
+    d = torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io, seed=seed_of(w.name) + 1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed_of(w.name) + 2)
+    dy = torch.randn(d["x"].shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    dims = ops.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk, ops.M3_BF16)
+    one = ops.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, w.chunk, ops.M3_BF16, flags=1)
+    assert ops.chunked_bwd_workspace_size(dims) > ops.chunked_bwd_workspace_size(one)  # segments are in use
+    say("backward long workload: chunked_bwd")
+    g = ops.chunked_bwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], dy, chunk=w.chunk)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    heads = [int(h) for h in rng.choice(w.nheads, 2, replace=False)]
+    say(f"backward long workload: oracle on heads {heads}")
+    host = lambda t: t.float().cpu().numpy().astype(np.float64)
+    cat = lambda t: np.concatenate([host(t[:, :, hi:hi + 1]) for hi in heads], 2)
+    ref = oracle.backward(cat(d["x"]), cat(d["B"]), cat(d["C"]), cat(d["dt"]), cat(d["A"]), cat(d["lam"]),
+                          cat(d["theta"]), cat(dy))
+    for k in ("dx", "dB", "dC", "ddt", "dA", "dlam", "dtheta"):
+        e = slice_err(cat(g[k]), ref[k], (0, 2))
+        say(f"   {k} {e:.2e}")
+        assert e < TOL["bf16"], (k, e)
+    e = slice_err(np.concatenate([host(g["dh0"][:, hi:hi + 1]) for hi in heads], 1), ref["dh0"], (0, 1))
+    say(f"   dh0 {e:.2e}")
+    assert e < TOL["bf16"]
+
+
 def test_backward_workspace_and_rejections(ops):
     d = ops.make_dims(2, 100, 3, 64, 64, 4, 64, ops.M3_BF16)
     assert ops.chunked_bwd_workspace_size(d) == 4 * 6 * (7 + 1) * 64 * 64
