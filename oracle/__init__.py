@@ -163,3 +163,7 @@ def rope_bc(B, C, dt, theta, angle0=None, mutant: int = 0):
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return Br, Cr, af
+
+
+# The B/C prologue (projection, RMS normalisation, bias, rotation) in numpy.
+from .prologue import bc_prologue  # noqa: E402

@@ -129,3 +129,57 @@ def torch_inputs(batch, seqlen, nheads, headdim, dstate, rank, io=BF16, seed=0, 
     if with_h0:
         out["h0"] = normal((b, H, N, P), h0_std)
     return out
+
+
+# The B/C prologue: the projection of the layer's token activations u to B and
+# C, RMS normalisation of every (token, head, rank) vector over N, a bias, and
+# the cumulative-angle rotation.  d_model = H*P/2 (an expansion of 2 from the
+# model width to the H*P inner width) gives 2048 for the 1.5B shapes.
+PROLOGUE = dict(batch=8, seqlen=4096, nheads=64, dstate=64, rank=4, d_model=2048)
+PROLOGUE_SEED = 1100
+
+# Prologue draws (std as the second argument of N):
+#   u ~ N(0, 1) (activations after the block's input norm), bf16;
+#   W ~ N(0, 1/D) i.e. std 1/sqrt(D), the rows of W_B then of W_C, bf16;
+#   gain = 1 + N(0, 0.1^2), bias ~ N(0, 0.1^2), fp32, shape (2, H, R, N) (B then C);
+#   dt, theta as for the core; angle0 ~ U(-pi, pi).
+
+
+def prologue_numpy(batch, seqlen, nheads, dstate, rank, d_model, seed=0, with_gain=True, with_bias=True,
+                   with_angle0=False):
+    """Inputs of the B/C prologue drawn with numpy (u and W bf16-representable)."""
+    rng = np.random.default_rng(seed)
+    b, L, H, N, R, D = batch, seqlen, nheads, dstate, rank, d_model
+    f = np.float32
+    out = dict(u=round_bf16_np(rng.standard_normal((b, L, D)).astype(f)),
+               W=round_bf16_np((rng.standard_normal((2 * H * R * N, D)) / math.sqrt(D)).astype(f)))
+    z = rng.normal(-2.0, 0.5, (b, L, H))
+    out["dt"] = np.logaddexp(0.0, z).astype(f)
+    out["theta"] = rng.uniform(-math.pi, math.pi, (b, L, H, N // 2)).astype(f)
+    if with_gain:
+        out["gain"] = (1.0 + 0.1 * rng.standard_normal((2, H, R, N))).astype(f)
+    if with_bias:
+        out["bias"] = (0.1 * rng.standard_normal((2, H, R, N))).astype(f)
+    if with_angle0:
+        out["angle0"] = rng.uniform(-math.pi, math.pi, (b, H, N // 2)).astype(f)
+    return out
+
+
+def prologue_torch(batch, seqlen, nheads, dstate, rank, d_model, seed=0, device="cuda"):
+    """Inputs of the B/C prologue drawn on the device (u, W bf16; the rest fp32)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    b, L, H, N, R, D = batch, seqlen, nheads, dstate, rank, d_model
+    f32 = torch.float32
+
+    def normal(shape, std=1.0, mean=0.0):
+        return torch.randn(shape, generator=g, device=device, dtype=f32).mul_(std).add_(mean)
+
+    u = normal((b, L, D)).to(torch.bfloat16)
+    W = normal((2 * H * R * N, D), 1.0 / math.sqrt(D)).to(torch.bfloat16)
+    dt = torch.nn.functional.softplus(normal((b, L, H), 0.5, -2.0))
+    theta = (torch.rand((b, L, H, N // 2), generator=g, device=device, dtype=f32) * 2.0 - 1.0) * math.pi
+    gain = normal((2, H, R, N), 0.1, 1.0)
+    bias = normal((2, H, R, N), 0.1)
+    return dict(u=u, W=W, dt=dt, theta=theta, gain=gain, bias=bias)
