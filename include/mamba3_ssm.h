@@ -220,6 +220,45 @@ m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C,
                          void* workspace, size_t workspace_bytes, void* stream);
 size_t mamba3_rope_bc_workspace_size(const m3_dims* d);
 
+/* B/C prologue: the projection of the token activations to B and C with the
+ * normalisation, bias and rotation applied on the way out, so that B_rot and
+ * C_rot are written once (the input projection of the block,
+ * papers.ananclaw.com/promo/explainers__2603-15569, "关键公式与“伪代码”"; RMS
+ * normalisation and bias of B and C, linkstar.cloud/article/869,
+ * "架构上的其他改动"; the rotation fused with the projection, same page,
+ * "第二刀"):
+ *   p_t = W u_t  (features ordered (B or C, head, rank, n)),
+ *   v = p / sqrt(mean_n p^2 + eps) * gain + bias  (per (token, B or C, head,
+ *       rank) vector of N entries),
+ *   B_rot, C_rot = R(-phi_t) v with phi_t = angle0 + sum_{s<=t} dt_s theta_s
+ *       (as mamba3_rope_bc), angle_final = phi_L.
+ * B_rot and C_rot are in the frame that chunked_fwd expects when it is given
+ * theta = 0 (then its h_final is in that frame too).
+ *   d: batch, seqlen, nheads, dstate (N), rank (R) as for the core; headdim and
+ *      chunk are ignored; io_dtype must be M3_BF16; flags 0.
+ *   d_model: D, a positive multiple of 64 (M3_ERR_UNSUPPORTED otherwise).
+ *   u: (B, L, D) bf16.  W: (2*H*R*N, D) bf16, row-major: the H*R*N rows of
+ *      W_B, then those of W_C.
+ *   gain, bias: nullable (2, H, R, N) fp32 (NULL: 1 and 0).
+ *   eps: >= 0 and finite (M3_ERR_UNSUPPORTED otherwise).  With eps = 0 an
+ *      all-zero projected vector gives NaN, as the formula does.
+ *   dt (B, L, H), theta (B, L, H, N/2), angle0 nullable (B, H, N/2): fp32.
+ *   B_rot, C_rot: (B, L, H, R, N) bf16, written (must not alias inputs).
+ *   angle_final: nullable (B, H, N/2) fp32, written.
+ *   workspace: at least mamba3_bc_prologue_workspace_size(d) bytes (the angles
+ *      of every token and their chunk totals, fp32); contents on entry do not
+ *      matter.
+ * Products: bf16 MFMAs with fp32 accumulation; normalisation, bias and
+ * rotation in fp32; outputs rounded to bf16 (nearest even).
+ * Alignment: u, W, B_rot, C_rot, gain, bias and the workspace 16-byte; the
+ * others 4-byte.  seqlen is limited to 65535 * 64 tokens. */
+m3_status mamba3_bc_prologue(const m3_dims* d, int64_t d_model, const void* u, const void* W,
+                             const float* gain, const float* bias, float eps,
+                             const float* dt, const float* theta, const float* angle0,
+                             void* B_rot, void* C_rot, float* angle_final,
+                             void* workspace, size_t workspace_bytes, void* stream);
+size_t mamba3_bc_prologue_workspace_size(const m3_dims* d);
+
 const char* mamba3_status_string(m3_status s);
 int mamba3_abi_version(void);
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmamba3_ssm.so")
-SOURCES = ["abi.cpp", "decode.hip", "rope.hip", "chunk.hip", "chunk_fast.hip", "chunk_subwalk.hip", "segments.hip", "backward.hip"]
+SOURCES = ["abi.cpp", "decode.hip", "rope.hip", "chunk.hip", "chunk_fast.hip", "chunk_subwalk.hip", "segments.hip", "backward.hip", "prologue.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]

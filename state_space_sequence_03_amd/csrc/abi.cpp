@@ -365,4 +365,64 @@ m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C, const f
   return e == hipSuccess ? M3_OK : M3_ERR_HIP;
 }
 
+// Workspace of the B/C prologue: the angle chunk totals, then the angles
+// (B, L, H, N/2) fp32, each 256-byte aligned.
+struct ProWs {
+  size_t totals, phi, bytes;
+};
+static ProWs pro_ws(const m3_dims* d) {
+  auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  const size_t K = (size_t)(d->dstate / 2);
+  const size_t nchunks = (size_t)((d->seqlen + m3::ROPE_CHUNK - 1) / m3::ROPE_CHUNK);
+  ProWs w{};
+  w.totals = 0;
+  w.phi = up(sizeof(float) * (size_t)(d->batch * d->nheads) * nchunks * K);
+  w.bytes = w.phi + up(sizeof(float) * (size_t)(d->batch * d->seqlen * d->nheads) * K);
+  return w;
+}
+
+size_t mamba3_bc_prologue_workspace_size(const m3_dims* d) {
+  if (check_dims(d, false, false) != M3_OK) return 0;
+  if (d->batch == 0 || d->nheads == 0 || d->seqlen == 0) return 0;
+  return pro_ws(d).bytes;
+}
+
+m3_status mamba3_bc_prologue(const m3_dims* d, int64_t d_model, const void* u, const void* W, const float* gain,
+                             const float* bias, float eps, const float* dt, const float* theta,
+                             const float* angle0, void* B_rot, void* C_rot, float* angle_final, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  m3_status st = check_dims(d, false, false);
+  if (st != M3_OK) return st;
+  if (d_model <= 0) return M3_ERR_SHAPE;
+  if (d->flags != 0 || d->io_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
+  if (d_model % 64 != 0 || !(eps >= 0.0f) || eps > 3.0e38f) return M3_ERR_UNSUPPORTED;
+  if ((d->seqlen + m3::ROPE_CHUNK - 1) / m3::ROPE_CHUNK > 65535) return M3_ERR_UNSUPPORTED;  // grid limit
+  const bool empty = d->batch == 0 || d->nheads == 0;
+  const bool has_tokens = !empty && d->seqlen > 0;
+  if (has_tokens && (!u || !W || !dt || !theta || !B_rot || !C_rot)) return M3_ERR_NULL;
+  if (!all_aligned({u, W, B_rot, C_rot, gain, bias, workspace}, {dt, theta, angle0, angle_final}, 4))
+    return M3_ERR_ALIGN;
+  const size_t need = mamba3_bc_prologue_workspace_size(d);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return M3_ERR_WORKSPACE;
+  if (empty) return M3_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const int N = (int)d->dstate;
+  m3::RopeArgs r{};
+  r.dt = dt; r.theta = theta; r.angle0 = angle0; r.angle_final = angle_final;
+  r.batch = d->batch; r.L = d->seqlen; r.H = d->nheads; r.R = (int)d->rank;
+  const ProWs w = pro_ws(d);
+  float* phi = nullptr;
+  if (has_tokens) {
+    r.totals = (float*)((char*)workspace + w.totals);
+    phi = (float*)((char*)workspace + w.phi);
+  }
+  hipError_t e = m3::launch_rope_phi(N, r, phi, s);
+  if (e != hipSuccess || !has_tokens) return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+  m3::ProArgs a{};
+  a.u = u; a.W = W; a.gain = gain; a.bias = bias; a.phi = phi; a.B_rot = B_rot; a.C_rot = C_rot; a.eps = eps;
+  a.M = d->batch * d->seqlen; a.D = d_model; a.H = (int)d->nheads; a.R = (int)d->rank;
+  e = m3::launch_bc_prologue(N, a, s);
+  return e == hipSuccess ? M3_OK : M3_ERR_HIP;
+}
+
 }  // extern "C"

@@ -47,6 +47,24 @@ struct RopeArgs {
 constexpr int ROPE_CHUNK = 64;
 hipError_t launch_rope(int io_bf16, int N, const RopeArgs& a, hipStream_t s);
 
+// The angles of rope_bc alone, written to phi (B, L, H, N/2) fp32; uses
+// a.totals as its workspace and writes a.angle_final when set.
+hipError_t launch_rope_phi(int N, const RopeArgs& a, float* phi, hipStream_t s);
+
+// The B/C prologue: projection, RMS normalisation, bias and rotation.
+struct ProArgs {
+  const void* u;       // (M, D) bf16, M = B*L tokens
+  const void* W;       // (2*H*R*N, D) bf16: rows of W_B, then of W_C
+  const float* gain;   // nullable (2*H*R*N), 16-byte aligned
+  const float* bias;   // nullable (2*H*R*N), 16-byte aligned
+  const float* phi;    // (M, H, N/2) angles from launch_rope_phi
+  void *B_rot, *C_rot; // (M, H, R, N) bf16
+  float eps;
+  int64_t M, D;        // D a multiple of 64
+  int H, R;
+};
+hipError_t launch_bc_prologue(int N, const ProArgs& a, hipStream_t s);
+
 struct WalkArgs {
   const void *x, *B, *C;
   const float *dt, *A, *lam, *theta;

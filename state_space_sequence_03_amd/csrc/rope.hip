@@ -153,6 +153,65 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
   for (int i = tid + 256 * BATCH; i < items; i += 256) rotate_store(i, ldg16<T>(a.B, off(i)), ldg16<T>(a.C, off(i)));
 }
 
+// The angles alone: phi_t per (token, head, pair), written to phi (B, L, H,
+// N/2) fp32 for a consumer that rotates B and C itself (the B/C prologue).
+// Per chunk as in launch 3: the chunk-local wave scan plus the chunk's offset,
+// then the chunk's angles written token by token.
+template <int N>
+__global__ __launch_bounds__(256) void rope_phi_kernel(RopeArgs a, int64_t nchunks, float* phi) {
+  constexpr int K = N / 2;
+  const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t c0 = c * ROPE_CHUNK;
+  const int nvalid = (int)((a.L - c0) < ROPE_CHUNK ? (a.L - c0) : ROPE_CHUNK);
+  __shared__ float om[ROPE_CHUNK][K + 1];
+  for (int i = tid; i < ROPE_CHUNK * K; i += 256) {
+    const int t = i / K, k = i % K;
+    float v = 0.0f;
+    if (t < nvalid) {
+      const int64_t idx = (b * a.L + c0 + t) * a.H + h;
+      v = a.dt[idx] * a.theta[idx * K + k];
+    }
+    om[t][k] = v;
+  }
+  __syncthreads();
+  const float* offs = a.totals + ((b * a.H + h) * nchunks + c) * K;
+  for (int k = wave; k < K; k += 4) {
+    const float v = wave_scan_dpp(om[lane][k]) + offs[k];
+    om[lane][k] = v;  // each wave reads and writes only its own pair's column
+  }
+  __syncthreads();
+  for (int i = tid; i < nvalid * K; i += 256) {
+    const int t = i / K, k = i % K;
+    phi[((b * a.L + c0 + t) * a.H + h) * K + k] = om[t][k];
+  }
+}
+
+template <int N>
+static hipError_t rope_phi_run(const RopeArgs& a, float* phi, hipStream_t s) {
+  const int64_t nchunks = (a.L + ROPE_CHUNK - 1) / ROPE_CHUNK;
+  const dim3 g3h((unsigned)a.H, (unsigned)nchunks, (unsigned)a.batch);
+  hipLaunchKernelGGL((rope_totals_kernel<N>), g3h, dim3(256), 0, s, a, nchunks);
+  hipLaunchKernelGGL((rope_scan_kernel<N>), dim3((unsigned)a.H, (unsigned)a.batch), dim3(256), 0, s, a, nchunks);
+  hipLaunchKernelGGL((rope_phi_kernel<N>), g3h, dim3(256), 0, s, a, nchunks, phi);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_phi(int N, const RopeArgs& a, float* phi, hipStream_t s) {
+  if (a.batch == 0 || a.H == 0) return hipSuccess;
+  if (a.L == 0) {
+    if (a.angle_final) return launch_copy_f32(a.angle_final, a.angle0, a.batch * a.H * (N / 2), s);
+    return hipSuccess;
+  }
+  switch (N) {
+    case 16: return rope_phi_run<16>(a, phi, s);
+    case 32: return rope_phi_run<32>(a, phi, s);
+    case 64: return rope_phi_run<64>(a, phi, s);
+    case 128: return rope_phi_run<128>(a, phi, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <typename T, int N>
 static hipError_t rope_run(const RopeArgs& a, hipStream_t s) {
   const int64_t nchunks = (a.L + ROPE_CHUNK - 1) / ROPE_CHUNK;

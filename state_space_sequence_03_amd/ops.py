@@ -25,7 +25,8 @@ M3_TOKEN_PATH_MAX_L = 16       # longest call the token path takes
 M3_TOKEN_PATH_SUBWALK_L = 8    # ... chosen by default when the sub-chunk walker covers the sizes
 ABI_SYMBOLS = ("mamba3_ssm_chunked_fwd", "mamba3_ssm_chunked_fwd_workspace_size", "mamba3_ssm_chunked_bwd",
                "mamba3_ssm_chunked_bwd_workspace_size", "mamba3_ssm_decode_step",
-               "mamba3_rope_bc", "mamba3_rope_bc_workspace_size", "mamba3_status_string", "mamba3_abi_version")
+               "mamba3_rope_bc", "mamba3_rope_bc_workspace_size", "mamba3_bc_prologue",
+               "mamba3_bc_prologue_workspace_size", "mamba3_status_string", "mamba3_abi_version")
 
 
 class Dims(ctypes.Structure):
@@ -67,6 +68,10 @@ def lib() -> ctypes.CDLL:
         L.mamba3_rope_bc.restype = ctypes.c_int
         L.mamba3_rope_bc_workspace_size.argtypes = [dp]
         L.mamba3_rope_bc_workspace_size.restype = sz
+        L.mamba3_bc_prologue.argtypes = [dp, ctypes.c_int64, vp, vp, vp, vp, ctypes.c_float] + [vp] * 6 + [vp, sz, vp]
+        L.mamba3_bc_prologue.restype = ctypes.c_int
+        L.mamba3_bc_prologue_workspace_size.argtypes = [dp]
+        L.mamba3_bc_prologue_workspace_size.restype = sz
         L.mamba3_status_string.argtypes = [ctypes.c_int]
         L.mamba3_status_string.restype = ctypes.c_char_p
         L.mamba3_abi_version.restype = ctypes.c_int
@@ -229,7 +234,40 @@ def mamba3_rope_bc(B, C, dt, theta, angle0=None, *, B_rot=None, C_rot=None, angl
     return B_rot, C_rot, angle_final
 
 
+def bc_prologue_workspace_size(dims: Dims) -> int:
+    return int(lib().mamba3_bc_prologue_workspace_size(ctypes.byref(dims)))
+
+
+def mamba3_bc_prologue(u, W, dt, theta, nheads, rank, dstate, gain=None, bias=None, eps=1e-5, angle0=None, *,
+                       B_rot=None, C_rot=None, angle_final=None, want_final=True, workspace=None, stream=None):
+    """Projection of u (B, L, D) by W (2*H*R*N, D) to B and C, RMS-normalised
+    per (token, head, rank) vector with gain and bias, and rotated by the
+    cumulative angle.  Returns (B_rot, C_rot, angle_final)."""
+    torch = _torch()
+    b, L, D = u.shape
+    H, R, N = nheads, rank, dstate
+    dims = make_dims(b, L, H, 16, N, R, 16, _io_code(u))
+    if B_rot is None:
+        B_rot = torch.empty((b, L, H, R, N), device=u.device, dtype=u.dtype)
+    if C_rot is None:
+        C_rot = torch.empty((b, L, H, R, N), device=u.device, dtype=u.dtype)
+    if angle_final is None and want_final:
+        angle_final = torch.empty((b, H, N // 2), device=u.device, dtype=torch.float32)
+    if tuple(W.shape) != (2 * H * R * N, D):
+        raise ValueError("W must be (2*H*R*N, D)")
+    ws_bytes = bc_prologue_workspace_size(dims)
+    if ws_bytes > 0 and workspace is None:
+        workspace = torch.empty(ws_bytes, device=u.device, dtype=torch.uint8)
+    st = lib().mamba3_bc_prologue(ctypes.byref(dims), ctypes.c_int64(D), _ptr(u), _ptr(W), _ptr(gain), _ptr(bias),
+                                  ctypes.c_float(eps), _ptr(dt), _ptr(theta), _ptr(angle0), _ptr(B_rot), _ptr(C_rot),
+                                  _ptr(angle_final), _ptr(workspace),
+                                  ctypes.c_size_t(workspace.numel() if workspace is not None else 0), _stream(stream))
+    _check(st, "mamba3_bc_prologue")
+    return B_rot, C_rot, angle_final
+
+
 chunked_fwd = mamba3_ssm_chunked_fwd
 chunked_bwd = mamba3_ssm_chunked_bwd
 decode_step = mamba3_ssm_decode_step
 rope_bc = mamba3_rope_bc
+bc_prologue = mamba3_bc_prologue
