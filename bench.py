@@ -276,6 +276,30 @@ def bench_backward(ops, inputs, w, steps, warmup, torch):
                 gbps=bytes_ / (ev * 1e-3) / 1e9, bytes=bytes_, mfma_floor_ms=mfma_floor_ms, hbm_floor_ms=hbm_floor_ms)
 
 
+def bench_prologue(ops, inputs, steps, warmup, torch):
+    """mamba3_bc_prologue at the 1.5B shapes: flops of the projection (2 M F D,
+    M = B L tokens, F = 2 H R N features) and bytes of u, W, dt, theta read
+    and B_rot, C_rot written (the angle pre-pass writes and re-reads 4 bytes
+    per token, head and pair on top)."""
+    c = inputs.PROLOGUE
+    b, L, H, R, N, D = c["batch"], c["seqlen"], c["nheads"], c["rank"], c["dstate"], c["d_model"]
+    d = inputs.prologue_torch(b, L, H, N, R, D, seed=inputs.PROLOGUE_SEED)
+    dims = ops.make_dims(b, L, H, 16, N, R, 16, ops.M3_BF16)
+    ws = torch.empty(ops.bc_prologue_workspace_size(dims), device="cuda", dtype=torch.uint8)
+    Bo = torch.empty((b, L, H, R, N), device="cuda", dtype=torch.bfloat16)
+    Co = torch.empty_like(Bo)
+    fn = lambda: ops.bc_prologue(d["u"], d["W"], d["dt"], d["theta"], H, R, N, gain=d["gain"], bias=d["bias"],
+                                 B_rot=Bo, C_rot=Co, want_final=False, workspace=ws)
+    wall, ev = timed(fn, steps, warmup, torch)
+    M, F = b * L, 2 * H * R * N
+    flops = 2.0 * M * F * D
+    bytes_ = 2 * M * D + 2 * F * D + 8 * F + M * H * (4 + 4 * N // 2) + 2 * M * F
+    del d, ws, Bo, Co
+    torch.cuda.empty_cache()
+    return dict(ms=ev, flops=flops, tflops=flops / (ev * 1e-3) / 1e12, bytes=bytes_, gbps=bytes_ / (ev * 1e-3) / 1e9,
+                tokens_per_s=M / (ev * 1e-3), shape=dict(batch=b, seqlen=L, nheads=H, rank=R, dstate=N, d_model=D))
+
+
 def bench_rope(ops, inputs, w, steps, warmup, torch):
     d = inputs.torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
                             seed=inputs.seed_of(w.name))
@@ -370,7 +394,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "rope", "copy", "all"], default="all")
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "rope", "prologue", "copy", "all"],
+                    default="all")
     ap.add_argument("--verify-k", type=int, default=8, help="tokens per call of the verify workload")
     ap.add_argument("--workload", default="mimo_bf16", choices=["mimo_bf16", "siso_bf16", "long_mimo_bf16"],
                     help="prefill workload timed by --only prefill (profiling); the headline line uses mimo_bf16")
@@ -404,6 +429,9 @@ def main():
     if args.only in ("backward", "all"):
         print(f"[bench] backward on {w.name}", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(ops, inputs, w, max(3, args.steps // 4), 2, torch)
+    if args.only in ("prologue", "all"):
+        print("[bench] bc_prologue at the 1.5B shapes", file=sys.stderr, flush=True)
+        out["prologue"] = bench_prologue(ops, inputs, max(3, args.steps // 2), 2, torch)
     if args.only in ("rope", "all"):
         print(f"[bench] rope_bc on {w.name} shapes", file=sys.stderr, flush=True)
         out["rope"] = bench_rope(ops, inputs, w, max(3, args.steps // 4), 2, torch)
@@ -470,6 +498,17 @@ def main():
         line["backward_long_mimo_bf16"] = backward_entry(
             out["backward_long"], "long_mimo_bf16 backward: batch 1, L=65536, H=32, P=64, N=128, R=4, 8-token "
                                   "chunks, each sequence walked as segments (library default)")
+    if "prologue" in out:
+        pr = out["prologue"]
+        sh = pr["shape"]
+        line["bc_prologue"] = {
+            "workload": f"mamba3_bc_prologue: batch {sh['batch']}, L={sh['seqlen']}, d_model={sh['d_model']} -> "
+                        f"B, C of H={sh['nheads']}, R={sh['rank']}, N={sh['dstate']} (projection, RMS norm, "
+                        f"bias, rotation; bf16 MFMA, fp32 accumulation)",
+            "ms": round(pr["ms"], 4), "tokens_per_s": round(pr["tokens_per_s"], 1), "bound": "mfma",
+            "achieved_TFLOPs": round(pr["tflops"], 1), "peak_TFLOPs": BF16_DENSE_TFLOPS,
+            "frac": round(pr["tflops"] / BF16_DENSE_TFLOPS, 4), "flops_per_call": pr["flops"],
+            "bytes_per_call": pr["bytes"], "achieved_GBps": round(pr["gbps"], 1)}
     if "rope" in out:
         line["rope_bc"] = {"ms": round(out["rope"]["ms"], 4), "achieved_GBps": round(out["rope"]["gbps"], 1),
                            "frac": round(out["rope"]["gbps"] / HBM_PEAK_GBPS, 4)}

@@ -236,7 +236,8 @@ size_t mamba3_rope_bc_workspace_size(const m3_dims* d);
  * theta = 0 (then its h_final is in that frame too).
  *   d: batch, seqlen, nheads, dstate (N), rank (R) as for the core; headdim and
  *      chunk are ignored; io_dtype must be M3_BF16; flags 0.
- *   d_model: D, a positive multiple of 64 (M3_ERR_UNSUPPORTED otherwise).
+ *   d_model: D, a positive multiple of 64 and at most 2^20
+ *      (M3_ERR_UNSUPPORTED otherwise).
  *   u: (B, L, D) bf16.  W: (2*H*R*N, D) bf16, row-major: the H*R*N rows of
  *      W_B, then those of W_C.
  *   gain, bias: nullable (2, H, R, N) fp32 (NULL: 1 and 0).

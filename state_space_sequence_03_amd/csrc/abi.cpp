@@ -395,7 +395,8 @@ m3_status mamba3_bc_prologue(const m3_dims* d, int64_t d_model, const void* u, c
   if (st != M3_OK) return st;
   if (d_model <= 0) return M3_ERR_SHAPE;
   if (d->flags != 0 || d->io_dtype != M3_BF16) return M3_ERR_UNSUPPORTED;
-  if (d_model % 64 != 0 || !(eps >= 0.0f) || eps > 3.0e38f) return M3_ERR_UNSUPPORTED;
+  // 32-bit offsets inside a 256-row operand tile
+  if (d_model % 64 != 0 || d_model > (int64_t(1) << 20) || !(eps >= 0.0f) || eps > 3.0e38f) return M3_ERR_UNSUPPORTED;
   if ((d->seqlen + m3::ROPE_CHUNK - 1) / m3::ROPE_CHUNK > 65535) return M3_ERR_UNSUPPORTED;  // grid limit
   const bool empty = d->batch == 0 || d->nheads == 0;
   const bool has_tokens = !empty && d->seqlen > 0;

@@ -60,7 +60,7 @@ struct ProArgs {
   const float* phi;    // (M, H, N/2) angles from launch_rope_phi
   void *B_rot, *C_rot; // (M, H, R, N) bf16
   float eps;
-  int64_t M, D;        // D a multiple of 64
+  int64_t M, D;        // D a multiple of 64, at most 2^20
   int H, R;
 };
 hipError_t launch_bc_prologue(int N, const ProArgs& a, hipStream_t s);
