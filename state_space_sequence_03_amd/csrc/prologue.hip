@@ -126,27 +126,50 @@ __global__ __launch_bounds__(256) void bc_prologue_kernel(ProArgs a, int ntb, in
   // per 32 rows) as immediates.  The lane values pass through an empty asm in
   // every stage so that the compiler recomputes the bases instead of keeping
   // one register per (stage, step, tile) for the whole loop.
-  auto compute = [&](int st) {
+  // The products of the stage in LDS buffer st, with the register set (wsrc,
+  // usrc) written to the other buffer in between: that buffer was last read
+  // before the previous barrier, so only the barrier after this stage remains
+  // on the path.
+  auto compute = [&](int st, const uint4* wsrc, const uint4* usrc) {
     int ll = l32, hh = lh;
     asm volatile("" : "+v"(ll), "+v"(hh));
     const int fsl = fsw<8>(ll);
     const int ba = st * 2 * TILE_BYTES + wf * 16384 + ll * 128;
     const int bb = st * 2 * TILE_BYTES + TILE_BYTES + wt * 16384 + ll * 128;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    // operands of step s + 1 are read while the products of step s run
+    bf16x8 fa[2][4], fbv[2][4];
+    auto rd = [&](int s, int bsel) {
       const int co = ((2 * s + hh) ^ fsl) << 4;
       const char* pa = smem + ba + co;
       const char* pb = smem + bb + co;
-      bf16x8 fa[4], fbv[4];
 #pragma unroll
-      for (int ft = 0; ft < 4; ++ft) fa[ft] = as_bf16x8(*(const uint4*)(pa + ft * 4096));
+      for (int ft = 0; ft < 4; ++ft) fa[bsel][ft] = as_bf16x8(*(const uint4*)(pa + ft * 4096));
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) fbv[tt] = as_bf16x8(*(const uint4*)(pb + tt * 4096));
+      for (int tt = 0; tt < 4; ++tt) fbv[bsel][tt] = as_bf16x8(*(const uint4*)(pb + tt * 4096));
+    };
+    rd(0, 0);
+    stage(wsrc, usrc, st ^ 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) rd(s + 1, (s + 1) & 1);
 #pragma unroll
       for (int ft = 0; ft < 4; ++ft)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) acc[ft][tt] = mfma32(fa[ft], fbv[tt], acc[ft][tt]);
+        for (int tt = 0; tt < 4; ++tt) acc[ft][tt] = mfma32(fa[s & 1][ft], fbv[s & 1][tt], acc[ft][tt]);
     }
+    // instruction order: the first step's 8 operand reads, then for steps
+    // 0..2 one read of the next step after every 2 products with the 16 LDS
+    // writes of the other buffer spread over the first 16 of those slots,
+    // then the last step's 16 products (otherwise each read lands just
+    // before its use and the writes pile up at the end)
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < 16) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
   };
 
   // stage kk sits in LDS buffer kk % 2; the loads of stage kk + 2 are issued
@@ -164,12 +187,10 @@ __global__ __launch_bounds__(256) void bc_prologue_kernel(ProArgs a, int ntb, in
   __syncthreads();
   for (int kk = 0; kk < nst2; kk += 2) {
     load(xw, xu, kk + 2);
-    compute(0);
-    stage(yw, yu, 1);
+    compute(0, yw, yu);  // stage kk; stage kk + 1 into buffer 1
     __syncthreads();
     load(yw, yu, kk + 3);
-    compute(1);
-    stage(xw, xu, 0);
+    compute(1, xw, xu);  // stage kk + 1; stage kk + 2 into buffer 0
     __syncthreads();
   }
 
@@ -194,6 +215,16 @@ __global__ __launch_bounds__(256) void bc_prologue_kernel(ProArgs a, int ntb, in
     const uint32_t rem = f >= HRN ? f - HRN : f;
     return (int64_t)(rem >> shRN) * K2 + ((rem & (N - 1)) >> 1);
   };
+  // gain and bias of the lane's 64 features, loaded once (the staging
+  // registers of the main loop are free now)
+  float4 gvs[16], bvs[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const uint32_t f = fw0 + 8 * c + 4 * lh;
+    const bool ok = (int64_t)f < F;
+    gvs[c] = a.gain && ok ? *(const float4*)(a.gain + f) : make_float4(1.f, 1.f, 1.f, 1.f);
+    bvs[c] = a.bias && ok ? *(const float4*)(a.bias + f) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   const int jl = lane >> 4, gl = lane & 15;  // staging: 4 rows x 16 chunks per instruction
   const int64_t colg = col(gl);
   const bool fvalid = (int64_t)fw0 + 8 * gl < F;
@@ -232,10 +263,7 @@ __global__ __launch_bounds__(256) void bc_prologue_kernel(ProArgs a, int ntb, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = ft * 4 + q;  // 16-byte chunk (8 features) of the lane's 4 features
-          const uint32_t f = fw0 + 8 * c + 4 * lh;
-          const bool ok = (int64_t)f < F;
-          const float4 gv = a.gain && ok ? *(const float4*)(a.gain + f) : make_float4(1.f, 1.f, 1.f, 1.f);
-          const float4 bv = a.bias && ok ? *(const float4*)(a.bias + f) : make_float4(0.f, 0.f, 0.f, 0.f);
+          const float4 gv = gvs[c], bv = bvs[c];
           // pairs 2(c*2 + lh) and + 1 within group c of the angle row
           const float2 ph = *(const float2*)(phs + j * 256 + ((c ^ (j & 15)) << 4) + lh * 8);
           const float iv = inv[(ft * 32 + 8 * q) / N];
