@@ -191,3 +191,40 @@ def test_rope_validation(L):
     assert lib.mamba3_rope_bc(ctypes.byref(d), *args(dt=ctypes.c_void_p(FAKE + 1)), f, ctypes.c_size_t(ws),
                               None) == L.M3_ERR_ALIGN
     assert lib.mamba3_rope_bc(ctypes.byref(dims(L, rank=8)), *args(), f, ctypes.c_size_t(ws), None) == L.M3_ERR_UNSUPPORTED
+
+
+PRO_PTRS = ("u", "W", "gain", "bias", "dt", "theta", "angle0", "Br", "Cr", "af")
+
+
+def call_pro(L, d, D=128, eps=1e-5, ws_bytes=None, **over):
+    p = {k: ctypes.c_void_p(FAKE) for k in PRO_PTRS}
+    p.update(gain=None, bias=None, angle0=None, af=None, ws=ctypes.c_void_p(FAKE))
+    p.update(over)
+    need = L.bc_prologue_workspace_size(d) if ws_bytes is None else ws_bytes
+    return L.lib().mamba3_bc_prologue(ctypes.byref(d), ctypes.c_int64(D), p["u"], p["W"], p["gain"], p["bias"],
+                                      ctypes.c_float(eps), p["dt"], p["theta"], p["angle0"], p["Br"], p["Cr"], p["af"],
+                                      p["ws"], ctypes.c_size_t(need), None)
+
+
+def test_prologue_validation(L):
+    d = dims(L, seqlen=70)
+    # workspace: the angle chunk totals, then the angles of every token (256-byte aligned)
+    tot = (4 * 2 * 3 * 2 * 32 + 255) // 256 * 256
+    assert L.bc_prologue_workspace_size(d) == tot + (4 * 2 * 70 * 3 * 32 + 255) // 256 * 256
+    assert call_pro(L, d, ws_bytes=0, ws=None) == L.M3_ERR_WORKSPACE
+    assert call_pro(L, d, ws_bytes=L.bc_prologue_workspace_size(d) - 4) == L.M3_ERR_WORKSPACE
+    assert call_pro(L, d, u=None) == L.M3_ERR_NULL
+    assert call_pro(L, d, Cr=None) == L.M3_ERR_NULL
+    assert call_pro(L, d, W=ctypes.c_void_p(FAKE + 8)) == L.M3_ERR_ALIGN
+    assert call_pro(L, d, gain=ctypes.c_void_p(FAKE + 4)) == L.M3_ERR_ALIGN    # read in 16-byte vectors
+    assert call_pro(L, d, dt=ctypes.c_void_p(FAKE + 2)) == L.M3_ERR_ALIGN
+    assert call_pro(L, d, D=0) == L.M3_ERR_SHAPE
+    assert call_pro(L, d, D=96) == L.M3_ERR_UNSUPPORTED                         # not a multiple of 64
+    assert call_pro(L, d, D=(1 << 20) + 64) == L.M3_ERR_UNSUPPORTED
+    assert call_pro(L, d, eps=-1.0) == L.M3_ERR_UNSUPPORTED
+    assert call_pro(L, d, eps=float("nan")) == L.M3_ERR_UNSUPPORTED
+    assert call_pro(L, dims(L, seqlen=70, io_dtype=L.M3_F32)) == L.M3_ERR_UNSUPPORTED
+    assert call_pro(L, dims(L, seqlen=70, flags=1)) == L.M3_ERR_UNSUPPORTED
+    assert call_pro(L, dims(L, seqlen=70, dstate=48)) == L.M3_ERR_UNSUPPORTED
+    # an empty batch reads nothing
+    assert call_pro(L, dims(L, batch=0), u=None, W=None, dt=None, theta=None, Br=None, Cr=None, ws=None) == L.M3_OK
