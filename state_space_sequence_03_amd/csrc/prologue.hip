@@ -215,30 +215,35 @@ __global__ __launch_bounds__(256) void bc_prologue_kernel(ProArgs a, int ntb, in
     const uint32_t rem = f >= HRN ? f - HRN : f;
     return (int64_t)(rem >> shRN) * K2 + ((rem & (N - 1)) >> 1);
   };
-  // gain and bias of the lane's 64 features, loaded once (the staging
-  // registers of the main loop are free now)
-  float4 gvs[16], bvs[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const uint32_t f = fw0 + 8 * c + 4 * lh;
-    const bool ok = (int64_t)f < F;
-    gvs[c] = a.gain && ok ? *(const float4*)(a.gain + f) : make_float4(1.f, 1.f, 1.f, 1.f);
-    bvs[c] = a.bias && ok ? *(const float4*)(a.bias + f) : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   const int jl = lane >> 4, gl = lane & 15;  // staging: 4 rows x 16 chunks per instruction
-  const int64_t colg = col(gl);
   const bool fvalid = (int64_t)fw0 + 8 * gl < F;
+  const int64_t colg = fvalid ? col(gl) : 0;
+  // the angles of both halves are requested at once (the staging registers of
+  // the main loop are free now): the second half's arrive during the first's
+  float4 phr[2][16];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int64_t mh = m0 + wt * 128 + hf * 64;  // first token of the half
-#pragma unroll 4
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // every lane loads (clamped to a valid token and column) and invalid
+      // ones drop the value: a load skipped on one path would make the
+      // compiler's waits drain the other half's loads too
+      const int64_t m = m0 + wt * 128 + hf * 64 + 4 * i + jl;
+      const int64_t mc = m < a.M ? m : a.M - 1;
+      const float4 v = *(const float4*)(a.phi + mc * (int64_t)a.H * K2 + colg);
+      phr[hf][i] = fvalid && m < a.M ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  auto write_phi = [&](int hf) {
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int jj = 4 * i + jl;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (fvalid && mh + jj < a.M) v = *(const float4*)(a.phi + (mh + jj) * (int64_t)a.H * K2 + colg);
-      *(float4*)(phs + jj * 256 + ((gl ^ (jj & 15)) << 4)) = v;
+      *(float4*)(phs + jj * 256 + ((gl ^ (jj & 15)) << 4)) = phr[hf][i];
     }
-    __syncthreads();
+  };
+  // normalisation, gain, bias and rotation of the half's two 32-token tiles
+  // into the staged output rows
+  float4 gvs[16], bvs[16];
+  auto compute_half = [&](int hf) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2) {
       const int tt = 2 * hf + t2;
@@ -282,20 +287,42 @@ __global__ __launch_bounds__(256) void bc_prologue_kernel(ProArgs a, int ntb, in
         }
       }
     }
-    __syncthreads();
-    // whole rows out: chunk gl of row jj holds features fw0 + 8 gl .. + 7 of
-    // token mh + jj, all in B_rot or all in C_rot (H R N is a multiple of 8)
-    const uint32_t fo = fw0 + 8 * gl;
-    const bool oc = fo >= HRN;
-    char* dst = (char*)(oc ? a.C_rot : a.B_rot) + (int64_t)(oc ? fo - HRN : fo) * 2;
+  };
+  // whole rows out: chunk gl of row jj holds features fw0 + 8 gl .. + 7 of
+  // token mh + jj, all in B_rot or all in C_rot (H R N is a multiple of 8)
+  const uint32_t fo = fw0 + 8 * gl;
+  const bool oc = fo >= HRN;
+  char* dst = (char*)(oc ? a.C_rot : a.B_rot) + (int64_t)(oc ? fo - HRN : fo) * 2;
+  auto store_half = [&](int hf) {
+    const int64_t mh = m0 + wt * 128 + hf * 64;  // first token of the half
 #pragma unroll 4
     for (int i = 0; i < 16; ++i) {
       const int jj = 4 * i + jl;
       const uint4 v = *(const uint4*)(ous + jj * 256 + ((gl ^ (jj & 15)) << 4));
       if (fvalid && mh + jj < a.M) *(uint4*)(dst + (mh + jj) * (int64_t)HRN * 2) = v;
     }
-    __syncthreads();
+  };
+  // Order: every load (angles, gain, bias) is requested before the first
+  // store.  One counter tracks vector loads and stores alike, and the stores
+  // are conditional, so a wait for a load issued after a store would also
+  // wait for the store.
+  write_phi(0);
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const uint32_t f = fw0 + 8 * c + 4 * lh;
+    const bool ok = (int64_t)f < F;
+    gvs[c] = a.gain && ok ? *(const float4*)(a.gain + f) : make_float4(1.f, 1.f, 1.f, 1.f);
+    bvs[c] = a.bias && ok ? *(const float4*)(a.bias + f) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
+  __syncthreads();
+  compute_half(0);
+  __syncthreads();
+  write_phi(1);  // the angle rows are free: every wave has finished half 0
+  store_half(0);
+  __syncthreads();
+  compute_half(1);
+  __syncthreads();
+  store_half(1);
 }
 
 template <int N>
