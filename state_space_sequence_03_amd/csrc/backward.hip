@@ -349,6 +349,11 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   for (int q = 0; q < OMP; ++q) seg_th[q] = 0.0f;
 
   for (int64_t c = c_begin; c < c_end; ++c) {
+    // This chunk's inputs were requested a chunk ago: wait for them before the
+    // state stores.  One counter tracks vector loads and stores alike and the
+    // stores are conditional, so a wait placed after them would also wait for
+    // the stores.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt left alone
     if (!local) store_state(c);
     if (tid < QB) {
       sT[tid] = tsv.scal();
@@ -824,6 +829,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // dt and lam of the first token of the chunk processed last time
   float pend_d = 0.0f, pend_l = 0.0f;
   if (c_begin < c_end) fetch(c_end - 1);
+  // the first chunk's inputs are waited for here, as every later chunk's are
+  // before the stores (below): the loop then starts with nothing to wait for
+  // on either path into it
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
   for (int64_t c = c_end - 1; c >= c_begin; --c) {
     const int64_t a0 = c * QB, t0c = tok_of(a0);  // block-uniform
@@ -1080,6 +1089,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
+    // The next chunk's inputs were requested at this chunk's start and have
+    // had the phases above to land: wait for them here, before this chunk's
+    // gradient stores.  One counter tracks vector loads and stores alike, and
+    // the stores sit behind branches, so a wait at the next chunk's start
+    // would also have to wait for every store still in flight.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); expcnt and lgkmcnt left alone
 
     // ---------------- products on the masked matrices ----------------
     // dX, dC~ and dB~ are computed transposed (feature rows, virtual-row
