@@ -252,7 +252,9 @@ size_t mamba3_rope_bc_workspace_size(const m3_dims* d);
  * Products: bf16 MFMAs with fp32 accumulation; normalisation, bias and
  * rotation in fp32; outputs rounded to bf16 (nearest even).
  * Alignment: u, W, B_rot, C_rot, gain, bias and the workspace 16-byte; the
- * others 4-byte.  seqlen is limited to 65535 * 64 tokens. */
+ * others 4-byte.  seqlen is limited to 65535 * 64 tokens, and the number of
+ * 256 x 256 (token, feature) tiles, rounded up to 16 x 16 groups, to 2^23
+ * groups (M3_ERR_UNSUPPORTED). */
 m3_status mamba3_bc_prologue(const m3_dims* d, int64_t d_model, const void* u, const void* W,
                              const float* gain, const float* bias, float eps,
                              const float* dt, const float* theta, const float* angle0,

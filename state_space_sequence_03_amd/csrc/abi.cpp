@@ -398,6 +398,12 @@ m3_status mamba3_bc_prologue(const m3_dims* d, int64_t d_model, const void* u, c
   // 32-bit offsets inside a 256-row operand tile
   if (d_model % 64 != 0 || d_model > (int64_t(1) << 20) || !(eps >= 0.0f) || eps > 3.0e38f) return M3_ERR_UNSUPPORTED;
   if ((d->seqlen + m3::ROPE_CHUNK - 1) / m3::ROPE_CHUNK > 65535) return M3_ERR_UNSUPPORTED;  // grid limit
+  {
+    // the product's grid: 256 blocks per 16 x 16 super-tile of 256-token x
+    // 256-feature tiles, in one 31-bit dimension
+    const int64_t ntb = (d->batch * d->seqlen + 255) / 256, nfb = (2 * d->nheads * d->rank * d->dstate + 255) / 256;
+    if (((ntb + 15) / 16) * ((nfb + 15) / 16) > ((int64_t(1) << 31) - 1) / 256) return M3_ERR_UNSUPPORTED;
+  }
   const bool empty = d->batch == 0 || d->nheads == 0;
   const bool has_tokens = !empty && d->seqlen > 0;
   if (has_tokens && (!u || !W || !dt || !theta || !B_rot || !C_rot)) return M3_ERR_NULL;

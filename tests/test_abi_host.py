@@ -226,5 +226,9 @@ def test_prologue_validation(L):
     assert call_pro(L, dims(L, seqlen=70, io_dtype=L.M3_F32)) == L.M3_ERR_UNSUPPORTED
     assert call_pro(L, dims(L, seqlen=70, flags=1)) == L.M3_ERR_UNSUPPORTED
     assert call_pro(L, dims(L, seqlen=70, dstate=48)) == L.M3_ERR_UNSUPPORTED
+    # grid limit: 2^31 / 256 groups of 16 x 16 tiles
+    big = dims(L, batch=65535, seqlen=65535 * 64, nheads=65535, rank=4, dstate=128)  # within the angle pass limits
+    assert call_pro(L, big) == L.M3_ERR_UNSUPPORTED
+    assert call_pro(L, dims(L, batch=1, seqlen=65535 * 64, nheads=64, rank=4, dstate=64), ws_bytes=0, ws=None) == L.M3_ERR_WORKSPACE
     # an empty batch reads nothing
     assert call_pro(L, dims(L, batch=0), u=None, W=None, dt=None, theta=None, Br=None, Cr=None, ws=None) == L.M3_OK
