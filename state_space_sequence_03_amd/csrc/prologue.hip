@@ -44,6 +44,7 @@
 namespace m3 {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -299,7 +300,10 @@ __global__ __launch_bounds__(256) void bc_prologue_kernel(ProArgs a, int ntb, in
     for (int i = 0; i < 16; ++i) {
       const int jj = 4 * i + jl;
       const uint4 v = *(const uint4*)(ous + jj * 256 + ((gl ^ (jj & 15)) << 4));
-      if (fvalid && mh + jj < a.M) *(uint4*)(dst + (mh + jj) * (int64_t)HRN * 2) = v;
+      // streamed out: the rows are not read again here, and the operand
+      // tiles that later blocks re-read stay in L2
+      if (fvalid && mh + jj < a.M)
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), (u32x4*)(dst + (mh + jj) * (int64_t)HRN * 2));
     }
   };
   // Order: every load (angles, gain, bias) is requested before the first
