@@ -109,6 +109,13 @@ template <typename T>
 __device__ __forceinline__ void stg16(void* base, int64_t elem, const typename io<T>::vec& v) {
   *(typename io<T>::vec*)((char*)base + elem * io<T>::BYTES) = v;
 }
+// The same with a non-temporal hint, for outputs that are written once and
+// not read again by the kernel (streamed past the caches).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ void stg16_nt(void* base, int64_t elem, const typename io<T>::vec& v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), (u32x4*)((char*)base + elem * io<T>::BYTES));
+}
 
 // ---------------------------------------------------------------------------
 // MFMA wrappers.  Lane l of a wave: m = l % 16, g = l / 16.

@@ -142,8 +142,8 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
       fc[2 * q] = r2.x * c0v + r2.y * c1v;
       fc[2 * q + 1] = r2.x * c1v - r2.y * c0v;
     }
-    stg16<T>(a.B_rot, off(i), io<T>::pack(fb));
-    stg16<T>(a.C_rot, off(i), io<T>::pack(fc));
+    stg16_nt<T>(a.B_rot, off(i), io<T>::pack(fb));
+    stg16_nt<T>(a.C_rot, off(i), io<T>::pack(fc));
   };
 #pragma unroll
   for (int j = 0; j < BATCH; ++j) {
