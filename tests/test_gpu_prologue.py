@@ -128,15 +128,21 @@ def test_prologue_rejections(ops):
     assert e.value.status == ops.M3_ERR_UNSUPPORTED
 
 
-def test_prologue_full_size_sampled(ops):
-    """The 1.5B shapes (batch 8, L=4096, H=64, R=4, N=64, d_model 2048) at full
-    size; 24 sampled tokens, all heads, against the oracle (each token run as a
-    one-token call whose angle0 is the oracle rope's angle after the tokens
-    before it)."""
-    c = PROLOGUE
+# the 1.5B shapes, and the long-context head shape (N = 128) with the same
+# reading of the model width (d_model = H P / 2)
+FULL = {"1p5b": PROLOGUE,
+        "long": dict(batch=1, seqlen=65536, nheads=32, dstate=128, rank=4, d_model=1024)}
+
+
+@pytest.mark.parametrize("shape", sorted(FULL))
+def test_prologue_full_size_sampled(ops, shape):
+    """Full size; 24 sampled tokens, all heads, against the oracle (each token
+    run as a one-token call whose angle0 is the oracle rope's angle after the
+    tokens before it)."""
+    c = FULL[shape]
     b, L, H, R, N, D = c["batch"], c["seqlen"], c["nheads"], c["rank"], c["dstate"], c["d_model"]
     say("bc_prologue full size: generating")
-    d = prologue_torch(b, L, H, N, R, D, seed=PROLOGUE_SEED)
+    d = prologue_torch(b, L, H, N, R, D, seed=PROLOGUE_SEED + (shape == "long"))
     say("bc_prologue full size: running")
     Bg, Cg, ag = ops.bc_prologue(d["u"], d["W"], d["dt"], d["theta"], H, R, N, gain=d["gain"], bias=d["bias"])
     torch.cuda.synchronize()
