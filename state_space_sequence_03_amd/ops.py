@@ -108,6 +108,20 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _expect(name, t, shape, dtype, device):
+    """Shape, dtype and device of an operand (None: absent).  The C ABI takes
+    raw pointers and cannot see shapes, so the binding checks them before any
+    call: a wrong shape would otherwise be read or written out of bounds."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+
+
 def _stream(stream):
     torch = _torch()
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -132,6 +146,20 @@ def rope_bc_workspace_size(dims: Dims) -> int:
     return int(lib().mamba3_rope_bc_workspace_size(ctypes.byref(dims)))
 
 
+def _core_operands(torch, x, B, C, dt, A, lam, theta, h0, prev_B, prev_x):
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    io, f32, dev = x.dtype, torch.float32, x.device
+    for name, t in (("B", B), ("C", C)):
+        _expect(name, t, (b, L, H, R, N), io, dev)
+    for name, t in (("dt", dt), ("A", A), ("lam", lam)):
+        _expect(name, t, (b, L, H), f32, dev)
+    _expect("theta", theta, (b, L, H, N // 2), f32, dev)
+    _expect("h0", h0, (b, H, N, P), f32, dev)
+    _expect("prev_B", prev_B, (b, H, R, N), io, dev)
+    _expect("prev_x", prev_x, (b, H, R, P), io, dev)
+
+
 def mamba3_ssm_chunked_fwd(x, B, C, dt, A, lam, theta, h0=None, prev_B=None, prev_x=None, *, chunk=64,
                            segments=0, chunk_walk=False, token_path=False, y=None, h_final=None, want_final=True,
                            workspace=None, stream=None):
@@ -141,6 +169,9 @@ def mamba3_ssm_chunked_fwd(x, B, C, dt, A, lam, theta, h0=None, prev_B=None, pre
     torch = _torch()
     b, L, H, R, P = x.shape
     N = B.shape[-1]
+    _core_operands(torch, x, B, C, dt, A, lam, theta, h0, prev_B, prev_x)
+    _expect("y", y, x.shape, x.dtype, x.device)
+    _expect("h_final", h_final, (b, H, N, P), torch.float32, x.device)
     flags = segments | (M3_FLAG_CHUNK_WALK if chunk_walk else 0) | (M3_FLAG_TOKEN_PATH if token_path else 0)
     dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x), flags=flags)
     if y is None:
@@ -172,6 +203,9 @@ def mamba3_ssm_chunked_bwd(x, B, C, dt, A, lam, theta, dy, h0=None, prev_B=None,
     torch = _torch()
     b, L, H, R, P = x.shape
     N = B.shape[-1]
+    _core_operands(torch, x, B, C, dt, A, lam, theta, h0, prev_B, prev_x)
+    _expect("dy", dy, x.shape, x.dtype, x.device)
+    _expect("dh_final", dh_final, (b, H, N, P), torch.float32, x.device)
     dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x), flags=segments)
     out = {"dx": torch.empty_like(x), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
            "ddt": torch.empty_like(dt), "dA": torch.empty_like(A), "dlam": torch.empty_like(lam),
@@ -201,6 +235,15 @@ def mamba3_ssm_decode_step(state, x, B, C, dt, A, lam, theta, prev_B=None, prev_
     torch = _torch()
     b, H, R, P = x.shape
     N = B.shape[-1]
+    io, f32, dev = x.dtype, torch.float32, x.device
+    _expect("state", state, (b, H, N, P), f32, dev)
+    for name, t in (("B", B), ("C", C), ("prev_B", prev_B)):
+        _expect(name, t, (b, H, R, N), io, dev)
+    _expect("prev_x", prev_x, (b, H, R, P), io, dev)
+    for name, t in (("dt", dt), ("A", A), ("lam", lam)):
+        _expect(name, t, (b, H), f32, dev)
+    _expect("theta", theta, (b, H, N // 2), f32, dev)
+    _expect("y", y, x.shape, io, dev)
     dims = make_dims(b, 1, H, P, N, R, 16, _io_code(x))
     if y is None:
         y = torch.empty_like(x)
@@ -216,6 +259,13 @@ def mamba3_rope_bc(B, C, dt, theta, angle0=None, *, B_rot=None, C_rot=None, angl
     """Cumulative-angle rotation.  Returns (B_rot, C_rot, angle_final)."""
     torch = _torch()
     b, L, H, R, N = B.shape
+    io, f32, dev = B.dtype, torch.float32, B.device
+    for name, t in (("C", C), ("B_rot", B_rot), ("C_rot", C_rot)):
+        _expect(name, t, B.shape, io, dev)
+    _expect("dt", dt, (b, L, H), f32, dev)
+    _expect("theta", theta, (b, L, H, N // 2), f32, dev)
+    _expect("angle0", angle0, (b, H, N // 2), f32, dev)
+    _expect("angle_final", angle_final, (b, H, N // 2), f32, dev)
     dims = make_dims(b, L, H, 16, N, R, 16, _io_code(B))
     if B_rot is None:
         B_rot = torch.empty_like(B)
@@ -246,6 +296,16 @@ def mamba3_bc_prologue(u, W, dt, theta, nheads, rank, dstate, gain=None, bias=No
     torch = _torch()
     b, L, D = u.shape
     H, R, N = nheads, rank, dstate
+    io, f32, dev = u.dtype, torch.float32, u.device
+    _expect("W", W, (2 * H * R * N, D), io, dev)
+    _expect("dt", dt, (b, L, H), f32, dev)
+    _expect("theta", theta, (b, L, H, N // 2), f32, dev)
+    for name, t in (("gain", gain), ("bias", bias)):
+        _expect(name, t, (2, H, R, N), f32, dev)
+    for name, t in (("B_rot", B_rot), ("C_rot", C_rot)):
+        _expect(name, t, (b, L, H, R, N), io, dev)
+    for name, t in (("angle0", angle0), ("angle_final", angle_final)):
+        _expect(name, t, (b, H, N // 2), f32, dev)
     dims = make_dims(b, L, H, 16, N, R, 16, _io_code(u))
     if B_rot is None:
         B_rot = torch.empty((b, L, H, R, N), device=u.device, dtype=u.dtype)
@@ -253,8 +313,6 @@ def mamba3_bc_prologue(u, W, dt, theta, nheads, rank, dstate, gain=None, bias=No
         C_rot = torch.empty((b, L, H, R, N), device=u.device, dtype=u.dtype)
     if angle_final is None and want_final:
         angle_final = torch.empty((b, H, N // 2), device=u.device, dtype=torch.float32)
-    if tuple(W.shape) != (2 * H * R * N, D):
-        raise ValueError("W must be (2*H*R*N, D)")
     ws_bytes = bc_prologue_workspace_size(dims)
     if ws_bytes > 0 and workspace is None:
         workspace = torch.empty(ws_bytes, device=u.device, dtype=torch.uint8)

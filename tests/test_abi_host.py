@@ -232,3 +232,32 @@ def test_prologue_validation(L):
     assert call_pro(L, dims(L, batch=1, seqlen=65535 * 64, nheads=64, rank=4, dstate=64), ws_bytes=0, ws=None) == L.M3_ERR_WORKSPACE
     # an empty batch reads nothing
     assert call_pro(L, dims(L, batch=0), u=None, W=None, dt=None, theta=None, Br=None, Cr=None, ws=None) == L.M3_OK
+
+
+def test_binding_checks_operand_shapes(L):
+    # the C ABI sees raw pointers only; the binding rejects a mis-shaped,
+    # mis-typed or misplaced operand before any call (CPU tensors here: the
+    # checks come first, nothing is launched)
+    import torch
+    x = torch.zeros((1, 8, 2, 1, 16))
+    B = torch.zeros((1, 8, 2, 1, 16))
+    s = torch.zeros((1, 8, 2))
+    th = torch.zeros((1, 8, 2, 8))
+    with pytest.raises(ValueError):
+        L.chunked_fwd(x, B, B, s, s, s, th[..., :4].contiguous())              # theta needs N/2 pairs
+    with pytest.raises(TypeError):
+        L.chunked_fwd(x, B, B, s.double(), s, s, th)                            # dt must be fp32
+    with pytest.raises(TypeError):
+        L.chunked_bwd(x, B.bfloat16(), B, s, s, s, th, x)                       # B in x's dtype
+    with pytest.raises(ValueError):
+        L.chunked_bwd(x, B, B, s, s, s, th, x[:, :4].contiguous())             # dy like x
+    with pytest.raises(ValueError):
+        L.rope_bc(B, B[:, :4].contiguous(), s, th)                              # C like B
+    with pytest.raises(ValueError):
+        L.decode_step(torch.zeros((1, 2, 16, 8)), x[:, 0], B[:, 0], B[:, 0], s[:, 0], s[:, 0], s[:, 0], th[:, 0])
+    u = torch.zeros((1, 8, 64), dtype=torch.bfloat16)
+    W = torch.zeros((64, 64), dtype=torch.bfloat16)                           # 2 H R N = 64 rows for N = 32
+    with pytest.raises(ValueError):
+        L.bc_prologue(u, W, s, th, 2, 1, 32, gain=torch.zeros((2, 2, 1, 16)))   # gain is (2, H, R, N)
+    with pytest.raises(ValueError):
+        L.bc_prologue(u, W[:32].contiguous(), s, th, 2, 1, 32)                  # W rows
