@@ -111,6 +111,23 @@ def test_prologue_feeds_the_core_in_its_frame(ops):
     assert e < TOL
 
 
+def test_prologue_empty_sequence(ops):
+    """L = 0: nothing is projected; angle_final is angle0 (zero without it)."""
+    b, H, R, N, D = 2, 3, 2, 16, 64
+    u = torch.zeros((b, 0, D), device="cuda", dtype=torch.bfloat16)
+    W = torch.randn((2 * H * R * N, D), device="cuda").to(torch.bfloat16)
+    dt = torch.zeros((b, 0, H), device="cuda")
+    th = torch.zeros((b, 0, H, N // 2), device="cuda")
+    a0 = torch.randn((b, H, N // 2), device="cuda")
+    Bo, Co, af = ops.bc_prologue(u, W, dt, th, H, R, N, angle0=a0)
+    torch.cuda.synchronize()
+    assert Bo.numel() == 0 and Co.numel() == 0
+    assert torch.equal(af, a0)
+    _, _, af0 = ops.bc_prologue(u, W, dt, th, H, R, N)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(af0).item() == 0
+
+
 def test_prologue_rejections(ops):
     d = ops.make_dims(1, 8, 1, 16, 16, 1, 16, ops.M3_BF16)
     u = torch.zeros((1, 8, 96), device="cuda", dtype=torch.bfloat16)
