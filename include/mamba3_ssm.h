@@ -1,13 +1,15 @@
 /*
  * mamba3_ssm.h -- C ABI of the MI355X (gfx950) Mamba-3 SSM layer core.
  *
- * Four operations, all asynchronous on a caller-given HIP stream:
+ * Five operations, all asynchronous on a caller-given HIP stream:
  *
  *   mamba3_ssm_chunked_fwd   whole-sequence forward (prefill / training
  *                            forward) by the chunked parallel form;
  *   mamba3_ssm_chunked_bwd   its backward (training);
  *   mamba3_ssm_decode_step   one-token state update (generation);
- *   mamba3_rope_bc           the cumulative-angle rotation of B and C.
+ *   mamba3_rope_bc           the cumulative-angle rotation of B and C;
+ *   mamba3_bc_prologue       the projection to B and C with their
+ *                            normalisation, bias and rotation fused.
  *
  * What they compute (pages cited by title and section):
  *
@@ -57,11 +59,14 @@
  * the caller's next synchronisation.
  *
  * Supported sizes: N in {16,32,64,128}; P in {16,32,64,128}; R in {1,2,4};
- * Q in {16,32,64}; io dtype fp32 or bf16.  The chunked forward also needs
- * Q*R <= 256 and its per-chunk tiles to fit in the 160 KiB of LDS of one
- * compute unit (this excludes bf16 with N = P = 128 and Q*R = 256, and fp32
- * io with Q*R = 256 unless N and P are small); M3_ERR_UNSUPPORTED otherwise.  batch, seqlen and nheads may be 0 (empty
- * input: nothing is read; h_final receives h0, or zeros).
+ * Q in {16,32,64}; io dtype fp32 or bf16: every combination, for the chunked
+ * forward and the backward alike; M3_ERR_UNSUPPORTED outside it.  Where a
+ * chunk's tiles would not fit in the 160 KiB of LDS of one compute unit
+ * (fp32 io with Q*R = 256, N = P = 128 with long chunks) the chunked forward
+ * walks each chunk as 2, 4 or 8 shorter pieces: the chunked form is exact for
+ * any split (linkstar.cloud/article/869, "第一刀"), so only the rounding order
+ * changes.  batch, seqlen and nheads may be 0 (empty input: nothing is read;
+ * h_final receives h0, or zeros).
  */
 #ifndef MAMBA3_SSM_H
 #define MAMBA3_SSM_H
@@ -98,7 +103,9 @@ typedef struct {
                        with P = 64 and N = 64 (Q in {32, 64}) or N = 128
                        (R in {2, 4}) the library walks each chunk as 32- or
                        16-token sub-chunks (the chunked form is exact for
-                       any split); segments and workspace follow Q. */
+                       any split); segments and workspace follow Q.  Where
+                       Q's tiles do not fit the LDS the walk (and with it
+                       segments and workspace) uses Q/2, Q/4 or Q/8. */
   int32_t io_dtype; /* m3_dtype of x, B, C, y, prev_B, prev_x, B_rot, C_rot */
   int32_t flags;    /* chunked_fwd: bits 0..15 = number of sequence segments
                        walked in parallel per (b,h) (0 = chosen by the
@@ -161,9 +168,10 @@ size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d);
  *        the gradient with respect to a zero initial state).
  *   dprev_B (B, H, R, N), dprev_x (B, H, R, P): nullable pair, io dtype,
  *        written when prev_B/prev_x are given.
- * Supported: N and P in {16, 32, 64, 128} but not both 128, R in {1, 2, 4},
- * io fp32 or bf16; d->chunk must be a supported chunk length but the backward
- * walks chunks of its own: 16 tokens, 8 when N or P is 128 and R = 4; nheads
+ * Supported: N and P in {16, 32, 64, 128}, R in {1, 2, 4}, io fp32 or bf16;
+ * d->chunk must be a supported chunk length but the backward walks chunks of
+ * its own: 16 tokens, 8 when N or P is 128 and R = 4, 16 / R when both are
+ * 128 (the chunked form is exact for any split); nheads
  * at most 65536 (M3_ERR_UNSUPPORTED otherwise: offsets inside a chunk are
  * 32-bit).  Products: fp32 for fp32 io; bf16 MFMAs with fp32 accumulation
  * for bf16 io (operands rounded to bf16; the state product of the checkpoint
@@ -212,8 +220,12 @@ m3_status mamba3_ssm_decode_step(const m3_dims* d, float* state,
  *   phi_t = angle0 + sum_{s<=t} dt_s theta_s (per pair), B_rot = R(-phi_t) B_t,
  *   C_rot = R(-phi_t) C_t, angle_final = phi_L.
  * angle0, angle_final: nullable.  B_rot / C_rot must not alias B / C.
- * workspace: at least mamba3_rope_bc_workspace_size(d) bytes.  chunk of d is
- * ignored.  seqlen is limited to 65535 * 64 tokens (M3_ERR_UNSUPPORTED). */
+ * workspace: at least mamba3_rope_bc_workspace_size(d) bytes: the angle
+ * totals of every 64-token chunk, which a first pass writes and the rotating
+ * pass scans, so that every chunk of a long sequence is rotated in parallel.
+ * The library allocates nothing and keeps no global state, so the caller
+ * provides this array.  chunk of d is ignored.  seqlen is limited to
+ * 65535 * 64 tokens (M3_ERR_UNSUPPORTED). */
 m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C,
                          const float* dt, const float* theta, const float* angle0,
                          void* B_rot, void* C_rot, float* angle_final,

@@ -154,7 +154,7 @@ const char* mamba3_status_string(m3_status s) {
 struct SegWs {
   size_t end, in, tot, meta, bytes;
 };
-SegWs seg_ws(const m3_dims* d, const SegPlan& sp) {
+static SegWs seg_ws(const m3_dims* d, const SegPlan& sp) {
   const int64_t BH = d->batch * d->nheads, K = d->dstate / 2, NP = d->dstate * d->headdim;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   SegWs w{};
@@ -167,27 +167,40 @@ SegWs seg_ws(const m3_dims* d, const SegPlan& sp) {
   return w;
 }
 
-size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d) {
-  if (check_dims(d, true, true) != M3_OK) return 0;
-  if (d->batch == 0 || d->nheads == 0 || d->seqlen == 0) return 0;
+// The sizes as walked: the requested dims with the chunk replaced by the one
+// the walk uses (m3::walk_chunk; the requested one unless its tiles do not fit
+// the LDS).  Segment plans and offsets are kept at this granularity.
+static m3_dims walked_dims(const m3_dims* d) {
+  m3_dims w = *d;
+  w.chunk = m3::walk_chunk(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank, d->nheads);
+  return w;
+}
+
+size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* dq) {
+  if (check_dims(dq, true, true) != M3_OK) return 0;
+  if (dq->batch == 0 || dq->nheads == 0 || dq->seqlen == 0) return 0;
+  const m3_dims dw = walked_dims(dq);
+  const m3_dims* d = &dw;
+  if (d->chunk <= 0) return 0;
   const SegPlan sp = seg_plan(d);
   if (sp.S <= 1) return 0;
   return seg_ws(d, sp).bytes;
 }
 
-m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B, const void* C,
+m3_status mamba3_ssm_chunked_fwd(const m3_dims* dq, const void* x, const void* B, const void* C,
                                  const float* dt, const float* A, const float* lam, const float* theta,
                                  const float* h0, const void* prev_B, const void* prev_x, void* y,
                                  float* h_final, void* workspace, size_t workspace_bytes, void* stream) {
-  m3_status st = check_dims(d, true, true);
+  m3_status st = check_dims(dq, true, true);
   if (st != M3_OK) return st;
-  if ((d->flags & ~(0xffff | M3_FLAG_CHUNK_WALK | M3_FLAG_TOKEN_PATH)) != 0) return M3_ERR_UNSUPPORTED;
-  if ((d->flags & M3_FLAG_CHUNK_WALK) && (d->flags & M3_FLAG_TOKEN_PATH)) return M3_ERR_UNSUPPORTED;
-  if ((d->flags & M3_FLAG_TOKEN_PATH) && d->seqlen > M3_TOKEN_PATH_MAX_L) return M3_ERR_UNSUPPORTED;
-  if (m3::walk_lds_bytes(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) == 0 &&
-      !m3::walk_fast_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank) &&
-      !m3::subwalk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank, d->nheads))
-    return M3_ERR_UNSUPPORTED;
+  if ((dq->flags & ~(0xffff | M3_FLAG_CHUNK_WALK | M3_FLAG_TOKEN_PATH)) != 0) return M3_ERR_UNSUPPORTED;
+  if ((dq->flags & M3_FLAG_CHUNK_WALK) && (dq->flags & M3_FLAG_TOKEN_PATH)) return M3_ERR_UNSUPPORTED;
+  if ((dq->flags & M3_FLAG_TOKEN_PATH) && dq->seqlen > M3_TOKEN_PATH_MAX_L) return M3_ERR_UNSUPPORTED;
+  // from here on the sizes as walked (a chunk whose tiles do not fit the LDS
+  // is walked as shorter chunks)
+  const m3_dims dw = walked_dims(dq);
+  const m3_dims* d = &dw;
+  if (d->chunk <= 0) return M3_ERR_UNSUPPORTED;
   const SegPlan sp = seg_plan(d);
   if (sp.S > 1 && (d->io_dtype != M3_BF16 || d->batch * d->nheads > 65535)) return M3_ERR_UNSUPPORTED;
   const bool empty = d->batch == 0 || d->nheads == 0;
@@ -198,7 +211,7 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d, const void* x, const void* B,
   if (!all_aligned({x, B, C, y, workspace}, {prev_B, prev_x}, esz) ||
       !all_aligned({theta}, {dt, A, lam, h0, h_final}, 4))
     return M3_ERR_ALIGN;
-  const size_t need = mamba3_ssm_chunked_fwd_workspace_size(d);
+  const size_t need = mamba3_ssm_chunked_fwd_workspace_size(dq);
   if (need > 0 && (!workspace || workspace_bytes < need)) return M3_ERR_WORKSPACE;
   if (empty) return M3_OK;
   hipStream_t s = (hipStream_t)stream;

@@ -33,8 +33,10 @@
 // products have: the reverse walk rounds each operand to bf16, and the
 // checkpoint walk, whose states accumulate over the whole sequence, splits
 // w B~ into bf16 hi and lo parts (two MFMAs, accurate to ~2^-17). The chunk is
-// 16 tokens (8 when N or P is 128 and R = 4, to fit LDS), V <= 64,
-// N, P <= 128, not both 128.
+// 16 tokens (8 when N or P is 128 and R = 4, 16 / R when both are, to fit
+// LDS), V <= 64, N, P <= 128.  When N = P = 128 leaves no room for the
+// chunk's incoming state in LDS, the reverse walk reads it from its
+// checkpoint in global memory (L2) instead.
 #include "m3_common.hpp"
 #include "m3_lanes.hpp"
 #include "m3_launch.hpp"
@@ -43,7 +45,7 @@ namespace m3 {
 
 bool bwd_supported(int N, int P, int R) {
   const bool n = N == 16 || N == 32 || N == 64 || N == 128, p = P == 16 || P == 32 || P == 64 || P == 128;
-  return n && p && !(N == 128 && P == 128) && (R == 1 || R == 2 || R == 4);
+  return n && p && (R == 1 || R == 2 || R == 4);
 }
 
 namespace {
@@ -732,9 +734,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   constexpr int LBV = V + 8, LBN = N + 8, LBP = P + 8;
   constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + K * 4 + QB * 16 + V * 8 + 4 + 512;
   constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 4 * V * LBN + P * LBN) + SMALL;
-  constexpr bool TL = BFO && TL_BYTES <= 160 * 1024;
+  constexpr int F32_BYTES = 4 * (2 * V * LDN + 2 * N * LDP + 2 * V * LDP + 2 * V * LDV) + SMALL;
+  // HG: the chunk's incoming state H_in is read from its checkpoint in
+  // global memory instead of an LDS copy (only where the copy does not fit:
+  // N = P = 128 in fp32, and in bf16 with 16-token chunks)
+  constexpr bool HG = BFO ? TL_BYTES > 160 * 1024 : F32_BYTES > 160 * 1024;
+  constexpr bool TL = BFO && TL_BYTES - (HG ? 4 * N * LDP : 0) <= 160 * 1024;
   static_assert(TL || !BFO, "bf16 io takes the bf16 tile layout at every supported size");
-  __shared__ __attribute__((aligned(16))) float sB[V * LDN], sC[V * LDN], sH[N * LDP];  // 16-byte reads
+  static_assert(BFO || F32_BYTES - (HG ? 4 * N * LDP : 0) <= 160 * 1024, "fp32 tiles fit the LDS");
+  __shared__ __attribute__((aligned(16))) float sB[V * LDN], sC[V * LDN], sH[HG ? 4 : N * LDP];  // 16-byte reads
   __shared__ float sX[TL ? 4 : V * LDP], sDY[TL ? 4 : V * LDP];
   __shared__ float sDZ[TL ? 4 : N * LDP], sGM[TL ? 4 : V * LDV], sDG[TL ? 4 : V * LDV];
   __shared__ __attribute__((aligned(16))) u16 tGMt[TL ? V * LBV : 8];  // (G o M)^T
@@ -774,7 +782,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 
   // Global inputs of a chunk are fetched into registers one chunk ahead, so
   // that their latency overlaps the previous chunk's products.
-  constexpr int THP = (QB * K + TH - 1) / TH, HP = (N * P / 4 + TH - 1) / TH;
+  constexpr int THP = (QB * K + TH - 1) / TH, HP = HG ? 1 : (N * P / 4 + TH - 1) / TH;
   RowVecs<T, N, V, TH> rb, rc;
   RowVecs<T, P, V, TH> rx, rdy;
   float thv[THP];
@@ -813,7 +821,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       const int e = tid + TH * q;
       uint32_t o = 4 * e;
       fresh(o);
-      if (e < N * P / 4) hv[q] = *(const float4*)(ck + c * (N * P) + o);
+      if (!HG && e < N * P / 4) hv[q] = *(const float4*)(ck + c * (N * P) + o);
     }
   };
   // H_out of the chunk (the carried state after it) in the layout of Gb: the
@@ -847,6 +855,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     void* const odx = (char*)a.dx + t0c * (R * P * io<T>::BYTES);
     void* const odB = (char*)a.dB + t0c * (R * N * io<T>::BYTES);
     void* const odC = (char*)a.dC + t0c * (R * N * io<T>::BYTES);
+    // H_in (n, p) of this chunk: the LDS copy, or its checkpoint (HG)
+    const float* const hg = ck + c * (N * P);
+    auto hin = [&](int n, int p) -> float {
+      if constexpr (HG) return hg[n * P + p];
+      else return sH[n * LDP + p];
+    };
     // ---------------- staging (from the registers fetched ahead) ----------------
 #pragma unroll
     for (int q = 0; q < THP; ++q) {
@@ -864,7 +878,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < HP; ++q) {
       const int e = tid + TH * q;
-      if (e < N * P / 4) {
+      if (!HG && e < N * P / 4) {
         float* dst = &sH[((4 * e) / P) * LDP + (4 * e) % P];
         dst[0] = hv[q].x; dst[1] = hv[q].y; dst[2] = hv[q].z; dst[3] = hv[q].w;
       }
@@ -989,7 +1003,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             float dth = -g0 * o1 + g1 * o0;
             dth = lane_sum<1, 16>(dth);
             if (m16 == 0) atomicAdd(&sDTheta[k], dth);
-            part += z0 * sH[n0 * LDP + p] + z1 * sH[(n0 + 1) * LDP + p];
+            part += z0 * hin(n0, p) + z1 * hin(n0 + 1, p);
             // dH_in starts as e^{Lam_end} dZ
             Gb[j][2 * q] = eQ * z0;
             Gb[j][2 * q + 1] = eQ * z1;
@@ -1006,7 +1020,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         const int ti = wave + NW * j;
         if (ti < S::NPT) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ho[j][i] = sH[((ti / TP) * 16 + 4 * g + i) * LDP + (ti % TP) * 16 + m16];
+          for (int i = 0; i < 4; ++i) ho[j][i] = hin((ti / TP) * 16 + 4 * g + i, (ti % TP) * 16 + m16);
         }
       }
       fetch(c - 1);
@@ -1017,7 +1031,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     // (an operand index r = 16 * tile + m16 is a row of the operand's tile
     // for rdT, a column for rdTr)
     auto rdWB = [&](int v, int kk, auto e) { return lds_f2bf<decltype(e)::value>(&sB[v * LDN + kk], sW[v / R]); };
-    auto rdH = [&](int n, int kk, auto e) { return lds_f2bf<decltype(e)::value>(&sH[n * LDP + kk], 1.0f); };
+    auto rdH = [&](int n, int kk, auto e) {
+      if constexpr (HG) return lds_f2bf<decltype(e)::value>(&hg[n * P + kk], 1.0f);
+      else return lds_f2bf<decltype(e)::value>(&sH[n * LDP + kk], 1.0f);
+    };
     // along a row: elements (r, kk .. kk+E-1)
     auto rdT = [&](const u16* base, int ld) {
       return [=](int r, int kk, auto e) { return lds_bf<decltype(e)::value>(base + r * ld + kk); };
@@ -1145,7 +1162,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       } else {
         mm<NW, TN, TV, V>([&](int n, int s) { return sB[s * LDN + n]; },
                                  [&](int s, int v) { return sDG[v * LDV + s]; }, cacc, wave, m16, g);
-        mm<NW, TN, TV, P>([&](int n, int p) { return sH[n * LDP + p]; },
+        mm<NW, TN, TV, P>([&](int n, int p) { return hin(n, p); },
                                [&](int p, int v) { return sDY[v * LDP + p]; }, eacc, wave, m16, g);
         mm<NW, TN, TV, V>([&](int n, int t) { return sC[t * LDN + n]; },
                                  [&](int t, int s) { return sDG[t * LDV + s]; }, bacc, wave, m16, g);
@@ -1385,17 +1402,26 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       }
     }
   }
-  // dH'_0 to LDS for the prev products
+  // dH'_0 to LDS for the prev products (HG: to the first checkpoint's slot in
+  // global memory, which nothing reads any more; agent-scope fences around the
+  // barrier make the other waves' writes visible past the L1, which may still
+  // hold that slot's earlier contents)
+  float* const hsc = HG ? a.ckpt + bh * (nch + 1) * (int64_t)(N * P) : sH;
+  constexpr int LDH = HG ? P : LDP;
+  if (has_prev) {
 #pragma unroll
-  for (int j = 0; j < NPW; ++j) {
-    const int ti = wave + NW * j;
-    if (ti < S::NPT) {
-      const int tr = ti / TP, tc = ti % TP;
+    for (int j = 0; j < NPW; ++j) {
+      const int ti = wave + NW * j;
+      if (ti < S::NPT) {
+        const int tr = ti / TP, tc = ti % TP;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sH[(tr * 16 + 4 * g + i) * LDP + tc * 16 + m16] = Gb[j][i];
+        for (int i = 0; i < 4; ++i) hsc[(tr * 16 + 4 * g + i) * LDH + tc * 16 + m16] = Gb[j][i];
+      }
     }
   }
+  if constexpr (HG) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
+  if constexpr (HG) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (L > 0) {
     const float d1 = a.dt[tok_of(0)], l1 = a.lam[tok_of(0)];
     const float eps1 = has_prev ? (1.0f - l1) * d1 : 0.0f;
@@ -1409,7 +1435,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         float q0 = 0.0f;
         for (int r = 0; r < R; ++r)
           q0 += ld_io<T>(a.prev_B, (bh * R + r) * N + n) * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
-        part += (double)sH[n * LDP + p] * (double)q0;
+        part += (double)hsc[n * LDH + p] * (double)q0;
       }
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) part += __shfl_xor(part, o, 64);
@@ -1418,13 +1444,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         for (int e = tid; e < R * N; e += TH) {
           const int r = e / N, n = e % N;
           float acc = 0.0f;
-          for (int p = 0; p < P; ++p) acc += sH[n * LDP + p] * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
+          for (int p = 0; p < P; ++p) acc += hsc[n * LDH + p] * ld_io<T>(a.prev_x, (bh * R + r) * P + p);
           io<T>::store1(a.dprev_B, (bh * R + r) * N + n, eps1 * acc);
         }
         for (int e = tid; e < R * P; e += TH) {
           const int r = e / P, p = e % P;
           float acc = 0.0f;
-          for (int n = 0; n < N; ++n) acc += sH[n * LDP + p] * ld_io<T>(a.prev_B, (bh * R + r) * N + n);
+          for (int n = 0; n < N; ++n) acc += hsc[n * LDH + p] * ld_io<T>(a.prev_B, (bh * R + r) * N + n);
           io<T>::store1(a.dprev_x, (bh * R + r) * P + p, eps1 * acc);
         }
       }
@@ -1538,9 +1564,7 @@ static hipError_t bwd_p(int P, const BwdArgs& a, hipStream_t s) {
     case 16: return bwd_r<T, N, 16>(a, s);
     case 32: return bwd_r<T, N, 32>(a, s);
     case 64: return bwd_r<T, N, 64>(a, s);
-    case 128:
-      if constexpr (N < 128) return bwd_r<T, N, 128>(a, s);
-      else return hipErrorInvalidValue;
+    case 128: return bwd_r<T, N, 128>(a, s);
     default: return hipErrorInvalidValue;
   }
 }

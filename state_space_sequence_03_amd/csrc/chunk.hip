@@ -748,6 +748,13 @@ static hipError_t walk_n(int N, int P, const WalkArgs& a, hipStream_t s) {
   }
 }
 
+int walk_chunk(int io_bf16, int N, int P, int Q, int R, int64_t H) {
+  if (subwalk_supported(io_bf16, N, P, Q, R, H) || walk_fast_supported(io_bf16, N, P, Q, R)) return Q;
+  for (int q = Q; q * R >= 16 && q >= 8; q /= 2)
+    if (walk_lds_bytes(io_bf16, N, P, q, R) > 0) return q;
+  return 0;
+}
+
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s) {
   if (subwalk_supported(io_bf16, N, P, a.Q, a.R, a.H)) return launch_subwalk(N, a, s);
   if (walk_fast_supported(io_bf16, N, P, a.Q, a.R)) return launch_walk_fast(N, P, a, s);

@@ -93,6 +93,11 @@ hipError_t launch_subwalk(int N, const WalkArgs& a, hipStream_t s);
 // Chunked forward walk: the sub-chunk walker or the fast walker when one
 // applies, the general walker otherwise.
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
+// The chunk length (tokens) the walk uses for a requested chunk Q: Q itself
+// when a walker takes it as it is, else the longest of Q/2, Q/4, ... (at
+// least 16 virtual rows) whose tiles fit the general walker's LDS; 0 if none.
+// The chunked form is exact for any split, so only the rounding order changes.
+int walk_chunk(int io_bf16, int N, int P, int Q, int R, int64_t H);
 
 // Backward of the chunked forward: gradients of <dy, y> + <dh_final, h_final>.
 struct BwdArgs {
@@ -122,8 +127,11 @@ struct BwdArgs {
   int ckpt_local;  // checkpoint walk: 1 = end states and totals only (segments from zero)
 };
 // tokens per chunk of the backward walk: 16, or 8 when N or P is 128 and
-// R = 4 (so that the chunk's tiles fit LDS)
-constexpr int bwd_chunk_len(int N, int P, int R) { return ((N > 64 || P > 64) && R == 4) ? 8 : 16; }
+// R = 4, or 16 / R (16 virtual rows) when both are 128, so that the chunk's
+// tiles fit LDS
+constexpr int bwd_chunk_len(int N, int P, int R) {
+  return (N > 64 && P > 64) ? 16 / R : (((N > 64 || P > 64) && R == 4) ? 8 : 16);
+}
 bool bwd_supported(int N, int P, int R);
 hipError_t launch_chunked_bwd(int io_bf16, int N, int P, const BwdArgs& a, hipStream_t s);
 

@@ -6,8 +6,10 @@ passed by ``data_ptr()``) and the stream (``torch.cuda.current_stream()``).
 If the library is missing this module raises; there is no fallback.
 
 Entry points keep the ABI's names:
-  mamba3_ssm_chunked_fwd, mamba3_ssm_decode_step, mamba3_rope_bc
-(and the friendlier aliases chunked_fwd, decode_step, rope_bc).
+  mamba3_ssm_chunked_fwd, mamba3_ssm_chunked_bwd, mamba3_ssm_decode_step,
+  mamba3_rope_bc, mamba3_bc_prologue
+(and the friendlier aliases chunked_fwd, chunked_bwd, decode_step, rope_bc,
+bc_prologue), plus the workspace size queries.
 """
 from __future__ import annotations
 

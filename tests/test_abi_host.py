@@ -80,8 +80,6 @@ def dims(L, **kw):
     (dict(flags=1 << 18), "M3_ERR_UNSUPPORTED"),
     (dict(flags=0x30000), "M3_ERR_UNSUPPORTED"),                                # both path flags
     (dict(flags=0x20000, seqlen=17), "M3_ERR_UNSUPPORTED"),                     # token path too long
-    (dict(dstate=128, headdim=128, rank=4, chunk=64), "M3_ERR_UNSUPPORTED"),     # tiles exceed LDS
-    (dict(io_dtype=0, rank=4, chunk=64), "M3_ERR_UNSUPPORTED"),                # fp32 tiles exceed LDS
 ])
 def test_chunked_fwd_rejects_bad_sizes(L, kw, expect):
     assert call_fwd(L, dims(L, **kw)) == getattr(L, expect)
@@ -137,7 +135,8 @@ def test_backward_validation(L):
     d = dims(L)  # batch 2, L 100, H 3, P 64, N 64, R 4, bf16
     assert L.chunked_bwd_workspace_size(d) == 4 * 6 * ((100 + 15) // 16 + 1) * 64 * 64
     assert call_bwd(L, dims(L, dstate=15)) == L.M3_ERR_SHAPE
-    assert call_bwd(L, dims(L, headdim=128, dstate=128)) == L.M3_ERR_UNSUPPORTED   # not both 128
+    # N = P = 128 at R = 4: 4-token chunks (16 virtual rows), one segment
+    assert L.chunked_bwd_workspace_size(dims(L, headdim=128, dstate=128, flags=1)) == 4 * 6 * (25 + 1) * 128 * 128
     long = dims(L, batch=1, seqlen=100, nheads=2, dstate=128, flags=1)             # 8-token chunks at R = 4, one segment
     assert L.chunked_bwd_workspace_size(long) == 4 * 2 * ((100 + 7) // 8 + 1) * 128 * 64
     # segments: 13 chunks of 8 tokens at B*H = 2 -> 3 segments of 5, 5, 3 chunks; checkpoints + four
@@ -261,3 +260,33 @@ def test_binding_checks_operand_shapes(L):
         L.bc_prologue(u, W, s, th, 2, 1, 32, gain=torch.zeros((2, 2, 1, 16)))   # gain is (2, H, R, N)
     with pytest.raises(ValueError):
         L.bc_prologue(u, W[:32].contiguous(), s, th, 2, 1, 32)                  # W rows
+
+
+SUPPORTED = [(io, N, P, R, Q) for io in (0, 1) for N in (16, 32, 64, 128) for P in (16, 32, 64, 128)
+             for R in (1, 2, 4) for Q in (16, 32, 64)]
+
+
+def test_whole_supported_set_is_accepted(L):
+    """Every size of the supported set (N, P in {16,32,64,128}, R in {1,2,4},
+    Q in {16,32,64}, fp32 or bf16 io: 288 combinations) passes validation of
+    the chunked forward and of the backward, and every long-sequence plan
+    (few (b,h), segments) too.  An empty batch makes the call return after
+    validation, so nothing is launched."""
+    lib = L.lib()
+    f = ctypes.c_void_p(FAKE)
+    assert len(SUPPORTED) == 288
+    for io, N, P, R, Q in SUPPORTED:
+        for seqlen, nheads in ((100, 3), (65536, 2)):
+            d = L.make_dims(0, seqlen, nheads, P, N, R, Q, io)
+            st = lib.mamba3_ssm_chunked_fwd(ctypes.byref(d), *([f] * 7), None, None, None, f, None, None,
+                                            ctypes.c_size_t(0), None)
+            assert st == L.M3_OK, ("fwd", io, N, P, R, Q, L.status_string(st))
+            st = lib.mamba3_ssm_chunked_bwd(ctypes.byref(d), *([f] * 7), None, None, None, f, None, *([f] * 7),
+                                            None, None, None, None, ctypes.c_size_t(0), None)
+            assert st == L.M3_OK, ("bwd", io, N, P, R, Q, L.status_string(st))
+            # the workspace the same sizes would need with a non-empty batch
+            # is defined (segments for the long bf16 plan, 0 otherwise)
+            d1 = L.make_dims(1, seqlen, nheads, P, N, R, Q, io)
+            ws = L.chunked_fwd_workspace_size(d1)
+            assert ws >= 0 and (ws > 0) == (io == 1 and seqlen == 65536), (io, N, P, R, Q, ws)
+            assert L.chunked_bwd_workspace_size(d1) > 0

@@ -92,6 +92,14 @@ BWD_CASES = [
     ("f32", 1, 33, 2, 128, 32, 2, True, False, True),
     ("f32", 1, 19, 1, 64, 128, 1, False, True, True),
     ("f32", 2, 25, 1, 128, 64, 4, True, True, False),
+    # N = P = 128: 16 / R-token chunks (16 virtual rows); fp32, and bf16 at
+    # R = 1, read the chunk's incoming state from its checkpoint (L2)
+    ("f32", 1, 40, 2, 128, 128, 1, True, True, True),
+    ("f32", 1, 23, 1, 128, 128, 2, False, True, True),
+    ("f32", 2, 17, 1, 128, 128, 4, True, False, True),
+    ("bf16", 1, 40, 2, 128, 128, 1, True, True, True),
+    ("bf16", 1, 29, 1, 128, 128, 2, True, True, False),
+    ("bf16", 1, 37, 2, 128, 128, 4, False, True, True),
 ]
 
 
@@ -112,6 +120,8 @@ SEG_CASES = [
     ("bf16", 2, 150, 1, 64, 128, 4, False, True, True, 5),
     ("f32", 1, 64, 2, 16, 16, 1, False, False, False, 4),
     ("bf16", 1, 129, 3, 64, 64, 1, True, False, False, 2),
+    ("f32", 1, 70, 1, 128, 128, 4, True, True, True, 3),
+    ("bf16", 1, 90, 1, 128, 128, 1, True, True, True, 2),
 ]
 
 
@@ -163,7 +173,11 @@ def test_backward_full_workload_sampled(ops):
     g = ops.chunked_bwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], dy, chunk=w.chunk)
     torch.cuda.synchronize()
     rng = np.random.default_rng(2)
-    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.nheads))) for _ in range(4)]
+    pairs = [(0, 0), (w.batch - 1, w.nheads - 1)]
+    while len(pairs) < 8:
+        p = (int(rng.integers(w.batch)), int(rng.integers(w.nheads)))
+        if p not in pairs:
+            pairs.append(p)
     say(f"backward full workload: oracle on slices {pairs}")
     host = lambda t: t.float().cpu().numpy().astype(np.float64)
     sl = lambda t, bi, hi: host(t[bi:bi + 1, :, hi:hi + 1])
@@ -215,10 +229,13 @@ def test_backward_long_workload_sampled(ops):
 def test_backward_workspace_and_rejections(ops):
     d = ops.make_dims(2, 100, 3, 64, 64, 4, 64, ops.M3_BF16)
     assert ops.chunked_bwd_workspace_size(d) == 4 * 6 * (7 + 1) * 64 * 64
-    x = torch.zeros((1, 8, 1, 1, 128), device="cuda")
+    # N = P = 128 at R = 4: 4-token chunks
+    d = ops.make_dims(1, 10, 1, 128, 128, 4, 64, ops.M3_F32)
+    assert ops.chunked_bwd_workspace_size(d) == 4 * (3 + 1) * 128 * 128
+    x = torch.zeros((1, 8, 1, 1, 96), device="cuda")
     B = torch.zeros((1, 8, 1, 1, 128), device="cuda")
     s = torch.zeros((1, 8, 1), device="cuda")
     th = torch.zeros((1, 8, 1, 64), device="cuda")
     with pytest.raises(ops.Mamba3Error) as e:
-        ops.chunked_bwd(x, B, B, s, s, s, th, x)   # N = P = 128 is not covered by the backward
+        ops.chunked_bwd(x, B, B, s, s, s, th, x)   # P = 96 is outside the supported set
     assert e.value.status == ops.M3_ERR_UNSUPPORTED

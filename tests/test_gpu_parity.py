@@ -80,8 +80,8 @@ def check_fwd(ops, inp, io, chunk, tol=None, **kw):
     yo, ho = oracle_fwd(inp)
     ey = slice_err(host(y), yo, (0, 2))
     eh = slice_err(host(hf), ho, (0, 1))
-    say(f"   y err {ey:.3e}  h_final err {eh:.3e}  (tol {tol})")
-    assert ey < tol and eh < tol
+    say(f"   y err {ey:.3e}  h_final err {eh:.3e}  (tol {tol}, final state {min(tol, 1e-3)})")
+    assert ey < tol and eh < min(tol, 1e-3)
     return y, hf
 
 
@@ -113,6 +113,14 @@ FWD_CASES = [
     ("bf16", 2, 75, 2, 64, 128, 2, 16, True, True),
     ("bf16", 1, 40, 3, 64, 128, 4, 32, False, True),
     ("bf16", 1, 15, 1, 64, 128, 4, 64, True, False),
+    # tiles that do not fit the LDS at the requested chunk: the general walker
+    # walks the chunk as shorter pieces (fp32 at the 1.5B MIMO head shape,
+    # bf16 with N = P = 128 at R = 4, fp32 N = P = 128 walked as 8 tokens)
+    ("f32", 1, 150, 2, 64, 64, 4, 64, True, True),
+    ("bf16", 1, 150, 2, 128, 128, 4, 64, True, True),
+    ("f32", 1, 70, 1, 128, 128, 4, 16, True, True),
+    ("f32", 2, 90, 1, 64, 128, 2, 64, False, True),
+    ("f32", 1, 67, 2, 128, 128, 1, 64, True, False),
 ]
 
 
@@ -368,6 +376,18 @@ def test_rope_matches_oracle(ops, io, L, N, R, ang):
 
 
 # ---------------------------------------------------------------- full-size workloads, sampled slices
+def sampled_pairs(batch, nheads, n, seed):
+    """n distinct (b, h) pairs: the first and the last pair of the grid (the
+    highest block indices) and n - 2 more drawn with a fixed seed."""
+    rng = np.random.default_rng(seed)
+    pairs = [(0, 0), (batch - 1, nheads - 1)]
+    while len(pairs) < min(n, batch * nheads):
+        p = (int(rng.integers(batch)), int(rng.integers(nheads)))
+        if p not in pairs:
+            pairs.append(p)
+    return pairs
+
+
 def sample_slices(d, pairs, keys_bl=("x", "B", "C", "dt", "A", "lam", "theta")):
     """Host fp64 copies of the (b,h) slices named in pairs, stacked along the
     batch axis with one head each (so the oracle runs them on parallel threads)."""
@@ -386,16 +406,14 @@ def test_full_workload_sampled(ops, name):
     d = torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io, seed=seed_of(name))
     say(f"full workload {name}: chunked_fwd")
     y, hf = run_fwd(ops, d, w.chunk)
-    rng = np.random.default_rng(0)
-    npairs = 2 if name == "long_mimo_bf16" else 4
-    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.nheads))) for _ in range(npairs)]
+    pairs = sampled_pairs(w.batch, w.nheads, 4 if name == "long_mimo_bf16" else 8, seed=0)
     say(f"full workload {name}: oracle on slices {pairs}")
     yo, ho = oracle_fwd(sample_slices(d, pairs))
     for i, (bi, hi) in enumerate(pairs):
         ey = slice_err(host(y[bi:bi + 1, :, hi:hi + 1]), yo[i:i + 1], (0, 2))
         eh = slice_err(host(hf[bi:bi + 1, hi:hi + 1]), ho[i:i + 1], (0, 1))
         say(f"   slice {(bi, hi)}: y {ey:.3e} h {eh:.3e}")
-        assert ey < TOL["bf16"] and eh < TOL["bf16"]
+        assert ey < TOL["bf16"] and eh < 1e-3
 
 
 def test_full_decode_workload_sampled(ops):
@@ -416,8 +434,7 @@ def test_full_decode_workload_sampled(ops):
         ops.decode_step(st, step_major["x"][t], step_major["B"][t], step_major["C"][t], step_major["dt"][t],
                         step_major["A"][t], step_major["lam"][t], step_major["theta"][t], pb, px, y=ys[t])
     torch.cuda.synchronize()
-    rng = np.random.default_rng(1)
-    pairs = [(int(rng.integers(w.batch)), int(rng.integers(w.nheads))) for _ in range(4)]
+    pairs = sampled_pairs(w.batch, w.nheads, 8, seed=1)
     say(f"full decode workload: oracle on slices {pairs}")
     yo, ho = oracle_fwd(sample_slices(d, pairs))
     for i, (bi, hi) in enumerate(pairs):
@@ -428,17 +445,25 @@ def test_full_decode_workload_sampled(ops):
 
 
 # ---------------------------------------------------------------- sequence segments
-@pytest.mark.parametrize("segs,slow,N,P", [(2, False, 64, 64), (3, True, 64, 64), (5, True, 128, 64),
-                                           (16, False, 128, 64), (4, True, 32, 16)])
-def test_segments_match_single_walk_and_oracle(ops, segs, slow, N, P):
+# segments=0: the library's own plan (B*H = 2 here, so it cuts the sequence)
+@pytest.mark.parametrize("segs,slow,N,P,R", [(2, False, 64, 64, 4), (3, True, 64, 64, 4), (5, True, 128, 64, 4),
+                                             (16, False, 128, 64, 4), (4, True, 32, 16, 4),
+                                             # the general walker and the generic fix-up (N or P = 128)
+                                             (3, True, 64, 128, 2), (0, True, 64, 128, 2),
+                                             (4, True, 128, 64, 1), (0, True, 128, 64, 1),
+                                             (3, True, 128, 128, 4), (0, False, 128, 128, 4)])
+def test_segments_match_single_walk_and_oracle(ops, segs, slow, N, P, R):
     """Segments walked from zero + segment scan + fix-up == one sequential walk.
     With slow decay (A near 0) every chunk of every segment needs the fix-up."""
-    say(f"segments S={segs} slow={slow} N{N} P{P}")
+    say(f"segments S={segs} slow={slow} N{N} P{P} R{R}")
     kw = dict(a_range=(-30.0, math.log(1e-2))) if slow else {}
-    inp = numpy_inputs(1, 1000, 2, P, N, 4, io="bf16", seed=90 + segs, with_h0=True, with_prev=True, **kw)
+    inp = numpy_inputs(1, 1000, 2, P, N, R, io="bf16", seed=90 + segs + 7 * R, with_h0=True, with_prev=True, **kw)
     if slow:
         inp["dt"] *= 0.2
     d = to_dev(inp, "bf16")
+    if segs == 0:
+        dims = ops.make_dims(1, 1000, 2, P, N, R, 64, ops.M3_BF16)
+        assert ops.chunked_fwd_workspace_size(dims) > 0  # the default plan walks segments
     y1, h1 = run_fwd(ops, d, 64, segments=1)
     ys, hs = run_fwd(ops, d, 64, segments=segs)
     yo, ho = oracle_fwd(inp)
