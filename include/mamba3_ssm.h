@@ -156,6 +156,26 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* d,
                                  void* workspace, size_t workspace_bytes, void* stream);
 size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it): mamba3_ssm_chunked_fwd with no workspace argument.  The workspace comes
+ * from a fixed array of M3_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on, until the process ends; this call allocates nothing.
+ * Sizes whose workspace (mamba3_ssm_chunked_fwd_workspace_size) exceeds it
+ * return M3_ERR_WORKSPACE before any HIP call (48 MiB covers, e.g., one
+ * 65,536-token sequence of 32 heads at N = 128, P = 64, R = 4 walked as
+ * segments).  Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (concurrent streams, or several host threads)
+ * race on it and must be serialised by the caller.  The array's contents
+ * carry over between calls; the forward needs none on entry.  Results are
+ * those of mamba3_ssm_chunked_fwd with the same arguments. */
+#define M3_NOALLOC_SCRATCH_BYTES (48u << 20)
+m3_status mamba3_ssm_chunked_fwd_noalloc(const m3_dims* d,
+                                         const void* x, const void* B, const void* C,
+                                         const float* dt, const float* A, const float* lam, const float* theta,
+                                         const float* h0, const void* prev_B, const void* prev_x,
+                                         void* y, float* h_final, void* stream);
+
 /* Backward of mamba3_ssm_chunked_fwd: the gradients of
  *     l = sum_t <dy_t, y_t> + <dh_final, h_final>
  * with respect to every input of the forward (the chain rule of the chunked

@@ -25,7 +25,9 @@ M3_FLAG_CHUNK_WALK = 0x10000   # chunked_fwd: walk chunks even for short sequenc
 M3_FLAG_TOKEN_PATH = 0x20000   # chunked_fwd: token by token (at most M3_TOKEN_PATH_MAX_L tokens)
 M3_TOKEN_PATH_MAX_L = 16       # longest call the token path takes
 M3_TOKEN_PATH_SUBWALK_L = 8    # ... chosen by default when the sub-chunk walker covers the sizes
-ABI_SYMBOLS = ("mamba3_ssm_chunked_fwd", "mamba3_ssm_chunked_fwd_workspace_size", "mamba3_ssm_chunked_bwd",
+M3_NOALLOC_SCRATCH_BYTES = 48 << 20  # the fixed workspace of mamba3_ssm_chunked_fwd_noalloc, per GPU
+ABI_SYMBOLS = ("mamba3_ssm_chunked_fwd", "mamba3_ssm_chunked_fwd_workspace_size", "mamba3_ssm_chunked_fwd_noalloc",
+               "mamba3_ssm_chunked_bwd",
                "mamba3_ssm_chunked_bwd_workspace_size", "mamba3_ssm_decode_step",
                "mamba3_rope_bc", "mamba3_rope_bc_workspace_size", "mamba3_bc_prologue",
                "mamba3_bc_prologue_workspace_size", "mamba3_status_string", "mamba3_abi_version")
@@ -58,6 +60,8 @@ def lib() -> ctypes.CDLL:
         dp = ctypes.POINTER(Dims)
         L.mamba3_ssm_chunked_fwd.argtypes = [dp] + [vp] * 12 + [vp, sz, vp]
         L.mamba3_ssm_chunked_fwd.restype = ctypes.c_int
+        L.mamba3_ssm_chunked_fwd_noalloc.argtypes = [dp] + [vp] * 12 + [vp]
+        L.mamba3_ssm_chunked_fwd_noalloc.restype = ctypes.c_int
         L.mamba3_ssm_chunked_fwd_workspace_size.argtypes = [dp]
         L.mamba3_ssm_chunked_fwd_workspace_size.restype = sz
         L.mamba3_ssm_chunked_bwd.argtypes = [dp] + [vp] * 22 + [vp, sz, vp]
@@ -189,6 +193,28 @@ def mamba3_ssm_chunked_fwd(x, B, C, dt, A, lam, theta, h0=None, prev_B=None, pre
                                       ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
                                       _stream(stream))
     _check(st, "mamba3_ssm_chunked_fwd")
+    return y, h_final
+
+
+def mamba3_ssm_chunked_fwd_noalloc(x, B, C, dt, A, lam, theta, h0=None, prev_B=None, prev_x=None, *, y, h_final,
+                                   chunk=64, segments=0, stream=None):
+    """mamba3_ssm_chunked_fwd with the workspace taken from the library's fixed
+    per-GPU array: the caller passes every output (y, h_final may be None) and
+    the call allocates nothing.  Calls that overlap on one GPU race on that
+    array."""
+    torch = _torch()
+    b, L, H, R, P = x.shape
+    N = B.shape[-1]
+    _core_operands(torch, x, B, C, dt, A, lam, theta, h0, prev_B, prev_x)
+    if y is None:
+        raise ValueError("y is required (this entry point allocates nothing)")
+    _expect("y", y, x.shape, x.dtype, x.device)
+    _expect("h_final", h_final, (b, H, N, P), torch.float32, x.device)
+    dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x), flags=segments)
+    st = lib().mamba3_ssm_chunked_fwd_noalloc(ctypes.byref(dims), _ptr(x), _ptr(B), _ptr(C), _ptr(dt), _ptr(A),
+                                              _ptr(lam), _ptr(theta), _ptr(h0), _ptr(prev_B), _ptr(prev_x), _ptr(y),
+                                              _ptr(h_final), _stream(stream))
+    _check(st, "mamba3_ssm_chunked_fwd_noalloc")
     return y, h_final
 
 
@@ -327,6 +353,7 @@ def mamba3_bc_prologue(u, W, dt, theta, nheads, rank, dstate, gain=None, bias=No
 
 
 chunked_fwd = mamba3_ssm_chunked_fwd
+chunked_fwd_noalloc = mamba3_ssm_chunked_fwd_noalloc
 chunked_bwd = mamba3_ssm_chunked_bwd
 decode_step = mamba3_ssm_decode_step
 rope_bc = mamba3_rope_bc
