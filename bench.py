@@ -41,13 +41,14 @@ def subwalk_applies(w):
     if w.io != "bf16" or w.headdim != 64:
         return False
     if w.dstate == 64:
-        return w.chunk in (32, 64) and w.rank in (1, 2, 4)
+        return w.chunk in (16, 32, 64) and w.rank in (1, 2, 4)
     return w.dstate == 128 and w.chunk in (16, 32, 64) and w.rank in (2, 4)
 
 
 def walked_chunk(w):
     """Chunk length the library walks with: the sub-chunk walker walks 32-token
-    (N = 64) or 16-token (N = 128) pieces of the requested chunk."""
+    (N = 64) or 16-token (N = 128) pieces of the requested chunk (a chunk of 16
+    at N = 64 as chunks of 32)."""
     if subwalk_applies(w):
         return 32 if w.dstate == 64 else 16
     return w.chunk
@@ -117,6 +118,18 @@ def step_percentiles(fn, steps, torch):
     return pick(0.1), pick(0.5), pick(0.9)
 
 
+def settle(fn, torch, seconds=0.3):
+    """Untimed calls for a fixed stretch of wall time, whatever the warm-up
+    count: the first launches after the inputs are drawn run slower while the
+    clocks settle, and a short warm-up would fold that into the timed mean."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
 def bench_prefill(ops, inputs, w, steps, warmup, torch):
     d = inputs.torch_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank, io=w.io,
                             seed=inputs.seed_of(w.name))
@@ -124,6 +137,7 @@ def bench_prefill(ops, inputs, w, steps, warmup, torch):
     hf = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), device="cuda", dtype=torch.float32)
     fn = lambda: ops.chunked_fwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], chunk=w.chunk,
                                  y=y, h_final=hf)
+    settle(fn, torch)
     wall, ev = timed(fn, steps, warmup, torch)
     pct = step_percentiles(fn, steps, torch)
     th = w.batch * w.seqlen * w.nheads
@@ -313,32 +327,66 @@ def bench_rope(ops, inputs, w, steps, warmup, torch):
     return dict(ms=ev, gbps=b / (ev * 1e-3) / 1e9, bytes=b)
 
 
-def cpu_baseline(inputs, w, budget_s=12.0):
-    """The fp64 oracle on (b,h) slices of the same workload (full L), one thread per slice."""
-    import oracle
-    cores = min(os.cpu_count() or 1, int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)))
-    # the same distributions as the device draw, drawn on the host, one head per slice
-    def draw(n, seed):
-        t = inputs.torch_inputs(n, w.seqlen, 1, w.headdim, w.dstate, w.rank, io=w.io, seed=seed, device="cpu")
-        return {k: v.float().numpy() for k, v in t.items()}
+def host_cores():
+    """(logical CPUs this process may run on, physical cores of the host)."""
+    try:
+        logical = len(os.sched_getaffinity(0))
+    except AttributeError:
+        logical = os.cpu_count() or 1
+    phys = set()
+    try:
+        pid = cid = None
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("physical id"):
+                pid = ln.split(":")[1].strip()
+            elif ln.startswith("core id"):
+                cid = ln.split(":")[1].strip()
+            elif not ln.strip() and cid is not None:
+                phys.add((pid, cid))
+                pid = cid = None
+        if cid is not None:
+            phys.add((pid, cid))
+    except OSError:
+        pass
+    return logical, (len(phys) or None)
 
-    one = draw(1, 5)
-    t0 = time.perf_counter()
-    oracle.forward(one["x"], one["B"], one["C"], one["dt"], one["A"], one["lam"], one["theta"], nthreads=1)
-    t_one = time.perf_counter() - t0
-    # whole multiples of the core count, for about budget_s of wall time; at
-    # most the whole workload (all B*H slices)
+
+def cpu_baseline(inputs, w, budget_s=8.0, decode=False):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload: a set
+    of (b,h) slices over the full sequence (for decode: the workload's 1024
+    consecutive steps, which the oracle's token-by-token recurrence is), one
+    host thread per slice, timed over repeated calls for about budget_s.  The
+    rate is scaled to the whole workload: tokens/s for prefill, steps/s (all
+    B*H slices advanced by one token) for decode."""
+    import oracle
+    logical, physical = host_cores()
+    cores = min(logical, int(os.environ.get("OMP_NUM_THREADS", logical)))
     total = w.batch * w.nheads
-    nsl = min(total, cores * max(1, int(round(budget_s / max(t_one, 1e-3)))))
-    batch = draw(nsl, 6)
-    t0 = time.perf_counter()
-    oracle.forward(batch["x"], batch["B"], batch["C"], batch["dt"], batch["A"], batch["lam"], batch["theta"],
-                   nthreads=min(cores, nsl))
-    dt = time.perf_counter() - t0
-    token_heads_per_s = nsl * w.seqlen / dt
-    return dict(value=token_heads_per_s / w.nheads, unit="tokens/s", cores=min(cores, nsl), kind="oracle",
-                sample=f"{nsl} of the {total} (b,h) slices x L={w.seqlen} of the {w.name} workload "
-                       f"({nsl * w.seqlen} token-heads in {dt:.1f} s); tokens/s = token-heads/s / H={w.nheads}")
+    L = w.decode_steps if decode else w.seqlen
+    nsl = min(total, cores)
+    t = inputs.torch_inputs(nsl, L, 1, w.headdim, w.dstate, w.rank, io=w.io, seed=6, device="cpu",
+                            with_h0=decode)
+    s = {k: v.float().numpy() for k, v in t.items()}
+    reps, el = 0, 0.0
+    while el < budget_s:
+        t0 = time.perf_counter()
+        oracle.forward(s["x"], s["B"], s["C"], s["dt"], s["A"], s["lam"], s["theta"], h0=s.get("h0"),
+                       nthreads=nsl)
+        el += time.perf_counter() - t0
+        reps += 1
+    slice_tokens_per_s = reps * nsl * L / el
+    out = dict(unit="steps/s" if decode else "tokens/s", cores=nsl, kind="oracle",
+               logical_cpus=logical, physical_cores=physical)
+    if decode:
+        out["value"] = slice_tokens_per_s / total
+        out["sample"] = (f"{nsl} of the {total} (b,h) slices x {L} consecutive steps of {w.name}, {reps} call(s) in "
+                         f"{el:.1f} s on {nsl} threads; steps/s = slice-steps/s / {total} slices")
+    else:
+        out["value"] = slice_tokens_per_s / w.nheads
+        out["sample"] = (f"{nsl} of the {total} (b,h) slices x L={L} of {w.name}, {reps} call(s) in {el:.1f} s on "
+                         f"{nsl} threads; tokens/s = token-heads/s / H={w.nheads}")
+    out["value"] = round(out["value"], 3)
+    return out
 
 
 def bench_copy(torch, nbytes=1 << 30, reps=3):
@@ -357,30 +405,142 @@ def bench_copy(torch, nbytes=1 << 30, reps=3):
     return dict(bytes_read=nbytes, bytes_written=nbytes, ms=ms, gbps=2 * nbytes / (ms * 1e-3) / 1e9)
 
 
-WALKER_SOURCES = ("state_space_sequence_03_amd/csrc/chunk_subwalk.hip", "state_space_sequence_03_amd/csrc/m3_common.hpp")
-TRAFFIC_SUMMARY = "profiles/subchunk_walk_kernel_64_4__mimo_bf16__hbm_traffic.md"
+def bench_floor(torch, w, reps=10):
+    """Memory floors of this GPU for the prefill walker's traffic (the probes
+    of libm3_floor.so move the same bytes with no arithmetic): the walker's own
+    access pattern (one block per (b,h), two per compute unit; and two adjacent
+    heads per block), the same bytes as contiguous streams (3:1 and 1:1
+    read:write), and an in-place read-modify-write below and above the 256 MB
+    memory-side cache (the decode state's traffic).  GB/s counts the bytes
+    each probe is given to move."""
+    import ctypes
+    from state_space_sequence_03_amd import build
+    lib = ctypes.CDLL(build.FLOOR_LIB)
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.m3f_stream.argtypes = [ci, vp, vp, vp, vp, i64, ci, vp]
+    lib.m3f_walk.argtypes = [vp] * 8 + [i64, i64, i64, ci, ci, vp]
+    lib.m3f_rmw.argtypes = [vp, i64, ci, vp]
+    b, L, H, P, N, R = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank
+    assert (P, N, R) == (64, 64, 4)
+    u8 = torch.uint8
+    x, Bt, Ct, y = (torch.zeros(b * L * H * R * P * 2, dtype=u8, device="cuda") for _ in range(4))
+    th = torch.zeros(b * L * H * N // 2 * 4, dtype=u8, device="cuda")
+    dt, A, lam = (torch.zeros(b * L * H * 4, dtype=u8, device="cuda") for _ in range(3))
+    s = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(s.cuda_stream)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def t_ms(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            fn()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    walk_bytes = b * L * H * prefill_bytes_per_token_head(w)
+    out = {}
+    for name, hpb, lds in (("walker_pattern_2_blocks_per_cu", 1, 80 * 1024), ("walker_pattern_2_heads_per_block", 2, 160 * 1024),
+                           ("walker_pattern_8_blocks_per_cu", 1, 0)):
+        fn = lambda: lib.m3f_walk(ptr(x), ptr(Bt), ptr(Ct), ptr(th), ptr(dt), ptr(A), ptr(lam), ptr(y), b, L, H, hpb, lds, sp)
+        ms = t_ms(fn)
+        out[name] = dict(ms=round(ms, 4), GBps=round(walk_bytes / (ms * 1e-3) / 1e9, 1))
+    n16 = x.numel() // 16
+    for name, nr in (("stream_3_read_1_write", 3), ("stream_1_read_1_write", 1)):
+        for blocks in (2048, 8192):
+            fn = lambda: lib.m3f_stream(nr, ptr(x), ptr(Bt), ptr(Ct), ptr(y), n16, blocks, sp)
+            ms = t_ms(fn)
+            out[f"{name}_{blocks}_blocks"] = dict(ms=round(ms, 4), GBps=round((nr + 1) * x.numel() / (ms * 1e-3) / 1e9, 1))
+    del x, Bt, Ct, y, th, dt, A, lam
+    torch.cuda.empty_cache()
+    for name, nbytes in (("rmw_268MB", 268435456), ("rmw_2GB", 2 << 30)):
+        buf = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+        fn = lambda: lib.m3f_rmw(ptr(buf), nbytes // 16, 4096, sp)
+        ms = t_ms(fn)
+        out[name] = dict(ms=round(ms, 4), GBps=round(2 * nbytes / (ms * 1e-3) / 1e9, 1))
+        del buf
+    torch.cuda.empty_cache()
+    return out
 
 
-def walker_source_sha256():
+def bench_decode_batches(ops, inputs, torch, batches=(256, 1024), steps=32):
+    """The library's decode step at the decode workload's head shape with the
+    fp32 state below (batch 256: 268 MB) and far above (batch 1024: 1.07 GB)
+    the 256 MB memory-side cache: 32 consecutive steps in one HIP graph,
+    median of 5 replays, algorithmic bytes per step / time."""
+    from types import SimpleNamespace
+    out = {}
+    for batch in batches:
+        d = inputs.torch_inputs(batch, steps, 64, 64, 64, 4, io="bf16", seed=5, with_h0=True)
+        sm = {k: d[k].transpose(0, 1).contiguous() for k in ("x", "B", "C", "dt", "A", "lam", "theta")}
+        st = d["h0"].clone()
+        y = torch.empty(sm["x"].shape[1:], dtype=torch.bfloat16, device="cuda")
+
+        def run():
+            for t in range(steps):
+                ops.decode_step(st, sm["x"][t], sm["B"][t], sm["C"][t], sm["dt"][t], sm["A"][t], sm["lam"][t],
+                                sm["theta"][t], sm["B"][t - 1] if t else None, sm["x"][t - 1] if t else None, y=y)
+
+        run()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / steps)
+        ms = sorted(ts)[len(ts) // 2]
+        b = decode_bytes_per_step(SimpleNamespace(batch=batch, nheads=64, dstate=64, headdim=64, rank=4))
+        out[f"decode_batch_{batch}"] = dict(state_MB=round(batch * 64 * 64 * 64 * 4 / 1e6, 1), ms_per_step=round(ms, 5),
+                                            GBps=round(b / (ms * 1e-3) / 1e9, 1))
+        del d, sm, st, y, g
+        torch.cuda.empty_cache()
+    return out
+
+
+# Counter summaries under profiles/ (FETCH_SIZE and WRITE_SIZE per dispatch,
+# each scaled by what the same counter reads for a plain copy of known size),
+# valid while the kernel's sources hash to the value recorded in them.
+TRAFFIC = {
+    "walker": ("profiles/subchunk_walk_kernel_64_4__mimo_bf16__hbm_traffic.md",
+               ("state_space_sequence_03_amd/csrc/chunk_subwalk.hip", "state_space_sequence_03_amd/csrc/m3_common.hpp")),
+    "decode": ("profiles/decode_step_kernel_64_64_4__decode_mimo_bf16__hbm_traffic.md",
+               ("state_space_sequence_03_amd/csrc/decode.hip", "state_space_sequence_03_amd/csrc/m3_common.hpp")),
+}
+
+
+def source_sha256(files):
     h = hashlib.sha256()
-    for f in WALKER_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch of the prefill walker from the committed counter
-    summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by what the same
-    counter reads for a plain copy of known size), or None when the summary is
-    missing or was taken on other walker sources."""
-    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+def walker_source_sha256():
+    return source_sha256(TRAFFIC["walker"][1])
+
+
+def measured_traffic(which="walker"):
+    """HBM bytes per dispatch of a kernel from its committed counter summary,
+    or None when the summary is missing or was taken on other sources."""
+    summary, sources = TRAFFIC[which]
+    path = os.path.join(ROOT, summary)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     vals = dict(re.findall(r"^- (\w+): ([0-9a-fA-F.e+-]+)\s*$", text, re.M))
     try:
-        if vals["walker_source_sha256"] != walker_source_sha256():
+        sha = vals.get("source_sha256", vals.get("walker_source_sha256"))
+        if sha != source_sha256(sources):
             return None
         return (float(vals["fetch_kib_per_dispatch"]) * float(vals["fetch_scale"])
                 + float(vals["write_kib_per_dispatch"]) * float(vals["write_scale"])) * 1024.0
@@ -394,7 +554,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "rope", "prologue", "copy", "all"],
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "backward", "rope", "prologue", "copy", "floor", "all"],
                     default="all")
     ap.add_argument("--verify-k", type=int, default=8, help="tokens per call of the verify workload")
     ap.add_argument("--workload", default="mimo_bf16", choices=["mimo_bf16", "siso_bf16", "long_mimo_bf16"],
@@ -408,6 +568,13 @@ def main():
     import torch
     if args.only == "copy":
         print(json.dumps({"copy": bench_copy(torch)}), flush=True)
+        return
+    if args.only == "floor":
+        from state_space_sequence_03_amd import inputs
+        from state_space_sequence_03_amd import ops
+        fl = bench_floor(torch, inputs.WORKLOADS["mimo_bf16"])
+        fl.update(bench_decode_batches(ops, inputs, torch))
+        print(json.dumps({"floor": fl}), flush=True)
         return
     from state_space_sequence_03_amd import ops, inputs
     ops.lib()
@@ -438,7 +605,10 @@ def main():
     if args.only == "all":
         for name in ("siso_bf16", "long_mimo_bf16"):
             print(f"[bench] prefill {name} (context)", file=sys.stderr, flush=True)
-            out[name] = bench_prefill(ops, inputs, W[name], 3, 1, torch)
+            out[name] = bench_prefill(ops, inputs, W[name], 5, 2, torch)
+        import dataclasses
+        print("[bench] prefill mimo_bf16 at chunk 16 = N/R (context)", file=sys.stderr, flush=True)
+        out["chunk16"] = bench_prefill(ops, inputs, dataclasses.replace(W["mimo_bf16"], chunk=16), 5, 2, torch)
         print("[bench] backward long_mimo_bf16 (context)", file=sys.stderr, flush=True)
         out["backward_long"] = bench_backward(ops, inputs, W["long_mimo_bf16"], 3, 1, torch)
 
@@ -473,6 +643,10 @@ def main():
                           "steps_per_s": round(dc["steps_per_s"], 1), "ms_per_step": round(dc["ms_per_step"], 5),
                           "achieved_GBps": round(dc["gbps"], 1), "peak_GBps": HBM_PEAK_GBPS,
                           "frac": round(dc["gbps"] / HBM_PEAK_GBPS, 4), "bytes_per_step": dc["bytes_per_step"]}
+        tr = measured_traffic("decode")
+        line["decode"]["traffic"] = None if tr is None else round(tr)
+        if tr is not None:  # DRAM-side rate from the counters (MALL hits excluded)
+            line["decode"]["traffic_GBps"] = round(tr / (dc["ms_per_step"] * 1e-3) / 1e9, 1)
     if "verify" in out:
         vf = out["verify"]
         line["verify"] = {"workload": f"verify_mimo_bf16: decode shapes (batch 256, H=64, P=64, N=64, R=4), "
@@ -517,11 +691,21 @@ def main():
             o = out[name]
             line[name] = {"tokens_per_s": round(o["tokens_per_s"], 1), "ms": round(o["ms"], 4),
                           "achieved_GBps": round(o["gbps"], 1), "frac_hbm": round(o["gbps"] / HBM_PEAK_GBPS, 4)}
+    if "chunk16" in out:
+        o = out["chunk16"]
+        line["mimo_bf16_chunk16"] = {"workload": "mimo_bf16 prefill requested with chunk 16 (= N/R, the pages' "
+                                                 "suggestion; walked as 32-token chunks)",
+                                     "ms": round(o["ms"], 4), "tokens_per_s": round(o["tokens_per_s"], 1),
+                                     "frac_hbm": round(o["gbps"] / HBM_PEAK_GBPS, 4)}
     if not args.no_cpu and "prefill" in out:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cb = cpu_baseline(inputs, w)
-        cb["value"] = round(cb["value"], 2)
-        line["cpu_baseline"] = cb
+        print(f"[bench] cpu baseline (oracle) on {w.name}", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(inputs, w)
+        if args.only == "all":
+            for name in ("siso_bf16", "long_mimo_bf16"):
+                print(f"[bench] cpu baseline (oracle) on {name}", file=sys.stderr, flush=True)
+                line[name]["cpu_baseline"] = cpu_baseline(inputs, W[name], budget_s=5.0)
+            print("[bench] cpu baseline (oracle) on decode_mimo_bf16", file=sys.stderr, flush=True)
+            line["decode"]["cpu_baseline"] = cpu_baseline(inputs, W["decode_mimo_bf16"], budget_s=5.0, decode=True)
     print(json.dumps(line), flush=True)
 
 

@@ -103,9 +103,11 @@ typedef struct {
                        with P = 64 and N = 64 (Q in {32, 64}) or N = 128
                        (R in {2, 4}) the library walks each chunk as 32- or
                        16-token sub-chunks (the chunked form is exact for
-                       any split); segments and workspace follow Q.  Where
-                       Q's tiles do not fit the LDS the walk (and with it
-                       segments and workspace) uses Q/2, Q/4 or Q/8. */
+                       any split); segments and workspace follow Q.  At
+                       N = 64 a chunk of 16 is walked (and segmented) as
+                       chunks of 32.  Where Q's tiles do not fit the LDS the
+                       walk (and with it segments and workspace) uses Q/2,
+                       Q/4 or Q/8. */
   int32_t io_dtype; /* m3_dtype of x, B, C, y, prev_B, prev_x, B_rot, C_rot */
   int32_t flags;    /* chunked_fwd: bits 0..15 = number of sequence segments
                        walked in parallel per (b,h) (0 = chosen by the

@@ -1,4 +1,5 @@
-"""Build the gfx950 shared library ``libmamba3_ssm.so`` in-tree with hipcc.
+"""Build the gfx950 shared library ``libmamba3_ssm.so`` in-tree with hipcc
+(and ``libm3_floor.so``, the memory-floor probes that bench.py times).
 
 Every HIP translation unit is compiled for gfx950 only, with packed-fp32 VALU
 instructions disabled (``-Xclang -target-feature -Xclang -packed-fp32-ops``);
@@ -16,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmamba3_ssm.so")
+# memory-floor probes timed by bench.py --only floor (not part of the library)
+FLOOR_LIB = os.path.join(HERE, "libm3_floor.so")
+FLOOR_SOURCES = ["floor.hip"]
 SOURCES = ["abi.cpp", "decode.hip", "rope.hip", "chunk.hip", "chunk_fast.hip", "chunk_subwalk.hip", "segments.hip", "backward.hip", "prologue.hip", "noalloc.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
@@ -48,8 +52,15 @@ def build(verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    fobjs = [_compile(src) for src in FLOOR_SOURCES]
+    tmp = FLOOR_LIB + f".tmp{os.getpid()}"
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + fobjs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, FLOOR_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {FLOOR_LIB}")
     return LIB
 
 

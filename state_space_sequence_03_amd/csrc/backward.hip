@@ -732,7 +732,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // runs down its columns with two transpose reads (ds_read_b64_tr_b16); B~,
   // C~ and H_in are also kept in fp32 for the element-wise adjoints.
   constexpr int LBV = V + 8, LBN = N + 8, LBP = P + 8;
-  constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + K * 4 + QB * 16 + V * 8 + 4 + 512;
+  constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + TP * K * 4 + QB * 16 + TN * V * 8 + 4 + 512;
   constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 4 * V * LBN + P * LBN) + SMALL;
   constexpr int F32_BYTES = 4 * (2 * V * LDN + 2 * N * LDP + 2 * V * LDP + 2 * V * LDV) + SMALL;
   // HG: the chunk's incoming state H_in is read from its checkpoint in
@@ -757,8 +757,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float2 sCS[QB][K];
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
-  __shared__ float sDM[QB][QB], sDphi[QB][K], sDTheta[K], sTh[QB][K], sThP[4][QB];
-  __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDe[V], sDw[V], sRedW[NW];
+  // per-tile partial sums, each slot written by one lane and summed in a
+  // fixed order by its reader (no atomics: the results do not depend on the
+  // order in which waves arrive): the angle adjoint of H_out per column tile
+  // and pair, and d e^{Lam}, d w per n-tile and virtual row
+  __shared__ float sDM[QB][QB], sDphi[QB][K], sDThP[TP][K], sTh[QB][K], sThP[4][QB];
+  __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDeP[TN][V], sDwP[TN][V], sRedW[NW];
   __shared__ double sRedD[NW];
 
   const float* ck = a.ckpt + bh * (nch + 1) * (int64_t)(N * P);
@@ -870,11 +874,6 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     if (tid < QB) {
       sT[tid] = tsv.scal();
     }
-    for (int e = tid; e < V; e += TH) {
-      sDe[e] = 0.0f;
-      sDw[e] = 0.0f;
-    }
-    for (int e = tid; e < K; e += TH) sDTheta[e] = 0.0f;
 #pragma unroll
     for (int q = 0; q < HP; ++q) {
       const int e = tid + TH * q;
@@ -1002,7 +1001,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             const float o0 = ho[j][2 * q], o1 = ho[j][2 * q + 1];
             float dth = -g0 * o1 + g1 * o0;
             dth = lane_sum<1, 16>(dth);
-            if (m16 == 0) atomicAdd(&sDTheta[k], dth);
+            if (m16 == 0) sDThP[tc][k] = dth;
             part += z0 * hin(n0, p) + z1 * hin(n0 + 1, p);
             // dH_in starts as e^{Lam_end} dZ
             Gb[j][2 * q] = eQ * z0;
@@ -1189,8 +1188,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
           de = lane_sum<16, 64>(de);
           dw = lane_sum<16, 64>(dw);
           if (g == 0) {
-            atomicAdd(&sDe[v], de);
-            atomicAdd(&sDw[v], dw);
+            sDeP[tr][v] = de;
+            sDwP[tr][v] = dw;
           }
           // per pair (u, w) = features (n0 + 2q, n0 + 2q + 1): the angle
           // adjoint du w - dw u, and the un-rotated gradients
@@ -1284,7 +1283,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             if (t + 8 < QB) dom += u;
           }
         }
-        dom += sDTheta[k];
+#pragma unroll
+        for (int tc = 0; tc < TP; ++tc) dom += sDThP[tc][k];
         uint32_t ot = (uint32_t)t * Hu * K + k;
         fresh(ot);
         if (a0 + t < L) (a.dtheta + t0c * K)[ot] = sT[t].d * dom;
@@ -1302,8 +1302,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       const int tt = ok ? t : 0;
       float dwt = 0.0f, det = 0.0f;
       for (int r = 0; r < R; ++r) {
-        dwt += sDw[tt * R + r];
-        det += sDe[tt * R + r];
+#pragma unroll
+        for (int tr = 0; tr < TN; ++tr) {
+          dwt += sDwP[tr][tt * R + r];
+          det += sDeP[tr][tt * R + r];
+        }
       }
       // w_t = e^{Lam_end - Lam_t} q_t; e^{Lam_t} of the inter-chunk output
       float cl = 0.0f, cq = 0.0f;

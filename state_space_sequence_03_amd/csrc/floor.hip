@@ -1,0 +1,171 @@
+// Memory-floor probes for the benchmark (not part of the library's
+// operations): kernels that move exactly the bytes of a workload with no
+// arithmetic beyond what keeps every load alive, so that their time is the
+// floor that the access pattern itself sets on this GPU.
+//
+//  * m3f_stream: nr contiguous input arrays read once and one output array
+//    written once (out = xor of the inputs), grid-stride, every load of an
+//    iteration issued before its first use.  nr = 3 is the 3:1 read:write mix
+//    of the prefill walker (x, B, C in, y out) as one contiguous stream.
+//  * m3f_walk: the prefill walker's own global access pattern for bf16 io,
+//    P = N = 64, R = 4 (the 1.5B MIMO head shape): one block of 256 threads
+//    per (b, h) walking 32-token sub-chunks in order, two blocks per compute
+//    unit, each thread loading the same pieces of B, x, C, theta and the
+//    scalars as the walker's staging and output phases (the next sub-chunk's
+//    loads issued before the current sub-chunk's stores of y), and storing y
+//    as the walker does (32 bytes per lane).  heads_per_block = 2 lets one
+//    block of 512 threads walk two adjacent heads together, so that each
+//    token's rows of a tensor are read as one 1 KB piece.
+//  * m3f_rmw: an in-place read-modify-write of a float array (the decode
+//    step's state traffic), for buffers below and above the 256 MB
+//    memory-side cache.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+__device__ __forceinline__ uint4 x4(uint4 a, uint4 b) { return make_uint4(a.x ^ b.x, a.y ^ b.y, a.z ^ b.z, a.w ^ b.w); }
+
+template <int NR>
+__global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ a0, const uint4* __restrict__ a1,
+                                                     const uint4* __restrict__ a2, uint4* __restrict__ out, int64_t n) {
+  constexpr int U = 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i0 < n; i0 += stride * U) {
+    uint4 v[U][NR];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n) {
+        v[u][0] = a0[i];
+        if constexpr (NR > 1) v[u][1] = a1[i];
+        if constexpr (NR > 2) v[u][2] = a2[i];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i < n) {
+        uint4 r = v[u][0];
+        if constexpr (NR > 1) r = x4(r, v[u][1]);
+        if constexpr (NR > 2) r = x4(r, v[u][2]);
+        out[i] = r;
+      }
+    }
+  }
+}
+
+struct WalkPtrs {
+  const unsigned char *x, *B, *C, *theta, *dt, *A, *lam;
+  unsigned char* y;
+  int64_t batch, L, H;
+};
+
+// HPB heads per block (adjacent), 256 threads per head.
+template <int HPB>
+__global__ __launch_bounds__(256 * HPB) void walk_kernel(WalkPtrs a) {
+  constexpr int R = 4, N = 64, P = 64, K = N / 2, QS = 32, CH = N / 8, NKS = N / 32;
+  const int tid = threadIdx.x & 255, hsub = threadIdx.x >> 8;
+  const int lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
+  const int st_t = tid / CH, st_c = tid % CH;
+  const int64_t bh = (int64_t)blockIdx.x * HPB + hsub;
+  const int64_t b = bh / a.H, h = bh % a.H;
+  const int ctl[2] = {7 - wave, wave};
+  auto tok = [&](int64_t t) { return (b * a.L + t) * a.H + h; };
+  uint4 rB[R], rX[R], rC[2][NKS], rTh;
+  float rd, ra, rl, rd1, rl1;
+  auto load = [&](int64_t c0) {
+    const int64_t tt = tok(c0 + st_t);
+#pragma unroll
+    for (int r = 0; r < R; ++r) rB[r] = *(const uint4*)(a.B + (tt * R + r) * N * 2 + 16 * st_c);
+#pragma unroll
+    for (int k = 0; k < R; ++k) rX[k] = *(const uint4*)(a.x + (tt * R + k) * P * 2 + 16 * st_c);
+    rTh = *(const uint4*)(a.theta + tt * K * 4 + 16 * st_c);
+    rd = *(const float*)(a.dt + tt * 4);
+    ra = *(const float*)(a.A + tt * 4);
+    rl = *(const float*)(a.lam + tt * 4);
+    const int64_t t1 = c0 + st_t + 1 < a.L ? tok(c0 + st_t + 1) : tt;
+    rd1 = *(const float*)(a.dt + t1 * 4);
+    rl1 = *(const float*)(a.lam + t1 * 4);
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) {
+      const int v = ctl[ci] * 16 + m16;
+      const int64_t tc = tok(c0 + (v >> 2));
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) rC[ci][ks] = *(const uint4*)(a.C + (tc * R + (v & 3)) * N * 2 + 16 * g + ks * 64);
+    }
+  };
+  load(0);
+  for (int64_t c0 = 0; c0 < a.L; c0 += QS) {
+    // fold this sub-chunk's registers into the values stored as y
+    uint4 s = x4(x4(x4(rB[0], rB[1]), x4(rB[2], rB[3])), x4(x4(rX[0], rX[1]), x4(rX[2], rX[3])));
+    s = x4(s, rTh);
+    s.x ^= __float_as_uint(rd) ^ __float_as_uint(ra) ^ __float_as_uint(rl);
+    s.y ^= __float_as_uint(rd1) ^ __float_as_uint(rl1);
+    uint4 yv[2];
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) yv[ci] = x4(x4(rC[ci][0], rC[ci][1]), s);
+    if (c0 + QS < a.L) load(c0 + QS);
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) {
+      const int v = ctl[ci] * 16 + m16;
+      unsigned char* yr = a.y + (tok(c0 + (v >> 2)) * R + (v & 3)) * P * 2 + 32 * g;
+      *(uint4*)yr = yv[ci];
+      *(uint4*)(yr + 16) = x4(yv[ci], s);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void rmw_kernel(float4* __restrict__ p, int64_t n, float a, float c) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float4 v = p[i];
+    v.x = v.x * a + c; v.y = v.y * a + c; v.z = v.z * a + c; v.w = v.w * a + c;
+    p[i] = v;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// nr in {1, 2, 3} inputs of n16 16-byte vectors each (unused ones may be NULL).
+int m3f_stream(int nr, const void* a0, const void* a1, const void* a2, void* out, int64_t n16, int blocks,
+               void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  const uint4 *p0 = (const uint4*)a0, *p1 = (const uint4*)a1, *p2 = (const uint4*)a2;
+  if (nr == 1) hipLaunchKernelGGL(stream_kernel<1>, dim3(blocks), dim3(256), 0, s, p0, p1, p2, (uint4*)out, n16);
+  else if (nr == 2) hipLaunchKernelGGL(stream_kernel<2>, dim3(blocks), dim3(256), 0, s, p0, p1, p2, (uint4*)out, n16);
+  else if (nr == 3) hipLaunchKernelGGL(stream_kernel<3>, dim3(blocks), dim3(256), 0, s, p0, p1, p2, (uint4*)out, n16);
+  else return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+// The walker's access pattern over (batch, L, H) with L a multiple of 32 and
+// H a multiple of heads_per_block (1 or 2); lds_bytes of dynamic LDS per
+// block sets the number of resident blocks per compute unit.
+int m3f_walk(const void* x, const void* B, const void* C, const void* theta, const void* dt, const void* A,
+             const void* lam, void* y, int64_t batch, int64_t L, int64_t H, int heads_per_block, int lds_bytes,
+             void* stream) {
+  if (L % 32 != 0 || (heads_per_block != 1 && heads_per_block != 2) || H % heads_per_block != 0) return 1;
+  WalkPtrs a{(const unsigned char*)x, (const unsigned char*)B, (const unsigned char*)C, (const unsigned char*)theta,
+             (const unsigned char*)dt, (const unsigned char*)A, (const unsigned char*)lam, (unsigned char*)y,
+             batch, L, H};
+  hipStream_t s = (hipStream_t)stream;
+  const unsigned blocks = (unsigned)(batch * H / heads_per_block);
+  if (heads_per_block == 1) {
+    hipFuncSetAttribute((const void*)walk_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL(walk_kernel<1>, dim3(blocks), dim3(256), lds_bytes, s, a);
+  } else {
+    hipFuncSetAttribute((const void*)walk_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL(walk_kernel<2>, dim3(blocks), dim3(512), lds_bytes, s, a);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int m3f_rmw(void* p, int64_t n4, int blocks, void* stream) {
+  hipLaunchKernelGGL(rmw_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, (float4*)p, n4, 0.999f, 0.001f);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+}  // extern "C"

@@ -94,9 +94,10 @@ hipError_t launch_subwalk(int N, const WalkArgs& a, hipStream_t s);
 // applies, the general walker otherwise.
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
 // The chunk length (tokens) the walk uses for a requested chunk Q: Q itself
-// when a walker takes it as it is, else the longest of Q/2, Q/4, ... (at
-// least 16 virtual rows) whose tiles fit the general walker's LDS; 0 if none.
-// The chunked form is exact for any split, so only the rounding order changes.
+// when a walker takes it as it is; 32 when Q = 16 and the sub-chunk walker
+// takes the sizes at 32; else the longest of Q/2, Q/4, ... (at least 16
+// virtual rows) whose tiles fit the general walker's LDS; 0 if none.  The
+// chunked form is exact for any split, so only the rounding order changes.
 int walk_chunk(int io_bf16, int N, int P, int Q, int R, int64_t H);
 
 // Backward of the chunked forward: gradients of <dy, y> + <dh_final, h_final>.

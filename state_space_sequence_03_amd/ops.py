@@ -17,7 +17,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmamba3_ssm.so")
+# M3_LIBRARY names another build of the same library (e.g. one whose host
+# code is compiled with sanitizers, for the host-side tests)
+LIB_PATH = os.environ.get("M3_LIBRARY") or os.path.join(HERE, "libmamba3_ssm.so")
 
 M3_OK, M3_ERR_NULL, M3_ERR_SHAPE, M3_ERR_UNSUPPORTED, M3_ERR_ALIGN, M3_ERR_WORKSPACE, M3_ERR_HIP = range(7)
 M3_F32, M3_BF16 = 0, 1
@@ -223,11 +225,12 @@ def chunked_bwd_workspace_size(dims: Dims) -> int:
 
 
 def mamba3_ssm_chunked_bwd(x, B, C, dt, A, lam, theta, dy, h0=None, prev_B=None, prev_x=None, dh_final=None, *,
-                           chunk=64, segments=0, want_dh0=True, workspace=None, stream=None):
+                           chunk=64, segments=0, want_dh0=True, workspace=None, out=None, stream=None):
     """Backward of the chunked forward.  Returns a dict with dx, dB, dC (io dtype),
     ddt, dA, dlam, dtheta (fp32), dh0 (fp32, if wanted) and, when prev is given,
     dprev_B and dprev_x (io dtype).  segments: 0 = the library's choice, else
-    the number of sequence segments walked in parallel (flags' low 16 bits)."""
+    the number of sequence segments walked in parallel (flags' low 16 bits).
+    out: optional dict of preallocated outputs (any of the keys above)."""
     torch = _torch()
     b, L, H, R, P = x.shape
     N = B.shape[-1]
@@ -235,6 +238,7 @@ def mamba3_ssm_chunked_bwd(x, B, C, dt, A, lam, theta, dy, h0=None, prev_B=None,
     _expect("dy", dy, x.shape, x.dtype, x.device)
     _expect("dh_final", dh_final, (b, H, N, P), torch.float32, x.device)
     dims = make_dims(b, L, H, P, N, R, chunk, _io_code(x), flags=segments)
+    given = dict(out or {})
     out = {"dx": torch.empty_like(x), "dB": torch.empty_like(B), "dC": torch.empty_like(C),
            "ddt": torch.empty_like(dt), "dA": torch.empty_like(A), "dlam": torch.empty_like(lam),
            "dtheta": torch.empty_like(theta)}
@@ -243,6 +247,11 @@ def mamba3_ssm_chunked_bwd(x, B, C, dt, A, lam, theta, dy, h0=None, prev_B=None,
     if prev_B is not None:
         out["dprev_B"] = torch.empty_like(prev_B)
         out["dprev_x"] = torch.empty_like(prev_x)
+    for k, t in given.items():
+        if k not in out:
+            raise ValueError(f"out: unexpected or unwanted output {k!r}")
+        _expect(k, t, out[k].shape, out[k].dtype, x.device)
+        out[k] = t
     ws_bytes = chunked_bwd_workspace_size(dims)
     if ws_bytes > 0 and workspace is None:
         workspace = torch.empty(ws_bytes, device=x.device, dtype=torch.uint8)
