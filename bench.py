@@ -41,16 +41,16 @@ def subwalk_applies(w):
     if w.io != "bf16" or w.headdim != 64:
         return False
     if w.dstate == 64:
-        return w.chunk in (16, 32, 64) and w.rank in (1, 2, 4)
+        return w.chunk in (16, 32, 64) and w.rank in (1, 2, 4)  # shorter chunks walked at the sub-chunk length
     return w.dstate == 128 and w.chunk in (16, 32, 64) and w.rank in (2, 4)
 
 
 def walked_chunk(w):
     """Chunk length the library walks with: the sub-chunk walker walks 32-token
-    (N = 64) or 16-token (N = 128) pieces of the requested chunk (a chunk of 16
-    at N = 64 as chunks of 32)."""
+    (N = 64; 64-token for R = 1) or 16-token (N = 128) pieces of the requested
+    chunk (a shorter requested chunk at its own length)."""
     if subwalk_applies(w):
-        return 32 if w.dstate == 64 else 16
+        return (64 if w.rank == 1 else 32) if w.dstate == 64 else 16
     return w.chunk
 
 

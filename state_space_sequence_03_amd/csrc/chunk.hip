@@ -750,9 +750,12 @@ static hipError_t walk_n(int N, int P, const WalkArgs& a, hipStream_t s) {
 
 int walk_chunk(int io_bf16, int N, int P, int Q, int R, int64_t H) {
   if (subwalk_supported(io_bf16, N, P, Q, R, H)) return Q;
-  // a chunk shorter than the sub-chunk walker's pieces (16 tokens at N = 64)
-  // is walked as 32-token chunks by it rather than by an older walker
-  if (Q < 32 && subwalk_supported(io_bf16, N, P, 32, R, H)) return 32;
+  // a chunk shorter than the sub-chunk walker's pieces (e.g. 16 tokens at
+  // N = 64) is walked by it at its own length rather than by an older walker
+  if (N == 64 || N == 128) {
+    const int qs = subwalk_qs(N, R);
+    if (Q < qs && subwalk_supported(io_bf16, N, P, qs, R, H)) return qs;
+  }
   if (walk_fast_supported(io_bf16, N, P, Q, R)) return Q;
   for (int q = Q; q * R >= 16 && q >= 8; q /= 2)
     if (walk_lds_bytes(io_bf16, N, P, q, R) > 0) return q;

@@ -1,6 +1,7 @@
 // Prefill walker for bf16 io with P = 64 and N in {64, 128} (the 1.5B-scale
 // and the long-context head shapes): the sequence is walked in sub-chunks of
-// QS tokens (32 for N = 64, 16 for N = 128), two blocks per compute unit.
+// QS tokens (32 for N = 64, 64 for N = 64 with R = 1, 16 for N = 128), two
+// blocks per compute unit.
 //
 // Computes what the other walkers compute (chunk.hip, chunk_fast.hip): the
 // chunked form of the exponential-trapezoidal recurrence with data-dependent
@@ -15,9 +16,10 @@
 //  * 256 threads and under 80 KB of LDS per block, so two blocks (two (b,h)
 //    sequences or segments) share a compute unit and one block's staging and
 //    loads overlap the other block's matrix work.
-//  * Coalesced loads.  Staging thread (t, c) owns token t of the sub-chunk and
-//    the 16-byte column c of each rank row of B (and of x, and of theta's
-//    row), so a wave instruction reads whole rows.  Each wave keeps the C rows
+//  * Coalesced loads.  Staging thread (t, c) owns token t of the sub-chunk (for
+//    R = 1: the adjacent tokens 2t, 2t + 1) and the 16-byte column c of each
+//    rank row of B (and of x, and of theta's row), so a wave instruction reads
+//    whole rows.  Each wave keeps the C rows
 //    of its own output tiles in the MFMA operand layout (16 bytes per lane).
 //  * Cumulative log-decay and angles: wave scans over the tokens a wave holds,
 //    plus an exchange of wave totals through LDS.  The wave scans of the next
@@ -50,8 +52,11 @@ namespace {
 // LDS layout of one block
 template <int N, int R>
 struct SW {
-  static constexpr int P = 64, K = N / 2, QS = N == 64 ? 32 : 16, V = QS * R;
-  static constexpr int CH = N / 8;        // 16-byte columns of a B / C rank row = staging threads per token
+  // sub-chunk length: 32 tokens at N = 64 (64 for R = 1, where a token is one
+  // virtual row), 16 at N = 128
+  static constexpr int P = 64, K = N / 2, QS = N == 64 ? (R == 1 ? 64 : 32) : 16, V = QS * R;
+  static constexpr int CH = N / 8;        // 16-byte columns of a B / C rank row = staging threads per token slot
+  static constexpr int TPT = QS * CH / 256;  // tokens per staging thread: 2 (adjacent tokens) for R = 1 at N = 64, else 1
   static constexpr int BROW = 2 * N;      // bytes per row of B~ [V][N]
   static constexpr int XP = 144;          // bytes per row of X [V][64] (128 + 16: transpose reads of 4 rows hit distinct banks)
   static constexpr int WROW = 2 * V;      // bytes per row of (w B~)^T [N][V]
@@ -70,7 +75,8 @@ struct SW {
   static constexpr int OFF_TH = OFF_TOT + 4 * TOTW * 4;  // sub-chunk total rotation [K] float2
   static constexpr int BYTES = OFF_TH + K * 8;
 };
-static_assert(SW<64, 4>::BYTES <= 80 * 1024 && SW<128, 4>::BYTES <= 80 * 1024, "two blocks per compute unit");
+static_assert(SW<64, 4>::BYTES <= 80 * 1024 && SW<128, 4>::BYTES <= 80 * 1024 && SW<64, 1>::BYTES <= 80 * 1024,
+              "two blocks per compute unit");
 
 // rows of (w B~)^T: 16 consecutive rows, and the rows 8 apart that one staging
 // instruction writes, spread over the banks
@@ -92,11 +98,13 @@ static_assert(fW_rows_of_column_ok<4>() && fW_rows_of_column_ok<8>() && fW_rows_
 
 }  // namespace
 
+int subwalk_qs(int N, int R) { return N == 64 ? (R == 1 ? SW<64, 1>::QS : SW<64, 2>::QS) : SW<128, 2>::QS; }
+
 bool subwalk_supported(int io_bf16, int N, int P, int Q, int R, int64_t H) {
   if (!io_bf16 || P != 64) return false;
   // per-thread offsets within a sub-chunk are 32-bit: 32 tokens of (H, R, N or P) bf16
   if (H <= 0 || H * R * (N > P ? N : P) > (int64_t(1) << 24)) return false;
-  if (N == 64) return (Q == 32 || Q == 64) && (R == 1 || R == 2 || R == 4);
+  if (N == 64) return R == 1 ? Q == 64 : ((Q == 32 || Q == 64) && (R == 2 || R == 4));
   if (N == 128) return (Q == 16 || Q == 32 || Q == 64) && (R == 2 || R == 4);
   return false;
 }
@@ -104,7 +112,8 @@ bool subwalk_supported(int io_bf16, int N, int P, int Q, int R, int64_t H) {
 template <int N, int R>
 __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   typedef SW<N, R> Ly;
-  constexpr int P = 64, K = Ly::K, QS = Ly::QS, V = Ly::V, NW = 4, CH = Ly::CH;
+  constexpr int P = 64, K = Ly::K, QS = Ly::QS, V = Ly::V, NW = 4, CH = Ly::CH, TPT = Ly::TPT;
+  constexpr int RC = TPT * R;               // (w B~)^T columns a staging thread writes: its tokens' ranks
   constexpr int lgR = R == 4 ? 2 : (R == 2 ? 1 : 0);
   constexpr int NKS = N / 32;               // 32-wide slabs of the state dimension (MFMA k steps)
   constexpr int NCT = V / 16;               // column tiles of Y (16 virtual rows each)
@@ -140,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
     g = lane >> 4;
     jj = m16 >> 2;          // transpose-read coordinates
     uu = lane & 3;
-    st_t = id / CH;         // staging: token, 16-byte column
+    st_t = id / CH;         // staging: token slot (tokens TPT st_t ..), 16-byte column
     st_c = id % CH;
   };
   coords(threadIdx.x);
@@ -179,9 +188,9 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   const int pt0 = PTW == 4 ? 0 : 2 * (wave >> 1);
 
   // ---------------- prefetch registers (next sub-chunk) ----------------
-  uint4 rB[R], rX[XIT];
-  float4 rTh;
-  float rdt, rA, rlam, rdt1, rlam1;
+  uint4 rB[TPT][R], rX[TPT][XIT];
+  float4 rTh[TPT];
+  float rdt[TPT], rA[TPT], rlam[TPT], rdt1[TPT], rlam1[TPT];
   uint4 rC[NCW][NKS];
 
   // Tokens past the end of the segment read the last valid token instead: only
@@ -189,36 +198,44 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   // from the scores, the outputs and the state while every operand stays finite.
   auto load_BX = [&](int64_t c0) __attribute__((always_inline)) {
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
-    const uint32_t tr = (uint32_t)(st_t < nvalid ? st_t : nvalid - 1) * Hu;  // token row offset
     const unsigned char* gB = rowp(a.B, c0, R * N * 2);
     const unsigned char* gX = rowp(a.x, c0, R * P * 2);
-    const uint32_t ob = tr * (R * N * 2) + 16 * st_c, ox = tr * (R * P * 2);
 #pragma unroll
-    for (int r = 0; r < R; ++r) rB[r] = *(const uint4*)(gB + (ob + r * N * 2));
+    for (int u = 0; u < TPT; ++u) {
+      const int t = TPT * st_t + u;
+      const uint32_t tr = (uint32_t)(t < nvalid ? t : nvalid - 1) * Hu;  // token row offset
+      const uint32_t ob = tr * (R * N * 2) + 16 * st_c, ox = tr * (R * P * 2);
 #pragma unroll
-    for (int k = 0; k < XIT; ++k) {
-      const int i = st_c + CH * k;  // piece i: rank i / 8, 16-byte column i % 8
-      rX[k] = *(const uint4*)(gX + (ox + (i >> 3) * P * 2 + 16 * (i & 7)));
+      for (int r = 0; r < R; ++r) rB[u][r] = *(const uint4*)(gB + (ob + r * N * 2));
+#pragma unroll
+      for (int k = 0; k < XIT; ++k) {
+        const int i = st_c + CH * k;  // piece i: rank i / 8, 16-byte column i % 8
+        rX[u][k] = *(const uint4*)(gX + (ox + (i >> 3) * P * 2 + 16 * (i & 7)));
+      }
     }
   };
   auto load_scal = [&](int64_t c0) __attribute__((always_inline)) {
     const int nvalid = (int)((t1 - c0) < QS ? (t1 - c0) : QS);
-    const bool tv = st_t < nvalid;
-    const uint32_t tr = (uint32_t)(tv ? st_t : nvalid - 1) * Hu;
-    rTh = *(const float4*)(rowp(a.theta, c0, K * 4) + (tr * (K * 4) + 16 * st_c));
-    const float d = *(const float*)(rowp(a.dt, c0, 4) + tr * 4);
-    const float av = *(const float*)(rowp(a.A, c0, 4) + tr * 4);
-    const float l = *(const float*)(rowp(a.lam, c0, 4) + tr * 4);
-    rdt = tv ? d : 0.0f;
-    rA = tv ? av : 0.0f;
-    rlam = tv ? l : 0.0f;
-    // the following token (its epsilon weights this token's input in the state)
-    const bool tv1 = c0 + st_t + 1 < t1;
-    const uint32_t tr1 = tv1 ? tr + Hu : tr;
-    const float d1 = *(const float*)(rowp(a.dt, c0, 4) + tr1 * 4);
-    const float l1 = *(const float*)(rowp(a.lam, c0, 4) + tr1 * 4);
-    rdt1 = tv1 ? d1 : 0.0f;
-    rlam1 = tv1 ? l1 : 0.0f;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int t = TPT * st_t + u;
+      const bool tv = t < nvalid;
+      const uint32_t tr = (uint32_t)(tv ? t : nvalid - 1) * Hu;
+      rTh[u] = *(const float4*)(rowp(a.theta, c0, K * 4) + (tr * (K * 4) + 16 * st_c));
+      const float d = *(const float*)(rowp(a.dt, c0, 4) + tr * 4);
+      const float av = *(const float*)(rowp(a.A, c0, 4) + tr * 4);
+      const float l = *(const float*)(rowp(a.lam, c0, 4) + tr * 4);
+      rdt[u] = tv ? d : 0.0f;
+      rA[u] = tv ? av : 0.0f;
+      rlam[u] = tv ? l : 0.0f;
+      // the following token (its epsilon weights this token's input in the state)
+      const bool tv1 = c0 + t + 1 < t1;
+      const uint32_t tr1 = tv1 ? tr + Hu : tr;
+      const float d1 = *(const float*)(rowp(a.dt, c0, 4) + tr1 * 4);
+      const float l1 = *(const float*)(rowp(a.lam, c0, 4) + tr1 * 4);
+      rdt1[u] = tv1 ? d1 : 0.0f;
+      rlam1[u] = tv1 ? l1 : 0.0f;
+    }
   };
 
   auto load_C = [&](int64_t c0) __attribute__((always_inline)) {
@@ -234,11 +251,27 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
     }
   };
 
-  // wave-level inclusive scans over this wave's tokens (lanes CH apart), for
-  // the sub-chunk held in the prefetch registers; wave totals go to LDS
-  float sc_l, sc_p[4];
+  // wave-level inclusive scans over this wave's token slots (lanes CH apart;
+  // a slot's TPT adjacent tokens summed in the thread first), for the
+  // sub-chunk held in the prefetch registers; wave totals go to LDS
+  float sc_l[TPT], sc_p[TPT][4];
   auto local_scan = [&]() __attribute__((always_inline)) {
-    float v[5] = {rdt * rA, rdt * rTh.x, rdt * rTh.y, rdt * rTh.z, rdt * rTh.w};
+    float e[TPT][5];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      e[u][0] = rdt[u] * rA[u];
+      e[u][1] = rdt[u] * rTh[u].x;
+      e[u][2] = rdt[u] * rTh[u].y;
+      e[u][3] = rdt[u] * rTh[u].z;
+      e[u][4] = rdt[u] * rTh[u].w;
+    }
+    float v[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      v[i] = e[0][i];
+#pragma unroll
+      for (int u = 1; u < TPT; ++u) v[i] += e[u][i];
+    }
 #pragma unroll
     for (int o = CH; o < 64; o <<= 1) {
 #pragma unroll
@@ -247,9 +280,18 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
         if (lane >= o) v[i] += u;
       }
     }
-    sc_l = v[0];
+    // inclusive values of each token of the slot: the slot's last token has v
+    float w[5];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sc_p[j] = v[1 + j];
+    for (int i = 0; i < 5; ++i) w[i] = v[i];
+#pragma unroll
+    for (int u = TPT - 1; u >= 0; --u) {
+      sc_l[u] = w[0];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc_p[u][j] = w[1 + j];
+#pragma unroll
+      for (int i = 0; i < 5; ++i) w[i] -= e[u][i];
+    }
     if (lane >= 64 - CH) {  // the wave's last token
       *(float4*)(sTot + wave * Ly::TOTW + 4 * st_c) = make_float4(v[1], v[2], v[3], v[4]);
       if (st_c == 0) sTot[wave * Ly::TOTW + K] = v[0];
@@ -339,24 +381,39 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
       }
       const float ltot = sTot[K] + sTot[Ly::TOTW + K] + sTot[2 * Ly::TOTW + K] + sTot[3 * Ly::TOTW + K];
       sub_lend = ltot;
-      const float lam_c = sc_l + lpre;  // Lambda_t, inclusive, from the sub-chunk start
-      const float gam = rlam * rdt;
-      const float q = gam + (1.0f - rlam1) * rdt1;  // gamma_t + epsilon_{t+1}
-      const float l2 = lam_c * LOG2E;
-      const float wt = __builtin_amdgcn_exp2f((ltot - lam_c) * LOG2E) * q;
+      float wt[TPT], cs[TPT][4], sn[TPT][4];
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int t = TPT * st_t + u;
+        const float lam_c = sc_l[u] + lpre;  // Lambda_t, inclusive, from the sub-chunk start
+        const float gam = rlam[u] * rdt[u];
+        const float q = gam + (1.0f - rlam1[u]) * rdt1[u];  // gamma_t + epsilon_{t+1}
+        const float l2 = lam_c * LOG2E;
+        wt[u] = __builtin_amdgcn_exp2f((ltot - lam_c) * LOG2E) * q;
+        if (st_c == 0) sSC[t] = make_float4(l2, q, gam, __builtin_amdgcn_exp2f(l2));
+      }
       // R >= 2: the next sub-chunk's scalars, B and x are requested as soon as
       // this staging has read their registers (measured: slower for R = 1)
       if constexpr (R >= 2)
         if (c0 + QS < t1) load_scal(c0 + QS);
-      if (st_c == 0) sSC[st_t] = make_float4(l2, q, gam, __builtin_amdgcn_exp2f(l2));
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        uint32_t tab[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sincos_rev(sc_p[u][j] + ppre[j], &sn[u][j], &cs[u][j]);
+          tab[j] = pack_bf2(cs[u][j], sn[u][j]);
+        }
+        *(uint4*)(sCS + swz<BCPR>(TPT * st_t + u, st_c)) = make_uint4(tab[0], tab[1], tab[2], tab[3]);
+      }
       if (S > 1) {  // segment-relative offsets at requested chunk starts, for the fix-up pass
         if (meta && tid == 0) a.chunk_meta[meta_at] = segLam;
         segLam += ltot;
       }
-      if (st_t == QS - 1) {  // last token: the sub-chunk's total angles
+      if (st_t == QS / TPT - 1) {  // last token: the sub-chunk's total angles
         float ptot[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ptot[j] = sc_p[j] + ppre[j];
+        for (int j = 0; j < 4; ++j) ptot[j] = sc_p[TPT - 1][j] + ppre[j];
         if (S > 1) {
           if (meta) {
 #pragma unroll
@@ -373,43 +430,40 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
           sTh[4 * st_c + j] = make_float2(c2, s2);
         }
       }
-      float cs[4], sn[4];
-      uint32_t tab[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sincos_rev(sc_p[j] + ppre[j], &sn[j], &cs[j]);
-        tab[j] = pack_bf2(cs[j], sn[j]);
-      }
-      *(uint4*)(sCS + swz<BCPR>(st_t, st_c)) = make_uint4(tab[0], tab[1], tab[2], tab[3]);
-
       // B~ = R(-phi) B for every rank; w B~ kept in fp32 for the hi/lo split
-      float wb[R][8];
+      // (column u R + r: rank r of the slot's token u)
+      float wb[RC][8];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t w4[4] = {rB[r].x, rB[r].y, rB[r].z, rB[r].w};
-        float bt[8];
+      for (int u = 0; u < TPT; ++u)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float u = bf_lo(w4[j]), w = bf_hi(w4[j]);
-          bt[2 * j] = cs[j] * u + sn[j] * w;
-          bt[2 * j + 1] = cs[j] * w - sn[j] * u;
+        for (int r = 0; r < R; ++r) {
+          const uint32_t w4[4] = {rB[u][r].x, rB[u][r].y, rB[u][r].z, rB[u][r].w};
+          float bt[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float bu = bf_lo(w4[j]), bw = bf_hi(w4[j]);
+            bt[2 * j] = cs[u][j] * bu + sn[u][j] * bw;
+            bt[2 * j + 1] = cs[u][j] * bw - sn[u][j] * bu;
+          }
+          *(uint4*)(sB + swz<BCPR>(RC * st_t + u * R + r, st_c)) =
+              make_uint4(pack_bf2(bt[0], bt[1]), pack_bf2(bt[2], bt[3]), pack_bf2(bt[4], bt[5]), pack_bf2(bt[6], bt[7]));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) wb[u * R + r][e] = wt[u] * bt[e];
         }
-        *(uint4*)(sB + swz<BCPR>(R * st_t + r, st_c)) =
-            make_uint4(pack_bf2(bt[0], bt[1]), pack_bf2(bt[2], bt[3]), pack_bf2(bt[4], bt[5]), pack_bf2(bt[6], bt[7]));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wb[r][e] = wt * bt[e];
-      }
+      for (int u = 0; u < TPT; ++u)
 #pragma unroll
-      for (int k = 0; k < XIT; ++k) {
-        const int i = st_c + CH * k;
-        *(uint4*)(sX + (R * st_t + (i >> 3)) * Ly::XP + 16 * (i & 7)) = make_uint4(rX[k].x, rX[k].y, rX[k].z, rX[k].w);
-      }
+        for (int k = 0; k < XIT; ++k) {
+          const int i = st_c + CH * k;
+          *(uint4*)(sX + (RC * st_t + u * R + (i >> 3)) * Ly::XP + 16 * (i & 7)) =
+              make_uint4(rX[u][k].x, rX[u][k].y, rX[u][k].z, rX[u][k].w);
+        }
       if constexpr (R >= 2)
         if (c0 + QS < t1) load_BX(c0 + QS);
       // (w B~)^T: row n = 8 st_c + e, columns (token, rank): the R ranks of token t are adjacent.
       // lo = w B~ - hi comes from one dot product per element: hi . (-1, 0) + w B~.
       {
-        const int byte = 2 * R * st_t;
+        const int byte = 2 * RC * st_t;
         const int cb = byte >> 4;
         int z0 = (cb ^ fW<Ly::WCPR>(8 * st_c)) << 4, z1 = (cb ^ fW<Ly::WCPR>(8 * st_c + 4)) << 4;
         asm volatile("" : "+v"(z0), "+v"(z1));  // keeps (z ^ 16k) + base as one xor-add per row
@@ -428,11 +482,11 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int off = (((e < 4 ? z0 : z1) ^ (16 * (e & 3))) + base) + e * Ly::WROW;
-          if constexpr (R == 4) {
+          if constexpr (RC == 4) {
             const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]), h23 = pack_bf2(wb[2][e], wb[3][e]);
             *(uint2*)(sWh + off) = make_uint2(h01, h23);
             *(uint2*)(sWl + off) = make_uint2(lo2(h01, wb[0][e], wb[1][e]), lo2(h23, wb[2][e], wb[3][e]));
-          } else if constexpr (R == 2) {
+          } else if constexpr (RC == 2) {
             const uint32_t h01 = pack_bf2(wb[0][e], wb[1][e]);
             *(uint32_t*)(sWh + off) = h01;
             *(uint32_t*)(sWl + off) = lo2(h01, wb[0][e], wb[1][e]);
@@ -668,7 +722,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   if (S > 1) {
     float* tot = a.seg_tot + blk * (1 + K);
     if (tid == 0) tot[0] = segLam;
-    if (st_t == QS - 1) {
+    if (st_t == QS / TPT - 1) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) tot[1 + 4 * st_c + j] = segPhi[j];
     }
@@ -685,7 +739,7 @@ static hipError_t sw_run(const WalkArgs& a, hipStream_t s) {
 
 hipError_t launch_subwalk(int N, const WalkArgs& a, hipStream_t s) {
   if (N == 64) {
-    if (a.Q % SW<64, 1>::QS != 0) return hipErrorInvalidValue;
+    if (a.Q % SW<64, 1>::QS != 0 && !(a.R > 1 && a.Q % SW<64, 2>::QS == 0)) return hipErrorInvalidValue;
     switch (a.R) {
       case 1: return sw_run<64, 1>(a, s);
       case 2: return sw_run<64, 2>(a, s);

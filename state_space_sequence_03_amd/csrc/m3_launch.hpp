@@ -85,19 +85,22 @@ size_t walk_lds_bytes(int io_bf16, int N, int P, int Q, int R);
 // The fast walker (bf16 io, N and P <= 64) applies to these sizes.
 bool walk_fast_supported(int io_bf16, int N, int P, int Q, int R);
 hipError_t launch_walk_fast(int N, int P, const WalkArgs& a, hipStream_t s);
-// The sub-chunk walker (bf16 io, P = 64, N = 64 with Q in {32, 64}, or
-// N = 128 with R in {2, 4}) applies to these sizes; it walks 32-token (N = 64)
-// or 16-token (N = 128) sub-chunks and records segment offsets every Q tokens.
+// The sub-chunk walker (bf16 io, P = 64, N = 64 with Q in {32, 64} (Q = 64
+// for R = 1), or N = 128 with R in {2, 4}) applies to these sizes; it walks
+// sub-chunks of subwalk_qs(N, R) tokens (32 at N = 64, 64 at N = 64 with
+// R = 1, 16 at N = 128) and records segment offsets every Q tokens.
 bool subwalk_supported(int io_bf16, int N, int P, int Q, int R, int64_t H);
+int subwalk_qs(int N, int R);
 hipError_t launch_subwalk(int N, const WalkArgs& a, hipStream_t s);
 // Chunked forward walk: the sub-chunk walker or the fast walker when one
 // applies, the general walker otherwise.
 hipError_t launch_walk(int io_bf16, int N, int P, const WalkArgs& a, hipStream_t s);
 // The chunk length (tokens) the walk uses for a requested chunk Q: Q itself
-// when a walker takes it as it is; 32 when Q = 16 and the sub-chunk walker
-// takes the sizes at 32; else the longest of Q/2, Q/4, ... (at least 16
-// virtual rows) whose tiles fit the general walker's LDS; 0 if none.  The
-// chunked form is exact for any split, so only the rounding order changes.
+// when a walker takes it as it is; the sub-chunk walker's own length when Q is
+// shorter and that walker takes the sizes at its length; else the longest of
+// Q/2, Q/4, ... (at least 16 virtual rows) whose tiles fit the general
+// walker's LDS; 0 if none.  The chunked form is exact for any split, so only
+// the rounding order changes.
 int walk_chunk(int io_bf16, int N, int P, int Q, int R, int64_t H);
 
 // Backward of the chunked forward: gradients of <dy, y> + <dh_final, h_final>.

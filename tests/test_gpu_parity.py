@@ -109,6 +109,12 @@ FWD_CASES = [
     ("bf16", 1, 31, 2, 64, 64, 2, 64, True, True),
     ("bf16", 1, 33, 1, 64, 64, 1, 32, False, False),
     ("bf16", 3, 64, 2, 64, 64, 4, 64, True, True),
+    # R = 1: 64-token sub-chunks, two adjacent tokens per staging thread (a
+    # tail ending inside a thread's pair, a single-token second sub-chunk,
+    # requested chunks of 16 and 32 walked at 64)
+    ("bf16", 1, 127, 2, 64, 64, 1, 64, True, True),
+    ("bf16", 2, 65, 1, 64, 64, 1, 16, False, True),
+    ("bf16", 1, 200, 3, 64, 64, 1, 32, True, False),
     # the sub-chunk walker at N = 128 (16-token sub-chunks)
     ("bf16", 2, 75, 2, 64, 128, 2, 16, True, True),
     ("bf16", 1, 40, 3, 64, 128, 4, 32, False, True),
@@ -451,7 +457,8 @@ def test_full_decode_workload_sampled(ops):
                                              # the general walker and the generic fix-up (N or P = 128)
                                              (3, True, 64, 128, 2), (0, True, 64, 128, 2),
                                              (4, True, 128, 64, 1), (0, True, 128, 64, 1),
-                                             (3, True, 128, 128, 4), (0, False, 128, 128, 4)])
+                                             (3, True, 128, 128, 4), (0, False, 128, 128, 4),
+                                             (3, True, 64, 64, 1), (0, False, 64, 64, 1)])
 def test_segments_match_single_walk_and_oracle(ops, segs, slow, N, P, R):
     """Segments walked from zero + segment scan + fix-up == one sequential walk.
     With slow decay (A near 0) every chunk of every segment needs the fix-up."""
