@@ -418,7 +418,7 @@ def bench_floor(torch, w, reps=10):
     lib = ctypes.CDLL(build.FLOOR_LIB)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.m3f_stream.argtypes = [ci, vp, vp, vp, vp, i64, ci, vp]
-    lib.m3f_walk.argtypes = [vp] * 8 + [i64, i64, i64, ci, ci, vp]
+    lib.m3f_walk.argtypes = [vp] * 8 + [i64, i64, i64, ci, ci, ci, vp]
     lib.m3f_rmw.argtypes = [vp, i64, ci, vp]
     b, L, H, P, N, R = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank
     assert (P, N, R) == (64, 64, 4)
@@ -445,9 +445,21 @@ def bench_floor(torch, w, reps=10):
     out = {}
     for name, hpb, lds in (("walker_pattern_2_blocks_per_cu", 1, 80 * 1024), ("walker_pattern_2_heads_per_block", 2, 160 * 1024),
                            ("walker_pattern_8_blocks_per_cu", 1, 0)):
-        fn = lambda: lib.m3f_walk(ptr(x), ptr(Bt), ptr(Ct), ptr(th), ptr(dt), ptr(A), ptr(lam), ptr(y), b, L, H, hpb, lds, sp)
+        fn = lambda: lib.m3f_walk(ptr(x), ptr(Bt), ptr(Ct), ptr(th), ptr(dt), ptr(A), ptr(lam), ptr(y), b, L, H, 4, hpb,
+                                  lds, sp)
+        assert fn() == 0
         ms = t_ms(fn)
         out[name] = dict(ms=round(ms, 4), GBps=round(walk_bytes / (ms * 1e-3) / 1e9, 1))
+    # the SISO walker's pattern (R = 1: rows of 128 B, 64-token sub-chunks) on the siso_bf16 bytes
+    import dataclasses
+    ws = dataclasses.replace(w, rank=1, name="siso_bf16")
+    siso_bytes = b * L * H * prefill_bytes_per_token_head(ws)
+    for name, hpb in (("siso_walker_pattern_2_blocks_per_cu", 1), ("siso_walker_pattern_2_heads_per_block", 2)):
+        fn = lambda: lib.m3f_walk(ptr(x), ptr(Bt), ptr(Ct), ptr(th), ptr(dt), ptr(A), ptr(lam), ptr(y), b, L, H, 1, hpb,
+                                  80 * 1024, sp)
+        assert fn() == 0
+        ms = t_ms(fn)
+        out[name] = dict(ms=round(ms, 4), GBps=round(siso_bytes / (ms * 1e-3) / 1e9, 1))
     n16 = x.numel() // 16
     for name, nr in (("stream_3_read_1_write", 3), ("stream_1_read_1_write", 1)):
         for blocks in (2048, 8192):

@@ -40,6 +40,7 @@
 #include "m3_common.hpp"
 #include "m3_lanes.hpp"
 #include "m3_launch.hpp"
+#include "m3_order.hpp"
 
 namespace m3 {
 
@@ -244,7 +245,9 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(BwdArgs a) {
   // block (bh, seg): the chunks [c_begin, c_end) of one segment of a (b,h)
   // sequence (one segment spanning all chunks when NS = 1)
   const int NS = a.S > 1 ? a.S : 1;
-  const int64_t bh = blockIdx.x / NS, seg = blockIdx.x % NS, b = bh / a.H, h = bh % a.H;
+  int64_t bh, seg;  // block order: adjacent heads on one XCD (m3_order.hpp)
+  walker_of_block(blockIdx.x, gridDim.x, a.batch * a.H, NS, bh, seg);
+  const int64_t b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
   const int64_t c_begin = NS > 1 ? seg * a.cps : 0, c_end = NS > 1 ? (c_begin + a.cps < nch ? c_begin + a.cps : nch) : nch;
@@ -511,7 +514,9 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdArgs a) {
   // block (bh, seg): the chunks [c_begin, c_end) of one segment of a (b,h)
   // sequence (one segment spanning all chunks when NS = 1)
   const int NS = a.S > 1 ? a.S : 1;
-  const int64_t bh = blockIdx.x / NS, seg = blockIdx.x % NS, b = bh / a.H, h = bh % a.H;
+  int64_t bh, seg;  // block order: adjacent heads on one XCD (m3_order.hpp)
+  walker_of_block(blockIdx.x, gridDim.x, a.batch * a.H, NS, bh, seg);
+  const int64_t b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
   const int64_t c_begin = NS > 1 ? seg * a.cps : 0, c_end = NS > 1 ? (c_begin + a.cps < nch ? c_begin + a.cps : nch) : nch;
@@ -719,7 +724,9 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // block (bh, seg): the chunks [c_begin, c_end) of one segment, entered with
   // the true state adjoint at the segment end (one segment when NS = 1)
   const int NS = a.S > 1 ? a.S : 1;
-  const int64_t bh = blockIdx.x / NS, seg = blockIdx.x % NS, b = bh / a.H, h = bh % a.H;
+  int64_t bh, seg;  // block order: adjacent heads on one XCD (m3_order.hpp)
+  walker_of_block(blockIdx.x, gridDim.x, a.batch * a.H, NS, bh, seg);
+  const int64_t b = bh / a.H, h = bh % a.H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int64_t L = a.L, nch = (L + QB - 1) / QB;
   const int64_t c_begin = NS > 1 ? seg * a.cps : 0, c_end = NS > 1 ? (c_begin + a.cps < nch ? c_begin + a.cps : nch) : nch;

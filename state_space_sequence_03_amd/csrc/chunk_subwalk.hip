@@ -44,6 +44,7 @@
 // accumulation; the chunk state uses w B~ split into bf16 hi + lo parts.
 #include "m3_common.hpp"
 #include "m3_launch.hpp"
+#include "m3_order.hpp"
 
 namespace m3 {
 
@@ -155,8 +156,10 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   coords(threadIdx.x);
 
   const int64_t S = a.S;
-  const int64_t blk = blockIdx.x;
-  const int64_t seg = blk % S, bh = blk / S;
+  // block order: adjacent heads on one XCD (m3_order.hpp)
+  int64_t seg, bh;
+  walker_of_block(blockIdx.x, gridDim.x, a.batch * a.H, S, bh, seg);
+  const int64_t blk = bh * S + seg;
   const int64_t b = bh / a.H, h = bh % a.H;
   const int64_t L = a.L, H = a.H;
   const int64_t t0 = seg * a.seg_len;

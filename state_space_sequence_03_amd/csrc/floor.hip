@@ -8,9 +8,11 @@
 //    iteration issued before its first use.  nr = 3 is the 3:1 read:write mix
 //    of the prefill walker (x, B, C in, y out) as one contiguous stream.
 //  * m3f_walk: the prefill walker's own global access pattern for bf16 io,
-//    P = N = 64, R = 4 (the 1.5B MIMO head shape): one block of 256 threads
+//    P = N = 64, R = 4 or 1 (the 1.5B MIMO and SISO head shapes): one block
+//    of 256 threads
 //    per (b, h) walking 32-token sub-chunks in order, two blocks per compute
-//    unit, each thread loading the same pieces of B, x, C, theta and the
+//    unit (64-token sub-chunks, two tokens per staging thread for R = 1), each
+//    thread loading the same pieces of B, x, C, theta and the
 //    scalars as the walker's staging and output phases (the next sub-chunk's
 //    loads issued before the current sub-chunk's stores of y), and storing y
 //    as the walker does (32 bytes per lane).  heads_per_block = 2 lets one
@@ -61,55 +63,75 @@ struct WalkPtrs {
   int64_t batch, L, H;
 };
 
-// HPB heads per block (adjacent), 256 threads per head.
-template <int HPB>
+// HPB heads per block (adjacent), 256 threads per head; rank R = 4 (32-token
+// sub-chunks, one token per staging thread) or R = 1 (64-token sub-chunks,
+// two adjacent tokens per staging thread), as the walker for P = N = 64.
+template <int HPB, int R>
 __global__ __launch_bounds__(256 * HPB) void walk_kernel(WalkPtrs a) {
-  constexpr int R = 4, N = 64, P = 64, K = N / 2, QS = 32, CH = N / 8, NKS = N / 32;
+  constexpr int N = 64, P = 64, K = N / 2, QS = R == 1 ? 64 : 32, CH = N / 8, NKS = N / 32, TPT = QS * CH / 256;
+  constexpr int V = QS * R, NCT = V / 16, NCW = NCT == 8 ? 2 : 1;
+  constexpr int lgR = R == 4 ? 2 : 0;
   const int tid = threadIdx.x & 255, hsub = threadIdx.x >> 8;
   const int lane = tid & 63, wave = tid >> 6, m16 = lane & 15, g = lane >> 4;
   const int st_t = tid / CH, st_c = tid % CH;
   const int64_t bh = (int64_t)blockIdx.x * HPB + hsub;
   const int64_t b = bh / a.H, h = bh % a.H;
-  const int ctl[2] = {7 - wave, wave};
+  int ctl[NCW];
+  if constexpr (NCW == 2) {
+    ctl[0] = 7 - wave;
+    ctl[1] = wave;
+  } else {
+    ctl[0] = wave;
+  }
   auto tok = [&](int64_t t) { return (b * a.L + t) * a.H + h; };
-  uint4 rB[R], rX[R], rC[2][NKS], rTh;
-  float rd, ra, rl, rd1, rl1;
+  uint4 rB[TPT][R], rX[TPT][R], rC[NCW][NKS], rTh[TPT];
+  float rd[TPT], ra[TPT], rl[TPT], rd1[TPT], rl1[TPT];
   auto load = [&](int64_t c0) {
-    const int64_t tt = tok(c0 + st_t);
 #pragma unroll
-    for (int r = 0; r < R; ++r) rB[r] = *(const uint4*)(a.B + (tt * R + r) * N * 2 + 16 * st_c);
+    for (int u = 0; u < TPT; ++u) {
+      const int64_t t = c0 + TPT * st_t + u;
+      const int64_t tt = tok(t);
 #pragma unroll
-    for (int k = 0; k < R; ++k) rX[k] = *(const uint4*)(a.x + (tt * R + k) * P * 2 + 16 * st_c);
-    rTh = *(const uint4*)(a.theta + tt * K * 4 + 16 * st_c);
-    rd = *(const float*)(a.dt + tt * 4);
-    ra = *(const float*)(a.A + tt * 4);
-    rl = *(const float*)(a.lam + tt * 4);
-    const int64_t t1 = c0 + st_t + 1 < a.L ? tok(c0 + st_t + 1) : tt;
-    rd1 = *(const float*)(a.dt + t1 * 4);
-    rl1 = *(const float*)(a.lam + t1 * 4);
+      for (int r = 0; r < R; ++r) rB[u][r] = *(const uint4*)(a.B + (tt * R + r) * N * 2 + 16 * st_c);
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci) {
+      for (int k = 0; k < R; ++k) rX[u][k] = *(const uint4*)(a.x + (tt * R + k) * P * 2 + 16 * st_c);
+      rTh[u] = *(const uint4*)(a.theta + tt * K * 4 + 16 * st_c);
+      rd[u] = *(const float*)(a.dt + tt * 4);
+      ra[u] = *(const float*)(a.A + tt * 4);
+      rl[u] = *(const float*)(a.lam + tt * 4);
+      const int64_t t1 = t + 1 < a.L ? tok(t + 1) : tt;
+      rd1[u] = *(const float*)(a.dt + t1 * 4);
+      rl1[u] = *(const float*)(a.lam + t1 * 4);
+    }
+#pragma unroll
+    for (int ci = 0; ci < NCW; ++ci) {
       const int v = ctl[ci] * 16 + m16;
-      const int64_t tc = tok(c0 + (v >> 2));
+      const int64_t tc = tok(c0 + (v >> lgR));
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) rC[ci][ks] = *(const uint4*)(a.C + (tc * R + (v & 3)) * N * 2 + 16 * g + ks * 64);
+      for (int ks = 0; ks < NKS; ++ks)
+        rC[ci][ks] = *(const uint4*)(a.C + (tc * R + (v & (R - 1))) * N * 2 + 16 * g + ks * 64);
     }
   };
   load(0);
   for (int64_t c0 = 0; c0 < a.L; c0 += QS) {
     // fold this sub-chunk's registers into the values stored as y
-    uint4 s = x4(x4(x4(rB[0], rB[1]), x4(rB[2], rB[3])), x4(x4(rX[0], rX[1]), x4(rX[2], rX[3])));
-    s = x4(s, rTh);
-    s.x ^= __float_as_uint(rd) ^ __float_as_uint(ra) ^ __float_as_uint(rl);
-    s.y ^= __float_as_uint(rd1) ^ __float_as_uint(rl1);
-    uint4 yv[2];
+    uint4 s = make_uint4(0, 0, 0, 0);
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci) yv[ci] = x4(x4(rC[ci][0], rC[ci][1]), s);
+    for (int u = 0; u < TPT; ++u) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s = x4(x4(s, rB[u][r]), rX[u][r]);
+      s = x4(s, rTh[u]);
+      s.x ^= __float_as_uint(rd[u]) ^ __float_as_uint(ra[u]) ^ __float_as_uint(rl[u]);
+      s.y ^= __float_as_uint(rd1[u]) ^ __float_as_uint(rl1[u]);
+    }
+    uint4 yv[NCW];
+#pragma unroll
+    for (int ci = 0; ci < NCW; ++ci) yv[ci] = x4(x4(rC[ci][0], rC[ci][1]), s);
     if (c0 + QS < a.L) load(c0 + QS);
 #pragma unroll
-    for (int ci = 0; ci < 2; ++ci) {
+    for (int ci = 0; ci < NCW; ++ci) {
       const int v = ctl[ci] * 16 + m16;
-      unsigned char* yr = a.y + (tok(c0 + (v >> 2)) * R + (v & 3)) * P * 2 + 32 * g;
+      unsigned char* yr = a.y + (tok(c0 + (v >> lgR)) * R + (v & (R - 1))) * P * 2 + 32 * g;
       *(uint4*)yr = yv[ci];
       *(uint4*)(yr + 16) = x4(yv[ci], s);
     }
@@ -141,24 +163,34 @@ int m3f_stream(int nr, const void* a0, const void* a1, const void* a2, void* out
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-// The walker's access pattern over (batch, L, H) with L a multiple of 32 and
-// H a multiple of heads_per_block (1 or 2); lds_bytes of dynamic LDS per
-// block sets the number of resident blocks per compute unit.
+// The walker's access pattern over (batch, L, H) at P = N = 64 and rank R
+// (1 or 4), with L a multiple of the sub-chunk (64 tokens for R = 1, 32 for
+// R = 4) and H a multiple of heads_per_block (1 or 2);
+// lds_bytes of dynamic LDS per block sets the number of resident blocks per
+// compute unit.
 int m3f_walk(const void* x, const void* B, const void* C, const void* theta, const void* dt, const void* A,
-             const void* lam, void* y, int64_t batch, int64_t L, int64_t H, int heads_per_block, int lds_bytes,
-             void* stream) {
-  if (L % 32 != 0 || (heads_per_block != 1 && heads_per_block != 2) || H % heads_per_block != 0) return 1;
+             const void* lam, void* y, int64_t batch, int64_t L, int64_t H, int R, int heads_per_block,
+             int lds_bytes, void* stream) {
+  if ((R != 1 && R != 4) || L % (R == 1 ? 64 : 32) != 0 || (heads_per_block != 1 && heads_per_block != 2) ||
+      H % heads_per_block != 0)
+    return 1;
   WalkPtrs a{(const unsigned char*)x, (const unsigned char*)B, (const unsigned char*)C, (const unsigned char*)theta,
              (const unsigned char*)dt, (const unsigned char*)A, (const unsigned char*)lam, (unsigned char*)y,
              batch, L, H};
   hipStream_t s = (hipStream_t)stream;
   const unsigned blocks = (unsigned)(batch * H / heads_per_block);
-  if (heads_per_block == 1) {
-    hipFuncSetAttribute((const void*)walk_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    hipLaunchKernelGGL(walk_kernel<1>, dim3(blocks), dim3(256), lds_bytes, s, a);
+  if (R == 1 && heads_per_block == 1) {
+    hipFuncSetAttribute((const void*)walk_kernel<1, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL((walk_kernel<1, 1>), dim3(blocks), dim3(256), lds_bytes, s, a);
+  } else if (R == 1) {
+    hipFuncSetAttribute((const void*)walk_kernel<2, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL((walk_kernel<2, 1>), dim3(blocks), dim3(512), lds_bytes, s, a);
+  } else if (heads_per_block == 1) {
+    hipFuncSetAttribute((const void*)walk_kernel<1, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL((walk_kernel<1, 4>), dim3(blocks), dim3(256), lds_bytes, s, a);
   } else {
-    hipFuncSetAttribute((const void*)walk_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    hipLaunchKernelGGL(walk_kernel<2>, dim3(blocks), dim3(512), lds_bytes, s, a);
+    hipFuncSetAttribute((const void*)walk_kernel<2, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL((walk_kernel<2, 4>), dim3(blocks), dim3(512), lds_bytes, s, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
