@@ -478,6 +478,31 @@ def bench_floor(torch, w, reps=10):
     return out
 
 
+def bench_gemm_reference(torch, inputs, reps=10):
+    """Context for the B/C prologue: the vendor library's plain bf16 GEMM
+    (torch.matmul, i.e. hipBLASLt) of the prologue's projection shape, with no
+    normalisation, rotation or fused stores.  Not part of any path."""
+    c = inputs.PROLOGUE
+    M, F, D = c["batch"] * c["seqlen"], 2 * c["nheads"] * c["rank"] * c["dstate"], c["d_model"]
+    u = torch.randn(M, D, device="cuda", dtype=torch.bfloat16)
+    W = torch.randn(F, D, device="cuda", dtype=torch.bfloat16)
+    fn = lambda: torch.matmul(W, u.t())
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del u, W
+    torch.cuda.empty_cache()
+    return {"library_gemm_prologue_shape": dict(M=M, F=F, D=D, ms=round(ms, 4),
+                                                TFLOPs=round(2.0 * M * F * D / (ms * 1e-3) / 1e12, 1))}
+
+
 def bench_decode_batches(ops, inputs, torch, batches=(256, 1024), steps=32):
     """The library's decode step at the decode workload's head shape with the
     fp32 state below (batch 256: 268 MB) and far above (batch 1024: 1.07 GB)
@@ -586,6 +611,7 @@ def main():
         from state_space_sequence_03_amd import ops
         fl = bench_floor(torch, inputs.WORKLOADS["mimo_bf16"])
         fl.update(bench_decode_batches(ops, inputs, torch))
+        fl.update(bench_gemm_reference(torch, inputs))
         print(json.dumps({"floor": fl}), flush=True)
         return
     from state_space_sequence_03_amd import ops, inputs
