@@ -122,14 +122,17 @@ typedef struct {
 } m3_dims;
 
 /* chunked_fwd: short calls (e.g. verifying k draft tokens of a decoder, with
- * the decode state as h0 and h_final) run token by token with the state held
- * on chip: the one-token update of decode_step applied to each token, the
- * state read once and written once.  The library takes that path for
- * seqlen <= M3_TOKEN_PATH_SUBWALK_L when the sub-chunk walker covers the sizes
- * (bf16 io, P = 64, N = 64 or 128) and for seqlen <= M3_TOKEN_PATH_MAX_L
+ * the decode state as h0 and h_final) read the state once and write it once.
+ * For bf16 io with P = 64 and N = 64 or 128, a call of at most
+ * M3_TOKEN_PATH_MAX_L tokens runs as one chunk of the chunked form on bf16
+ * MFMAs (two 8-token pieces for R = 4 past 8 tokens).  Other sizes run token
+ * by token with the state held on chip (the one-token update of decode_step
+ * applied to each token) for seqlen <= M3_TOKEN_PATH_SUBWALK_L when the
+ * sub-chunk walker covers the sizes and seqlen <= M3_TOKEN_PATH_MAX_L
  * otherwise.  M3_FLAG_CHUNK_WALK forces the chunk walk; M3_FLAG_TOKEN_PATH
- * forces the token path (seqlen <= M3_TOKEN_PATH_MAX_L, else
- * M3_ERR_UNSUPPORTED); not both.  Both paths compute the same function. */
+ * forces the token-by-token path (seqlen <= M3_TOKEN_PATH_MAX_L, else
+ * M3_ERR_UNSUPPORTED); not both.  Every path computes the same function (the
+ * chunked ones to the rounding of their bf16 products). */
 #define M3_FLAG_CHUNK_WALK 0x10000
 #define M3_FLAG_TOKEN_PATH 0x20000
 #define M3_TOKEN_PATH_MAX_L 16

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libmamba3_ssm.so")
 # memory-floor probes timed by bench.py --only floor (not part of the library)
 FLOOR_LIB = os.path.join(HERE, "libm3_floor.so")
 FLOOR_SOURCES = ["floor.hip"]
-SOURCES = ["abi.cpp", "decode.hip", "rope.hip", "chunk.hip", "chunk_fast.hip", "chunk_subwalk.hip", "segments.hip", "backward.hip", "prologue.hip", "noalloc.cpp"]
+SOURCES = ["abi.cpp", "decode.hip", "rope.hip", "chunk.hip", "chunk_fast.hip", "chunk_subwalk.hip", "segments.hip", "backward.hip", "prologue.hip", "short_chunk.hip", "noalloc.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops", "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]

@@ -228,16 +228,21 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* dq, const void* x, const void* B
       m3::subwalk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->chunk, (int)d->rank, d->nheads)
           ? M3_TOKEN_PATH_SUBWALK_L
           : M3_TOKEN_PATH_MAX_L;
-  const bool token_path = (d->flags & M3_FLAG_TOKEN_PATH) ||
-                          (d->seqlen <= tok_max && sp.S == 1 && !(d->flags & M3_FLAG_CHUNK_WALK));
-  if (token_path) {
-    // a few tokens: token by token with the state in registers
+  // short calls as one chunk on MFMAs where that kernel covers the sizes
+  const bool one_chunk = !(d->flags & (M3_FLAG_TOKEN_PATH | M3_FLAG_CHUNK_WALK)) && sp.S == 1 &&
+                         d->seqlen <= M3_TOKEN_PATH_MAX_L &&
+                         m3::short_chunk_supported(io_bf16(d), (int)d->dstate, (int)d->headdim, (int)d->rank);
+  const bool token_path = !one_chunk && ((d->flags & M3_FLAG_TOKEN_PATH) ||
+                                         (d->seqlen <= tok_max && sp.S == 1 && !(d->flags & M3_FLAG_CHUNK_WALK)));
+  if (one_chunk || token_path) {
     m3::TokensArgs t{};
     t.h0 = h0; t.h_final = h_final; t.x = x; t.B = B; t.C = C;
     t.dt = dt; t.A = A; t.lam = lam; t.theta = theta; t.prev_B = prev_B; t.prev_x = prev_x; t.y = y;
     t.batch = d->batch; t.L = d->seqlen; t.H = d->nheads; t.R = (int)d->rank;
-    return m3::launch_decode_tokens(io_bf16(d), (int)d->dstate, (int)d->headdim, t, s) == hipSuccess ? M3_OK
-                                                                                                : M3_ERR_HIP;
+    // a few tokens: as one chunk on MFMAs, or token by token with the state in registers
+    const hipError_t e = one_chunk ? m3::launch_short_chunk((int)d->dstate, t, s)
+                                   : m3::launch_decode_tokens(io_bf16(d), (int)d->dstate, (int)d->headdim, t, s);
+    return e == hipSuccess ? M3_OK : M3_ERR_HIP;
   }
   m3::WalkArgs a{};
   a.x = x; a.B = B; a.C = C; a.dt = dt; a.A = A; a.lam = lam; a.theta = theta;

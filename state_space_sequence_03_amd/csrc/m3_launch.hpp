@@ -34,6 +34,10 @@ struct TokensArgs {
 };
 constexpr int TOKENS_MAX = 16;  // at most this many tokens (all staged in LDS)
 hipError_t launch_decode_tokens(int io_bf16, int N, int P, const TokensArgs& a, hipStream_t s);
+// The same short call as one chunk of the chunked form on bf16 MFMAs (bf16
+// io, P = 64, N in {64, 128}; at most TOKENS_MAX tokens).
+bool short_chunk_supported(int io_bf16, int N, int P, int R);
+hipError_t launch_short_chunk(int N, const TokensArgs& a, hipStream_t s);
 
 struct RopeArgs {
   const void *B, *C;

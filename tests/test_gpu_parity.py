@@ -155,6 +155,13 @@ TOKEN_CASES = [
     ("bf16", 1, 16, 3, 128, 32, 2, True, True),
     ("bf16", 2, 2, 2, 16, 64, 4, True, True),
     ("bf16", 1, 11, 2, 64, 128, 4, True, True),   # long-context head shape
+    # the one-chunk MFMA path (bf16, P = 64, N = 64 or 128): every rank, 1 to 16 tokens
+    ("bf16", 2, 1, 3, 64, 64, 1, True, True),
+    ("bf16", 1, 16, 2, 64, 64, 2, True, False),
+    ("bf16", 3, 5, 2, 64, 128, 2, False, True),
+    ("bf16", 1, 16, 1, 64, 128, 4, True, True),
+    ("bf16", 2, 13, 2, 64, 64, 4, False, False),
+    ("bf16", 1, 7, 2, 64, 128, 1, True, True),
 ]
 
 
@@ -193,6 +200,36 @@ def test_verify_step_in_place(ops):
         pb, px = d["B"][:, t].contiguous(), d["x"][:, t].contiguous()
     torch.cuda.synchronize()
     assert slice_err(host(st), host(state), (0, 1)) < 1e-5
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_verify_one_chunk_in_place(ops, N):
+    """k = 8 tokens on a decode state by the library's default short path (one
+    chunk on MFMAs), h_final aliasing h0: y against the oracle, the state
+    against the oracle and against 8 one-token steps (the chunked-vs-sequential
+    bound)."""
+    b, L, H, P, R = 4, 8, 8, 64, 4
+    inp = numpy_inputs(b, L, H, P, N, R, io="bf16", seed=22 + N, with_h0=True, with_prev=True)
+    d = to_dev(inp, "bf16")
+    say(f"verify one chunk in place N{N}")
+    state = d["h0"].clone()
+    y, hf = ops.chunked_fwd(d["x"], d["B"], d["C"], d["dt"], d["A"], d["lam"], d["theta"], h0=state,
+                            prev_B=d["prev_B"], prev_x=d["prev_x"], chunk=16, h_final=state)
+    torch.cuda.synchronize()
+    assert hf.data_ptr() == state.data_ptr()
+    yo, ho = oracle_fwd(inp)
+    ey, eh = slice_err(host(y), yo, (0, 2)), slice_err(host(state), ho, (0, 1))
+    say(f"   y err {ey:.3e} state err {eh:.3e}")
+    assert ey < TOL["bf16"] and eh < 1e-3
+    st = d["h0"].clone()
+    pb, px = d["prev_B"], d["prev_x"]
+    for t in range(L):
+        ops.decode_step(st, d["x"][:, t].contiguous(), d["B"][:, t].contiguous(), d["C"][:, t].contiguous(),
+                        d["dt"][:, t].contiguous(), d["A"][:, t].contiguous(), d["lam"][:, t].contiguous(),
+                        d["theta"][:, t].contiguous(), pb, px)
+        pb, px = d["B"][:, t].contiguous(), d["x"][:, t].contiguous()
+    torch.cuda.synchronize()
+    assert slice_err(host(st), host(state), (0, 1)) < 1e-3
 
 
 @pytest.mark.parametrize("io,N,P,R,Q", [("f32", 16, 32, 2, 32), ("bf16", 64, 64, 4, 64), ("bf16", 128, 64, 4, 64)])
