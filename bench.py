@@ -419,7 +419,7 @@ def bench_floor(torch, w, reps=10):
     lib = ctypes.CDLL(build.FLOOR_LIB)
     vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.m3f_stream.argtypes = [ci, vp, vp, vp, vp, i64, ci, vp]
-    lib.m3f_walk.argtypes = [vp] * 8 + [i64, i64, i64, ci, ci, ci, vp]
+    lib.m3f_walk.argtypes = [vp] * 8 + [i64, i64, i64, ci, ci, ci, ci, vp]
     lib.m3f_rmw.argtypes = [vp, i64, ci, vp]
     b, L, H, P, N, R = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.rank
     assert (P, N, R) == (64, 64, 4)
@@ -446,8 +446,8 @@ def bench_floor(torch, w, reps=10):
     out = {}
     for name, hpb, lds in (("walker_pattern_2_blocks_per_cu", 1, 80 * 1024), ("walker_pattern_2_heads_per_block", 2, 160 * 1024),
                            ("walker_pattern_8_blocks_per_cu", 1, 0)):
-        fn = lambda: lib.m3f_walk(ptr(x), ptr(Bt), ptr(Ct), ptr(th), ptr(dt), ptr(A), ptr(lam), ptr(y), b, L, H, 4, hpb,
-                                  lds, sp)
+        fn = lambda: lib.m3f_walk(ptr(x), ptr(Bt), ptr(Ct), ptr(th), ptr(dt), ptr(A), ptr(lam), ptr(y), b, L, H, 64, 4,
+                                  hpb, lds, sp)
         assert fn() == 0
         ms = t_ms(fn)
         out[name] = dict(ms=round(ms, 4), GBps=round(walk_bytes / (ms * 1e-3) / 1e9, 1))
@@ -456,8 +456,8 @@ def bench_floor(torch, w, reps=10):
     ws = dataclasses.replace(w, rank=1, name="siso_bf16")
     siso_bytes = b * L * H * prefill_bytes_per_token_head(ws)
     for name, hpb in (("siso_walker_pattern_2_blocks_per_cu", 1), ("siso_walker_pattern_2_heads_per_block", 2)):
-        fn = lambda: lib.m3f_walk(ptr(x), ptr(Bt), ptr(Ct), ptr(th), ptr(dt), ptr(A), ptr(lam), ptr(y), b, L, H, 1, hpb,
-                                  80 * 1024, sp)
+        fn = lambda: lib.m3f_walk(ptr(x), ptr(Bt), ptr(Ct), ptr(th), ptr(dt), ptr(A), ptr(lam), ptr(y), b, L, H, 64, 1,
+                                  hpb, 80 * 1024, sp)
         assert fn() == 0
         ms = t_ms(fn)
         out[name] = dict(ms=round(ms, 4), GBps=round(siso_bytes / (ms * 1e-3) / 1e9, 1))
@@ -468,6 +468,25 @@ def bench_floor(torch, w, reps=10):
             ms = t_ms(fn)
             out[f"{name}_{blocks}_blocks"] = dict(ms=round(ms, 4), GBps=round((nr + 1) * x.numel() / (ms * 1e-3) / 1e9, 1))
     del x, Bt, Ct, y, th, dt, A, lam
+    torch.cuda.empty_cache()
+    # the long-context walker's pattern (N = 128, R = 4, 16-token sub-chunks) on the long_mimo_bf16 bytes, as
+    # the library walks it: 512 walkers (32 heads x 16 segments of 4,096 tokens), here a batch of 16 sequences
+    # of 4,096 tokens (the same rows and strides within a segment)
+    from state_space_sequence_03_amd import inputs as inputs_mod
+    wl = inputs_mod.WORKLOADS["long_mimo_bf16"]
+    lb, lL, lH, lN = 16, wl.seqlen // 16, wl.nheads, wl.dstate
+    ntok = lb * lL * lH
+    lx, ly = (torch.zeros(ntok * R * P * 2, dtype=u8, device="cuda") for _ in range(2))
+    lB, lC = (torch.zeros(ntok * R * lN * 2, dtype=u8, device="cuda") for _ in range(2))
+    lth = torch.zeros(ntok * lN // 2 * 4, dtype=u8, device="cuda")
+    ldt, lA, llam = (torch.zeros(ntok * 4, dtype=u8, device="cuda") for _ in range(3))
+    fn = lambda: lib.m3f_walk(ptr(lx), ptr(lB), ptr(lC), ptr(lth), ptr(ldt), ptr(lA), ptr(llam), ptr(ly), lb, lL, lH,
+                              lN, 4, 1, 80 * 1024, sp)
+    assert fn() == 0
+    ms = t_ms(fn)
+    out["long_walker_pattern_2_blocks_per_cu"] = dict(
+        ms=round(ms, 4), GBps=round(ntok * prefill_bytes_per_token_head(wl) / (ms * 1e-3) / 1e9, 1))
+    del lx, ly, lB, lC, lth, ldt, lA, llam
     torch.cuda.empty_cache()
     for name, nbytes in (("rmw_268MB", 268435456), ("rmw_2GB", 2 << 30)):
         buf = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")

@@ -66,9 +66,10 @@ struct WalkPtrs {
 // HPB heads per block (adjacent), 256 threads per head; rank R = 4 (32-token
 // sub-chunks, one token per staging thread) or R = 1 (64-token sub-chunks,
 // two adjacent tokens per staging thread), as the walker for P = N = 64.
-template <int HPB, int R>
+template <int HPB, int R, int N = 64>
 __global__ __launch_bounds__(256 * HPB) void walk_kernel(WalkPtrs a) {
-  constexpr int N = 64, P = 64, K = N / 2, QS = R == 1 ? 64 : 32, CH = N / 8, NKS = N / 32, TPT = QS * CH / 256;
+  constexpr int P = 64, K = N / 2, QS = N == 128 ? 16 : (R == 1 ? 64 : 32), CH = N / 8, NKS = N / 32;
+  constexpr int TPT = QS * CH / 256, XIT = R * 8 / CH;  // x row pieces per thread: rank i / 8, column i % 8
   constexpr int V = QS * R, NCT = V / 16, NCW = NCT == 8 ? 2 : 1;
   constexpr int lgR = R == 4 ? 2 : 0;
   const int tid = threadIdx.x & 255, hsub = threadIdx.x >> 8;
@@ -84,7 +85,7 @@ __global__ __launch_bounds__(256 * HPB) void walk_kernel(WalkPtrs a) {
     ctl[0] = wave;
   }
   auto tok = [&](int64_t t) { return (b * a.L + t) * a.H + h; };
-  uint4 rB[TPT][R], rX[TPT][R], rC[NCW][NKS], rTh[TPT];
+  uint4 rB[TPT][R], rX[TPT][XIT], rC[NCW][NKS], rTh[TPT];
   float rd[TPT], ra[TPT], rl[TPT], rd1[TPT], rl1[TPT];
   auto load = [&](int64_t c0) {
 #pragma unroll
@@ -94,7 +95,10 @@ __global__ __launch_bounds__(256 * HPB) void walk_kernel(WalkPtrs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r) rB[u][r] = *(const uint4*)(a.B + (tt * R + r) * N * 2 + 16 * st_c);
 #pragma unroll
-      for (int k = 0; k < R; ++k) rX[u][k] = *(const uint4*)(a.x + (tt * R + k) * P * 2 + 16 * st_c);
+      for (int k = 0; k < XIT; ++k) {
+        const int i = st_c + CH * k;
+        rX[u][k] = *(const uint4*)(a.x + (tt * R + (i >> 3)) * P * 2 + 16 * (i & 7));
+      }
       rTh[u] = *(const uint4*)(a.theta + tt * K * 4 + 16 * st_c);
       rd[u] = *(const float*)(a.dt + tt * 4);
       ra[u] = *(const float*)(a.A + tt * 4);
@@ -119,14 +123,20 @@ __global__ __launch_bounds__(256 * HPB) void walk_kernel(WalkPtrs a) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) s = x4(x4(s, rB[u][r]), rX[u][r]);
+      for (int r = 0; r < R; ++r) s = x4(s, rB[u][r]);
+#pragma unroll
+      for (int k = 0; k < XIT; ++k) s = x4(s, rX[u][k]);
       s = x4(s, rTh[u]);
       s.x ^= __float_as_uint(rd[u]) ^ __float_as_uint(ra[u]) ^ __float_as_uint(rl[u]);
       s.y ^= __float_as_uint(rd1[u]) ^ __float_as_uint(rl1[u]);
     }
     uint4 yv[NCW];
 #pragma unroll
-    for (int ci = 0; ci < NCW; ++ci) yv[ci] = x4(x4(rC[ci][0], rC[ci][1]), s);
+    for (int ci = 0; ci < NCW; ++ci) {
+      yv[ci] = s;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) yv[ci] = x4(yv[ci], rC[ci][ks]);
+    }
     if (c0 + QS < a.L) load(c0 + QS);
 #pragma unroll
     for (int ci = 0; ci < NCW; ++ci) {
@@ -163,15 +173,17 @@ int m3f_stream(int nr, const void* a0, const void* a1, const void* a2, void* out
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-// The walker's access pattern over (batch, L, H) at P = N = 64 and rank R
-// (1 or 4), with L a multiple of the sub-chunk (64 tokens for R = 1, 32 for
-// R = 4) and H a multiple of heads_per_block (1 or 2);
+// The walker's access pattern over (batch, L, H) at P = 64, N = 64 with rank
+// R (1 or 4) or N = 128 with R = 4, with L a multiple of the sub-chunk (64
+// tokens for R = 1, 32 for N = 64 and R = 4, 16 for N = 128) and H a multiple
+// of heads_per_block (1 or 2; 1 at N = 128);
 // lds_bytes of dynamic LDS per block sets the number of resident blocks per
 // compute unit.
 int m3f_walk(const void* x, const void* B, const void* C, const void* theta, const void* dt, const void* A,
-             const void* lam, void* y, int64_t batch, int64_t L, int64_t H, int R, int heads_per_block,
+             const void* lam, void* y, int64_t batch, int64_t L, int64_t H, int N, int R, int heads_per_block,
              int lds_bytes, void* stream) {
-  if ((R != 1 && R != 4) || L % (R == 1 ? 64 : 32) != 0 || (heads_per_block != 1 && heads_per_block != 2) ||
+  if ((R != 1 && R != 4) || (N != 64 && N != 128) || (N == 128 && (R != 4 || heads_per_block != 1)) ||
+      L % (N == 128 ? 16 : (R == 1 ? 64 : 32)) != 0 || (heads_per_block != 1 && heads_per_block != 2) ||
       H % heads_per_block != 0)
     return 1;
   WalkPtrs a{(const unsigned char*)x, (const unsigned char*)B, (const unsigned char*)C, (const unsigned char*)theta,
@@ -179,7 +191,10 @@ int m3f_walk(const void* x, const void* B, const void* C, const void* theta, con
              batch, L, H};
   hipStream_t s = (hipStream_t)stream;
   const unsigned blocks = (unsigned)(batch * H / heads_per_block);
-  if (R == 1 && heads_per_block == 1) {
+  if (N == 128) {
+    hipFuncSetAttribute((const void*)walk_kernel<1, 4, 128>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    hipLaunchKernelGGL((walk_kernel<1, 4, 128>), dim3(blocks), dim3(256), lds_bytes, s, a);
+  } else if (R == 1 && heads_per_block == 1) {
     hipFuncSetAttribute((const void*)walk_kernel<1, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     hipLaunchKernelGGL((walk_kernel<1, 1>), dim3(blocks), dim3(256), lds_bytes, s, a);
   } else if (R == 1) {
