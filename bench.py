@@ -674,8 +674,9 @@ def main():
             "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": f"mimo_bf16 prefill: batch 8, L=4096, H=64, P=64, N=64, R=4, chunk 64 "
-                                   f"(walked as {walked_chunk(w)}-token chunks), bf16 io, fp32 state",
+            "config": {"workload": f"{w.name} prefill: batch {w.batch}, L={w.seqlen}, H={w.nheads}, P={w.headdim}, "
+                                   f"N={w.dstate}, R={w.rank}, chunk {w.chunk} (walked as {walked_chunk(w)}-token "
+                                   f"chunks), {w.io} io, fp32 state",
                        "global_batch": w.batch, "seq_len": w.seqlen,
                        "parallelism": "single GPU"}}
     if "prefill" in out:

@@ -110,8 +110,11 @@ bool subwalk_supported(int io_bf16, int N, int P, int Q, int R, int64_t H) {
   return false;
 }
 
-template <int N, int R>
-__global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
+// HPB heads per block: 1, or 2 adjacent (b,h) sequences walked in lockstep
+// by the two halves of a 512-thread block, each with its own LDS region (R =
+// 1: each token's 128-byte rows of the two heads are then read together)
+template <int N, int R, int HPB>
+__global__ __launch_bounds__(256 * HPB, 2 / HPB) void subchunk_walk_kernel(WalkArgs a) {
   typedef SW<N, R> Ly;
   constexpr int P = 64, K = Ly::K, QS = Ly::QS, V = Ly::V, NW = 4, CH = Ly::CH, TPT = Ly::TPT;
   constexpr int RC = TPT * R;               // (w B~)^T columns a staging thread writes: its tokens' ranks
@@ -127,7 +130,9 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   constexpr float LOG2E = 1.4426950408889634f;
   static_assert(XIT >= 1 && NCT >= 2, "shape");
 
-  __shared__ __align__(16) unsigned char smem[Ly::BYTES];
+  __shared__ __align__(16) unsigned char smem_all[HPB * Ly::BYTES];
+  const int half = HPB == 1 ? 0 : (int)(threadIdx.x >> 8);
+  unsigned char* smem = smem_all + half * Ly::BYTES;
   unsigned char* sB = smem + Ly::OFF_B;
   unsigned char* sX = smem + Ly::OFF_X;
   unsigned char* sWh = smem + Ly::OFF_WH;
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
   float* sTot = (float*)(smem + Ly::OFF_TOT);  // per wave: K angle totals, log-decay total
   float2* sTh = (float2*)(smem + Ly::OFF_TH);
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = (threadIdx.x >> 6) & 3;
   // lane coordinates; re-derived from an opaque copy of the thread id in every
   // sub-chunk so that the compiler recomputes the LDS addresses next to their
   // uses instead of hoisting dozens of them into registers for the whole walk
@@ -153,12 +158,13 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
     st_t = id / CH;         // staging: token slot (tokens TPT st_t ..), 16-byte column
     st_c = id % CH;
   };
-  coords(threadIdx.x);
+  coords(threadIdx.x & 255);
 
   const int64_t S = a.S;
   // block order: adjacent heads on one XCD (m3_order.hpp)
   int64_t seg, bh;
-  walker_of_block(blockIdx.x, gridDim.x, a.batch * a.H, S, bh, seg);
+  walker_of_block(blockIdx.x, gridDim.x, a.batch * a.H / HPB, S, bh, seg);
+  bh = bh * HPB + half;
   const int64_t blk = bh * S + seg;
   const int64_t b = bh / a.H, h = bh % a.H;
   const int64_t L = a.L, H = a.H;
@@ -734,9 +740,16 @@ __global__ __launch_bounds__(256, 2) void subchunk_walk_kernel(WalkArgs a) {
 
 template <int N, int R>
 static hipError_t sw_run(const WalkArgs& a, hipStream_t s) {
-  auto kern = subchunk_walk_kernel<N, R>;  // LDS is static (SW<N, R>::BYTES)
-  const int64_t blocks = a.batch * a.H * a.S;
-  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  // LDS is static (SW<N, R>::BYTES per head).  R = 1: two adjacent heads per
+  // block when B*H is even (the pair shares its segment bounds)
+  const int64_t BH = a.batch * a.H;
+  if constexpr (R == 1) {
+    if (BH % 2 == 0) {
+      hipLaunchKernelGGL((subchunk_walk_kernel<N, R, 2>), dim3((unsigned)(BH / 2 * a.S)), dim3(512), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((subchunk_walk_kernel<N, R, 1>), dim3((unsigned)(BH * a.S)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
