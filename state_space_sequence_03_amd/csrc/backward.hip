@@ -739,7 +739,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // runs down its columns with two transpose reads (ds_read_b64_tr_b16); B~,
   // C~ and H_in are also kept in fp32 for the element-wise adjoints.
   constexpr int LBV = V + 8, LBN = N + 8, LBP = P + 8;
-  constexpr int SMALL = QB * K * 8 + QB * 16 + QB * 16 + QB * QB * 4 + QB * K * 8 + TP * K * 4 + QB * 16 + TN * V * 8 + 4 + 512;
+  constexpr int SMALL = K * (QB + 1) * 8 + QB * 16 + QB * 16 + QB * QB * 4 + K * (QB + 1) * 8 + TP * K * 4 + QB * 16 + TN * V * 8 + 4 + 512;
   constexpr int TL_BYTES = 4 * (2 * V * LDN + N * LDP) + 2 * (2 * V * LBV + 2 * V * LBP + 4 * V * LBN + P * LBN) + SMALL;
   constexpr int F32_BYTES = 4 * (2 * V * LDN + 2 * N * LDP + 2 * V * LDP + 2 * V * LDV) + SMALL;
   // HG: the chunk's incoming state H_in is read from its checkpoint in
@@ -761,14 +761,18 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 tBl[TL ? V * LBN : 8];  // B~ - hi (lo part)
   __shared__ __attribute__((aligned(16))) u16 tCl[TL ? V * LBN : 8];  // C~ - hi (lo part)
   __shared__ __attribute__((aligned(16))) u16 tDZt[TL ? P * LBN : 8];  // dZ^T
-  __shared__ __attribute__((aligned(16))) float2 sCS[QB][K];
+  // per-(pair, token) arrays are stored pair-major with rows of QB + 1: the
+  // loops that scan over tokens put the QB tokens of a pair on adjacent
+  // lanes, which a token-major row of 32 or 64 words would put in one bank
+  constexpr int QT = QB + 1;
+  __shared__ float2 sCS[K][QT];
   __shared__ TokScal sT[QB];
   __shared__ float sLam[QB], sEL[QB], sQ[QB], sW[QB];
   // per-tile partial sums, each slot written by one lane and summed in a
   // fixed order by its reader (no atomics: the results do not depend on the
   // order in which waves arrive): the angle adjoint of H_out per column tile
   // and pair, and d e^{Lam}, d w per n-tile and virtual row
-  __shared__ float sDM[QB][QB], sDphi[QB][K], sDThP[TP][K], sTh[QB][K], sThP[4][QB];
+  __shared__ float sDM[QB][QB], sDphi[K][QT], sDThP[TP][K], sTh[K][QT], sThP[4][QB];
   __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDeP[TN][V], sDwP[TN][V], sRedW[NW];
   __shared__ double sRedD[NW];
 
@@ -876,7 +880,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
     for (int q = 0; q < THP; ++q) {
       const int e = tid + TH * q;
-      if (e < QB * K) sTh[e / K][e % K] = thv[q];
+      if (e < QB * K) sTh[e % K][e / K] = thv[q];
     }
     if (tid < QB) {
       sT[tid] = tsv.scal();
@@ -907,7 +911,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
     for (int e = tid; e < QB * K; e += TH) {  // QB K is a multiple of 64: whole waves
       const int t = e % QB, k = e / QB;
-      float ph = sT[t].d * sTh[t][k];
+      float ph = sT[t].d * sTh[k][t];
       {
         float u = row_up<1>(ph);
         if (t >= 1) ph += u;
@@ -925,7 +929,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       // bf16 io, the full-precision library routine for fp32 io
       if constexpr (sizeof(T) == 2) sincos_rev(ph, &sn, &cs);
       else sincosf(ph, &sn, &cs);
-      sCS[t][k] = make_float2(cs, sn);
+      sCS[k][t] = make_float2(cs, sn);
     }
     __syncthreads();
     const float lamQ = sLam[QB - 1], eQ = sEL[QB - 1];
@@ -943,7 +947,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
           io<T>::unpack(rc.r[q], fc);
 #pragma unroll
           for (int j = 0; j < VEC / 2; ++j) {
-            const float2 cs = sCS[t][n0 / 2 + j];
+            const float2 cs = sCS[n0 / 2 + j][t];
             const float b0 = cs.x * fb[2 * j] + cs.y * fb[2 * j + 1], b1 = cs.x * fb[2 * j + 1] - cs.y * fb[2 * j];
             const float c0 = cs.x * fc[2 * j] + cs.y * fc[2 * j + 1], c1 = cs.x * fc[2 * j + 1] - cs.y * fc[2 * j];
             sB[v * LDN + n0 + 2 * j] = b0;
@@ -996,7 +1000,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             const int n0 = tr * 16 + 4 * g + 2 * q, k = n0 / 2;
-            const float2 cs = sCS[QB - 1][k];
+            const float2 cs = sCS[k][QB - 1];
             const float g0 = Gb[j][2 * q], g1 = Gb[j][2 * q + 1];
             const float z0 = cs.x * g0 + cs.y * g1, z1 = cs.x * g1 - cs.y * g0;
             if constexpr (TL) {
@@ -1201,8 +1205,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
           // per pair (u, w) = features (n0 + 2q, n0 + 2q + 1): the angle
           // adjoint du w - dw u, and the un-rotated gradients
           // R(phi) (du, dw) = (c du - s dw, s du + c dw)
-          const float4 csq = *(const float4*)&sCS[t][k0];
-          const float cs[2][2] = {{csq.x, csq.y}, {csq.z, csq.w}};
+          const float2 cs0 = sCS[k0][t], cs1 = sCS[k0 + 1][t];
+          const float cs[2][2] = {{cs0.x, cs0.y}, {cs1.x, cs1.y}};
           float gB[4], gC[4], dph[2];
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
@@ -1223,8 +1227,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
           dph[0] = lane_sum<1, R>(dph[0]);
           dph[1] = lane_sum<1, R>(dph[1]);
           if (m16 % R == 0) {
-            sDphi[t][k0] = dph[0];
-            sDphi[t][k0 + 1] = dph[1];
+            sDphi[k0][t] = dph[0];
+            sDphi[k0 + 1][t] = dph[1];
           }
         }
       }
@@ -1276,7 +1280,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       float thd = 0.0f;
       for (int e = tid - 256; e < QB * K; e += TH - 256) {  // QB K is a multiple of 64: whole waves
         const int t = e % QB, k = e / QB;
-        float dom = sDphi[t][k];
+        float dom = sDphi[k][t];
         // suffix sum over the token's QB-lane group
         {
           float u = row_down<1>(dom);
@@ -1295,7 +1299,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         uint32_t ot = (uint32_t)t * Hu * K + k;
         fresh(ot);
         if (a0 + t < L) (a.dtheta + t0c * K)[ot] = sT[t].d * dom;
-        thd += sTh[t][k] * dom;
+        thd += sTh[k][t] * dom;
       }
       thd = lane_sum<QB, 64>(thd);
       if (lane < QB) sThP[wave - 4][lane] = thd;

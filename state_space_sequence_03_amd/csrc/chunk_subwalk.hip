@@ -43,6 +43,7 @@
 // Precision matches the other bf16 walkers: bf16 MFMA operands with fp32
 // accumulation; the chunk state uses w B~ split into bf16 hi + lo parts.
 #include "m3_common.hpp"
+#include "m3_lanes.hpp"
 #include "m3_launch.hpp"
 #include "m3_order.hpp"
 
@@ -282,13 +283,7 @@ __global__ __launch_bounds__(256 * HPB, 2 / HPB) void subchunk_walk_kernel(WalkA
       for (int u = 1; u < TPT; ++u) v[i] += e[u][i];
     }
 #pragma unroll
-    for (int o = CH; o < 64; o <<= 1) {
-#pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const float u = __shfl_up(v[i], o, 64);
-        if (lane >= o) v[i] += u;
-      }
-    }
+    for (int i = 0; i < 5; ++i) v[i] = slot_scan<CH>(v[i], lane);
     // inclusive values of each token of the slot: the slot's last token has v
     float w[5];
 #pragma unroll

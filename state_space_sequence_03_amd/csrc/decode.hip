@@ -15,6 +15,7 @@
 // the small inputs are staged; y = C^T h is reduced with wave shuffles, then
 // across the four waves in LDS.
 #include "m3_common.hpp"
+#include "m3_lanes.hpp"
 #include "m3_launch.hpp"
 
 namespace m3 {
@@ -121,9 +122,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float v = yp[r][j];
-#pragma unroll
-      for (int o = CG; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
-      yp[r][j] = v;
+      yp[r][j] = lane_sum<CG, 64>(v);
     }
   if (lane < CG) {
 #pragma unroll

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace m3 {
@@ -141,14 +142,21 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_b
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, on the VALU: row shifts
+// by 1, 2, 4, 8 inside each 16-lane row (lanes shifted in from outside the
+// row read 0), then the last lane of a row added to the rows after it (row
+// broadcasts 15 and 31, masked to the receiving rows).
 __device__ __forceinline__ float wave_incl_scan(float v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    float u = __shfl_up(v, o, 64);
-    if (l >= o) v += u;
-  }
+  auto shr = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                                                 0xf, 0xf, true));
+  };
+  v += shr(v, std::integral_constant<int, 0x111>{});  // row_shr:1
+  v += shr(v, std::integral_constant<int, 0x112>{});  // row_shr:2
+  v += shr(v, std::integral_constant<int, 0x114>{});  // row_shr:4
+  v += shr(v, std::integral_constant<int, 0x118>{});  // row_shr:8
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
   return v;
 }
 

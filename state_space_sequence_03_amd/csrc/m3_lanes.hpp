@@ -61,17 +61,39 @@ __device__ __forceinline__ float row_down(float v) { return dpp<0x100 + O>(v); }
 template <int O>
 __device__ __forceinline__ float row_up(float v) { return dpp<0x110 + O>(v); }    // row_shr:O
 
-// Inclusive prefix sum over the 64 lanes of a wave: row shifts inside each
-// 16-lane row, then the last lane of a row added to the rows after it (row
-// broadcasts 15 and 31, masked to the receiving rows).
-__device__ __forceinline__ float wave_scan_dpp(float v) {
-  v += row_up<1>(v);
-  v += row_up<2>(v);
-  v += row_up<4>(v);
-  v += row_up<8>(v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf, false));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xc, 0xf, false));
-  return v;
+// Inclusive scan over the 64 / C slots of C lanes (slot s = lanes C s ..
+// C s + C - 1; C = 8 or 16), for each lane position within a slot separately:
+// lane l receives v of lanes l, l - C, l - 2C, ... summed.  With C = 8 the
+// upper slot of each 16-lane row first adds the lower one (row shift by 8);
+// then each row adds the totals of the rows before it, which the row swaps
+// bring over: row r ^ 1's total (permlane16_swap) for the odd rows, the total
+// of rows 0 and 1 (permlane32_swap of the pair sums) for rows 2 and 3.  Both
+// copies going into a swap and its results pass through empty asm, as in
+// swap_sum16.
+template <int C>
+__device__ __forceinline__ float slot_scan(float v, int lane) {
+  static_assert(C == 8 || C == 16, "slots of 8 or 16 lanes");
+  float tot = v;
+  if constexpr (C == 8) {
+    v += row_up<8>(v);
+    const float rt = dpp<0x128>(v);  // row_ror:8: the lower slot reads the row total of its position
+    tot = (lane & 8) ? v : rt;
+  }
+  uint32_t a = __builtin_bit_cast(uint32_t, tot), b = a;
+  asm volatile("" : "+v"(b));
+  const auto s = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  uint32_t s0 = s[0], s1 = s[1];
+  asm volatile("" : "+v"(s0), "+v"(s1));
+  const float prev = __builtin_bit_cast(float, s0);                // odd rows: the total of row r - 1
+  uint32_t c = __builtin_bit_cast(uint32_t, prev + __builtin_bit_cast(float, s1)), d = c;  // rows (0, 1) or (2, 3)
+  asm volatile("" : "+v"(d));
+  const auto q = __builtin_amdgcn_permlane32_swap(c, d, false, false);
+  uint32_t q0 = q[0];
+  asm volatile("" : "+v"(q0));
+  const int row = lane >> 4;
+  float add = (row & 1) ? prev : 0.0f;
+  if (row >= 2) add += __builtin_bit_cast(float, q0);  // rows 2, 3: the total of rows 0 and 1
+  return v + add;
 }
 
 }  // namespace m3

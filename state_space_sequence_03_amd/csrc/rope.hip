@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
   __syncthreads();
   const float* offs = a.totals + ((b * a.H + h) * nchunks + c) * K;
   for (int k = wave; k < K; k += 4) {
-    const float v = wave_scan_dpp(om[lane][k]) + offs[k];
+    const float v = wave_incl_scan(om[lane][k]) + offs[k];
     float s, co;
     // bf16 io: the hardware sine/cosine (in revolutions; the reduction by the
     // nearest whole revolution is exact); fp32 io: the library routine
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(256) void rope_phi_kernel(RopeArgs a, int64_t nchun
   __syncthreads();
   const float* offs = a.totals + ((b * a.H + h) * nchunks + c) * K;
   for (int k = wave; k < K; k += 4) {
-    const float v = wave_scan_dpp(om[lane][k]) + offs[k];
+    const float v = wave_incl_scan(om[lane][k]) + offs[k];
     om[lane][k] = v;  // each wave reads and writes only its own pair's column
   }
   __syncthreads();
