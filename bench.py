@@ -566,11 +566,15 @@ def bench_decode_batches(ops, inputs, torch, batches=(256, 1024), steps=32):
 # Counter summaries under profiles/ (FETCH_SIZE and WRITE_SIZE per dispatch,
 # each scaled by what the same counter reads for a plain copy of known size),
 # valid while the kernel's sources hash to the value recorded in them.
+_CS = "state_space_sequence_03_amd/csrc/"
+WALKER_SOURCES = tuple(_CS + f for f in ("chunk_subwalk.hip", "m3_common.hpp", "m3_lanes.hpp", "m3_order.hpp"))
+# counter summary of the dominant kernel per workload, and the sources that kernel is built from
 TRAFFIC = {
-    "walker": ("profiles/subchunk_walk_kernel_64_4__mimo_bf16__hbm_traffic.md",
-               ("state_space_sequence_03_amd/csrc/chunk_subwalk.hip", "state_space_sequence_03_amd/csrc/m3_common.hpp")),
+    "mimo_bf16": ("profiles/subchunk_walk_kernel_64_4__mimo_bf16__hbm_traffic.md", WALKER_SOURCES),
+    "siso_bf16": ("profiles/subchunk_walk_kernel_64_1__siso_bf16__hbm_traffic.md", WALKER_SOURCES),
+    "long_mimo_bf16": ("profiles/subchunk_walk_kernel_128_4__long_mimo_bf16__hbm_traffic.md", WALKER_SOURCES),
     "decode": ("profiles/decode_step_kernel_64_64_4__decode_mimo_bf16__hbm_traffic.md",
-               ("state_space_sequence_03_amd/csrc/decode.hip", "state_space_sequence_03_amd/csrc/m3_common.hpp")),
+               tuple(_CS + f for f in ("decode.hip", "m3_common.hpp", "m3_lanes.hpp"))),
 }
 
 
@@ -582,11 +586,7 @@ def source_sha256(files):
     return h.hexdigest()
 
 
-def walker_source_sha256():
-    return source_sha256(TRAFFIC["walker"][1])
-
-
-def measured_traffic(which="walker"):
+def measured_traffic(which="mimo_bf16"):
     """HBM bytes per dispatch of a kernel from its committed counter summary,
     or None when the summary is missing or was taken on other sources."""
     summary, sources = TRAFFIC[which]
@@ -683,7 +683,7 @@ def main():
         pf = out["prefill"]
         line["value"] = round(pf["tokens_per_s"], 1)
         line["ms_per_step"] = round(pf["ms"], 4)
-        traffic = measured_traffic() if w.name == "mimo_bf16" else None
+        traffic = measured_traffic(w.name) if w.name in TRAFFIC else None
         line["roofline"] = {"bound": "hbm", "achieved": round(pf["gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(pf["gbps"] / HBM_PEAK_GBPS, 4),
                             "traffic": None if traffic is None else round(traffic),
@@ -750,8 +750,10 @@ def main():
     for name in ("siso_bf16", "long_mimo_bf16"):
         if name in out:
             o = out[name]
+            tr = measured_traffic(name)
             line[name] = {"tokens_per_s": round(o["tokens_per_s"], 1), "ms": round(o["ms"], 4),
-                          "achieved_GBps": round(o["gbps"], 1), "frac_hbm": round(o["gbps"] / HBM_PEAK_GBPS, 4)}
+                          "achieved_GBps": round(o["gbps"], 1), "frac_hbm": round(o["gbps"] / HBM_PEAK_GBPS, 4),
+                          "kernel": walker_kernel(W[name]), "traffic": None if tr is None else round(tr)}
     if "chunk16" in out:
         o = out["chunk16"]
         line["mimo_bf16_chunk16"] = {"workload": "mimo_bf16 prefill requested with chunk 16 (= N/R, the pages' "
