@@ -586,6 +586,36 @@ def source_sha256(files):
     return h.hexdigest()
 
 
+# SQ counter summary of the dominant prefill kernel per workload (SQ_INSTS_MFMA per dispatch)
+SQ_SUMMARY = {
+    "mimo_bf16": "profiles/subchunk_walk_kernel_64_4__mimo_bf16__sq_counters.md",
+    "siso_bf16": "profiles/subchunk_walk_kernel_64_1__siso_bf16__sq_counters.md",
+    "long_mimo_bf16": "profiles/subchunk_walk_kernel_128_4__long_mimo_bf16__sq_counters.md",
+}
+
+
+def summary_values(path, sources):
+    """The '- key: value' lines of a committed counter summary, or None when it
+    is missing or was taken on other sources."""
+    path = os.path.join(ROOT, path)
+    if not os.path.exists(path):
+        return None
+    vals = dict(re.findall(r"^- (\w+): ([0-9a-fA-F.e+-]+)\s*$", open(path).read(), re.M))
+    if vals.get("source_sha256") != source_sha256(sources):
+        return None
+    return vals
+
+
+def issued_mfma_flops(name):
+    """MFMA flops one dispatch of the workload's walker issues, from the
+    SQ_INSTS_MFMA counter of its committed summary (None if stale)."""
+    vals = summary_values(SQ_SUMMARY[name], WALKER_SOURCES) if name in SQ_SUMMARY else None
+    try:
+        return float(vals["mfma_insts_per_dispatch"]) * float(vals["flop_per_mfma"]) if vals else None
+    except (KeyError, ValueError):
+        return None
+
+
 def measured_traffic(which="mimo_bf16"):
     """HBM bytes per dispatch of a kernel from its committed counter summary,
     or None when the summary is missing or was taken on other sources."""
@@ -695,6 +725,10 @@ def main():
                         "tflops_dense_at_configured_chunk": round(pf["tflops_dense_cfg"], 1),
                         "frac_dense_at_configured_chunk": round(pf["tflops_dense_cfg"] / BF16_DENSE_TFLOPS, 4),
                         "frac_causal": round(pf["tflops_causal"] / BF16_DENSE_TFLOPS, 4), "peak_tflops": BF16_DENSE_TFLOPS}
+        fl = issued_mfma_flops(w.name)
+        if fl is not None:  # what the matrix cores executed: SQ_INSTS_MFMA of the committed profile, this run's time
+            line["mfma"]["tflops_issued_counters"] = round(fl / (pf["ms"] * 1e-3) / 1e12, 1)
+            line["mfma"]["frac_issued_counters"] = round(fl / (pf["ms"] * 1e-3) / 1e12 / BF16_DENSE_TFLOPS, 4)
     if "decode" in out:
         dc = out["decode"]
         line["decode"] = {"workload": "decode_mimo_bf16: batch 256, H=64, P=64, N=64, R=4, fp32 state, 1024 steps "
