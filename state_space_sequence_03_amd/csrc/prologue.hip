@@ -25,16 +25,20 @@
 //   * the N features of one (token, head, rank) vector lie in the lane and in
 //     lane l ^ 32 only: the sum of squares is the lane's own sum plus one row
 //     swap.
-// K advances 64 at a time through two LDS stages.  Operands come in through
-// buffer loads into two register sets, issued two stages ahead so that each
-// load has two stages of products to land.  With two waves per SIMD one
+// K advances 64 at a time through two LDS stages.  Operands go from global
+// memory straight into LDS (buffer_load ... lds: one wave instruction fills
+// 1 KB, lane l's 16 bytes at l * 16), one stage ahead: no staging registers
+// and no LDS write instructions (4.48 -> 4.24 ms against loads into
+// registers two stages ahead, then LDS writes).  With two waves per SIMD one
 // wave's operand reads and barrier waits overlap the other's products
 // (measured against one wave per SIMD with 128 x 128 per wave: 5.04 ->
 // 4.47 ms at the 1.5B shapes; a 128 x 256 tile with two blocks per CU, so
 // that one block's epilogue overlaps the other's products, took 5.19 ms:
 // the smaller tile's extra operand traffic and barriers cost more).
 // Tiles of 256 rows x 128 bytes are swizzled by 16-byte chunks so that the
-// 32 rows an operand read touches fall in distinct bank groups.
+// 32 rows an operand read touches fall in distinct bank groups; the loads
+// apply the swizzle on the global side (each lane fetches the chunk that
+// belongs at its LDS slot).
 //
 // Block order: workgroups go to the 8 XCDs in turn, so block ids are mapped
 // such that each XCD's 32 concurrent blocks cover a 4 x 8 rectangle of
@@ -55,7 +59,6 @@ constexpr int PT = 256;   // tokens per block
 constexpr int PK = 64;    // k per stage (128-byte rows)
 constexpr int TILE_BYTES = 256 * PK * 2;
 
-__device__ __forceinline__ int soff(int row, int chunk) { return row * 128 + ((chunk ^ fsw<8>(row)) << 4); }
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -94,27 +97,23 @@ __global__ __launch_bounds__(512) void bc_prologue_kernel(ProArgs a, int ntb, in
       __builtin_amdgcn_make_buffer_rsrc((void*)((const char*)a.u + m0 * rowb), 0, ntr * rowb, 0x00020000);
   // thread rows tid / 8 + 64 i (i < 4), 16-byte chunk tid % 8; rows 64 apart
   // share the swizzle, so they are 8192 bytes apart in LDS
-  const int lrow = tid >> 3, lch = tid & 7;
-  const int voff = lrow * rowb + lch * 16;
-  const int loff = soff(lrow, lch);
-  uint4 xw[4], xu[4], yw[4], yu[4];
+  // stage loads straight into LDS (buffer_load ... lds): instruction i of wave w
+  // fills rows 64 i + 8 w .. + 7 of a tile (1 KB, lane l -> 16 bytes at l * 16),
+  // so lane l loads the global chunk that the swizzle puts at its slot
+  const int wl = lane >> 3, wp = lane & 7;
+  const int wch = wp ^ wl ^ (wave & 1);                     // fsw<8>(row) ^ slot
+  const int dvoff = (8 * wave + wl) * rowb + wch * 16;
   const int nkb = (int)(a.D / PK), pad = nkb & 1, nst2 = nkb + pad;
-  auto load = [&](uint4* sw_, uint4* su_, int st) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto dma = [&](int buf, int st) {
     const int kb = st - pad;
     const bool out = kb < 0 || kb >= nkb;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int so = out ? 0x40000000 : i * 64 * rowb + kb * 128;
-      sw_[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsw, voff, so, 0));
-      su_[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsu, voff, so, 0));
-    }
-  };
-  auto stage = [&](const uint4* sw_, const uint4* su_, int st) {
-    char* bw = smem + st * 2 * TILE_BYTES + loff;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(uint4*)(bw + i * 8192) = sw_[i];
-      *(uint4*)(bw + TILE_BYTES + i * 8192) = su_[i];
+      char* dw = smem + buf * 2 * TILE_BYTES + (64 * i + 8 * wave) * 128;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsw, (lds_void*)dw, 16, dvoff, so, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsu, (lds_void*)(dw + TILE_BYTES), 16, dvoff, so, 0, 0);
     }
   };
 
@@ -127,7 +126,7 @@ __global__ __launch_bounds__(512) void bc_prologue_kernel(ProArgs a, int ntb, in
       for (int v = 0; v < 16; ++v) acc[ft][tt][v] = 0.0f;
 
   const int l32 = lane & 31, lh = lane >> 5;
-  auto compute = [&](int st, const uint4* wsrc, const uint4* usrc) {
+  auto compute = [&](int st) {
     int ll = l32, hh = lh;
     asm volatile("" : "+v"(ll), "+v"(hh));
     const int fsl = fsw<8>(ll);
@@ -144,7 +143,6 @@ __global__ __launch_bounds__(512) void bc_prologue_kernel(ProArgs a, int ntb, in
       for (int tt = 0; tt < 2; ++tt) fbv[bsel][tt] = as_bf16x8(*(const uint4*)(pb + tt * 4096));
     };
     rd(0, 0);
-    stage(wsrc, usrc, st ^ 1);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s < 3) rd(s + 1, (s + 1) & 1);
@@ -153,29 +151,26 @@ __global__ __launch_bounds__(512) void bc_prologue_kernel(ProArgs a, int ntb, in
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) acc[ft][tt] = mfma32(fa[s & 1][ft], fbv[s & 1][tt], acc[ft][tt]);
     }
-    // the first step's 6 operand reads, then one product, one read of a later
-    // step and (for the first 8) one LDS write of the other buffer in turn,
-    // then the last step's products
     __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
     for (int i = 0; i < 24; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < 18) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      if (i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
-  load(xw, xu, 0);
-  load(yw, yu, 1);
-  stage(xw, xu, 0);
+  dma(0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
   for (int kk = 0; kk < nst2; kk += 2) {
-    load(xw, xu, kk + 2);
-    compute(0, yw, yu);
+    dma(1, kk + 1);
+    compute(0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    load(yw, yu, kk + 3);
-    compute(1, xw, xu);
+    dma(0, kk + 2);
+    compute(1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
   }
 
