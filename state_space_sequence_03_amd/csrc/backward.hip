@@ -161,6 +161,23 @@ __device__ __forceinline__ void mmv(FA fa, FB fb, f32x4* acc, int wave, int m16,
   constexpr int NT = TM * TNC, TPW = (NT + NW - 1) / NW;
   static_assert(KD % 16 == 0, "k in steps of 16");
   constexpr int K32 = KD / 32 * 32;
+  if constexpr (NT % NW == 0 && K32 > 0) {
+    // every operand of the product first, then the products: the LDS reads
+    // are in flight together instead of one MFMA waiting on each pair
+    bf16x8 oa[K32 / 32][TPW], ob[K32 / 32][TPW];
+#pragma unroll
+    for (int k0 = 0; k0 < K32; k0 += 32)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const int ti = wave + NW * j, tr = ti / TNC, tc = ti % TNC, kk = k0 + 8 * g;
+        oa[k0 / 32][j] = fa(tr * 16 + m16, kk, IC<8>{});
+        ob[k0 / 32][j] = fb(tc * 16 + m16, kk, IC<8>{});
+      }
+#pragma unroll
+    for (int k0 = 0; k0 < K32; k0 += 32)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) acc[j] = mfma_bf16(oa[k0 / 32][j], ob[k0 / 32][j], acc[j]);
+  } else {
 #pragma unroll
   for (int k0 = 0; k0 < K32; k0 += 32) {
 #pragma unroll
@@ -171,6 +188,7 @@ __device__ __forceinline__ void mmv(FA fa, FB fb, f32x4* acc, int wave, int m16,
         acc[j] = mfma_bf16(fa(tr * 16 + m16, kk, IC<8>{}), fb(tc * 16 + m16, kk, IC<8>{}), acc[j]);
       }
     }
+  }
   }
   if constexpr (KD % 32 == 16) {
 #pragma unroll
@@ -201,6 +219,22 @@ __device__ __forceinline__ float ld_io(const void* p, int64_t i) {
 // 32-bit offset) instead of hoisting a 64-bit per-thread address out of the
 // chunk loop, where it would occupy (or spill) vector register pairs.
 __device__ __forceinline__ void fresh(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
+// Four consecutive gradient elements through a buffer resource whose byte
+// count ends at the chunk's last token inside the sequence: the hardware drops
+// the rows of tokens past L, so the store needs no branch (a branch splits
+// the products phase into blocks the scheduler cannot interleave across).
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ void store4_rs(__amdgpu_buffer_rsrc_t r, uint32_t i, const float* f) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x2_t v = {pack_bf2(f[0], f[1]), pack_bf2(f[2], f[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)(i * 2), 0, 0);
+  } else {
+    const u32x4 v = {__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)(i * 4), 0, 0);
+  }
+}
 
 // Raw rows of a chunk held in registers: item e of a thread covers row
 // v = e / (W / VEC) (token v / R, rank v % R) and the VEC elements from
@@ -870,6 +904,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     void* const odx = (char*)a.dx + t0c * (R * P * io<T>::BYTES);
     void* const odB = (char*)a.dB + t0c * (R * N * io<T>::BYTES);
     void* const odC = (char*)a.dC + t0c * (R * N * io<T>::BYTES);
+    const int nvt = (int)(L - a0 < QB ? L - a0 : QB);  // tokens of the chunk inside the sequence
+    const __amdgpu_buffer_rsrc_t rdx = __builtin_amdgcn_make_buffer_rsrc(odx, 0, nvt * (int)Hu * (R * P * io<T>::BYTES), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdB = __builtin_amdgcn_make_buffer_rsrc(odB, 0, nvt * (int)Hu * (R * N * io<T>::BYTES), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rdC = __builtin_amdgcn_make_buffer_rsrc(odC, 0, nvt * (int)Hu * (R * N * io<T>::BYTES), 0x00020000);
     // H_in (n, p) of this chunk: the LDS copy, or its checkpoint (HG)
     const float* const hg = ck + c * (N * P);
     auto hin = [&](int n, int p) -> float {
@@ -1150,7 +1188,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
           uint32_t off = (uint32_t)t * Hu * (R * P) + (uint32_t)((v % R) * P + p0);
           fresh(off);
           const float f[4] = {xacc[j][0], xacc[j][1], xacc[j][2], xacc[j][3]};
-          if (a0 + t < L) io<T>::store4(odx, off, f);
+          store4_rs<T>(rdx, off, f);
         }
       }
     }
@@ -1217,11 +1255,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             gC[u] = cs[q][0] * dCt[u] - cs[q][1] * dCt[w];
             gC[w] = cs[q][1] * dCt[u] + cs[q][0] * dCt[w];
           }
-          if (a0 + t < L) {
+          {
             uint32_t off = (uint32_t)t * Hu * (R * N) + (uint32_t)((v % R) * N + n0);
             fresh(off);
-            io<T>::store4(odB, off, gB);
-            io<T>::store4(odC, off, gC);
+            store4_rs<T>(rdB, off, gB);
+            store4_rs<T>(rdC, off, gC);
           }
           // the token's angle adjoint sums its R ranks (R adjacent lanes)
           dph[0] = lane_sum<1, R>(dph[0]);
