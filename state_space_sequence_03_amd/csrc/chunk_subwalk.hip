@@ -15,16 +15,19 @@
 // gfx950 data flow:
 //  * 256 threads and under 80 KB of LDS per block, so two blocks (two (b,h)
 //    sequences or segments) share a compute unit and one block's staging and
-//    loads overlap the other block's matrix work.
+//    loads overlap the other block's matrix work.  For R = 1 with an even
+//    number of (b,h), one 512-thread block walks two adjacent heads instead
+//    (each half with its own LDS region): each token's rows of the two heads
+//    are then read together, 256 bytes instead of 128.
 //  * Coalesced loads.  Staging thread (t, c) owns token t of the sub-chunk (for
 //    R = 1: the adjacent tokens 2t, 2t + 1) and the 16-byte column c of each
 //    rank row of B (and of x, and of theta's row), so a wave instruction reads
-//    whole rows.  Each wave keeps the C rows
-//    of its own output tiles in the MFMA operand layout (16 bytes per lane).
-//  * Cumulative log-decay and angles: wave scans over the tokens a wave holds,
-//    plus an exchange of wave totals through LDS.  The wave scans of the next
-//    sub-chunk run at the end of the current one, so the exchange shares the
-//    sub-chunk's first barrier.
+//    whole rows.  Each wave keeps the C rows of its own output tiles in the
+//    MFMA operand layout (16 bytes per lane).
+//  * Cumulative log-decay and angles: wave scans over the tokens a wave holds
+//    (slot_scan: DPP and row swaps, no LDS permutes), plus an exchange of wave
+//    totals through LDS.  The wave scans of the next sub-chunk run at the end
+//    of the current one, so the exchange shares the sub-chunk's first barrier.
 //  * sin/cos are computed once per (token, pair) by the staging thread, which
 //    rotates all R ranks of B with them and stores them as a bf16 table for
 //    the rotation of C: two bf16 dot products per pair (fp32 sums), the result

@@ -281,14 +281,32 @@ __global__ __launch_bounds__(512) void bc_prologue_kernel(ProArgs a, int ntb, in
 
 
 
+// Blocks of one launch: a dispatch holds fewer than 2^32 work-items.
+constexpr int64_t kMaxPrologueBlocks = ((int64_t(1) << 32) - 1) / 512;
+
 template <int N>
 static hipError_t prologue_run(const ProArgs& a, hipStream_t s) {
-  const int ntb = (int)((a.M + PT - 1) / PT);
+  // Token rows go in slices of whole 16 x 16 tile groups, one launch each, so
+  // that every call the ABI accepts stays within the dispatch limit.
   const int nfb = (int)((2 * (int64_t)a.H * a.R * N + PF - 1) / PF);
-  const int nst = (ntb + 15) / 16, nsf = (nfb + 15) / 16;
-  const int64_t blocks = (int64_t)nst * nsf * 256;
-  hipLaunchKernelGGL((bc_prologue_kernel<N>), dim3((unsigned)blocks), dim3(512), 0, s, a, ntb, nfb, nsf);
-  return hipGetLastError();
+  const int nsf = (nfb + 15) / 16;
+  const int64_t groups = kMaxPrologueBlocks / ((int64_t)nsf * 256);
+  if (groups < 1) return hipErrorInvalidValue;  // the ABI rejects such feature counts first
+  const int64_t rows = groups * 16 * PT;
+  for (int64_t m0 = 0; m0 < a.M; m0 += rows) {
+    ProArgs b = a;
+    b.M = a.M - m0 < rows ? a.M - m0 : rows;
+    b.u = (const char*)a.u + m0 * a.D * 2;
+    b.phi = a.phi + m0 * (int64_t)a.H * (N / 2);
+    b.B_rot = (char*)a.B_rot + m0 * (int64_t)a.H * a.R * N * 2;
+    b.C_rot = (char*)a.C_rot + m0 * (int64_t)a.H * a.R * N * 2;
+    const int ntb = (int)((b.M + PT - 1) / PT);
+    const int64_t blocks = (int64_t)((ntb + 15) / 16) * nsf * 256;
+    hipLaunchKernelGGL((bc_prologue_kernel<N>), dim3((unsigned)blocks), dim3(512), 0, s, b, ntb, nfb, nsf);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_bc_prologue(int N, const ProArgs& a, hipStream_t s) {
