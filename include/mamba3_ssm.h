@@ -66,7 +66,12 @@
  * walks each chunk as 2, 4 or 8 shorter pieces: the chunked form is exact for
  * any split (linkstar.cloud/article/869, "第一刀"), so only the rounding order
  * changes.  batch, seqlen and nheads may be 0 (empty input: nothing is read;
- * h_final receives h0, or zeros).
+ * h_final receives h0, or zeros).  Size limits (M3_ERR_UNSUPPORTED beyond
+ * them): batch and nheads at most 65535 each; the chunked forward and the
+ * backward run one block of up to 512 threads per (b, h, segment) and the
+ * decode step one of 256 threads per (b, h), and a launch holds fewer than
+ * 2^32 threads, so batch * nheads * segments is at most 8,388,607 (16,777,215
+ * for decode_step); split larger batches over several calls.
  */
 #ifndef MAMBA3_SSM_H
 #define MAMBA3_SSM_H

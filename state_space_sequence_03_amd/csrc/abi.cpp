@@ -53,6 +53,9 @@ m3_status check_dims(const m3_dims* d, bool need_chunk, bool need_p) {
 
 int io_bf16(const m3_dims* d) { return d->io_dtype == M3_BF16 ? 1 : 0; }
 
+// A launch holds fewer than 2^32 threads: `blocks` blocks of `threads` each.
+static bool launch_fits(int64_t blocks, int threads) { return blocks <= ((int64_t(1) << 32) - 1) / threads; }
+
 // Number of sequence segments walked in parallel per (b,h) and their length
 // (whole chunks).  Requested through the low 16 bits of flags, else chosen so
 // that at least ~512 walkers exist when B*H is small (bf16 io only; each
@@ -203,6 +206,7 @@ m3_status mamba3_ssm_chunked_fwd(const m3_dims* dq, const void* x, const void* B
   if (d->chunk <= 0) return M3_ERR_UNSUPPORTED;
   const SegPlan sp = seg_plan(d);
   if (sp.S > 1 && (d->io_dtype != M3_BF16 || d->batch * d->nheads > 65535)) return M3_ERR_UNSUPPORTED;
+  if (!launch_fits(d->batch * d->nheads * sp.S, 512)) return M3_ERR_UNSUPPORTED;  // one block per (b, h, segment)
   const bool empty = d->batch == 0 || d->nheads == 0;
   const bool has_tokens = !empty && d->seqlen > 0;
   if ((prev_B == nullptr) != (prev_x == nullptr)) return M3_ERR_NULL;
@@ -282,6 +286,13 @@ m3_status mamba3_ssm_chunked_bwd(const m3_dims* d, const void* x, const void* B,
   if ((d->flags & ~0xffff) != 0) return M3_ERR_UNSUPPORTED;
   if (!m3::bwd_supported((int)d->dstate, (int)d->headdim, (int)d->rank)) return M3_ERR_UNSUPPORTED;
   if (d->nheads > 65536) return M3_ERR_UNSUPPORTED;  // 32-bit offsets inside a chunk
+  {
+    // one block per (b, h, segment); the segment scans run one thread per
+    // (b, h, pair, column)
+    const BwdSegPlan sp0 = bwd_seg_plan(d);
+    if (!launch_fits(d->batch * d->nheads * sp0.S, 512)) return M3_ERR_UNSUPPORTED;
+    if (sp0.S > 1 && !launch_fits(d->batch * d->nheads * (d->dstate / 2) * d->headdim, 1)) return M3_ERR_UNSUPPORTED;
+  }
   const bool empty = d->batch == 0 || d->nheads == 0;
   const bool has_tokens = !empty && d->seqlen > 0;
   if ((prev_B == nullptr) != (prev_x == nullptr) || (dprev_B == nullptr) != (dprev_x == nullptr)) return M3_ERR_NULL;
@@ -339,6 +350,7 @@ m3_status mamba3_ssm_decode_step(const m3_dims* d, float* state, const void* x, 
   m3_status st = check_dims(d, false, true);
   if (st != M3_OK) return st;
   if (d->flags != 0) return M3_ERR_UNSUPPORTED;
+  if (!launch_fits(d->batch * d->nheads, 256)) return M3_ERR_UNSUPPORTED;  // one block per (b, h)
   const bool empty = d->batch == 0 || d->nheads == 0;
   if ((prev_B == nullptr) != (prev_x == nullptr)) return M3_ERR_NULL;
   if (!empty && (!state || !x || !B || !C || !dt || !A || !lam || !theta || !y)) return M3_ERR_NULL;

@@ -292,3 +292,21 @@ def test_whole_supported_set_is_accepted(L):
             ws = L.chunked_fwd_workspace_size(d1)
             assert ws >= 0 and (ws > 0) == (io == 1 and seqlen == 65536), (io, N, P, R, Q, ws)
             assert L.chunked_bwd_workspace_size(d1) > 0
+
+
+def test_launch_size_limits(L):
+    # one block per (b, h, segment): a launch holds fewer than 2^32 threads, so
+    # B*H*S is at most 2^23 - 1 for the forward and the backward (blocks of up
+    # to 512 threads) and 2^24 - 1 for the decode step (256 threads); checked
+    # before any pointer, so nothing is launched
+    over = dict(x=None, y=None)
+    assert call_fwd(L, dims(L, batch=65535, nheads=129, seqlen=16), **over) == L.M3_ERR_UNSUPPORTED  # 8.45M > 2^23 - 1
+    assert call_fwd(L, dims(L, batch=65535, nheads=128, seqlen=16), **over) == L.M3_ERR_NULL         # 8,388,480: fits
+    big_bwd = dims(L, batch=65535, nheads=129, seqlen=16)
+    assert call_bwd(L, big_bwd, dx=None) == L.M3_ERR_UNSUPPORTED
+    assert call_bwd(L, dims(L, batch=65535, nheads=128, seqlen=16), dx=None, ws=None, ws_bytes=0) != L.M3_ERR_UNSUPPORTED
+    # forced segments multiply the blocks: 2^20 (b, h) pairs x 16 segments
+    seg_bwd = dims(L, batch=1024, nheads=1024, seqlen=16 * 64, flags=16)
+    assert call_bwd(L, seg_bwd, dx=None) == L.M3_ERR_UNSUPPORTED
+    assert call_decode(L, dims(L, batch=65535, nheads=257), state=None) == L.M3_ERR_UNSUPPORTED      # 16.8M > 2^24 - 1
+    assert call_decode(L, dims(L, batch=65535, nheads=256), state=None) == L.M3_ERR_NULL              # 16,776,960: fits
