@@ -242,14 +242,15 @@ hipError_t launch_rope(int io_bf16, int N, const RopeArgs& a, hipStream_t s) {
   return io_bf16 ? rope_dispatch<bf16_t>(N, a, s) : rope_dispatch<float>(N, a, s);
 }
 
+// grid-stride, so that any n fits one launch of at most 65536 blocks
 __global__ void copy_f32_kernel(float* dst, const float* src, int64_t n) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = src ? src[i] : 0.0f;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += step) dst[i] = src ? src[i] : 0.0f;
 }
 
 hipError_t launch_copy_f32(float* dst, const float* src, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const int64_t blocks = (n + 255) / 256;
+  const int64_t blocks = (n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536;
   hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, dst, src, n);
   return hipGetLastError();
 }
