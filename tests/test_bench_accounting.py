@@ -66,3 +66,33 @@ def test_prologue_flops():
     M = PROLOGUE["batch"] * PROLOGUE["seqlen"]
     F = 2 * PROLOGUE["nheads"] * PROLOGUE["rank"] * PROLOGUE["dstate"]
     assert 2 * M * F * PROLOGUE["d_model"] == 4_398_046_511_104
+
+
+@pytest.mark.parametrize("name", sorted(bench.TRAFFIC))
+def test_counter_summary_traffic_is_near_algorithmic(name):
+    """Each committed HBM-traffic summary parses, and while it was taken on the
+    current sources (its recorded hash) the calibrated counter bytes lie within
+    a few percent above the algorithmic bytes: no wasted re-reads."""
+    t = bench.measured_traffic(name)
+    if t is None:
+        pytest.skip(f"{bench.TRAFFIC[name][0]} was taken on other sources; take the counters again")
+    if name == "decode":
+        algo = bench.decode_bytes_per_step(WORKLOADS["decode_mimo_bf16"])
+    else:
+        w = WORKLOADS[name]
+        algo = w.batch * w.seqlen * w.nheads * bench.prefill_bytes_per_token_head(w)
+    assert 1.0 <= t / algo <= 1.06, (name, t / algo)
+
+
+@pytest.mark.parametrize("name", sorted(bench.SQ_SUMMARY))
+def test_counter_summary_mfma_count(name):
+    """The walkers' SQ_INSTS_MFMA x 16,384 flop lies between the causal and the
+    dense flop count of the walked chunk (tiles above the causal diagonal are
+    skipped, the state's hi + lo products are counted twice)."""
+    fl = bench.issued_mfma_flops(name)
+    if fl is None:
+        pytest.skip(f"{bench.SQ_SUMMARY[name]} was taken on other sources; take the counters again")
+    w = WORKLOADS[name]
+    th = w.batch * w.seqlen * w.nheads
+    assert th * bench.prefill_flops_per_token_head(w, causal=True) <= fl
+    assert fl <= 1.5 * th * bench.prefill_flops_per_token_head(w, causal=False)
