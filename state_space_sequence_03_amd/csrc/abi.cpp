@@ -449,15 +449,15 @@ m3_status mamba3_bc_prologue(const m3_dims* d, int64_t d_model, const void* u, c
   r.dt = dt; r.theta = theta; r.angle0 = angle0; r.angle_final = angle_final;
   r.batch = d->batch; r.L = d->seqlen; r.H = d->nheads; r.R = (int)d->rank;
   const ProWs w = pro_ws(d);
-  float* phi = nullptr;
+  uint32_t* cs = nullptr;
   if (has_tokens) {
     r.totals = (float*)((char*)workspace + w.totals);
-    phi = (float*)((char*)workspace + w.phi);
+    cs = (uint32_t*)((char*)workspace + w.phi);
   }
-  hipError_t e = m3::launch_rope_phi(N, r, phi, s);
+  hipError_t e = m3::launch_rope_phi(N, r, cs, s);
   if (e != hipSuccess || !has_tokens) return e == hipSuccess ? M3_OK : M3_ERR_HIP;
   m3::ProArgs a{};
-  a.u = u; a.W = W; a.gain = gain; a.bias = bias; a.phi = phi; a.B_rot = B_rot; a.C_rot = C_rot; a.eps = eps;
+  a.u = u; a.W = W; a.gain = gain; a.bias = bias; a.cs = cs; a.B_rot = B_rot; a.C_rot = C_rot; a.eps = eps;
   a.M = d->batch * d->seqlen; a.D = d_model; a.H = (int)d->nheads; a.R = (int)d->rank;
   e = m3::launch_bc_prologue(N, a, s);
   return e == hipSuccess ? M3_OK : M3_ERR_HIP;

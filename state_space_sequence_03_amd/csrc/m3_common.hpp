@@ -18,6 +18,7 @@ struct bf16_t {  // storage tag for bf16 io
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // fp32 -> bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32 on gfx950);
 // lo goes to bits 0..15.

@@ -51,9 +51,10 @@ struct RopeArgs {
 constexpr int ROPE_CHUNK = 64;
 hipError_t launch_rope(int io_bf16, int N, const RopeArgs& a, hipStream_t s);
 
-// The angles of rope_bc alone, written to phi (B, L, H, N/2) fp32; uses
-// a.totals as its workspace and writes a.angle_final when set.
-hipError_t launch_rope_phi(int N, const RopeArgs& a, float* phi, hipStream_t s);
+// The angles of rope_bc alone, as (cos, sin) pairs rounded to fp16 (one
+// 32-bit word per (token, head, pair): cs (B, L, H, N/2)); uses a.totals as
+// its workspace and writes a.angle_final when set.
+hipError_t launch_rope_phi(int N, const RopeArgs& a, uint32_t* cs, hipStream_t s);
 
 // The B/C prologue: projection, RMS normalisation, bias and rotation.
 struct ProArgs {
@@ -61,7 +62,7 @@ struct ProArgs {
   const void* W;       // (2*H*R*N, D) bf16: rows of W_B, then of W_C
   const float* gain;   // nullable (2*H*R*N), 16-byte aligned
   const float* bias;   // nullable (2*H*R*N), 16-byte aligned
-  const float* phi;    // (M, H, N/2) angles from launch_rope_phi
+  const uint32_t* cs;  // (M, H, N/2) fp16 (cos, sin) of the angles, from launch_rope_phi
   void *B_rot, *C_rot; // (M, H, R, N) bf16
   float eps;
   int64_t M, D;        // D a multiple of 64, at most 2^20

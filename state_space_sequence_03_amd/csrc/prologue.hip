@@ -12,8 +12,9 @@
 //                                   notes that it can be fused with the
 //                                   projection)
 // so that B and C are written once, already normalised and rotated, and never
-// read back.  The angles phi_t come from a small pre-pass over dt and theta
-// (rope.hip).
+// read back.  A small pre-pass over dt and theta (rope.hip) writes cos and
+// sin of the angles phi_t once per (token, head, pair), as fp16 pairs, which
+// every rank of B and C then uses.
 //
 // The product is computed transposed, D^T = W u^T, on bf16 32x32x16 MFMAs
 // with fp32 accumulation: a block owns 256 features x 256 tokens, its eight
@@ -199,21 +200,21 @@ __global__ __launch_bounds__(512) void bc_prologue_kernel(ProArgs a, int ntb, in
   const int jl = lane >> 4, gl = lane & 15;
   const bool fvalid = (int64_t)fw0 + 8 * gl < F;
   const int64_t colg = fvalid ? col(gl) : 0;
-  float4 phr[2][8];
+  uint4 phr[2][8];
 #pragma unroll
   for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t m = m0 + wt * 64 + hf * 32 + 4 * i + jl;
       const int64_t mc = m < a.M ? m : a.M - 1;
-      const float4 v = *(const float4*)(a.phi + mc * (int64_t)a.H * K2 + colg);
-      phr[hf][i] = fvalid && m < a.M ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+      const uint4 v = *(const uint4*)(a.cs + mc * (int64_t)a.H * K2 + colg);
+      phr[hf][i] = fvalid && m < a.M ? v : make_uint4(0u, 0u, 0u, 0u);
     }
   auto write_phi = [&](int hf) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int jj = 4 * i + jl;
-      *(float4*)(phs + jj * 256 + ((gl ^ (jj & 15)) << 4)) = phr[hf][i];
+      *(uint4*)(phs + jj * 256 + ((gl ^ (jj & 15)) << 4)) = phr[hf][i];
     }
   };
   auto compute_half = [&](int tt) {
@@ -238,15 +239,15 @@ __global__ __launch_bounds__(512) void bc_prologue_kernel(ProArgs a, int ntb, in
         const int c = ft * 4 + q;
         const int fo = wf * 128 + 8 * c + 4 * lh;  // the lane's 4 features in the tile
         const float4 gv = *(const float4*)(gsh + fo), bv = *(const float4*)(gsh + 256 + fo);
-        const float2 ph = *(const float2*)(phs + jr * 256 + ((c ^ (jr & 15)) << 4) + lh * 8);
+        // fp16 (cos, sin) of pairs 2(c*2 + lh) and + 1
+        const uint2 pc = *(const uint2*)(phs + jr * 256 + ((c ^ (jr & 15)) << 4) + lh * 8);
         const float iv = inv[(ft * 32 + 8 * q) / N];
         const float x0 = acc[ft][tt][4 * q + 0] * iv * gv.x + bv.x;
         const float x1 = acc[ft][tt][4 * q + 1] * iv * gv.y + bv.y;
         const float x2 = acc[ft][tt][4 * q + 2] * iv * gv.z + bv.z;
         const float x3 = acc[ft][tt][4 * q + 3] * iv * gv.w + bv.w;
-        float s0, c0, s1, c1;
-        sincos_rev(ph.x, &s0, &c0);
-        sincos_rev(ph.y, &s1, &c1);
+        const f16x2 h0 = __builtin_bit_cast(f16x2, pc.x), h1 = __builtin_bit_cast(f16x2, pc.y);
+        const float c0 = (float)h0[0], s0 = (float)h0[1], c1 = (float)h1[0], s1 = (float)h1[1];
         uint2 o;
         o.x = pack_bf2(c0 * x0 + s0 * x1, c0 * x1 - s0 * x0);
         o.y = pack_bf2(c1 * x2 + s1 * x3, c1 * x3 - s1 * x2);
@@ -297,7 +298,7 @@ static hipError_t prologue_run(const ProArgs& a, hipStream_t s) {
     ProArgs b = a;
     b.M = a.M - m0 < rows ? a.M - m0 : rows;
     b.u = (const char*)a.u + m0 * a.D * 2;
-    b.phi = a.phi + m0 * (int64_t)a.H * (N / 2);
+    b.cs = a.cs + m0 * (int64_t)a.H * (N / 2);
     b.B_rot = (char*)a.B_rot + m0 * (int64_t)a.H * a.R * N * 2;
     b.C_rot = (char*)a.C_rot + m0 * (int64_t)a.H * a.R * N * 2;
     const int ntb = (int)((b.M + PT - 1) / PT);

@@ -158,7 +158,7 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
 // Per chunk as in launch 3: the chunk-local wave scan plus the chunk's offset,
 // then the chunk's angles written token by token.
 template <int N>
-__global__ __launch_bounds__(256) void rope_phi_kernel(RopeArgs a, int64_t nchunks, float* phi) {
+__global__ __launch_bounds__(256) void rope_phi_kernel(RopeArgs a, int64_t nchunks, uint32_t* cs) {
   constexpr int K = N / 2;
   const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -181,33 +181,39 @@ __global__ __launch_bounds__(256) void rope_phi_kernel(RopeArgs a, int64_t nchun
     om[lane][k] = v;  // each wave reads and writes only its own pair's column
   }
   __syncthreads();
+  // (cos, sin) of the angle, each rounded to fp16 (absolute error <= 2^-12,
+  // below the bf16 rounding of the rotated outputs): the consumer rotates
+  // every rank of B and C with them and computes no sine itself
   for (int i = tid; i < nvalid * K; i += 256) {
     const int t = i / K, k = i % K;
-    phi[((b * a.L + c0 + t) * a.H + h) * K + k] = om[t][k];
+    float sn, c;
+    sincos_rev(om[t][k], &sn, &c);
+    const f32x2 v = {c, sn};
+    cs[((b * a.L + c0 + t) * a.H + h) * K + k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
 }
 
 template <int N>
-static hipError_t rope_phi_run(const RopeArgs& a, float* phi, hipStream_t s) {
+static hipError_t rope_phi_run(const RopeArgs& a, uint32_t* cs, hipStream_t s) {
   const int64_t nchunks = (a.L + ROPE_CHUNK - 1) / ROPE_CHUNK;
   const dim3 g3h((unsigned)a.H, (unsigned)nchunks, (unsigned)a.batch);
   hipLaunchKernelGGL((rope_totals_kernel<N>), g3h, dim3(256), 0, s, a, nchunks);
   hipLaunchKernelGGL((rope_scan_kernel<N>), dim3((unsigned)a.H, (unsigned)a.batch), dim3(256), 0, s, a, nchunks);
-  hipLaunchKernelGGL((rope_phi_kernel<N>), g3h, dim3(256), 0, s, a, nchunks, phi);
+  hipLaunchKernelGGL((rope_phi_kernel<N>), g3h, dim3(256), 0, s, a, nchunks, cs);
   return hipGetLastError();
 }
 
-hipError_t launch_rope_phi(int N, const RopeArgs& a, float* phi, hipStream_t s) {
+hipError_t launch_rope_phi(int N, const RopeArgs& a, uint32_t* cs, hipStream_t s) {
   if (a.batch == 0 || a.H == 0) return hipSuccess;
   if (a.L == 0) {
     if (a.angle_final) return launch_copy_f32(a.angle_final, a.angle0, a.batch * a.H * (N / 2), s);
     return hipSuccess;
   }
   switch (N) {
-    case 16: return rope_phi_run<16>(a, phi, s);
-    case 32: return rope_phi_run<32>(a, phi, s);
-    case 64: return rope_phi_run<64>(a, phi, s);
-    case 128: return rope_phi_run<128>(a, phi, s);
+    case 16: return rope_phi_run<16>(a, cs, s);
+    case 32: return rope_phi_run<32>(a, cs, s);
+    case 64: return rope_phi_run<64>(a, cs, s);
+    case 128: return rope_phi_run<128>(a, cs, s);
     default: return hipErrorInvalidValue;
   }
 }
