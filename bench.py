@@ -413,7 +413,8 @@ def bench_floor(torch, w, reps=10):
     heads per block), the same bytes as contiguous streams (3:1 and 1:1
     read:write), and an in-place read-modify-write below and above the 256 MB
     memory-side cache (the decode state's traffic).  GB/s counts the bytes
-    each probe is given to move."""
+    each probe is given to move.  Also the achievable bf16 MFMA rate of
+    16x16x32 and 32x32x16 products with no memory traffic."""
     import ctypes
     from state_space_sequence_03_amd import build
     lib = ctypes.CDLL(build.FLOOR_LIB)
@@ -495,6 +496,18 @@ def bench_floor(torch, w, reps=10):
         out[name] = dict(ms=round(ms, 4), GBps=round(2 * nbytes / (ms * 1e-3) / 1e9, 1))
         del buf
     torch.cuda.empty_cache()
+    # the achievable bf16 MFMA rate: 8 independent chains per wave, operands in
+    # registers, 512 blocks of 4 waves (two waves per SIMD)
+    lib.m3f_mfma.argtypes = [ci, ci, ci, ci, vp, vp]
+    blocks, iters = 512, 4096
+    sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+    for name, kind, fpm in (("mfma_loop_16x16x32_bf16", 0, 16384), ("mfma_loop_32x32x16_bf16", 1, 32768)):
+        fn = lambda: lib.m3f_mfma(kind, iters, blocks, 0, ptr(sink), sp)
+        assert fn() == 0
+        ms = t_ms(fn)
+        tf = blocks * 4 * 8 * iters * fpm / (ms * 1e-3) / 1e12
+        out[name] = dict(ms=round(ms, 4), TFLOPs=round(tf, 1), frac_of_peak=round(tf / BF16_DENSE_TFLOPS, 4))
+    del sink
     return out
 
 

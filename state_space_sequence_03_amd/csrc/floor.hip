@@ -21,6 +21,9 @@
 //  * m3f_rmw: an in-place read-modify-write of a float array (the decode
 //    step's state traffic), for buffers below and above the 256 MB
 //    memory-side cache.
+//  * m3f_mfma: the achievable bf16 MFMA rate: each wave runs 8 independent
+//    accumulator chains of 16x16x32 or 32x32x16 bf16 products with operands
+//    held in registers (no memory traffic), two waves per SIMD.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -157,9 +160,61 @@ __global__ __launch_bounds__(256) void rmw_kernel(float4* __restrict__ p, int64_
   }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// KIND 0: 16x16x32 bf16 (16,384 flop), 1: 32x32x16 bf16 (32,768 flop).  The
+// operands come from the thread id through an empty asm, so nothing folds;
+// the sums are stored only when a flag the host never sets is set.
+template <int KIND>
+__global__ __launch_bounds__(256, 2) void mfma_loop_kernel(int iters, int store, float* out) {
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v = (float)((threadIdx.x + i) & 7) * 0.125f;
+    asm volatile("" : "+v"(v));
+    a[i] = (__bf16)v;
+    b[i] = (__bf16)(1.0f - v);
+  }
+  float sum = 0.0f;
+  if constexpr (KIND == 0) {
+    f32x4_t acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += acc[j][0] + acc[j][3];
+  } else {
+    f32x16_t acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += acc[j][0] + acc[j][15];
+  }
+  if (store) out[blockIdx.x * blockDim.x + threadIdx.x] = sum;
+}
+
 }  // namespace
 
 extern "C" {
+
+// kind 0: 16x16x32, 1: 32x32x16 bf16; blocks of 256 threads, each wave
+// issuing 8 x iters MFMAs; out (blocks * 256 floats) is written only if store.
+int m3f_mfma(int kind, int iters, int blocks, int store, float* out, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (kind == 0) hipLaunchKernelGGL(mfma_loop_kernel<0>, dim3(blocks), dim3(256), 0, s, iters, store, out);
+  else if (kind == 1) hipLaunchKernelGGL(mfma_loop_kernel<1>, dim3(blocks), dim3(256), 0, s, iters, store, out);
+  else return 1;
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
 
 // nr in {1, 2, 3} inputs of n16 16-byte vectors each (unused ones may be NULL).
 int m3f_stream(int nr, const void* a0, const void* a1, const void* a2, void* out, int64_t n16, int blocks,
@@ -192,19 +247,19 @@ int m3f_walk(const void* x, const void* B, const void* C, const void* theta, con
   hipStream_t s = (hipStream_t)stream;
   const unsigned blocks = (unsigned)(batch * H / heads_per_block);
   if (N == 128) {
-    hipFuncSetAttribute((const void*)walk_kernel<1, 4, 128>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (hipFuncSetAttribute((const void*)walk_kernel<1, 4, 128>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess) return 2;
     hipLaunchKernelGGL((walk_kernel<1, 4, 128>), dim3(blocks), dim3(256), lds_bytes, s, a);
   } else if (R == 1 && heads_per_block == 1) {
-    hipFuncSetAttribute((const void*)walk_kernel<1, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (hipFuncSetAttribute((const void*)walk_kernel<1, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess) return 2;
     hipLaunchKernelGGL((walk_kernel<1, 1>), dim3(blocks), dim3(256), lds_bytes, s, a);
   } else if (R == 1) {
-    hipFuncSetAttribute((const void*)walk_kernel<2, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (hipFuncSetAttribute((const void*)walk_kernel<2, 1>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess) return 2;
     hipLaunchKernelGGL((walk_kernel<2, 1>), dim3(blocks), dim3(512), lds_bytes, s, a);
   } else if (heads_per_block == 1) {
-    hipFuncSetAttribute((const void*)walk_kernel<1, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (hipFuncSetAttribute((const void*)walk_kernel<1, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess) return 2;
     hipLaunchKernelGGL((walk_kernel<1, 4>), dim3(blocks), dim3(256), lds_bytes, s, a);
   } else {
-    hipFuncSetAttribute((const void*)walk_kernel<2, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (hipFuncSetAttribute((const void*)walk_kernel<2, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess) return 2;
     hipLaunchKernelGGL((walk_kernel<2, 4>), dim3(blocks), dim3(512), lds_bytes, s, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : 2;
