@@ -599,6 +599,12 @@ def source_sha256(files):
     return h.hexdigest()
 
 
+# sources bc_prologue_kernel is built from, and the summary of its measured graphics clock
+PROLOGUE_SOURCES = tuple(_CS + f for f in ("prologue.hip", "m3_common.hpp", "m3_lanes.hpp", "m3_launch.hpp"))
+CLOCK_SUMMARY = "profiles/gpu_clock__per_kernel.md"
+ENGINE_CLOCK_GHZ = 2.4  # the engine clock the published peaks are quoted at
+
+
 # SQ counter summary of the dominant prefill kernel per workload (SQ_INSTS_MFMA per dispatch)
 SQ_SUMMARY = {
     "mimo_bf16": "profiles/subchunk_walk_kernel_64_4__mimo_bf16__sq_counters.md",
@@ -625,6 +631,16 @@ def issued_mfma_flops(name):
     vals = summary_values(SQ_SUMMARY[name], WALKER_SOURCES) if name in SQ_SUMMARY else None
     try:
         return float(vals["mfma_insts_per_dispatch"]) * float(vals["flop_per_mfma"]) if vals else None
+    except (KeyError, ValueError):
+        return None
+
+
+def prologue_clock_ghz():
+    """Average graphics clock of bc_prologue_kernel from its committed
+    GRBM_COUNT summary (None if missing or taken on other sources)."""
+    vals = summary_values(CLOCK_SUMMARY, PROLOGUE_SOURCES)
+    try:
+        return float(vals["prologue_clock_ghz"]) if vals else None
     except (KeyError, ValueError):
         return None
 
@@ -791,6 +807,12 @@ def main():
             "achieved_TFLOPs": round(pr["tflops"], 1), "peak_TFLOPs": BF16_DENSE_TFLOPS,
             "frac": round(pr["tflops"] / BF16_DENSE_TFLOPS, 4), "flops_per_call": pr["flops"],
             "bytes_per_call": pr["bytes"], "achieved_GBps": round(pr["gbps"], 1)}
+        clk = prologue_clock_ghz()
+        # the same peak at the clock the kernel was measured to run at (GRBM_COUNT
+        # over its dispatches, committed summary); frac above is against 2.4 GHz
+        line["bc_prologue"]["clock_GHz_counters"] = clk
+        line["bc_prologue"]["frac_at_measured_clock"] = (
+            round(pr["tflops"] / (BF16_DENSE_TFLOPS * clk / ENGINE_CLOCK_GHZ), 4) if clk else None)
     if "rope" in out:
         line["rope_bc"] = {"ms": round(out["rope"]["ms"], 4), "achieved_GBps": round(out["rope"]["gbps"], 1),
                            "frac": round(out["rope"]["gbps"] / HBM_PEAK_GBPS, 4)}

@@ -96,3 +96,14 @@ def test_counter_summary_mfma_count(name):
     th = w.batch * w.seqlen * w.nheads
     assert th * bench.prefill_flops_per_token_head(w, causal=True) <= fl
     assert fl <= 1.5 * th * bench.prefill_flops_per_token_head(w, causal=False)
+
+
+def test_clock_summary():
+    """The prologue's measured clock, when its summary matches the current
+    sources, lies between the lowest clock the power management uses under load
+    and the 2.4 GHz engine clock (a little above it: the GRBM count and the
+    dispatch timestamps are not taken at exactly the same instants)."""
+    clk = bench.prologue_clock_ghz()
+    if clk is None:
+        pytest.skip(f"{bench.CLOCK_SUMMARY} was taken on other sources; take the counters again")
+    assert 1.0 < clk < 2.6
