@@ -47,9 +47,10 @@
  * complex component k.
  *
  * Ownership: the caller owns every buffer (device memory unless stated).  The
- * library allocates nothing and keeps no mutable global state, so calls are
- * reentrant and may run on concurrent streams when their buffers are
- * disjoint.  Alignment: x, B, C, theta, y and the workspace of chunked_fwd,
+ * library allocates nothing and, apart from the fixed per-GPU array of
+ * mamba3_ssm_chunked_fwd_noalloc, keeps no mutable global state: every other
+ * call is reentrant and may run on concurrent streams when its buffers are
+ * disjoint from the other calls' buffers.  Alignment: x, B, C, theta, y and the workspace of chunked_fwd,
  * B, C, B_rot and C_rot of rope_bc, and the state of decode_step must be
  * 16-byte aligned; every other pointer must be aligned to its element size.
  *
@@ -253,8 +254,8 @@ m3_status mamba3_ssm_decode_step(const m3_dims* d, float* state,
  * workspace: at least mamba3_rope_bc_workspace_size(d) bytes: the angle
  * totals of every 64-token chunk, which a first pass writes and the rotating
  * pass scans, so that every chunk of a long sequence is rotated in parallel.
- * The library allocates nothing and keeps no global state, so the caller
- * provides this array.  chunk of d is ignored.  seqlen is limited to
+ * The library allocates nothing, so the caller provides this array.  chunk
+ * of d is ignored.  seqlen is limited to
  * 65535 * 64 tokens (M3_ERR_UNSUPPORTED). */
 m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C,
                          const float* dt, const float* theta, const float* angle0,
@@ -288,9 +289,10 @@ size_t mamba3_rope_bc_workspace_size(const m3_dims* d);
  *   dt (B, L, H), theta (B, L, H, N/2), angle0 nullable (B, H, N/2): fp32.
  *   B_rot, C_rot: (B, L, H, R, N) bf16, written (must not alias inputs).
  *   angle_final: nullable (B, H, N/2) fp32, written.
- *   workspace: at least mamba3_bc_prologue_workspace_size(d) bytes (the angles
- *      of every token and their chunk totals, fp32); contents on entry do not
- *      matter.
+ *   workspace: at least mamba3_bc_prologue_workspace_size(d) bytes (the fp32
+ *      angle totals of every 64-token chunk, then the cosine and sine of every
+ *      token's angles as fp16 pairs, 4 bytes per (token, head, pair));
+ *      contents on entry do not matter.
  * Products: bf16 MFMAs with fp32 accumulation; normalisation, bias and
  * rotation in fp32; outputs rounded to bf16 (nearest even).
  * Alignment: u, W, B_rot, C_rot, gain, bias and the workspace 16-byte; the

@@ -397,8 +397,10 @@ m3_status mamba3_rope_bc(const m3_dims* d, const void* B, const void* C, const f
 
 // Workspace of the B/C prologue: the angle chunk totals, then the angles
 // (B, L, H, N/2) fp32, each 256-byte aligned.
+// prologue workspace: fp32 angle totals per (b, h, 64-token chunk, pair), then
+// the fp16 (cos, sin) pair of every (token, head, pair) as one 32-bit word
 struct ProWs {
-  size_t totals, phi, bytes;
+  size_t totals, cs, bytes;
 };
 static ProWs pro_ws(const m3_dims* d) {
   auto up = [](size_t v) { return (v + 255) & ~(size_t)255; };
@@ -406,8 +408,8 @@ static ProWs pro_ws(const m3_dims* d) {
   const size_t nchunks = (size_t)((d->seqlen + m3::ROPE_CHUNK - 1) / m3::ROPE_CHUNK);
   ProWs w{};
   w.totals = 0;
-  w.phi = up(sizeof(float) * (size_t)(d->batch * d->nheads) * nchunks * K);
-  w.bytes = w.phi + up(sizeof(float) * (size_t)(d->batch * d->seqlen * d->nheads) * K);
+  w.cs = up(sizeof(float) * (size_t)(d->batch * d->nheads) * nchunks * K);
+  w.bytes = w.cs + up(sizeof(uint32_t) * (size_t)(d->batch * d->seqlen * d->nheads) * K);
   return w;
 }
 
@@ -452,7 +454,7 @@ m3_status mamba3_bc_prologue(const m3_dims* d, int64_t d_model, const void* u, c
   uint32_t* cs = nullptr;
   if (has_tokens) {
     r.totals = (float*)((char*)workspace + w.totals);
-    cs = (uint32_t*)((char*)workspace + w.phi);
+    cs = (uint32_t*)((char*)workspace + w.cs);
   }
   hipError_t e = m3::launch_rope_phi(N, r, cs, s);
   if (e != hipSuccess || !has_tokens) return e == hipSuccess ? M3_OK : M3_ERR_HIP;

@@ -153,10 +153,11 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
   for (int i = tid + 256 * BATCH; i < items; i += 256) rotate_store(i, ldg16<T>(a.B, off(i)), ldg16<T>(a.C, off(i)));
 }
 
-// The angles alone: phi_t per (token, head, pair), written to phi (B, L, H,
-// N/2) fp32 for a consumer that rotates B and C itself (the B/C prologue).
-// Per chunk as in launch 3: the chunk-local wave scan plus the chunk's offset,
-// then the chunk's angles written token by token.
+// The angles alone, for a consumer that rotates B and C itself (the B/C
+// prologue): cos and sin of phi_t per (token, head, pair), written to cs
+// (B, L, H, N/2) as one 32-bit word of two fp16 values.  Per chunk as in
+// launch 3: the chunk-local wave scan plus the chunk's offset, then the
+// chunk's values written token by token.
 template <int N>
 __global__ __launch_bounds__(256) void rope_phi_kernel(RopeArgs a, int64_t nchunks, uint32_t* cs) {
   constexpr int K = N / 2;
