@@ -177,9 +177,11 @@ size_t mamba3_ssm_chunked_fwd_workspace_size(const m3_dims* d);
  * 65,536-token sequence of 32 heads at N = 128, P = 64, R = 4 walked as
  * segments).  Every call on one GPU shares that GPU's array: calls that
  * overlap in time on one GPU (concurrent streams, or several host threads)
- * race on it and must be serialised by the caller.  The array's contents
- * carry over between calls; the forward needs none on entry.  Results are
- * those of mamba3_ssm_chunked_fwd with the same arguments. */
+ * race on it and must be serialised by the caller.  The array used is that of
+ * the calling thread's current device (hipGetDevice), which must be the
+ * device that stream belongs to.  The array's contents carry over between
+ * calls; the forward needs none on entry.  Results are those of
+ * mamba3_ssm_chunked_fwd with the same arguments. */
 #define M3_NOALLOC_SCRATCH_BYTES (48u << 20)
 m3_status mamba3_ssm_chunked_fwd_noalloc(const m3_dims* d,
                                          const void* x, const void* B, const void* C,
