@@ -806,7 +806,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // fixed order by its reader (no atomics: the results do not depend on the
   // order in which waves arrive): the angle adjoint of H_out per column tile
   // and pair, and d e^{Lam}, d w per n-tile and virtual row
-  __shared__ float sDM[QB][QB], sDphi[K][QT], sDThP[TP][K], sTh[K][QT], sThP[4][QB];
+  __shared__ float sDM[QB][QB], sDphi[K][QT], sDThP[TP][K], sTh[K][QT], sThP[NW - 4][QB];
   __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDeP[TN][V], sDwP[TN][V], sRedW[NW];
   __shared__ double sRedD[NW];
 
@@ -1283,7 +1283,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     __syncthreads();
 
     // ---------------- scalar adjoints of the chunk ----------------
-    // Waves 0-3: the masked decay's adjoints; waves 4-7: the angle adjoints.
+    // Waves 0-3: the masked decay's adjoints; the other waves: the angle adjoints.
     if (tid < 256) {
       // dM on s < t and the diagonal; lane (t, s) = t QB + s. Row sums over s
       // (the QB lanes of a row) and partial column sums over the rows a wave
@@ -1314,7 +1314,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       // d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega.
       // Lane e = k QB + t: the suffix sum over t runs within QB lanes with
       // shuffles; theta_t . d omega_t is summed over the wave's pairs k here
-      // and over the four waves by the per-token phase.
+      // and over the waves from 4 on by the per-token phase.
       float thd = 0.0f;
       for (int e = tid - 256; e < QB * K; e += TH - 256) {  // QB K is a multiple of 64: whole waves
         const int t = e % QB, k = e / QB;
@@ -1394,7 +1394,10 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         const float deps = t > 0 ? dq_prev : 0.0f;  // eps_t weighs the previous token
         float ddt = ts.A * dda + ts.lam * dgam + (1.0f - ts.lam) * deps;
         const float dlam = ts.d * dgam - ts.d * deps;
-        ddt += sThP[0][t] + sThP[1][t] + sThP[2][t] + sThP[3][t];  // theta_t . d omega_t
+        float thd = 0.0f;  // theta_t . d omega_t, the waves' partials in a fixed order
+#pragma unroll
+        for (int w = 0; w < NW - 4; ++w) thd += sThP[w][t];
+        ddt += thd;
         uint32_t tk = (uint32_t)t * Hu;
         fresh(tk);
         if (a0 + t < L) {
