@@ -92,6 +92,8 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
   };
   __shared__ float om[ROPE_CHUNK][K + 1];
   __shared__ float2 cs[ROPE_CHUNK][K];
+  __shared__ float offs[K];  // the chunk's angle offset per pair (scan of the chunk totals)
+  if (tid < K) offs[tid] = a.totals[((b * a.H + h) * nchunks + c) * K + tid];
 
   // first batch of B and C vectors: in flight while the angles are scanned
   typename io<T>::vec vb[BATCH], vc[BATCH];
@@ -113,7 +115,6 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
     om[t][k] = v;
   }
   __syncthreads();
-  const float* offs = a.totals + ((b * a.H + h) * nchunks + c) * K;
   for (int k = wave; k < K; k += 4) {
     const float v = wave_incl_scan(om[lane][k]) + offs[k];
     float s, co;
@@ -157,40 +158,50 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(RopeArgs a, int64_t nch
 // prologue): cos and sin of phi_t per (token, head, pair), written to cs
 // (B, L, H, N/2) as one 32-bit word of two fp16 values.  Per chunk as in
 // launch 3: the chunk-local wave scan plus the chunk's offset, then the
-// chunk's values written token by token.
-template <int N>
+// chunk's values written token by token.  A block takes HB adjacent heads,
+// so that each token's theta and cs rows are read and written as one piece of
+// HB * N/2 * 4 bytes (512 bytes when H allows) instead of one per head.
+template <int N, int HB>
 __global__ __launch_bounds__(256) void rope_phi_kernel(RopeArgs a, int64_t nchunks, uint32_t* cs) {
-  constexpr int K = N / 2;
-  const int64_t h = blockIdx.x, c = blockIdx.y, b = blockIdx.z;
+  constexpr int K = N / 2, W = HB * K;  // columns of the block: HB heads x K pairs
+  constexpr int PER = ROPE_CHUNK * W / 256;
+  static_assert(ROPE_CHUNK * W % 256 == 0, "whole passes of the block over the chunk's columns");
+  const int64_t h0 = (int64_t)blockIdx.x * HB, c = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t c0 = c * ROPE_CHUNK;
   const int nvalid = (int)((a.L - c0) < ROPE_CHUNK ? (a.L - c0) : ROPE_CHUNK);
-  __shared__ float om[ROPE_CHUNK][K + 1];
-  for (int i = tid; i < ROPE_CHUNK * K; i += 256) {
-    const int t = i / K, k = i % K;
-    float v = 0.0f;
-    if (t < nvalid) {
-      const int64_t idx = (b * a.L + c0 + t) * a.H + h;
-      v = a.dt[idx] * a.theta[idx * K + k];
-    }
-    om[t][k] = v;
+  __shared__ float om[ROPE_CHUNK][W + 1];
+  __shared__ float offs[W];  // the chunk's angle offset per column (scan of the chunk totals)
+  if (tid < W) offs[tid] = a.totals[((b * a.H + h0 + tid / K) * nchunks + c) * K + tid % K];
+  // every load of the thread is issued before the first product
+  float dv[PER], tv[PER];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = tid + 256 * q, t = i / W, j = i % W;
+    const int64_t row = (b * a.L + c0 + t) * a.H + h0;  // (token, first head of the block)
+    dv[q] = t < nvalid ? a.dt[row + j / K] : 0.0f;
+    tv[q] = t < nvalid ? a.theta[row * K + j] : 0.0f;
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int i = tid + 256 * q;
+    om[i / W][i % W] = dv[q] * tv[q];
   }
   __syncthreads();
-  const float* offs = a.totals + ((b * a.H + h) * nchunks + c) * K;
-  for (int k = wave; k < K; k += 4) {
-    const float v = wave_incl_scan(om[lane][k]) + offs[k];
-    om[lane][k] = v;  // each wave reads and writes only its own pair's column
+  for (int j = wave; j < W; j += 4) {
+    const float v = wave_incl_scan(om[lane][j]) + offs[j];
+    om[lane][j] = v;  // each wave reads and writes only its own columns
   }
   __syncthreads();
   // (cos, sin) of the angle, each rounded to fp16 (absolute error <= 2^-12,
   // below the bf16 rounding of the rotated outputs): the consumer rotates
   // every rank of B and C with them and computes no sine itself
-  for (int i = tid; i < nvalid * K; i += 256) {
-    const int t = i / K, k = i % K;
-    float sn, c;
-    sincos_rev(om[t][k], &sn, &c);
-    const f32x2 v = {c, sn};
-    cs[((b * a.L + c0 + t) * a.H + h) * K + k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  for (int i = tid; i < nvalid * W; i += 256) {
+    const int t = i / W, j = i % W;
+    float sn, cn;
+    sincos_rev(om[t][j], &sn, &cn);
+    const f32x2 v = {cn, sn};
+    cs[((b * a.L + c0 + t) * a.H + h0) * K + j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   }
 }
 
@@ -200,7 +211,13 @@ static hipError_t rope_phi_run(const RopeArgs& a, uint32_t* cs, hipStream_t s) {
   const dim3 g3h((unsigned)a.H, (unsigned)nchunks, (unsigned)a.batch);
   hipLaunchKernelGGL((rope_totals_kernel<N>), g3h, dim3(256), 0, s, a, nchunks);
   hipLaunchKernelGGL((rope_scan_kernel<N>), dim3((unsigned)a.H, (unsigned)a.batch), dim3(256), 0, s, a, nchunks);
-  hipLaunchKernelGGL((rope_phi_kernel<N>), g3h, dim3(256), 0, s, a, nchunks, cs);
+  constexpr int HB = 256 / N;  // heads whose rows of N/2 floats make 512 bytes
+  if (a.H % HB == 0) {
+    const dim3 g((unsigned)(a.H / HB), (unsigned)nchunks, (unsigned)a.batch);
+    hipLaunchKernelGGL((rope_phi_kernel<N, HB>), g, dim3(256), 0, s, a, nchunks, cs);
+  } else {
+    hipLaunchKernelGGL((rope_phi_kernel<N, 1>), g3h, dim3(256), 0, s, a, nchunks, cs);
+  }
   return hipGetLastError();
 }
 

@@ -73,6 +73,10 @@ CASES = [
     (2, 520, 4, 4, 64, 256, True, True, True, 1e-5),
     (1, 700, 2, 2, 64, 64, False, False, False, 0.1),
     (3, 1, 2, 4, 64, 64, True, True, True, 1e-5),
+    # H a multiple of 256 / N: the angle pass takes several adjacent heads per block
+    (1, 130, 16, 1, 16, 64, True, True, True, 1e-5),
+    (2, 100, 8, 2, 32, 64, False, True, True, 1e-5),
+    (1, 150, 2, 4, 128, 64, True, False, True, 1e-5),
 ]
 
 
