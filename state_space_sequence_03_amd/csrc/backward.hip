@@ -1028,7 +1028,23 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       }
     }
     // dZ = R(-Theta) dH_out; dTheta = <dH_out, J H_out> per pair; <dZ, H_in>
+    // The LDS operands first, so that they share one wait: the chunk's total
+    // angle of the wave's pairs and H_in at the wave's state elements (also
+    // the H_out of the chunk processed next).
+    float rh[NPW][4];
     {
+      float2 rcs[NPW][2];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        const int ti = wave + NW * j;
+        if (ti < S::NPT) {
+          const int tr = ti / TP, p = (ti % TP) * 16 + m16;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) rcs[j][q] = sCS[(tr * 16 + 4 * g + 2 * q) / 2][QB - 1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rh[j][i] = hin(tr * 16 + 4 * g + i, p);
+        }
+      }
       float part = 0.0f;
 #pragma unroll
       for (int j = 0; j < NPW; ++j) {
@@ -1038,7 +1054,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             const int n0 = tr * 16 + 4 * g + 2 * q, k = n0 / 2;
-            const float2 cs = sCS[k][QB - 1];
+            const float2 cs = rcs[j][q];
             const float g0 = Gb[j][2 * q], g1 = Gb[j][2 * q + 1];
             const float z0 = cs.x * g0 + cs.y * g1, z1 = cs.x * g1 - cs.y * g0;
             if constexpr (TL) {
@@ -1051,7 +1067,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
             float dth = -g0 * o1 + g1 * o0;
             dth = lane_sum<1, 16>(dth);
             if (m16 == 0) sDThP[tc][k] = dth;
-            part += z0 * hin(n0, p) + z1 * hin(n0 + 1, p);
+            part += z0 * rh[j][2 * q] + z1 * rh[j][2 * q + 1];
             // dH_in starts as e^{Lam_end} dZ
             Gb[j][2 * q] = eQ * z0;
             Gb[j][2 * q + 1] = eQ * z1;
@@ -1068,7 +1084,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         const int ti = wave + NW * j;
         if (ti < S::NPT) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ho[j][i] = hin((ti / TP) * 16 + 4 * g + i, (ti % TP) * 16 + m16);
+          for (int i = 0; i < 4; ++i) ho[j][i] = rh[j][i];
         }
       }
       fetch(c - 1);
@@ -1290,13 +1306,15 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       // holds are formed with shuffles; the waves' column partials are added
       // by the per-token phase below.
       const int t = tid / QB, s = tid % QB;
+      // the operands first (one wait), clamped to valid slots past QB x QB
+      const int tq = tid < QB * QB ? t : 0;
+      const float dm = sDM[tq][s], lam_t = sLam[tq], lam_s = sLam[s], q_s = sQ[s];
       float dmm = 0.0f, dme = 0.0f;
       if (tid < QB * QB) {
-        const float dm = sDM[t][s];
         if (s < t) {
-          const float e = __expf(fminf(sLam[t] - sLam[s], 0.0f));
+          const float e = __expf(fminf(lam_t - lam_s, 0.0f));
           dme = dm * e;
-          dmm = dme * sQ[s];
+          dmm = dme * q_s;
         } else if (s == t) {
           sDgam[t] = dm;
         }
@@ -1315,10 +1333,28 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       // Lane e = k QB + t: the suffix sum over t runs within QB lanes with
       // shuffles; theta_t . d omega_t is summed over the wave's pairs k here
       // and over the waves from 4 on by the per-token phase.
-      float thd = 0.0f;
-      for (int e = tid - 256; e < QB * K; e += TH - 256) {  // QB K is a multiple of 64: whole waves
+      // Every LDS operand of the wave's items is read before any of them is
+      // used, so that the reads share one wait instead of one each.
+      constexpr int NIT = (QB * K + TH - 257) / (TH - 256);
+      float rphi[NIT], rth[NIT], rd[NIT], rtp[NIT][TP];
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        int e = tid - 256 + (TH - 256) * it;
+        e = e < QB * K ? e : QB * K - 1;  // past the end: a valid slot, result unused
         const int t = e % QB, k = e / QB;
-        float dom = sDphi[k][t];
+        rphi[it] = sDphi[k][t];
+        rth[it] = sTh[k][t];
+        rd[it] = sT[t].d;
+#pragma unroll
+        for (int tc = 0; tc < TP; ++tc) rtp[it][tc] = sDThP[tc][k];
+      }
+      float thd = 0.0f;
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        const int e = tid - 256 + (TH - 256) * it;
+        if (e >= QB * K) break;  // QB K is a multiple of 64: whole waves
+        const int t = e % QB, k = e / QB;
+        float dom = rphi[it];
         // suffix sum over the token's QB-lane group
         {
           float u = row_down<1>(dom);
@@ -1333,11 +1369,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
           }
         }
 #pragma unroll
-        for (int tc = 0; tc < TP; ++tc) dom += sDThP[tc][k];
+        for (int tc = 0; tc < TP; ++tc) dom += rtp[it][tc];
         uint32_t ot = (uint32_t)t * Hu * K + k;
         fresh(ot);
-        if (a0 + t < L) (a.dtheta + t0c * K)[ot] = sT[t].d * dom;
-        thd += sTh[k][t] * dom;
+        if (a0 + t < L) (a.dtheta + t0c * K)[ot] = rd[it] * dom;
+        thd += rth[it] * dom;
       }
       thd = lane_sum<QB, 64>(thd);
       if (lane < QB) sThP[wave - 4][lane] = thd;
@@ -1349,29 +1385,53 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       const int t = tid;
       const bool ok = t < QB;
       const int tt = ok ? t : 0;
-      float dwt = 0.0f, det = 0.0f;
+      // Every LDS operand of the phase is read here, before any is used: the
+      // reads then share one wait instead of one each (the sums below keep
+      // their order).
+      float rwp[R][TN], rep[R][TN], rcl[4], rcq[4], rrw[NW], rthp[NW - 4];
+#pragma unroll
       for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int tr = 0; tr < TN; ++tr) {
-          dwt += sDwP[tr][tt * R + r];
-          det += sDeP[tr][tt * R + r];
+          rwp[r][tr] = sDwP[tr][tt * R + r];
+          rep[r][tr] = sDeP[tr][tt * R + r];
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        rcl[w] = sColL[w][tt];
+        rcq[w] = sColQ[w][tt];
+      }
+#pragma unroll
+      for (int w = 0; w < NW; ++w) rrw[w] = sRedW[w];
+#pragma unroll
+      for (int w = 0; w < NW - 4; ++w) rthp[w] = sThP[w][tt];
+      const TokScal ts = sT[tt];
+      const float r_dlam = sDLam[tt], r_el = sEL[tt], r_w = sW[tt], r_lam = sLam[tt], r_dgam = sDgam[tt];
+      float dwt = 0.0f, det = 0.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int tr = 0; tr < TN; ++tr) {
+          dwt += rwp[r][tr];
+          det += rep[r][tr];
         }
       }
       // w_t = e^{Lam_end - Lam_t} q_t; e^{Lam_t} of the inter-chunk output
       float cl = 0.0f, cq = 0.0f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        cl += sColL[w][tt];
-        cq += sColQ[w][tt];
+        cl += rcl[w];
+        cq += rcq[w];
       }
-      float dlam_t = ok ? sDLam[tt] - cl + det * sEL[tt] - dwt * sW[tt] : 0.0f;
-      const float dq_t = ok ? cq + dwt * __expf(lamQ - sLam[tt]) : 0.0f;
+      float dlam_t = ok ? r_dlam - cl + det * r_el - dwt * r_w : 0.0f;
+      const float dq_t = ok ? cq + dwt * __expf(lamQ - r_lam) : 0.0f;
       // d Lam_end: e^{Lam_end} <dZ, H_in> plus every token's share through w
-      float dlq = ok ? dwt * sW[tt] : 0.0f;
+      float dlq = ok ? dwt * r_w : 0.0f;
       dlq = lane_sum<1, 16>(dlq);
       float dzh = 0.0f;  // <dZ, H_in>
 #pragma unroll
-      for (int w = 0; w < NW; ++w) dzh += sRedW[w];
+      for (int w = 0; w < NW; ++w) dzh += rrw[w];
       if (t == QB - 1) dlam_t += dlq + eQ * dzh;
       // d(dt A)_t = sum_{i >= t} dLam_i
       float dda = dlam_t;
@@ -1389,14 +1449,13 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       // d eps of the token after this chunk
       const float de_next = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, dq_t), QB - 1));
       if (ok) {
-        const TokScal ts = sT[t];
-        const float dgam = sDgam[t] + dq_t;         // q_t = gamma_t + eps_{t+1}
+        const float dgam = r_dgam + dq_t;           // q_t = gamma_t + eps_{t+1}
         const float deps = t > 0 ? dq_prev : 0.0f;  // eps_t weighs the previous token
         float ddt = ts.A * dda + ts.lam * dgam + (1.0f - ts.lam) * deps;
         const float dlam = ts.d * dgam - ts.d * deps;
         float thd = 0.0f;  // theta_t . d omega_t, the waves' partials in a fixed order
 #pragma unroll
-        for (int w = 0; w < NW - 4; ++w) thd += sThP[w][t];
+        for (int w = 0; w < NW - 4; ++w) thd += rthp[w];
         ddt += thd;
         uint32_t tk = (uint32_t)t * Hu;
         fresh(tk);
