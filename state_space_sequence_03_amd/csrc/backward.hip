@@ -806,7 +806,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
   // fixed order by its reader (no atomics: the results do not depend on the
   // order in which waves arrive): the angle adjoint of H_out per column tile
   // and pair, and d e^{Lam}, d w per n-tile and virtual row
-  __shared__ float sDM[QB][QB], sDphi[K][QT], sDThP[TP][K], sTh[K][QT], sThP[NW - 4][QB];
+  __shared__ float sDM[QB][QB], sDphi[K][QT], sDThP[TP][K], sTh[K][QT], sThP[NW][QB];
   __shared__ float sDLam[QB], sDgam[QB], sColL[4][QB], sColQ[4][QB], sDeP[TN][V], sDwP[TN][V], sRedW[NW];
   __shared__ double sRedD[NW];
 
@@ -1233,6 +1233,38 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         mm<NW, TN, TV, P>([&](int n, int p) { return sDZ[n * LDP + p]; },
                                [&](int p, int v) { return sX[v * LDP + p]; }, facc, wave, m16, g);
       }
+      // Waves 0-3, while their products run: the masked decay's adjoints
+      // (they need only dGM o G and the chunk's scalars, complete since the
+      // last barrier; the per-token phase reads them two barriers on).
+      if (tid < 256) {
+        // dM on s < t and the diagonal; lane (t, s) = t QB + s. Row sums over s
+        // (the QB lanes of a row) and partial column sums over the rows a wave
+        // holds are formed with shuffles; the waves' column partials are added
+        // by the per-token phase below.
+        const int t = tid / QB, s = tid % QB;
+        // the operands first (one wait), clamped to valid slots past QB x QB
+        const int tq = tid < QB * QB ? t : 0;
+        const float dm = sDM[tq][s], lam_t = sLam[tq], lam_s = sLam[s], q_s = sQ[s];
+        float dmm = 0.0f, dme = 0.0f;
+        if (tid < QB * QB) {
+          if (s < t) {
+            const float e = __expf(fminf(lam_t - lam_s, 0.0f));
+            dme = dm * e;
+            dmm = dme * q_s;
+          } else if (s == t) {
+            sDgam[t] = dm;
+          }
+        }
+        float row = dmm, colL = dmm, colQ = dme;
+        row = lane_sum<1, QB>(row);
+        colL = lane_sum<QB, 64>(colL);
+        colQ = lane_sum<QB, 64>(colQ);
+        if (tid < QB * QB && s == 0) sDLam[t] = row;
+        if (lane < QB) {
+          sColL[wave][s] = colL;
+          sColQ[wave][s] = colQ;
+        }
+      }
 #pragma unroll
       for (int j = 0; j < VNW; ++j) {
         const int ti = wave + NW * j;
@@ -1298,48 +1330,19 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
     }
     __syncthreads();
 
-    // ---------------- scalar adjoints of the chunk ----------------
-    // Waves 0-3: the masked decay's adjoints; the other waves: the angle adjoints.
-    if (tid < 256) {
-      // dM on s < t and the diagonal; lane (t, s) = t QB + s. Row sums over s
-      // (the QB lanes of a row) and partial column sums over the rows a wave
-      // holds are formed with shuffles; the waves' column partials are added
-      // by the per-token phase below.
-      const int t = tid / QB, s = tid % QB;
-      // the operands first (one wait), clamped to valid slots past QB x QB
-      const int tq = tid < QB * QB ? t : 0;
-      const float dm = sDM[tq][s], lam_t = sLam[tq], lam_s = sLam[s], q_s = sQ[s];
-      float dmm = 0.0f, dme = 0.0f;
-      if (tid < QB * QB) {
-        if (s < t) {
-          const float e = __expf(fminf(lam_t - lam_s, 0.0f));
-          dme = dm * e;
-          dmm = dme * q_s;
-        } else if (s == t) {
-          sDgam[t] = dm;
-        }
-      }
-      float row = dmm, colL = dmm, colQ = dme;
-      row = lane_sum<1, QB>(row);
-      colL = lane_sum<QB, 64>(colL);
-      colQ = lane_sum<QB, 64>(colQ);
-      if (tid < QB * QB && s == 0) sDLam[t] = row;
-      if (lane < QB) {
-        sColL[wave][s] = colL;
-        sColQ[wave][s] = colQ;
-      }
-    } else {
+    // ---------------- angle adjoints of the chunk ----------------
+    {
       // d omega_t = sum_{i >= t} dphi_i + dTheta; dtheta = dt d omega.
       // Lane e = k QB + t: the suffix sum over t runs within QB lanes with
       // shuffles; theta_t . d omega_t is summed over the wave's pairs k here
-      // and over the waves from 4 on by the per-token phase.
+      // and over the waves by the per-token phase.
       // Every LDS operand of the wave's items is read before any of them is
       // used, so that the reads share one wait instead of one each.
-      constexpr int NIT = (QB * K + TH - 257) / (TH - 256);
+      constexpr int NIT = (QB * K + TH - 1) / TH;
       float rphi[NIT], rth[NIT], rd[NIT], rtp[NIT][TP];
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        int e = tid - 256 + (TH - 256) * it;
+        int e = tid + TH * it;
         e = e < QB * K ? e : QB * K - 1;  // past the end: a valid slot, result unused
         const int t = e % QB, k = e / QB;
         rphi[it] = sDphi[k][t];
@@ -1351,7 +1354,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       float thd = 0.0f;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        const int e = tid - 256 + (TH - 256) * it;
+        const int e = tid + TH * it;
         if (e >= QB * K) break;  // QB K is a multiple of 64: whole waves
         const int t = e % QB, k = e / QB;
         float dom = rphi[it];
@@ -1376,7 +1379,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         thd += rth[it] * dom;
       }
       thd = lane_sum<QB, 64>(thd);
-      if (lane < QB) sThP[wave - 4][lane] = thd;
+      if (lane < QB) sThP[wave][lane] = thd;  // zero for a wave without items
     }
     __syncthreads();
     // Per-token gradients: lane t < QB of wave 0, sums across tokens with
@@ -1388,7 +1391,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
       // Every LDS operand of the phase is read here, before any is used: the
       // reads then share one wait instead of one each (the sums below keep
       // their order).
-      float rwp[R][TN], rep[R][TN], rcl[4], rcq[4], rrw[NW], rthp[NW - 4];
+      float rwp[R][TN], rep[R][TN], rcl[4], rcq[4], rrw[NW], rthp[NW];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -1405,7 +1408,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) rrw[w] = sRedW[w];
 #pragma unroll
-      for (int w = 0; w < NW - 4; ++w) rthp[w] = sThP[w][tt];
+      for (int w = 0; w < NW; ++w) rthp[w] = sThP[w][tt];
       const TokScal ts = sT[tt];
       const float r_dlam = sDLam[tt], r_el = sEL[tt], r_w = sW[tt], r_lam = sLam[tt], r_dgam = sDgam[tt];
       float dwt = 0.0f, det = 0.0f;
@@ -1455,7 +1458,7 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         const float dlam = ts.d * dgam - ts.d * deps;
         float thd = 0.0f;  // theta_t . d omega_t, the waves' partials in a fixed order
 #pragma unroll
-        for (int w = 0; w < NW - 4; ++w) thd += rthp[w];
+        for (int w = 0; w < NW; ++w) thd += rthp[w];
         ddt += thd;
         uint32_t tk = (uint32_t)t * Hu;
         fresh(tk);
