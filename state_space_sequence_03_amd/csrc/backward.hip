@@ -1491,7 +1491,11 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(BwdArgs a) {
         }
       }
     }
-    __syncthreads();  // LDS reads of this chunk done before the next staging
+    // No barrier here: the next chunk's staging writes the angles, the token
+    // scalars and H_in. The per-token phase above (wave 0) reads none of
+    // those but the token scalars, whose slot each lane rewrites itself after
+    // reading it; every other read of them ended before the last barrier.
+    // The other waves therefore stage the next chunk while wave 0 finishes.
     }
   }
 
